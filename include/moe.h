@@ -1,0 +1,199 @@
+/*
+ * moe.h - C ABI of a quantised mixture-of-experts feed-forward layer for one
+ * AMD Instinct MI355X (gfx950): DeepSeek-V4.1-style routing with Q2_K / Q3_K
+ * routed experts read against q8_1-quantised activations.
+ *
+ * What the layer computes, per token t of x [m, dim] (bf16):
+ *   z = x W_R^T (f32 accumulation);  s = sqrt(softplus(z / gate_temp)), where
+ *   softplus returns its argument above 20;  keys = s + bias;  T = the topk
+ *   experts by key, descending, equal keys ordered by ascending expert id;
+ *   G_i = s_{T_i} / (sum_j s_{T_j} + 1e-20) when norm_topk_prob and topk > 1,
+ *   times route_scale;  y = sum_i G_i E_{T_i}(x) + y_shared(x);  out = bf16(y).
+ *   A routed expert E(x) = W2 q8_1(h) with h = min(g,L) sigma(min(g,L))
+ *   clip(u,-L,L) (no clamps when L <= 0), g = W1 q8_1(x), u = W3 q8_1(x); W1 and
+ *   W3 are Q2_K blocks, W2 Q3_K blocks.
+ * Sources: the metrale moe_v41 module documentation and moe_v41.rs source view
+ * (docs.metrale.ai; fns route_from_logits, softplus, bf16_bytes; struct
+ * MoeV41Cfg; methods forward / route / route_launch of struct MoeV41), and the
+ * Open Model Atlas page "DeepSeek V4.1 · Mixture of experts" (router and
+ * expert equations; the Gate / Expert / MoE code excerpts; config.json). The
+ * Q2_K (84 B), Q3_K (110 B) and q8_1 (32 x int8 + fp16 d + fp16 d*sum) block
+ * layouts are the public GGUF ones; the pages only name them.
+ *
+ * Conventions for every function:
+ *   - returns MOE_OK (0) or a negative MOE_E* code; moe_strerror() names it;
+ *   - no exception, abort or exit crosses this boundary;
+ *   - pointers marked "device" are HIP device memory on the current device,
+ *     borrowed for the duration of the work queued on `stream` (the caller
+ *     keeps them alive until that work is done); "host" pointers are read
+ *     before the call returns unless stated otherwise;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     every device-side call is asynchronous on it unless stated otherwise;
+ *   - a context is not thread-safe: one host thread (or stream) per context;
+ *     two calls on one context must not overlap on different streams.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* an argument is out of range or NULL */
+#define MOE_ENOMEM (-2)        /* a device or pinned-host allocation failed */
+#define MOE_EHIP (-3)          /* a HIP runtime call failed */
+#define MOE_ENONFINITE (-4)    /* a routing key (score + bias) was NaN */
+#define MOE_ENOTRESIDENT (-5)  /* a picked expert had no slot and no host arena */
+#define MOE_ESTATE (-6)        /* a call needs state that is not set (e.g. no slots) */
+
+/* shared expert formats */
+#define MOE_SHARED_NONE 0
+#define MOE_SHARED_BF16 1      /* w1/w3 bf16 [inter, dim], w2 bf16 [dim, inter], row-major */
+#define MOE_SHARED_KQUANT 2    /* w1/w3 Q2_K blocks [inter][dim/256], w2 Q3_K blocks [dim][inter/256] */
+
+/* Layer configuration (the fields of metrale's MoeV41Cfg). */
+typedef struct moe_cfg {
+    int32_t dim;            /* model dim D: a multiple of 256, 256..8192 */
+    int32_t inter;          /* expert intermediate dim I: a multiple of 256, 256..8192 */
+    int32_t n_routed;       /* routed experts E: 1..1024 */
+    int32_t topk;           /* experts per token k: 1..min(E, 64) */
+    float gate_temp;        /* router temperature, > 0 */
+    int32_t norm_topk_prob; /* nonzero: renormalise the picked scores (only when topk > 1) */
+    float route_scale;      /* routing weight multiplier */
+    float swiglu_limit;     /* clamp L; <= 0 disables both clamps */
+    int32_t max_tokens;     /* largest m any call may pass: 1..65536; sizes the scratch */
+} moe_cfg;
+
+/* One layer's resident weights (metrale's MoeV41LayerWeights). Routed experts
+ * are not here: they are found through the slot table (moe_set_slots). */
+typedef struct moe_weights {
+    const void* router_w;      /* device, bf16 [n_routed, dim] row-major */
+    const float* router_bias;  /* device, f32 [n_routed] */
+    int32_t shared_fmt;        /* MOE_SHARED_* */
+    const void* shared_w1;     /* device; see MOE_SHARED_* for the layout */
+    const void* shared_w3;     /* device */
+    const void* shared_w2;     /* device */
+} moe_weights;
+
+/* Counters of the calls since creation or moe_reset_stats (metrale's MoeV41Timing:
+ * hits, misses and bytes_read; host-clock milliseconds of the routing read-back
+ * and of the miss copies; only calls that stream misses read routing back). */
+typedef struct moe_stats {
+    uint64_t calls;         /* moe_forward / moe_forward_ex calls */
+    uint64_t hits;          /* picked experts found resident, per streamed call */
+    uint64_t misses;        /* picked experts copied from the host arena */
+    uint64_t bytes_copied;  /* host-to-device bytes of those copies */
+    uint64_t waves;         /* slot waves run by streamed calls */
+    double route_ms;        /* host time waiting for the routing read-back */
+    double fetch_ms;        /* host time spent issuing and waiting on miss copies */
+} moe_stats;
+
+typedef struct moe_ctx moe_ctx;
+
+/* Create a context on the current HIP device: validates cfg, allocates the
+ * scratch for cfg->max_tokens tokens. *out is set only on success.
+ * MOE_EINVAL (bad cfg / NULL), MOE_ENOMEM, MOE_EHIP. */
+int moe_create(const moe_cfg* cfg, moe_ctx** out);
+
+/* Free what the context owns (scratch, table, streams, events). Synchronises
+ * the device first. NULL is accepted. */
+int moe_destroy(moe_ctx* ctx);
+
+/* Byte layout of one routed expert's slice (the analogue of metrale's
+ * arena_of): [W1 Q2_K | W3 Q2_K | W2 Q3_K], raw GGUF block bytes, rows in
+ * order; W1/W3 are [inter][dim/256] blocks of 84 B, W2 [dim][inter/256]
+ * blocks of 110 B. All four outputs are required. MOE_EINVAL on a bad cfg. */
+int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, size_t* off_w3,
+                      size_t* off_w2);
+
+/* Give the context a caller-owned device arena of n_slots slices of slot_bytes
+ * (256-byte aligned base) and reset the slot table to "nothing resident".
+ * MOE_EINVAL for NULL / n_slots < 1 / a misaligned base. */
+int moe_set_slots(moe_ctx* ctx, void* arena_dev, int32_t n_slots);
+
+/* Slot table (metrale's slot_table_set): expert -> slot, -1 = not resident.
+ * bind: the caller has put the expert's slice in that slot; MOE_EINVAL for an
+ * id out of range or a slot already bound to another expert; MOE_ESTATE
+ * without an arena. evict: forget the expert's slot. slot_of: read it. The
+ * device copy of the table is refreshed on the next forward/route call. */
+int moe_slot_bind(moe_ctx* ctx, int32_t expert, int32_t slot);
+int moe_slot_evict(moe_ctx* ctx, int32_t expert);
+int moe_slot_of(const moe_ctx* ctx, int32_t expert, int32_t* slot);
+
+/* Optional page-locked host arena holding every routed expert's slice,
+ * expert e at host + e * expert_stride (expert_stride >= slot_bytes). With it,
+ * moe_forward streams the experts it needs that are not resident into the
+ * device slots (least-recently-used eviction, hipMemcpyAsync on a side stream,
+ * fenced by events), in waves of at most n_slots experts. NULL disables it.
+ * The memory must come from hipHostMalloc (or equivalent pinned allocation). */
+int moe_set_host_arena(moe_ctx* ctx, const void* pinned_host, size_t expert_stride);
+
+/* Routing only (metrale's route / route_launch, with the selection on the
+ * device): writes weights_out f32 [m, topk] and idx_out i32 [m, topk] (device),
+ * each token's picks in descending key order. Asynchronous. MOE_EINVAL when m
+ * is outside 1..max_tokens or a pointer is NULL. A NaN key is reported by
+ * moe_check as MOE_ENONFINITE (NaN keys are ordered last). */
+int moe_route(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, float* weights_out,
+              int32_t* idx_out, void* stream);
+
+/* The whole layer (metrale's forward): out_bf16 [m, dim] bf16 (device,
+ * caller-owned). Asynchronous when every picked expert is resident or no host
+ * arena is set; with a host arena it blocks once on the routing read-back and
+ * then streams the misses. A picked expert that is not resident without a host
+ * arena contributes zero and is reported by moe_check as MOE_ENOTRESIDENT. */
+int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
+                void* stream);
+
+/* moe_forward that also writes the routing (either pointer may be NULL). */
+int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
+                   float* weights_out, int32_t* idx_out, void* stream);
+
+/* The layer's activation quantiser alone (q8_1 of bf16 rows), exposed so its
+ * output can be checked bit for bit: x_bf16 [rows, cols] (device, 16-byte
+ * aligned, cols a multiple of 32); q_out int8 [rows, cols] and d_out f32
+ * [rows, cols/32] holding fp16(d) (device). Per 32 values: d = amax/127,
+ * q = round-half-away-from-zero(x/d) with the unrounded d (0 when d = 0).
+ * Asynchronous. MOE_EINVAL for NULL, rows < 1 or a bad cols. */
+int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_out, float* d_out, void* stream);
+
+/* Synchronise `stream` and return (then clear) the device error word of the
+ * calls queued so far: MOE_OK, MOE_ENONFINITE or MOE_ENOTRESIDENT. */
+int moe_check(moe_ctx* ctx, void* stream);
+
+/* Per-kernel timing for benchmarks. With profiling on, every kernel launch of
+ * moe_forward / moe_forward_ex is bracketed by HIP events recorded on the
+ * call's stream (a small gap is added between kernels). moe_kernel_times
+ * synchronises the device and fills, for kernel class i < n (MOE_K_* order),
+ * the summed milliseconds and the number of launches since profiling was
+ * switched on or last read; then it restarts the sums. n < MOE_K_COUNT reads
+ * the first n classes. MOE_EINVAL for NULL. */
+#define MOE_K_ROUTER 0        /* router logits */
+#define MOE_K_QUANT 1         /* q8_1 of x */
+#define MOE_K_TOPK 2          /* selection and weights */
+#define MOE_K_BUCKET 3        /* token -> expert bucketing */
+#define MOE_K_GATEUP 4        /* routed (and K-quant shared) gate/up + SwiGLU */
+#define MOE_K_SHARED_GATEUP 5 /* bf16 shared gate/up + SwiGLU */
+#define MOE_K_DOWN 6          /* routed (and K-quant shared) down */
+#define MOE_K_SHARED_DOWN 7   /* bf16 shared down */
+#define MOE_K_COMBINE 8       /* weighted combine + bf16 store */
+#define MOE_K_COUNT 9
+int moe_set_profiling(moe_ctx* ctx, int32_t on);
+int moe_kernel_times(moe_ctx* ctx, double* ms_sum, int64_t* launches, int32_t n);
+
+/* Copy out / clear the counters. */
+int moe_get_stats(const moe_ctx* ctx, moe_stats* out);
+int moe_reset_stats(moe_ctx* ctx);
+
+/* Static text for a status code. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

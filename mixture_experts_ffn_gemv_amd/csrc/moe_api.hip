@@ -1,0 +1,531 @@
+// Host side of the C ABI declared in include/moe.h: the context (scratch,
+// slot table, host arena), argument checks, and the launch sequence of one
+// MoE layer call on a HIP stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "moe.h"
+#include "moe_common.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// bump allocator over one device allocation
+struct Carver {
+    size_t off = 0;
+    template <typename TT>
+    size_t take(size_t count) {
+        const size_t o = align_up(off, 256);
+        off = o + count * sizeof(TT);
+        return o;
+    }
+};
+
+}  // namespace
+
+struct moe_ctx {
+    moe_cfg cfg;
+    int device = 0;
+    int max_pairs = 0;
+    int max_chunks = 0;   // chunk-list capacity
+    uint8_t* dev = nullptr;
+    // scratch views
+    float* logits = nullptr;
+    int32_t* idx = nullptr;
+    float* gw = nullptr;
+    int8_t* xq = nullptr;
+    float* xd = nullptr;
+    int32_t* xs16 = nullptr;
+    int32_t* offsets = nullptr;
+    int32_t* active = nullptr;
+    int32_t* n_active = nullptr;
+    int32_t* n_chunks = nullptr;
+    int32_t* perm = nullptr;
+    int32_t* inv = nullptr;
+    Chunk* chunks = nullptr;
+    float* h_routed = nullptr;
+    float* h_shared = nullptr;
+    float* e_rows = nullptr;
+    float* ys = nullptr;
+    int32_t* err = nullptr;
+    int32_t* slot_table_dev = nullptr;
+    // slots
+    uint8_t* arena = nullptr;
+    int n_slots = 0;
+    size_t slot_bytes = 0, off_w1 = 0, off_w3 = 0, off_w2 = 0;
+    int32_t* slot_host = nullptr;   // pinned mirror of the table
+    std::vector<int32_t> slot_owner; // slot -> expert or -1
+    bool table_dirty = true;
+    hipEvent_t table_ev = nullptr;
+    bool table_ev_pending = false;
+    // host arena
+    const uint8_t* host_arena = nullptr;
+    size_t host_stride = 0;
+    moe_stats stats;
+    // per-kernel timing
+    bool prof = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_next = 0;
+    struct Mark {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::vector<Mark> marks;
+    double k_ms[MOE_K_COUNT] = {};
+    int64_t k_n[MOE_K_COUNT] = {};
+};
+
+namespace {
+
+int check_cfg(const moe_cfg* c) {
+    if (c == nullptr) return MOE_EINVAL;
+    if (c->dim < 256 || c->dim > 8192 || c->dim % 256) return MOE_EINVAL;
+    if (c->inter < 256 || c->inter > 8192 || c->inter % 256) return MOE_EINVAL;
+    if (c->n_routed < 1 || c->n_routed > 1024) return MOE_EINVAL;
+    if (c->topk < 1 || c->topk > 64 || c->topk > c->n_routed) return MOE_EINVAL;
+    if (!(c->gate_temp > 0.f)) return MOE_EINVAL;
+    if (c->max_tokens < 1 || c->max_tokens > 65536) return MOE_EINVAL;
+    if ((int64_t)c->max_tokens * c->topk > (1 << 22)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+void layout_of(const moe_cfg& c, size_t& slot, size_t& o1, size_t& o3, size_t& o2) {
+    const size_t n13 = (size_t)c.inter * (c.dim / QK) * Q2K_BYTES;
+    const size_t n2 = (size_t)c.dim * (c.inter / QK) * Q3K_BYTES;
+    o1 = 0;
+    o3 = n13;
+    o2 = 2 * n13;
+    slot = 2 * n13 + n2;
+}
+
+// upper bound of routed GEMV chunks for m tokens: sum_e ceil(c_e / 8) <= (P + 7 * min(E, P)) / 8
+int routed_chunk_bound(const moe_cfg& c, int m) {
+    const int P = m * c.topk;
+    const int act = std::min(c.n_routed, P);
+    return (P + (GEMV_ROWS - 1) * act) / GEMV_ROWS + 1;
+}
+
+int shared_chunk_count(int m) { return (m + GEMV_ROWS - 1) / GEMV_ROWS; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+hipEvent_t prof_event(moe_ctx* ctx) {
+    if (ctx->ev_next == ctx->ev_pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        ctx->ev_pool.push_back(e);
+    }
+    return ctx->ev_pool[ctx->ev_next++];
+}
+
+// launch through `fn` (returns hipError_t), bracketed by events when profiling
+template <typename F>
+int timed(moe_ctx* ctx, hipStream_t st, int kind, F fn) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (ctx->prof) {
+        a = prof_event(ctx);
+        b = prof_event(ctx);
+        if (a == nullptr || b == nullptr || hipEventRecord(a, st) != hipSuccess) return MOE_EHIP;
+    }
+    if (fn() != hipSuccess) return MOE_EHIP;
+    if (ctx->prof) {
+        if (hipEventRecord(b, st) != hipSuccess) return MOE_EHIP;
+        ctx->marks.push_back({kind, a, b});
+    }
+    return MOE_OK;
+}
+
+int upload_table(moe_ctx* ctx, hipStream_t st) {
+    if (!ctx->table_dirty) return MOE_OK;
+    if (hipMemcpyAsync(ctx->slot_table_dev, ctx->slot_host, sizeof(int32_t) * ctx->cfg.n_routed,
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+        return MOE_EHIP;
+    if (hipEventRecord(ctx->table_ev, st) != hipSuccess) return MOE_EHIP;
+    ctx->table_ev_pending = true;
+    ctx->table_dirty = false;
+    return MOE_OK;
+}
+
+// the pinned mirror may still be read by a queued upload: wait before changing it
+int table_mutable(moe_ctx* ctx) {
+    if (ctx->table_ev_pending) {
+        if (hipEventSynchronize(ctx->table_ev) != hipSuccess) return MOE_EHIP;
+        ctx->table_ev_pending = false;
+    }
+    return MOE_OK;
+}
+
+int check_weights(const moe_ctx* ctx, const moe_weights* w) {
+    if (w == nullptr || w->router_w == nullptr || w->router_bias == nullptr) return MOE_EINVAL;
+    if (!aligned(w->router_w, 16) || !aligned(w->router_bias, 4)) return MOE_EINVAL;
+    if (w->shared_fmt == MOE_SHARED_NONE) return MOE_OK;
+    if (w->shared_fmt != MOE_SHARED_BF16 && w->shared_fmt != MOE_SHARED_KQUANT) return MOE_EINVAL;
+    if (w->shared_w1 == nullptr || w->shared_w3 == nullptr || w->shared_w2 == nullptr) return MOE_EINVAL;
+    if (!aligned(w->shared_w1, 16) || !aligned(w->shared_w3, 16) || !aligned(w->shared_w2, 16)) return MOE_EINVAL;
+    if (w->shared_fmt == MOE_SHARED_BF16 && ctx->cfg.dim > 8192) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+// router logits + q8_1(x) + top-k into (idx, gw)
+int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int32_t* idx, float* gw,
+              hipStream_t st) {
+    const moe_cfg& c = ctx->cfg;
+    int rc = timed(ctx, st, MOE_K_ROUTER, [&] {
+        return launch_router_gemv(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
+    });
+    if (rc != MOE_OK) return rc;
+    return timed(ctx, st, MOE_K_TOPK, [&] {
+        return launch_topk(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp, c.norm_topk_prob,
+                           c.route_scale, idx, gw, ctx->err, st);
+    });
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ENOMEM: return "out of memory";
+        case MOE_EHIP: return "HIP runtime error";
+        case MOE_ENONFINITE: return "NaN routing key";
+        case MOE_ENOTRESIDENT: return "picked expert not resident";
+        case MOE_ESTATE: return "required state not set";
+        default: return "unknown status";
+    }
+}
+
+int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, size_t* off_w3, size_t* off_w2) {
+    if (check_cfg(cfg) != MOE_OK || !slot_bytes || !off_w1 || !off_w3 || !off_w2) return MOE_EINVAL;
+    layout_of(*cfg, *slot_bytes, *off_w1, *off_w3, *off_w2);
+    return MOE_OK;
+}
+
+int moe_create(const moe_cfg* cfg, moe_ctx** out) {
+    if (out == nullptr) return MOE_EINVAL;
+    const int rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    moe_ctx* ctx = new (std::nothrow) moe_ctx();
+    if (ctx == nullptr) return MOE_ENOMEM;
+    ctx->cfg = *cfg;
+    std::memset(&ctx->stats, 0, sizeof(ctx->stats));
+    if (hipGetDevice(&ctx->device) != hipSuccess) {
+        delete ctx;
+        return MOE_EHIP;
+    }
+    const moe_cfg& c = ctx->cfg;
+    const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
+    const size_t P = M * c.topk;
+    ctx->max_pairs = (int)P;
+    ctx->max_chunks = routed_chunk_bound(c, (int)M) + shared_chunk_count((int)M) + 1;
+    layout_of(c, ctx->slot_bytes, ctx->off_w1, ctx->off_w3, ctx->off_w2);
+
+    Carver cv;
+    const size_t o_logits = cv.take<float>(M * E);
+    const size_t o_idx = cv.take<int32_t>(P);
+    const size_t o_gw = cv.take<float>(P);
+    const size_t o_xq = cv.take<int8_t>(M * D);
+    const size_t o_xd = cv.take<float>(M * D / QB);
+    const size_t o_xs = cv.take<int32_t>(M * D / 16);
+    const size_t o_off = cv.take<int32_t>(E + 1);
+    const size_t o_act = cv.take<int32_t>(E);
+    const size_t o_nact = cv.take<int32_t>(1);
+    const size_t o_nch = cv.take<int32_t>(1);
+    const size_t o_perm = cv.take<int32_t>(P);
+    const size_t o_inv = cv.take<int32_t>(P);
+    const size_t o_ch = cv.take<Chunk>(ctx->max_chunks);
+    const size_t o_hr = cv.take<float>(P * I);
+    const size_t o_hs = cv.take<float>(M * I);
+    const size_t o_er = cv.take<float>(P * D);
+    const size_t o_ys = cv.take<float>(M * D);
+    const size_t o_err = cv.take<int32_t>(1);
+    const size_t o_tab = cv.take<int32_t>(E);
+    const size_t total = align_up(cv.off, 256);
+    if (hipMalloc((void**)&ctx->dev, total) != hipSuccess) {
+        delete ctx;
+        return MOE_ENOMEM;
+    }
+    uint8_t* b = ctx->dev;
+    ctx->logits = (float*)(b + o_logits);
+    ctx->idx = (int32_t*)(b + o_idx);
+    ctx->gw = (float*)(b + o_gw);
+    ctx->xq = (int8_t*)(b + o_xq);
+    ctx->xd = (float*)(b + o_xd);
+    ctx->xs16 = (int32_t*)(b + o_xs);
+    ctx->offsets = (int32_t*)(b + o_off);
+    ctx->active = (int32_t*)(b + o_act);
+    ctx->n_active = (int32_t*)(b + o_nact);
+    ctx->n_chunks = (int32_t*)(b + o_nch);
+    ctx->perm = (int32_t*)(b + o_perm);
+    ctx->inv = (int32_t*)(b + o_inv);
+    ctx->chunks = (Chunk*)(b + o_ch);
+    ctx->h_routed = (float*)(b + o_hr);
+    ctx->h_shared = (float*)(b + o_hs);
+    ctx->e_rows = (float*)(b + o_er);
+    ctx->ys = (float*)(b + o_ys);
+    ctx->err = (int32_t*)(b + o_err);
+    ctx->slot_table_dev = (int32_t*)(b + o_tab);
+    if (hipMemset(ctx->dev, 0, total) != hipSuccess) {
+        moe_destroy(ctx);
+        return MOE_EHIP;
+    }
+    if (hipHostMalloc((void**)&ctx->slot_host, sizeof(int32_t) * E, hipHostMallocDefault) != hipSuccess) {
+        moe_destroy(ctx);
+        return MOE_ENOMEM;
+    }
+    for (size_t e = 0; e < E; ++e) ctx->slot_host[e] = -1;
+    if (hipEventCreateWithFlags(&ctx->table_ev, hipEventDisableTiming) != hipSuccess) {
+        moe_destroy(ctx);
+        return MOE_EHIP;
+    }
+    ctx->table_dirty = true;
+    *out = ctx;
+    return MOE_OK;
+}
+
+int moe_destroy(moe_ctx* ctx) {
+    if (ctx == nullptr) return MOE_OK;
+    (void)hipDeviceSynchronize();
+    if (ctx->table_ev) (void)hipEventDestroy(ctx->table_ev);
+    for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
+    if (ctx->slot_host) (void)hipHostFree(ctx->slot_host);
+    if (ctx->dev) (void)hipFree(ctx->dev);
+    delete ctx;
+    return MOE_OK;
+}
+
+int moe_set_slots(moe_ctx* ctx, void* arena_dev, int32_t n_slots) {
+    if (ctx == nullptr || arena_dev == nullptr || n_slots < 1 || !aligned(arena_dev, 256)) return MOE_EINVAL;
+    const int rc = table_mutable(ctx);
+    if (rc != MOE_OK) return rc;
+    ctx->arena = (uint8_t*)arena_dev;
+    ctx->n_slots = n_slots;
+    ctx->slot_owner.assign(n_slots, -1);
+    for (int e = 0; e < ctx->cfg.n_routed; ++e) ctx->slot_host[e] = -1;
+    ctx->table_dirty = true;
+    return MOE_OK;
+}
+
+int moe_slot_bind(moe_ctx* ctx, int32_t expert, int32_t slot) {
+    if (ctx == nullptr) return MOE_EINVAL;
+    if (ctx->arena == nullptr) return MOE_ESTATE;
+    if (expert < 0 || expert >= ctx->cfg.n_routed || slot < 0 || slot >= ctx->n_slots) return MOE_EINVAL;
+    const int owner = ctx->slot_owner[slot];
+    if (owner >= 0 && owner != expert) return MOE_EINVAL;
+    const int rc = table_mutable(ctx);
+    if (rc != MOE_OK) return rc;
+    const int old = ctx->slot_host[expert];
+    if (old >= 0 && old != slot) ctx->slot_owner[old] = -1;
+    ctx->slot_host[expert] = slot;
+    ctx->slot_owner[slot] = expert;
+    ctx->table_dirty = true;
+    return MOE_OK;
+}
+
+int moe_slot_evict(moe_ctx* ctx, int32_t expert) {
+    if (ctx == nullptr) return MOE_EINVAL;
+    if (ctx->arena == nullptr) return MOE_ESTATE;
+    if (expert < 0 || expert >= ctx->cfg.n_routed) return MOE_EINVAL;
+    const int rc = table_mutable(ctx);
+    if (rc != MOE_OK) return rc;
+    const int old = ctx->slot_host[expert];
+    if (old >= 0) ctx->slot_owner[old] = -1;
+    ctx->slot_host[expert] = -1;
+    ctx->table_dirty = true;
+    return MOE_OK;
+}
+
+int moe_slot_of(const moe_ctx* ctx, int32_t expert, int32_t* slot) {
+    if (ctx == nullptr || slot == nullptr || expert < 0 || expert >= ctx->cfg.n_routed) return MOE_EINVAL;
+    *slot = ctx->slot_host[expert];
+    return MOE_OK;
+}
+
+int moe_set_host_arena(moe_ctx* ctx, const void* pinned_host, size_t expert_stride) {
+    if (ctx == nullptr) return MOE_EINVAL;
+    if (pinned_host != nullptr && expert_stride < ctx->slot_bytes) return MOE_EINVAL;
+    ctx->host_arena = (const uint8_t*)pinned_host;
+    ctx->host_stride = expert_stride;
+    return MOE_OK;
+}
+
+int moe_route(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, float* weights_out,
+              int32_t* idx_out, void* stream) {
+    if (ctx == nullptr || x_bf16 == nullptr || weights_out == nullptr || idx_out == nullptr) return MOE_EINVAL;
+    if (m < 1 || m > ctx->cfg.max_tokens || !aligned(x_bf16, 16)) return MOE_EINVAL;
+    int rc = check_weights(ctx, w);
+    if (rc != MOE_OK) return rc;
+    return run_route(ctx, w, (const uint16_t*)x_bf16, m, idx_out, weights_out, (hipStream_t)stream);
+}
+
+int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
+                   float* weights_out, int32_t* idx_out, void* stream) {
+    if (ctx == nullptr || x_bf16 == nullptr || out_bf16 == nullptr) return MOE_EINVAL;
+    if (m < 1 || m > ctx->cfg.max_tokens) return MOE_EINVAL;
+    if (!aligned(x_bf16, 16) || !aligned(out_bf16, 16)) return MOE_EINVAL;
+    int rc = check_weights(ctx, w);
+    if (rc != MOE_OK) return rc;
+    if (ctx->arena == nullptr) return MOE_ESTATE;
+    const moe_cfg& c = ctx->cfg;
+    const hipStream_t st = (hipStream_t)stream;
+    const uint16_t* x = (const uint16_t*)x_bf16;
+    const int P = m * c.topk;
+
+    rc = upload_table(ctx, st);
+    if (rc != MOE_OK) return rc;
+    rc = run_route(ctx, w, x, m, ctx->idx, ctx->gw, st);
+    if (rc != MOE_OK) return rc;
+    rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_rows(x, m, c.dim, ctx->xq, ctx->xd, ctx->xs16, st); });
+    if (rc != MOE_OK) return rc;
+    const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
+    rc = timed(ctx, st, MOE_K_BUCKET, [&] {
+        return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, ctx->offsets, ctx->active, ctx->n_active,
+                             ctx->perm, ctx->inv, ctx->chunks, ctx->n_chunks, st);
+    });
+    if (rc != MOE_OK) return rc;
+
+    ExpertArgs a;
+    a.chunks = ctx->chunks;
+    a.n_chunks = ctx->n_chunks;
+    a.perm = ctx->perm;
+    a.topk = c.topk;
+    a.slot_table = ctx->slot_table_dev;
+    a.arena = ctx->arena;
+    a.slot_bytes = ctx->slot_bytes;
+    a.off_w1 = ctx->off_w1;
+    a.off_w3 = ctx->off_w3;
+    a.off_w2 = ctx->off_w2;
+    a.sh_w1 = kq ? (const uint8_t*)w->shared_w1 : nullptr;
+    a.sh_w3 = kq ? (const uint8_t*)w->shared_w3 : nullptr;
+    a.sh_w2 = kq ? (const uint8_t*)w->shared_w2 : nullptr;
+    a.xq = ctx->xq;
+    a.xd = ctx->xd;
+    a.xs16 = ctx->xs16;
+    a.h_routed = ctx->h_routed;
+    a.h_shared = ctx->h_shared;
+    a.e_rows = ctx->e_rows;
+    a.ys = ctx->ys;
+    a.D = c.dim;
+    a.I = c.inter;
+    a.limit = c.swiglu_limit;
+    a.err = ctx->err;
+    const int rows_max = std::min(m, GEMV_ROWS);
+    const int chunks = routed_chunk_bound(c, m) + (kq ? shared_chunk_count(m) : 0);
+    rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, chunks, st); });
+    if (rc != MOE_OK) return rc;
+    if (w->shared_fmt == MOE_SHARED_BF16) {
+        rc = timed(ctx, st, MOE_K_SHARED_GATEUP, [&] {
+            return launch_shared_bf16_gateup(x, m, c.dim, c.inter, (const uint16_t*)w->shared_w1,
+                                             (const uint16_t*)w->shared_w3, (uint16_t*)ctx->h_shared,
+                                             c.swiglu_limit, st);
+        });
+        if (rc != MOE_OK) return rc;
+    }
+    rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, chunks, st); });
+    if (rc != MOE_OK) return rc;
+    if (w->shared_fmt == MOE_SHARED_BF16) {
+        rc = timed(ctx, st, MOE_K_SHARED_DOWN, [&] {
+            return launch_shared_bf16_down((const uint16_t*)ctx->h_shared, m, c.dim, c.inter,
+                                           (const uint16_t*)w->shared_w2, ctx->ys, st);
+        });
+        if (rc != MOE_OK) return rc;
+    }
+    const float* ys = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
+    rc = timed(ctx, st, MOE_K_COMBINE, [&] {
+        return launch_combine(ctx->e_rows, ys, ctx->gw, ctx->inv, m, c.topk, c.dim, (uint16_t*)out_bf16, st);
+    });
+    if (rc != MOE_OK) return rc;
+    if (weights_out != nullptr &&
+        hipMemcpyAsync(weights_out, ctx->gw, sizeof(float) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return MOE_EHIP;
+    if (idx_out != nullptr &&
+        hipMemcpyAsync(idx_out, ctx->idx, sizeof(int32_t) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return MOE_EHIP;
+    ctx->stats.calls++;
+    return MOE_OK;
+}
+
+int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16, void* stream) {
+    return moe_forward_ex(ctx, w, x_bf16, m, out_bf16, nullptr, nullptr, stream);
+}
+
+int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_out, float* d_out, void* stream) {
+    if (x_bf16 == nullptr || q_out == nullptr || d_out == nullptr || rows < 1 || cols < QB || cols % QB) return MOE_EINVAL;
+    if (!aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(d_out, 4)) return MOE_EINVAL;
+    return hip_status(launch_quantize_rows((const uint16_t*)x_bf16, rows, cols, q_out, d_out, nullptr, (hipStream_t)stream));
+}
+
+int moe_check(moe_ctx* ctx, void* stream) {
+    if (ctx == nullptr) return MOE_EINVAL;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_EHIP;
+    int32_t word = 0;
+    if (hipMemcpy(&word, ctx->err, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
+    const int32_t zero = 0;
+    if (hipMemcpy(ctx->err, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return MOE_EHIP;
+    if (word & ERR_NONFINITE) return MOE_ENONFINITE;
+    if (word & ERR_NOTRESIDENT) return MOE_ENOTRESIDENT;
+    return MOE_OK;
+}
+
+int moe_set_profiling(moe_ctx* ctx, int32_t on) {
+    if (ctx == nullptr) return MOE_EINVAL;
+    if (ctx->prof && !on) {
+        // drop what was recorded
+        if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
+        ctx->marks.clear();
+        ctx->ev_next = 0;
+    }
+    ctx->prof = on != 0;
+    for (int i = 0; i < MOE_K_COUNT; ++i) {
+        ctx->k_ms[i] = 0.0;
+        ctx->k_n[i] = 0;
+    }
+    return MOE_OK;
+}
+
+int moe_kernel_times(moe_ctx* ctx, double* ms_sum, int64_t* launches, int32_t n) {
+    if (ctx == nullptr || ms_sum == nullptr || launches == nullptr || n < 0) return MOE_EINVAL;
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
+    for (const auto& mk : ctx->marks) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, mk.a, mk.b) != hipSuccess) return MOE_EHIP;
+        ctx->k_ms[mk.kind] += ms;
+        ctx->k_n[mk.kind] += 1;
+    }
+    ctx->marks.clear();
+    ctx->ev_next = 0;
+    for (int i = 0; i < n && i < MOE_K_COUNT; ++i) {
+        ms_sum[i] = ctx->k_ms[i];
+        launches[i] = ctx->k_n[i];
+        ctx->k_ms[i] = 0.0;
+        ctx->k_n[i] = 0;
+    }
+    return MOE_OK;
+}
+
+int moe_get_stats(const moe_ctx* ctx, moe_stats* out) {
+    if (ctx == nullptr || out == nullptr) return MOE_EINVAL;
+    *out = ctx->stats;
+    return MOE_OK;
+}
+
+int moe_reset_stats(moe_ctx* ctx) {
+    if (ctx == nullptr) return MOE_EINVAL;
+    std::memset(&ctx->stats, 0, sizeof(ctx->stats));
+    return MOE_OK;
+}
+
+}  // extern "C"

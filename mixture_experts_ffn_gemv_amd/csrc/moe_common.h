@@ -1,0 +1,122 @@
+// Device helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+namespace moe {
+
+constexpr int QK = 256;          // weights per K-quant superblock
+constexpr int Q2K_BYTES = 84;    // scales[16] | qs[64] | d | dmin
+constexpr int Q3K_BYTES = 110;   // hmask[32] | qs[64] | scales[12] | d
+constexpr int QB = 32;           // values per q8_1 block
+constexpr int GEMV_ROWS = 8;     // token rows per GEMV chunk
+
+// device error word bits
+constexpr int ERR_NONFINITE = 1;
+constexpr int ERR_NOTRESIDENT = 2;
+
+// One unit of expert work: up to GEMV_ROWS token rows of one expert.
+// expert >= 0: routed expert; row0 is a position in the expert-sorted pair list.
+// expert == -1: the shared expert; row0 is a token index.
+struct Chunk {
+    int32_t expert;
+    int32_t row0;
+    int32_t nrows;
+    int32_t pad;
+};
+
+// Everything the expert kernels read and write.
+struct ExpertArgs {
+    const Chunk* chunks;
+    const int32_t* n_chunks;
+    const int32_t* perm;        // position -> pair (token * topk + pick)
+    int32_t topk;
+    const int32_t* slot_table;  // expert -> slot or -1
+    const uint8_t* arena;
+    size_t slot_bytes, off_w1, off_w3, off_w2;
+    const uint8_t* sh_w1;       // K-quant shared expert (NULL when bf16 / none)
+    const uint8_t* sh_w3;
+    const uint8_t* sh_w2;
+    const int8_t* xq;           // q8_1 of x: int8 [m, D], d f32 [m, D/32], 16-sums i32 [m, D/16]
+    const float* xd;
+    const int32_t* xs16;
+    float* h_routed;            // f32 [pairs, I] in position order
+    float* h_shared;            // f32 [m, I]
+    float* e_rows;              // f32 [pairs, D] in position order
+    float* ys;                  // f32 [m, D]
+    int32_t D, I;
+    float limit;
+    int32_t* err;
+};
+
+MOE_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+MOE_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// nearest-even f32 -> bf16 (NaN not special-cased)
+MOE_DEV uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+MOE_DEV float half_bits_to_f32(uint32_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+    return (float)v;
+}
+
+MOE_DEV float round_to_fp16(float f) { return (float)(_Float16)f; }
+
+MOE_DEV int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// (hi:lo) >> sh for sh in {0, 16}
+MOE_DEV uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbit(hi, lo, sh);
+}
+
+// Clamped SwiGLU: g <= L, -L <= u <= L when L > 0; h = g * sigmoid(g) * u.
+MOE_DEV float swiglu(float g, float u, float limit) {
+    if (limit > 0.f) {
+        g = fminf(g, limit);
+        u = fminf(fmaxf(u, -limit), limit);
+    }
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// q8_1 of 32 f32 values held by one lane: d = amax / 127 (IEEE division),
+// q = round-half-away(v / d) with the unrounded d, 0 when d == 0.
+// Outputs the packed int8 quants, fp16(d) as f32, and the sums of the two
+// 16-value halves of q.
+MOE_DEV void q8_1_block(const float* v, uint32_t* q, float& d16, int& s_lo, int& s_hi) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax / 127.0f;
+    int sl = 0, sh = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int qi = (d == 0.f) ? 0 : (int)roundf(v[4 * c + b] / d);
+            packed |= ((uint32_t)(qi & 0xFF)) << (8 * b);
+            if (c < 4) sl += qi; else sh += qi;
+        }
+        q[c] = packed;
+    }
+    d16 = round_to_fp16(d);
+    s_lo = sl;
+    s_hi = sh;
+}
+
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+}  // namespace moe

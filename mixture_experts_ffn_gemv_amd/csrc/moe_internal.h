@@ -1,0 +1,41 @@
+// Launchers shared between the kernel translation units and the host library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_common.h"
+
+namespace moe {
+
+struct GemvGeom {
+    int P;          // rows processed in parallel
+    int threads;    // workgroup size
+    int R;          // rows per tile
+    int tiles;      // tiles per chunk
+    int lds_base;   // LDS bytes before the per-row-slot reduction area
+    int lds_per_t;  // reduction bytes per token row
+};
+
+GemvGeom gateup_geom(int D, int I);
+GemvGeom down_geom(int D, int I);
+
+hipError_t launch_router_gemv(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
+                              hipStream_t st);
+hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
+                                hipStream_t st);
+hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp, int norm,
+                       float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st);
+hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, int32_t* offsets,
+                         int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv, Chunk* chunks,
+                         int32_t* n_chunks, hipStream_t st);
+hipError_t launch_gateup_q2k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
+hipError_t launch_down_q3k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
+hipError_t launch_shared_bf16_gateup(const uint16_t* x, int m, int D, int I, const uint16_t* w1,
+                                     const uint16_t* w3, uint16_t* h_bf16, float limit, hipStream_t st);
+hipError_t launch_shared_bf16_down(const uint16_t* h_bf16, int m, int D, int I, const uint16_t* w2, float* ys,
+                                   hipStream_t st);
+hipError_t launch_combine(const float* e_rows, const float* ys, const float* gw, const int32_t* inv, int m,
+                          int k, int D, uint16_t* out, hipStream_t st);
+
+}  // namespace moe

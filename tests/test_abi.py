@@ -1,0 +1,67 @@
+"""CPU checks of the C ABI library: it loads, exports every function that
+include/moe.h declares, and its host-only calls behave (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_gemv_amd as moe
+import synthetic as S
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_expert_layout_matches_block_sizes(lib):
+    for shape in (S.TINY, S.REAL, S.LayerShape(512, 768, 40, 9)):
+        cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=4)
+        assert moe.moe_expert_layout(cfg) == S.expert_layout(shape)
+
+
+@pytest.mark.parametrize("bad", [dict(dim=300), dict(dim=0), dict(inter=100), dict(n_routed=0),
+                                 dict(topk=0), dict(topk=17), dict(max_tokens=0), dict(gate_temp=0.0),
+                                 dict(dim=8448)])
+def test_expert_layout_rejects_bad_cfg(lib, bad):
+    kw = dict(dim=256, inter=256, n_routed=16, topk=2, gate_temp=1.0, max_tokens=4)
+    kw.update(bad)
+    cfg = moe.make_cfg(kw["dim"], kw["inter"], kw["n_routed"], kw["topk"], gate_temp=kw["gate_temp"],
+                       max_tokens=kw["max_tokens"])
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_expert_layout(cfg)
+    assert e.value.code == moe.MOE_EINVAL
+
+
+def test_strerror_and_null_handling(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert moe.strerror(code)
+    assert moe.strerror(-99) == "unknown status"
+    assert lib.moe_destroy(None) == moe.MOE_OK
+    assert lib.moe_create(None, None) == moe.MOE_EINVAL
+    assert lib.moe_check(None, None) == moe.MOE_EINVAL
+    assert lib.moe_get_stats(None, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_q8_1(None, 1, 32, None, None, None) == moe.MOE_EINVAL
+    out = ctypes.c_void_p()
+    bad = moe.make_cfg(300, 256, 16, 2)
+    assert lib.moe_create(ctypes.byref(bad), ctypes.byref(out)) == moe.MOE_EINVAL
+    assert out.value is None

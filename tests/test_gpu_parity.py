@@ -1,0 +1,211 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars: routing indices bit-exact except for near-ties (gap < 1e-5 on the
+oracle's keys, counted); outputs within 2e-3 * max|y| + half a bf16 ulp of the
+oracle's unrounded y; q8_1 quants and scales bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_gemv_amd as moe
+import oracle
+import synthetic as S
+from layer_fixture import Layer, bits, compare_routing
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_layer(layer, x, label, sample_rows=None):
+    m = x.shape[0]
+    say(f"[{label}] forward m={m}")
+    out, gw, idx = layer.forward(x.to(layer.dev))
+    rc = layer.check()
+    assert rc == moe.MOE_OK, moe.strerror(rc)
+    idx_h, gw_h = idx.cpu().numpy(), gw.cpu().numpy()
+    ridx, rg, rkeys, _ = layer.oracle_route(x)
+    exempt = compare_routing(idx_h, gw_h, ridx, rg, rkeys)
+    rows = list(range(m)) if sample_rows is None else sample_rows
+    say(f"[{label}] routing ok ({exempt} near-tie exemptions); oracle on rows {rows}")
+    ref = layer.oracle(x[rows])
+    got = out.float().cpu().numpy().astype(np.float64)[rows]
+    worst = 0.0
+    for j, t in enumerate(rows):
+        if list(idx_h[t]) != list(ref["idx"][j]):
+            continue   # an exempted near-tie: the two sides used different experts
+        ok, ratio = oracle.within_tolerance(got[j], ref["y"][j])
+        assert ok, f"{label}: token {t} off by {ratio:.3f} x tolerance"
+        worst = max(worst, ratio)
+    say(f"[{label}] outputs ok, worst {worst:.4f} of tolerance")
+    return out, gw, idx
+
+
+# ----------------------------------------------------------------------------- q8_1
+
+def test_quantize_q8_1_bit_exact():
+    torch.manual_seed(0)
+    rows, cols = 37, 1024
+    x = (torch.randn(rows, cols) * torch.exp2(torch.randint(-6, 6, (rows, 1)).float())).to(torch.bfloat16)
+    x[0, :32] = 0                                 # zero block
+    x[1, :32] = torch.tensor([127.0, 2.5, -2.5, 0.5, -0.5] + [0.0] * 27).to(torch.bfloat16)   # ties
+    x[2, 32:64] = -3.0                            # constant block
+    d_x = x.cuda()
+    q = torch.empty(rows, cols, dtype=torch.int8, device="cuda")
+    d = torch.empty(rows, cols // 32, dtype=torch.float32, device="cuda")
+    moe.moe_quantize_q8_1(d_x, rows, cols, q, d)
+    torch.cuda.synchronize()
+    rq, rd, _ = oracle.quantize_q8_1(oracle.bf16_bits_to_f64(bits(x)).astype(np.float32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(d.cpu().numpy().astype(np.float64), rd)
+
+
+# ----------------------------------------------------------------------------- tiny layer
+
+TINY_VARIANTS = {
+    "bf16_shared": dict(),
+    "kquant_shared": dict(shared_fmt="kquant"),
+    "no_shared": dict(shared_fmt="none"),
+    "clamps_0.25": dict(limit=0.25),
+    "no_clamps": dict(limit=0.0),
+    "gate_temp_2": dict(gate_temp=2.0),
+    "norm_off": dict(norm=False),
+}
+
+
+@pytest.mark.parametrize("variant", list(TINY_VARIANTS))
+@pytest.mark.parametrize("m", [1, 4, 13])
+def test_tiny_layer(variant, m):
+    layer = Layer(S.TINY, 0, max_tokens=16, **TINY_VARIANTS[variant])
+    try:
+        x = S.make_tokens(m, S.TINY.dim, 0, index=m)
+        check_layer(layer, x, f"tiny {variant}")
+    finally:
+        layer.close()
+
+
+def test_tiny_topk1():
+    shape = S.LayerShape(256, 256, 16, 1)
+    layer = Layer(shape, 3, max_tokens=8)
+    try:
+        check_layer(layer, S.make_tokens(5, 256, 3), "tiny k=1")
+    finally:
+        layer.close()
+
+
+def test_tiny_wide_topk_ragged():
+    shape = S.LayerShape(512, 768, 40, 9)       # 9 picks, ragged groups, three K superblocks of W2
+    layer = Layer(shape, 4, max_tokens=40, shared_fmt="kquant")
+    try:
+        check_layer(layer, S.make_tokens(37, 512, 4), "wide k=9 m=37", sample_rows=[0, 17, 36])
+    finally:
+        layer.close()
+
+
+def test_tiny_deterministic():
+    layer = Layer(S.TINY, 0, max_tokens=16)
+    try:
+        x = S.make_tokens(13, S.TINY.dim, 9).cuda()
+        a = layer.forward(x)[0].clone()
+        for _ in range(3):
+            b = layer.forward(x)[0]
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    finally:
+        layer.close()
+
+
+def test_route_only_matches_forward():
+    layer = Layer(S.TINY, 0, max_tokens=16)
+    try:
+        x = S.make_tokens(9, S.TINY.dim, 5).cuda()
+        gw = torch.empty(9, 2, dtype=torch.float32, device="cuda")
+        idx = torch.empty(9, 2, dtype=torch.int32, device="cuda")
+        moe.moe_route(layer.ctx, layer.w, x, 9, gw, idx)
+        _, gw2, idx2 = layer.forward(x)
+        assert torch.equal(idx, idx2) and torch.equal(gw, gw2)
+    finally:
+        layer.close()
+
+
+def test_nan_key_reported():
+    layer = Layer(S.TINY, 0, max_tokens=4)
+    try:
+        layer.d_bias[3] = float("nan")
+        layer.forward(S.make_tokens(2, 256, 1).cuda())
+        assert layer.check() == moe.MOE_ENONFINITE
+        assert layer.check() == moe.MOE_OK          # the word is cleared by the read
+    finally:
+        layer.close()
+
+
+def test_not_resident_reported():
+    layer = Layer(S.TINY, 0, max_tokens=4)
+    try:
+        x = S.make_tokens(1, 256, 2)
+        ridx = layer.oracle_route(x)[0]
+        moe.moe_slot_evict(layer.ctx, int(ridx[0, 0]))
+        layer.forward(x.cuda())
+        assert layer.check() == moe.MOE_ENOTRESIDENT
+    finally:
+        layer.close()
+
+
+def test_invalid_arguments():
+    layer = Layer(S.TINY, 0, max_tokens=4)
+    try:
+        x = S.make_tokens(4, 256, 2).cuda()
+        out = torch.empty(5, 256, dtype=torch.bfloat16, device="cuda")
+        for m in (0, 5, -1):
+            with pytest.raises(moe.MoeError) as e:
+                moe.moe_forward(layer.ctx, layer.w, x, m, out)
+            assert e.value.code == moe.MOE_EINVAL
+        with pytest.raises(moe.MoeError):
+            moe.moe_slot_bind(layer.ctx, 16, 0)
+        with pytest.raises(moe.MoeError):
+            moe.moe_slot_bind(layer.ctx, 0, 1)          # slot 1 belongs to expert 1
+    finally:
+        layer.close()
+
+
+# ----------------------------------------------------------------------------- real layer
+
+@pytest.fixture(scope="module")
+def real_experts():
+    say("[real] drawing 384 experts on the GPU")
+    a = S.make_experts(S.REAL, 1, device="cuda")
+    torch.cuda.synchronize()
+    yield a
+    del a
+    torch.cuda.empty_cache()
+
+
+def test_real_decode_m1(real_experts):
+    layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=8, experts=real_experts)
+    try:
+        pool = S.make_tokens(256, S.REAL.dim, 1)
+        for t in (0, 131):
+            check_layer(layer, pool[t:t + 1], f"decode m=1 token {t}")
+    finally:
+        layer.close()
+
+
+def test_real_small_batch_m8_kquant_shared(real_experts):
+    layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=8, experts=real_experts,
+                  shared_fmt="kquant")
+    try:
+        x = S.make_tokens(8, S.REAL.dim, 1, index=1)
+        check_layer(layer, x, "small batch m=8", sample_rows=[0, 7])
+    finally:
+        layer.close()
+
+
+def test_real_prefill_m512(real_experts):
+    layer = Layer(S.REAL, 1, bias=None, router_std=0.02, max_tokens=512, experts=real_experts)
+    try:
+        x = S.make_tokens(512, S.REAL.dim, 1, index=2)
+        check_layer(layer, x, "prefill m=512", sample_rows=[0, 511])
+    finally:
+        layer.close()
