@@ -172,10 +172,10 @@ int moe_check(moe_ctx* ctx, void* stream);
  * the summed milliseconds and the number of launches since profiling was
  * switched on or last read; then it restarts the sums. n < MOE_K_COUNT reads
  * the first n classes. MOE_EINVAL for NULL. */
-#define MOE_K_ROUTER 0        /* router logits */
-#define MOE_K_QUANT 1         /* q8_1 of x */
-#define MOE_K_TOPK 2          /* selection and weights */
-#define MOE_K_BUCKET 3        /* token -> expert bucketing */
+#define MOE_K_ROUTER 0        /* router logits (+ q8_1 of x in the same launch) */
+#define MOE_K_QUANT 1         /* q8_1 of the SwiGLU output h */
+#define MOE_K_TOPK 2          /* selection and weights (+ bucketing when m <= 8) */
+#define MOE_K_BUCKET 3        /* token -> expert bucketing (m > 8) */
 #define MOE_K_GATEUP 4        /* routed (and K-quant shared) gate/up + SwiGLU */
 #define MOE_K_SHARED_GATEUP 5 /* bf16 shared gate/up + SwiGLU */
 #define MOE_K_DOWN 6          /* routed (and K-quant shared) down */

@@ -33,7 +33,7 @@ EXPORTED = (
     "moe_kernel_times",
 )
 
-KERNEL_CLASSES = ("router", "quant", "topk", "bucket", "gateup", "shared_gateup", "down", "shared_down",
+KERNEL_CLASSES = ("router", "quant_h", "topk", "bucket", "gateup", "shared_gateup", "down", "shared_down",
                   "combine")
 
 

@@ -20,7 +20,7 @@
 
 namespace moe {
 
-// chunk -> (weights of the expert, token rows); returns false when the expert has no slot
+// token rows of a chunk
 struct ChunkRows {
     int tok[GEMV_ROWS];
     int nrows;
@@ -38,6 +38,32 @@ MOE_DEV ChunkRows chunk_rows(const ExpertArgs& a, const Chunk& ch) {
         cr.tok[i] = t;
     }
     return cr;
+}
+
+// Copy chunks [0, n) of a then [0, n) of b (16 B each) to dst, which is 2n
+// chunks long, with up to eight loads in flight per thread before the LDS
+// writes. Named registers, not an array: an array here was placed in scratch
+// memory. Indices past the end are clamped to the last chunk, which is then
+// written several times with the same bytes.
+MOE_DEV void stage_two(uint4* dst, const uint4* a, const uint4* b, int n, int tid, int bd) {
+    const int total = (a == b) ? n : 2 * n;
+    auto src = [&](int q) { return q < n ? a[q] : b[q - n]; };
+    for (int q0 = tid; q0 < total; q0 += 8 * bd) {
+        const int q1 = min(q0 + bd, total - 1), q2 = min(q0 + 2 * bd, total - 1);
+        const int q3 = min(q0 + 3 * bd, total - 1), q4 = min(q0 + 4 * bd, total - 1);
+        const int q5 = min(q0 + 5 * bd, total - 1), q6 = min(q0 + 6 * bd, total - 1);
+        const int q7 = min(q0 + 7 * bd, total - 1);
+        const uint4 v0 = src(q0), v1 = src(q1), v2 = src(q2), v3 = src(q3);
+        const uint4 v4 = src(q4), v5 = src(q5), v6 = src(q6), v7 = src(q7);
+        dst[q0] = v0;
+        dst[q1] = v1;
+        dst[q2] = v2;
+        dst[q3] = v3;
+        dst[q4] = v4;
+        dst[q5] = v5;
+        dst[q6] = v6;
+        dst[q7] = v7;
+    }
 }
 
 MOE_DEV const uint8_t* expert_base(const ExpertArgs& a, int expert) {
@@ -114,7 +140,7 @@ __global__ __launch_bounds__(512) void gateup_q2k_kernel(ExpertArgs a, int R, in
         const uint4* g1 = reinterpret_cast<const uint4*>(w1 + (size_t)r0 * rowbytes);
         const uint4* g3 = reinterpret_cast<const uint4*>(w3 + (size_t)r0 * rowbytes);
         uint4* dst = reinterpret_cast<uint4*>(tw);
-        for (int q = tid; q < 2 * n16; q += blockDim.x) dst[q] = q < n16 ? g1[q] : g3[q - n16];
+        stage_two(dst, g1, g3, n16, tid, (int)blockDim.x);
     }
     __syncthreads();
 
@@ -137,19 +163,13 @@ __global__ __launch_bounds__(512) void gateup_q2k_kernel(ExpertArgs a, int R, in
             for (int q = 0; q < 4; ++q) il = sdot4(W[q], av[i][q], il);
 #pragma unroll
             for (int q = 4; q < 8; ++q) ih = sdot4(W[q], av[i][q], ih);
-            const int isum = sc_lo * il + sc_hi * ih;
-            const int msum = m_lo * slo[i] + m_hi * shi[i];
+            const int isum = __mul24(sc_lo, il) + __mul24(sc_hi, ih);
+            const int msum = __mul24(m_lo, slo[i]) + __mul24(m_hi, shi[i]);
             part[i] = dx[i] * (d * (float)isum - dmin * (float)msum);
         }
 #pragma unroll
-        for (int i = 0; i < T; ++i) {
-            float v = part[i];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            part[i] = v;
-        }
-        if ((kb & 7) == 0) {
+        for (int i = 0; i < T; ++i) part[i] = group8_sum(part[i]);
+        if ((kb & 7) == 7) {
 #pragma unroll
             for (int i = 0; i < T; ++i) red[((r * 2 + mtx) * nsb + s) * T + i] = part[i];
         }
@@ -158,10 +178,19 @@ __global__ __launch_bounds__(512) void gateup_q2k_kernel(ExpertArgs a, int R, in
     for (int q = tid; q < R * T; q += blockDim.x) {
         const int r = q / T, i = q % T;
         if (i >= cr.nrows) continue;
+        const float* rg = red + (size_t)(r * 2 + 0) * nsb * T + i;
+        const float* ru = red + (size_t)(r * 2 + 1) * nsb * T + i;
         float g = 0.f, u = 0.f;
-        for (int sbi = 0; sbi < nsb; ++sbi) {
-            g += red[((r * 2 + 0) * nsb + sbi) * T + i];
-            u += red[((r * 2 + 1) * nsb + sbi) * T + i];
+        int sbi = 0;
+        for (; sbi + 4 <= nsb; sbi += 4) {   // four independent reads per step, summed in order
+            const float g0 = rg[(sbi + 0) * T], g1 = rg[(sbi + 1) * T], g2 = rg[(sbi + 2) * T], g3 = rg[(sbi + 3) * T];
+            const float u0 = ru[(sbi + 0) * T], u1 = ru[(sbi + 1) * T], u2 = ru[(sbi + 2) * T], u3 = ru[(sbi + 3) * T];
+            g = (((g + g0) + g1) + g2) + g3;
+            u = (((u + u0) + u1) + u2) + u3;
+        }
+        for (; sbi < nsb; ++sbi) {
+            g += rg[sbi * T];
+            u += ru[sbi * T];
         }
         hout[(size_t)i * I + r0 + r] = swiglu(g, u, a.limit);
     }
@@ -170,7 +199,7 @@ __global__ __launch_bounds__(512) void gateup_q2k_kernel(ExpertArgs a, int R, in
 // ------------------------------------------------------------------ Q3_K down
 // Lanes: tid = pr * L + kb (L = I/32). The prologue forms the lane's q8_1 block of h.
 template <int T>
-__global__ __launch_bounds__(1024) void down_q3k_kernel(ExpertArgs a, int R, int P) {
+__global__ __launch_bounds__(640) void down_q3k_kernel(ExpertArgs a, int R, int P) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
     const int L = I / QB;
@@ -183,7 +212,6 @@ __global__ __launch_bounds__(1024) void down_q3k_kernel(ExpertArgs a, int R, int
     const int r0 = tile * R;
     const ChunkRows cr = chunk_rows(a, ch);
     float* eout = (cr.shared ? a.ys : a.e_rows) + (size_t)ch.row0 * D;
-    const float* hin = (cr.shared ? a.h_shared : a.h_routed) + (size_t)ch.row0 * I;
     const uint8_t* w2;
     if (cr.shared) {
         w2 = a.sh_w2;
@@ -204,17 +232,20 @@ __global__ __launch_bounds__(1024) void down_q3k_kernel(ExpertArgs a, int R, int
     uint32_t av[T][8];
     float dx[T];
     int slo[T], shi[T];
+    const int8_t* hq = cr.shared ? a.hq_shared : a.hq_routed;
+    const float* hd = cr.shared ? a.hd_shared : a.hd_routed;
+    const int32_t* hs = cr.shared ? a.hs_shared : a.hs_routed;
 #pragma unroll
     for (int i = 0; i < T; ++i) {
         if (i < cr.nrows) {
-            const float4* src = reinterpret_cast<const float4*>(hin + (size_t)i * I + kb * QB);
-            float v[32];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 f = src[q];
-                v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-            }
-            q8_1_block(v, av[i], dx[i], slo[i], shi[i]);
+            const size_t row = (size_t)ch.row0 + i;
+            const uint4* src = reinterpret_cast<const uint4*>(hq + row * I + kb * QB);
+            const uint4 u0 = src[0], u1 = src[1];
+            av[i][0] = u0.x; av[i][1] = u0.y; av[i][2] = u0.z; av[i][3] = u0.w;
+            av[i][4] = u1.x; av[i][5] = u1.y; av[i][6] = u1.z; av[i][7] = u1.w;
+            dx[i] = hd[row * L + kb];
+            slo[i] = hs[row * 2 * L + 2 * kb];
+            shi[i] = hs[row * 2 * L + 2 * kb + 1];
         } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q) av[i][q] = 0;
@@ -229,7 +260,7 @@ __global__ __launch_bounds__(1024) void down_q3k_kernel(ExpertArgs a, int R, int
         const int n16 = R * rowbytes / 16;
         const uint4* g = reinterpret_cast<const uint4*>(w2 + (size_t)r0 * rowbytes);
         uint4* dst = reinterpret_cast<uint4*>(tw);
-        for (int q = tid; q < n16; q += blockDim.x) dst[q] = g[q];
+        stage_two(dst, g, g, n16, tid, (int)blockDim.x);   // second half empty: copies g[0, n16)
     }
     __syncthreads();
 
@@ -281,17 +312,11 @@ __global__ __launch_bounds__(1024) void down_q3k_kernel(ExpertArgs a, int R, int
             for (int q = 4; q < 8; ++q) ih = sdot4(V[q], av[i][q], ih);
             il -= 4 * slo[i];
             ih -= 4 * shi[i];
-            part[i] = dx[i] * (d * (float)(s6_lo * il + s6_hi * ih));
+            part[i] = dx[i] * (d * (float)(__mul24(s6_lo, il) + __mul24(s6_hi, ih)));
         }
 #pragma unroll
-        for (int i = 0; i < T; ++i) {
-            float v = part[i];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            part[i] = v;
-        }
-        if ((kb & 7) == 0) {
+        for (int i = 0; i < T; ++i) part[i] = group8_sum(part[i]);
+        if ((kb & 7) == 7) {
 #pragma unroll
             for (int i = 0; i < T; ++i) red[(r * nsb + s) * T + i] = part[i];
         }
@@ -300,10 +325,53 @@ __global__ __launch_bounds__(1024) void down_q3k_kernel(ExpertArgs a, int R, int
     for (int q = tid; q < R * T; q += blockDim.x) {
         const int r = q / T, i = q % T;
         if (i >= cr.nrows) continue;
+        const float* re = red + (size_t)r * nsb * T + i;
         float e = 0.f;
-        for (int sbi = 0; sbi < nsb; ++sbi) e += red[(r * nsb + sbi) * T + i];
+        int sbi = 0;
+        for (; sbi + 4 <= nsb; sbi += 4) {
+            const float e0 = re[(sbi + 0) * T], e1 = re[(sbi + 1) * T], e2 = re[(sbi + 2) * T], e3 = re[(sbi + 3) * T];
+            e = (((e + e0) + e1) + e2) + e3;
+        }
+        for (; sbi < nsb; ++sbi) e += re[sbi * T];
         eout[(size_t)i * D + r0 + r] = e;
     }
+}
+
+// ------------------------------------------------------------------ q8_1 of h
+// One lane per 32-value block of the SwiGLU output rows (routed positions, then
+// the K-quant shared expert's token rows): the activation of the down projection.
+__global__ __launch_bounds__(256) void quantize_h_kernel(ExpertArgs a, int routed_rows, int shared_rows) {
+    const int L = a.I / QB;
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    const int total = (routed_rows + shared_rows) * L;
+    if (b >= total) return;
+    const bool sh = b >= routed_rows * L;
+    const int bb = sh ? b - routed_rows * L : b;
+    const float* src = (sh ? a.h_shared : a.h_routed) + (size_t)bb * QB;
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 f = reinterpret_cast<const float4*>(src)[q];
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    }
+    uint32_t qv[8];
+    float d;
+    int sl, shs;
+    q8_1_block(v, qv, d, sl, shs);
+    uint4* dst = reinterpret_cast<uint4*>((sh ? a.hq_shared : a.hq_routed) + (size_t)bb * QB);
+    dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+    dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
+    (sh ? a.hd_shared : a.hd_routed)[bb] = d;
+    int32_t* hs = (sh ? a.hs_shared : a.hs_routed) + 2 * (size_t)bb;
+    hs[0] = sl;
+    hs[1] = shs;
+}
+
+hipError_t launch_quantize_h(const ExpertArgs& a, int routed_rows, int shared_rows, hipStream_t st) {
+    const int total = (routed_rows + shared_rows) * (a.I / QB);
+    if (total == 0) return hipSuccess;
+    quantize_h_kernel<<<(total + 255) / 256, 256, 0, st>>>(a, routed_rows, shared_rows);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launch geometry
@@ -313,7 +381,6 @@ GemvGeom gateup_geom(int D, int I) {
     g.P = L2 >= 256 ? 1 : 256 / L2;
     g.threads = L2 * g.P;
     g.R = g.P > GEMV_ROWS ? g.P : GEMV_ROWS;
-    while (I % g.R) g.R += GEMV_ROWS;   // I % 256 == 0 keeps this small
     g.tiles = I / g.R;
     const int rowbytes = (D / QK) * Q2K_BYTES;
     g.lds_base = 2 * g.R * rowbytes;
@@ -326,7 +393,7 @@ GemvGeom down_geom(int D, int I) {
     const int L = I / QB;
     int P = 1;
     while (L * P < 256 || (L * P) % 64 != 0) {
-        if (L * (P + 1) > 1024) break;
+        if (L * (P + 1) > 640) break;     // the kernel's launch bound
         ++P;
     }
     g.P = P;

@@ -35,6 +35,8 @@ struct Carver {
 struct moe_ctx {
     moe_cfg cfg;
     int device = 0;
+    int n_cu = 256;          // compute units of the device
+    bool stream_ok = false;  // the streaming GEMVs fit this shape
     int max_pairs = 0;
     int max_chunks = 0;   // chunk-list capacity
     uint8_t* dev = nullptr;
@@ -54,6 +56,16 @@ struct moe_ctx {
     Chunk* chunks = nullptr;
     float* h_routed = nullptr;
     float* h_shared = nullptr;
+    int8_t* hq_routed = nullptr;
+    float* hd_routed = nullptr;
+    int32_t* hs_routed = nullptr;
+    int8_t* hq_shared = nullptr;
+    float* hd_shared = nullptr;
+    int32_t* hs_shared = nullptr;
+    // the bf16 shared expert runs on a side stream: fork after the call's input is
+    // ready, join before the combine
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     float* e_rows = nullptr;
     float* ys = nullptr;
     int32_t* err = nullptr;
@@ -177,12 +189,13 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
     return MOE_OK;
 }
 
-// router logits + q8_1(x) + top-k into (idx, gw)
-int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int32_t* idx, float* gw,
+// router logits (+ q8_1(x) when quant) and the top-k into (idx, gw)
+int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int32_t* idx, float* gw, bool quant,
               hipStream_t st) {
     const moe_cfg& c = ctx->cfg;
     int rc = timed(ctx, st, MOE_K_ROUTER, [&] {
-        return launch_router_gemv(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
+        return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits,
+                                   quant ? ctx->xq : nullptr, ctx->xd, ctx->xs16, st);
     });
     if (rc != MOE_OK) return rc;
     return timed(ctx, st, MOE_K_TOPK, [&] {
@@ -227,6 +240,12 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
         return MOE_EHIP;
     }
     const moe_cfg& c = ctx->cfg;
+    {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, ctx->device) == hipSuccess && prop.multiProcessorCount > 0)
+            ctx->n_cu = prop.multiProcessorCount;
+    }
+    ctx->stream_ok = stream_gemv_supported(c.dim, c.inter);
     const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
     const size_t P = M * c.topk;
     ctx->max_pairs = (int)P;
@@ -249,6 +268,12 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     const size_t o_ch = cv.take<Chunk>(ctx->max_chunks);
     const size_t o_hr = cv.take<float>(P * I);
     const size_t o_hs = cv.take<float>(M * I);
+    const size_t o_hqr = cv.take<int8_t>(P * I);
+    const size_t o_hdr = cv.take<float>(P * I / QB);
+    const size_t o_hsr = cv.take<int32_t>(P * I / 16);
+    const size_t o_hqs = cv.take<int8_t>(M * I);
+    const size_t o_hds = cv.take<float>(M * I / QB);
+    const size_t o_hss = cv.take<int32_t>(M * I / 16);
     const size_t o_er = cv.take<float>(P * D);
     const size_t o_ys = cv.take<float>(M * D);
     const size_t o_err = cv.take<int32_t>(1);
@@ -274,6 +299,12 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     ctx->chunks = (Chunk*)(b + o_ch);
     ctx->h_routed = (float*)(b + o_hr);
     ctx->h_shared = (float*)(b + o_hs);
+    ctx->hq_routed = (int8_t*)(b + o_hqr);
+    ctx->hd_routed = (float*)(b + o_hdr);
+    ctx->hs_routed = (int32_t*)(b + o_hsr);
+    ctx->hq_shared = (int8_t*)(b + o_hqs);
+    ctx->hd_shared = (float*)(b + o_hds);
+    ctx->hs_shared = (int32_t*)(b + o_hss);
     ctx->e_rows = (float*)(b + o_er);
     ctx->ys = (float*)(b + o_ys);
     ctx->err = (int32_t*)(b + o_err);
@@ -287,7 +318,10 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
         return MOE_ENOMEM;
     }
     for (size_t e = 0; e < E; ++e) ctx->slot_host[e] = -1;
-    if (hipEventCreateWithFlags(&ctx->table_ev, hipEventDisableTiming) != hipSuccess) {
+    if (hipEventCreateWithFlags(&ctx->table_ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming) != hipSuccess ||
+        hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking) != hipSuccess) {
         moe_destroy(ctx);
         return MOE_EHIP;
     }
@@ -300,6 +334,9 @@ int moe_destroy(moe_ctx* ctx) {
     if (ctx == nullptr) return MOE_OK;
     (void)hipDeviceSynchronize();
     if (ctx->table_ev) (void)hipEventDestroy(ctx->table_ev);
+    if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+    if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+    if (ctx->side) (void)hipStreamDestroy(ctx->side);
     for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
     if (ctx->slot_host) (void)hipHostFree(ctx->slot_host);
     if (ctx->dev) (void)hipFree(ctx->dev);
@@ -368,7 +405,7 @@ int moe_route(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m,
     if (m < 1 || m > ctx->cfg.max_tokens || !aligned(x_bf16, 16)) return MOE_EINVAL;
     int rc = check_weights(ctx, w);
     if (rc != MOE_OK) return rc;
-    return run_route(ctx, w, (const uint16_t*)x_bf16, m, idx_out, weights_out, (hipStream_t)stream);
+    return run_route(ctx, w, (const uint16_t*)x_bf16, m, idx_out, weights_out, false, (hipStream_t)stream);
 }
 
 int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
@@ -386,16 +423,47 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
 
     rc = upload_table(ctx, st);
     if (rc != MOE_OK) return rc;
-    rc = run_route(ctx, w, x, m, ctx->idx, ctx->gw, st);
-    if (rc != MOE_OK) return rc;
-    rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_rows(x, m, c.dim, ctx->xq, ctx->xd, ctx->xs16, st); });
-    if (rc != MOE_OK) return rc;
+    const bool bf16_shared = w->shared_fmt == MOE_SHARED_BF16;
+    if (bf16_shared) {
+        // the shared expert needs only x: run it beside the routing and the routed experts
+        if (hipEventRecord(ctx->ev_fork, st) != hipSuccess || hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0) != hipSuccess)
+            return MOE_EHIP;
+        rc = timed(ctx, ctx->side, MOE_K_SHARED_GATEUP, [&] {
+            return launch_shared_bf16_gateup(x, m, c.dim, c.inter, (const uint16_t*)w->shared_w1,
+                                             (const uint16_t*)w->shared_w3, (uint16_t*)ctx->h_shared,
+                                             c.swiglu_limit, ctx->side);
+        });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, ctx->side, MOE_K_SHARED_DOWN, [&] {
+            return launch_shared_bf16_down((const uint16_t*)ctx->h_shared, m, c.dim, c.inter,
+                                           (const uint16_t*)w->shared_w2, ctx->ys, ctx->side);
+        });
+        if (rc != MOE_OK) return rc;
+        if (hipEventRecord(ctx->ev_join, ctx->side) != hipSuccess) return MOE_EHIP;
+    }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
-    rc = timed(ctx, st, MOE_K_BUCKET, [&] {
-        return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, ctx->offsets, ctx->active, ctx->n_active,
-                             ctx->perm, ctx->inv, ctx->chunks, ctx->n_chunks, st);
-    });
-    if (rc != MOE_OK) return rc;
+    if (m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS) {
+        rc = timed(ctx, st, MOE_K_ROUTER, [&] {
+            return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
+                                       ctx->xd, ctx->xs16, st);
+        });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_TOPK, [&] {
+            return launch_route_small(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp,
+                                      c.norm_topk_prob, c.route_scale, ctx->idx, ctx->gw, ctx->err, kq ? 1 : 0,
+                                      ctx->offsets, ctx->active, ctx->n_active, ctx->perm, ctx->inv, ctx->chunks,
+                                      ctx->n_chunks, st);
+        });
+        if (rc != MOE_OK) return rc;
+    } else {
+        rc = run_route(ctx, w, x, m, ctx->idx, ctx->gw, true, st);
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_BUCKET, [&] {
+            return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, ctx->offsets, ctx->active,
+                                 ctx->n_active, ctx->perm, ctx->inv, ctx->chunks, ctx->n_chunks, st);
+        });
+        if (rc != MOE_OK) return rc;
+    }
 
     ExpertArgs a;
     a.chunks = ctx->chunks;
@@ -416,6 +484,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.xs16 = ctx->xs16;
     a.h_routed = ctx->h_routed;
     a.h_shared = ctx->h_shared;
+    a.hq_routed = ctx->hq_routed;
+    a.hd_routed = ctx->hd_routed;
+    a.hs_routed = ctx->hs_routed;
+    a.hq_shared = ctx->hq_shared;
+    a.hd_shared = ctx->hd_shared;
+    a.hs_shared = ctx->hs_shared;
     a.e_rows = ctx->e_rows;
     a.ys = ctx->ys;
     a.D = c.dim;
@@ -424,25 +498,17 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.err = ctx->err;
     const int rows_max = std::min(m, GEMV_ROWS);
     const int chunks = routed_chunk_bound(c, m) + (kq ? shared_chunk_count(m) : 0);
+    const bool streaming = rows_max <= 1 && ctx->stream_ok;
     rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, chunks, st); });
     if (rc != MOE_OK) return rc;
-    if (w->shared_fmt == MOE_SHARED_BF16) {
-        rc = timed(ctx, st, MOE_K_SHARED_GATEUP, [&] {
-            return launch_shared_bf16_gateup(x, m, c.dim, c.inter, (const uint16_t*)w->shared_w1,
-                                             (const uint16_t*)w->shared_w3, (uint16_t*)ctx->h_shared,
-                                             c.swiglu_limit, st);
-        });
-        if (rc != MOE_OK) return rc;
-    }
-    rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, chunks, st); });
+    rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
     if (rc != MOE_OK) return rc;
-    if (w->shared_fmt == MOE_SHARED_BF16) {
-        rc = timed(ctx, st, MOE_K_SHARED_DOWN, [&] {
-            return launch_shared_bf16_down((const uint16_t*)ctx->h_shared, m, c.dim, c.inter,
-                                           (const uint16_t*)w->shared_w2, ctx->ys, st);
-        });
-        if (rc != MOE_OK) return rc;
-    }
+    rc = timed(ctx, st, MOE_K_DOWN, [&] {
+        return streaming ? launch_down_q3k_stream(a, ctx->n_cu * 2, st)
+                         : launch_down_q3k(a, rows_max, chunks, st);
+    });
+    if (rc != MOE_OK) return rc;
+    if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
     const float* ys = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
     rc = timed(ctx, st, MOE_K_COMBINE, [&] {
         return launch_combine(ctx->e_rows, ys, ctx->gw, ctx->inv, m, c.topk, c.dim, (uint16_t*)out_bf16, st);

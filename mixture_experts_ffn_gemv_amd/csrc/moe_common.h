@@ -46,6 +46,12 @@ struct ExpertArgs {
     const int32_t* xs16;
     float* h_routed;            // f32 [pairs, I] in position order
     float* h_shared;            // f32 [m, I]
+    int8_t* hq_routed;          // q8_1 of h_routed: int8 [pairs, I], d f32 [pairs, I/32], 16-sums i32 [pairs, I/16]
+    float* hd_routed;
+    int32_t* hs_routed;
+    int8_t* hq_shared;          // q8_1 of h_shared (K-quant shared expert): [m, I] ...
+    float* hd_shared;
+    int32_t* hs_shared;
     float* e_rows;              // f32 [pairs, D] in position order
     float* ys;                  // f32 [m, D]
     int32_t D, I;
@@ -111,6 +117,42 @@ MOE_DEV void q8_1_block(const float* v, uint32_t* q, float& d16, int& s_lo, int&
     d16 = round_to_fp16(d);
     s_lo = sl;
     s_hi = sh;
+}
+
+// DPP lane moves (GFX9 encodings): quad permutes, and a rotate by 4 inside a 16-lane row
+MOE_DEV float dpp_quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+MOE_DEV float dpp_quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+MOE_DEV float dpp_row_ror4(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of 8 lanes; the result is valid in lanes 4..7 of the group.
+MOE_DEV float group8_sum(float v) {
+    v += dpp_quad_xor1(v);
+    v += dpp_quad_xor2(v);
+    v += dpp_row_ror4(v);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts
+// and row broadcasts; lanes a move does not reach (outside the row, or rows the
+// row mask leaves out) add 0.
+template <int CTRL, int ROW_MASK>
+MOE_DEV int dpp_or_zero(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+MOE_DEV int wave_inclusive_scan(int v) {
+    v += dpp_or_zero<0x111, 0xF>(v);   // row_shr:1
+    v += dpp_or_zero<0x112, 0xF>(v);   // row_shr:2
+    v += dpp_or_zero<0x114, 0xF>(v);   // row_shr:4
+    v += dpp_or_zero<0x118, 0xF>(v);   // row_shr:8
+    v += dpp_or_zero<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_or_zero<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
 }
 
 MOE_DEV float wave_sum(float v) {

@@ -13,16 +13,53 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------- router logits
-// z[t, e] = sum_d x[t, d] * W_R[e, d], f32 accumulation. One workgroup per
+// ---------------------------------------------------------------- router logits + q8_1(x)
+// One launch, two kinds of workgroups. Blocks [0, E * ntg): router logits
+// z[t, e] = sum_d x[t, d] * W_R[e, d] with f32 accumulation, one workgroup per
 // (expert row, group of TT tokens); each thread walks 4-element chunks of the
-// row, so a row's 10 KB are read once per token group with coalesced loads.
+// row so the row's bytes are read once per token group with coalesced loads.
+// Blocks past that: q8_1 of x, one lane per 32-value block (int8 quants,
+// fp16(d) as f32, and the two 16-value sums of the quants used by the Q2_K
+// min term): d = amax / 127, q = round-half-away(x / d).
+MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* __restrict__ xq,
+                                 float* __restrict__ xd, int32_t* __restrict__ xs16) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)b * QB);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint4 u = src[c];
+        v[8 * c + 0] = bf16_lo(u.x); v[8 * c + 1] = bf16_hi(u.x);
+        v[8 * c + 2] = bf16_lo(u.y); v[8 * c + 3] = bf16_hi(u.y);
+        v[8 * c + 4] = bf16_lo(u.z); v[8 * c + 5] = bf16_hi(u.z);
+        v[8 * c + 6] = bf16_lo(u.w); v[8 * c + 7] = bf16_hi(u.w);
+    }
+    uint32_t q[8];
+    float d;
+    int sl, sh;
+    q8_1_block(v, q, d, sl, sh);
+    uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)b * QB);
+    dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+    dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+    xd[b] = d;
+    if (xs16 != nullptr) {
+        xs16[2 * b] = sl;
+        xs16[2 * b + 1] = sh;
+    }
+}
+
 template <int TT>
-__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __restrict__ x, int m,
-                                                          const uint16_t* __restrict__ wr, int D, int E,
-                                                          float* __restrict__ logits) {
-    const int e = blockIdx.x;
-    const int t0 = blockIdx.y * TT;
+__global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __restrict__ x, int m,
+                                                           const uint16_t* __restrict__ wr, int D, int E, int ntg,
+                                                           float* __restrict__ logits, int8_t* __restrict__ xq,
+                                                           float* __restrict__ xd, int32_t* __restrict__ xs16) {
+    const int nrouter = E * ntg;
+    if ((int)blockIdx.x >= nrouter) {
+        const int b = (blockIdx.x - nrouter) * 256 + threadIdx.x;
+        if (b < m * (D / QB)) quantize_block_bf16(x, b, xq, xd, xs16);
+        return;
+    }
+    const int e = blockIdx.x % E;
+    const int t0 = (blockIdx.x / E) * TT;
     const uint2* w = reinterpret_cast<const uint2*>(wr + (size_t)e * D);
     float acc[TT];
 #pragma unroll
@@ -59,135 +96,156 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- q8_1 of rows
-// One lane per 32-value block of x [m, D] (bf16): int8 quants, fp16(d) as f32,
-// and the two 16-value sums of the quants (used by the Q2_K min term).
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int nblocks,
                                                             int8_t* __restrict__ xq, float* __restrict__ xd,
                                                             int32_t* __restrict__ xs16) {
     const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b >= nblocks) return;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)b * QB);
-    float v[32];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint4 u = src[c];
-        v[8 * c + 0] = bf16_lo(u.x); v[8 * c + 1] = bf16_hi(u.x);
-        v[8 * c + 2] = bf16_lo(u.y); v[8 * c + 3] = bf16_hi(u.y);
-        v[8 * c + 4] = bf16_lo(u.z); v[8 * c + 5] = bf16_hi(u.z);
-        v[8 * c + 6] = bf16_lo(u.w); v[8 * c + 7] = bf16_hi(u.w);
-    }
-    uint32_t q[8];
-    float d;
-    int sl, sh;
-    q8_1_block(v, q, d, sl, sh);
-    uint4* dst = reinterpret_cast<uint4*>(xq + (size_t)b * QB);
-    dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-    dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-    xd[b] = d;
-    if (xs16 != nullptr) {
-        xs16[2 * b] = sl;
-        xs16[2 * b + 1] = sh;
-    }
+    if (b < nblocks) quantize_block_bf16(x, b, xq, xd, xs16);
 }
 
 // ---------------------------------------------------------------- top-k
-// One wavefront per token. Each lane holds the keys of experts lane, lane+64,
-// ... (at most 16 per lane, E <= 1024). k rounds of a wave-wide arg-max with the
-// total order (key descending, id ascending); NaN keys raise the error bit and
-// are ordered as -inf so a pick always exists.
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
-                                                   const float* __restrict__ bias, int m, int E, int k,
-                                                   float gate_temp, int norm, float route_scale,
-                                                   int32_t* __restrict__ idx, float* __restrict__ gw,
-                                                   int32_t* __restrict__ err) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= m) return;
-    float key[16], sc[16];
-    bool nan_seen = false;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = -INFINITY;
-        sc[i] = 0.f;
-        if (e < E) {
-            const float v = logits[(size_t)t * E + e] / gate_temp;
-            const float sp = v > 20.f ? v : log1pf(expf(v));
-            const float s = sqrtf(sp);
-            float kv = s + bias[e];
-            if (kv != kv) {
-                nan_seen = true;
-                kv = -INFINITY;
-            }
-            key[i] = kv;
-            sc[i] = s;
+// Scores and keys: v = z / gate_temp; softplus(v) = v above 20, else ln(1 + e^v);
+// s = sqrt(softplus); key = s + bias. A NaN key raises the error bit and is
+// ordered as -inf, so k picks always exist.
+MOE_DEV void score_key(const float* __restrict__ logits_row, const float* __restrict__ bias, int e, int E,
+                       float gate_temp, float& s, float& key, bool& bad) {
+    key = -INFINITY;
+    s = 0.f;
+    bad = false;
+    if (e < E) {
+        const float v = logits_row[e] / gate_temp;
+        const float sp = v > 20.f ? v : log1pf(expf(v));
+        s = sqrtf(sp);
+        key = s + bias[e];
+        if (key != key) {
+            bad = true;
+            key = -INFINITY;
         }
     }
-    if (__any(nan_seen) && lane == 0) atomicOr(err, ERR_NONFINITE);
-    uint32_t taken = 0;
-    float picked_s = 0.f;   // lane r keeps the score of pick r
-    for (int r = 0; r < k; ++r) {
-        float bk = -INFINITY;
-        int bi = 0x7fffffff;
+}
+
+// rank_e = #{f : key_f > key_e or (key_f == key_e and f < e)} over n (multiple of
+// 16) keys in LDS; the picks are the experts of rank < k, in rank order.
+MOE_DEV int key_rank(const float* keys, int n, float key, int e) {
+    const float4* k4 = reinterpret_cast<const float4*>(keys);
+    int rank = 0;
+    for (int q = 0; q < n / 4; q += 4) {
+        float4 kk[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u)) {
-                if (key[i] > bk || (key[i] == bk && e < bi)) {
-                    bk = key[i];
-                    bi = e;
-                }
-            }
-        }
+        for (int u = 0; u < 4; ++u) kk[u] = k4[q + u];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ok = __shfl_xor(bk, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ok > bk || (ok == bk && oi < bi)) {
-                bk = ok;
-                bi = oi;
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int f = 4 * (q + u);
+            rank += (kk[u].x > key || (kk[u].x == key && f + 0 < e)) ? 1 : 0;
+            rank += (kk[u].y > key || (kk[u].y == key && f + 1 < e)) ? 1 : 0;
+            rank += (kk[u].z > key || (kk[u].z == key && f + 2 < e)) ? 1 : 0;
+            rank += (kk[u].w > key || (kk[u].w == key && f + 3 < e)) ? 1 : 0;
         }
-        // bi is now uniform across the wave
-        const int owner = bi & 63, slot = bi >> 6;
-        float s_owner = 0.f;
-        if (lane == owner) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (i == slot) s_owner = sc[i];
-            taken |= 1u << slot;
-        }
-        const float s_pick = __shfl(s_owner, owner);
-        if (lane == r) picked_s = s_pick;
-        if (lane == 0) idx[(size_t)t * k + r] = bi;
     }
-    // weights: the unbiased scores in pick order, renormalised, scaled
-    float denom = 1.f;
+    return rank;
+}
+
+// Top-k of the n keys in LDS `keys` (n = a multiple of 64, thread e of the group
+// owns key e) in two steps: every wavefront ranks its own 64 keys, the k best
+// of each wavefront become candidates (the overall k best are among them), then
+// each candidate is ranked among all candidates. Writes pick_e / pick_s[0, k).
+// `cand_key` / `cand_id` hold at least n/64 * min(k, 64) entries; `ncand` is an
+// LDS counter. Must be called by every thread of the block (it has barriers);
+// `own` is false for threads outside the group.
+MOE_DEV void topk_two_step(const float* keys, int n, float key, float s, int e, bool own, int k, float* cand_key,
+                           int* cand_id, float* cand_s, int* ncand, int* pick_e, float* pick_s) {
+    const int kw = min(k, 64);
+    if (threadIdx.x == 0) *ncand = 0;
+    __syncthreads();
+    if (own) {
+        const int base = e & ~63;
+        const int wrank = key_rank(keys + base, 64, key, e - base);
+        if (wrank < kw) {
+            const int slot = atomicAdd(ncand, 1);
+            cand_key[slot] = key;
+            cand_id[slot] = e;
+            cand_s[slot] = s;
+        }
+    }
+    __syncthreads();
+    const int nc = *ncand;
+    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+        const float ck = cand_key[c];
+        const int ci = cand_id[c];
+        int rank = 0;
+        int q = 0;
+        for (; q + 8 <= nc; q += 8) {   // eight independent LDS reads per step
+            float qk[8];
+            int qi[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                qk[u] = cand_key[q + u];
+                qi[u] = cand_id[q + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += (qk[u] > ck || (qk[u] == ck && qi[u] < ci)) ? 1 : 0;
+        }
+        for (; q < nc; ++q) {
+            const float qk = cand_key[q];
+            rank += (qk > ck || (qk == ck && cand_id[q] < ci)) ? 1 : 0;
+        }
+        if (rank < k) {
+            pick_e[rank] = ci;
+            pick_s[rank] = cand_s[c];
+        }
+    }
+    __syncthreads();
+}
+
+// weights: the unbiased scores of the picks, divided by (their sum in pick order
+// + 1e-20) when norm and k > 1, times route_scale
+MOE_DEV float pick_weight(const float* pick_s, int r, int k, int norm, float route_scale) {
+    float wgt = pick_s[r];
     if (norm && k > 1) {
         float sum = 0.f;
-        for (int r = 0; r < k; ++r) sum += __shfl(picked_s, r);
-        denom = sum + 1e-20f;
+        for (int q = 0; q < k; ++q) sum += pick_s[q];
+        wgt = wgt / (sum + 1e-20f);
     }
-    if (lane < k) {
-        float wgt = (norm && k > 1) ? picked_s / denom : picked_s;
-        gw[(size_t)t * k + lane] = wgt * route_scale;
+    return wgt * route_scale;
+}
+
+// One workgroup per token, thread e owns expert e (blockDim = E rounded up to 64).
+__global__ __launch_bounds__(1024) void topk_rank_kernel(const float* __restrict__ logits,
+                                                         const float* __restrict__ bias, int E, int k,
+                                                         float gate_temp, int norm, float route_scale,
+                                                         int32_t* __restrict__ idx, float* __restrict__ gw,
+                                                         int32_t* __restrict__ err) {
+    __shared__ __align__(16) float keys[1024];
+    __shared__ float cand_key[1024], cand_s[1024];
+    __shared__ int cand_id[1024];
+    __shared__ float pick_s[64];
+    __shared__ int pick_e[64];
+    __shared__ int ncand;
+    const int t = blockIdx.x;
+    const int e = threadIdx.x;
+    float key, s;
+    bool bad;
+    score_key(logits + (size_t)t * E, bias, e, E, gate_temp, s, key, bad);
+    keys[e] = key;                       // threads >= E pad with -inf (never beat a real key)
+    if (__any(bad) && (e & 63) == 0) atomicOr(err, ERR_NONFINITE);
+    __syncthreads();
+    topk_two_step(keys, (int)blockDim.x, key, s, e, e < E, k, cand_key, cand_id, cand_s, &ncand, pick_e, pick_s);
+    if (e < k) {
+        idx[(size_t)t * k + e] = pick_e[e];
+        gw[(size_t)t * k + e] = pick_weight(pick_s, e, k, norm, route_scale);
     }
 }
 
 // ---------------------------------------------------------------- bucketing
 MOE_DEV int block_exclusive_scan(int v, int* lds, int& total) {
-    // 1024 threads = 16 waves; lds holds 16 ints
+    // any block size up to 1024 (16 wavefronts); lds holds 16 ints
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
+    const int nw = (blockDim.x + 63) >> 6;
+    const int incl = wave_inclusive_scan(v);
     if (lane == 63) lds[wv] = incl;
     __syncthreads();
     int base = 0, tot = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < nw; ++w) {
         const int s = lds[w];
         if (w < wv) base += s;
         tot += s;
@@ -281,17 +339,118 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __rest
     }
 }
 
+// ---------------------------------------------------------------- small batches: top-k + bucketing
+// One workgroup of 1024 threads for m <= 8 tokens: the rank selection for
+// floor(1024 / E') tokens at a time (E' = E rounded up to 64), then the
+// bucketing of the m * k picks (counts, offsets, active experts, chunk list,
+// stable placement) without leaving the workgroup.
+__global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ bias, int m, int E, int k,
+                                                           float gate_temp, int norm, float route_scale,
+                                                           int32_t* __restrict__ idx, float* __restrict__ gw,
+                                                           int32_t* __restrict__ err, int shared_chunks,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ active,
+                                                           int32_t* __restrict__ n_active,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                           Chunk* __restrict__ chunks,
+                                                           int32_t* __restrict__ n_chunks) {
+    __shared__ __align__(16) float keys[1024];
+    __shared__ float cand_key[1024], cand_s[1024];
+    __shared__ int cand_id[1024];
+    __shared__ float pick_s[512];
+    __shared__ int pick_e[512];
+    __shared__ int cnt[1024];
+    __shared__ int offs[1025];
+    __shared__ int scan_lds[16];
+    __shared__ int ncand;
+    const int tid = threadIdx.x;
+    const int Ep = (E + 63) / 64 * 64;
+    bool bad_any = false;
+    for (int t = 0; t < m; ++t) {
+        float s = 0.f, key = -INFINITY;
+        bool bad = false;
+        if (tid < Ep) score_key(logits + (size_t)t * E, bias, tid, E, gate_temp, s, key, bad);
+        if (tid < Ep) keys[tid] = key;
+        bad_any |= bad;
+        __syncthreads();
+        topk_two_step(keys, Ep, key, s, tid, tid < E, k, cand_key, cand_id, cand_s, &ncand, pick_e + t * k,
+                      pick_s + t * k);
+    }
+    if (__any(bad_any) && (tid & 63) == 0) atomicOr(err, ERR_NONFINITE);
+    const int P = m * k;
+    for (int p = tid; p < P; p += 1024) {
+        const int t = p / k, r = p % k;
+        idx[p] = pick_e[p];
+        gw[p] = pick_weight(pick_s + t * k, r, k, norm, route_scale);
+    }
+    cnt[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[pick_e[p]], 1);
+    __syncthreads();
+    const int v = tid < E ? cnt[tid] : 0;
+    int total;
+    const int excl = block_exclusive_scan(v, scan_lds, total);
+    if (tid < E) {
+        offsets[tid] = excl;
+        offs[tid] = excl;
+    }
+    if (tid == 0) {
+        offsets[E] = total;
+        offs[E] = total;
+    }
+    int nact;
+    const int aexcl = block_exclusive_scan((tid < E && v > 0) ? 1 : 0, scan_lds, nact);
+    if (tid < E && v > 0) active[aexcl] = tid;
+    if (tid == 0) *n_active = nact;
+    const int nc = tid < E ? (v + GEMV_ROWS - 1) / GEMV_ROWS : 0;
+    int ntot;
+    const int cexcl = block_exclusive_scan(nc, scan_lds, ntot);
+    for (int q = 0; q < nc; ++q) {
+        Chunk c;
+        c.expert = tid;
+        c.row0 = excl + q * GEMV_ROWS;
+        c.nrows = min(GEMV_ROWS, v - q * GEMV_ROWS);
+        c.pad = 0;
+        chunks[cexcl + q] = c;
+    }
+    const int nsh = shared_chunks ? (m + GEMV_ROWS - 1) / GEMV_ROWS : 0;
+    if (tid < nsh) {
+        Chunk c;
+        c.expert = -1;
+        c.row0 = tid * GEMV_ROWS;
+        c.nrows = min(GEMV_ROWS, m - tid * GEMV_ROWS);
+        c.pad = 0;
+        chunks[ntot + tid] = c;
+    }
+    if (tid == 0) *n_chunks = ntot + nsh;
+    __syncthreads();
+    // stable placement: position = offset of the expert + earlier pairs that picked it
+    for (int p = tid; p < P; p += 1024) {
+        const int pe = pick_e[p];
+        int before = 0;
+        for (int q = 0; q < p; ++q) before += pick_e[q] == pe ? 1 : 0;
+        const int pos = offs[pe] + before;
+        perm[pos] = p;
+        inv[p] = pos;
+    }
+}
+
 // ---------------------------------------------------------------- launchers
-hipError_t launch_router_gemv(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                              hipStream_t st) {
-    if (m == 1) {
-        router_gemv_kernel<1><<<dim3(E, 1), 256, 0, st>>>(x, m, wr, D, E, logits);
-    } else if (m <= 2) {
-        router_gemv_kernel<2><<<dim3(E, 1), 256, 0, st>>>(x, m, wr, D, E, logits);
+hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
+                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st) {
+    const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
+    if (m <= 2) {
+        const int ntg = (m + 1) / 2;
+        if (m == 1)
+            router_quant_kernel<1><<<E + nq, 256, 0, st>>>(x, m, wr, D, E, 1, logits, xq, xd, xs16);
+        else
+            router_quant_kernel<2><<<E * ntg + nq, 256, 0, st>>>(x, m, wr, D, E, ntg, logits, xq, xd, xs16);
     } else if (m <= 4) {
-        router_gemv_kernel<4><<<dim3(E, 1), 256, 0, st>>>(x, m, wr, D, E, logits);
+        router_quant_kernel<4><<<E + nq, 256, 0, st>>>(x, m, wr, D, E, 1, logits, xq, xd, xs16);
     } else {
-        router_gemv_kernel<8><<<dim3(E, (m + 7) / 8), 256, 0, st>>>(x, m, wr, D, E, logits);
+        const int ntg = (m + 7) / 8;
+        router_quant_kernel<8><<<E * ntg + nq, 256, 0, st>>>(x, m, wr, D, E, ntg, logits, xq, xd, xs16);
     }
     return hipGetLastError();
 }
@@ -303,9 +462,19 @@ hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, flo
     return hipGetLastError();
 }
 
+hipError_t launch_route_small(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
+                              int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
+                              int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
+                              Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
+    route_small_kernel<<<1, 1024, 0, st>>>(logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
+                                           shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                        int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st) {
-    topk_kernel<<<(m + 3) / 4, 256, 0, st>>>(logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err);
+    const int threads = (E + 63) / 64 * 64;
+    topk_rank_kernel<<<m, threads, 0, st>>>(logits, bias, E, k, gate_temp, norm, route_scale, idx, gw, err);
     return hipGetLastError();
 }
 
