@@ -1,0 +1,171 @@
+// bf16 MFMA GEMM with f32 accumulation for the batched (m > 8) steps that are
+// plain dense products: the router logits z = x W_R^T, and the bf16 shared
+// expert (gate/up with the clamped-SwiGLU epilogue, then down). The pages use
+// metrale's `gemm` / `gemm_f32out` kernels for these (kernel table of
+// moe_v41.rs); the shared expert's math is the Open Model Atlas
+// "Shared expert" equations with the Expert excerpt's clamps.
+//
+// C[M, N] = A[M, K] B[N, K]^T, both operands K-contiguous bf16. Workgroup tile
+// 64 (A rows) x 128 (B rows) x 64 (K), four wavefronts, each owning 32 B rows;
+// v_mfma_f32_16x16x32_bf16 tiles; LDS double buffer with padded rows.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int BM = 64, BN = 128, BK = 64;
+constexpr int PITCH = BK + 8;   // bf16 elements per LDS row (16 bytes of padding)
+
+enum Epilogue { EPI_F32 = 0, EPI_SWIGLU = 1 };
+
+// one 16-byte chunk per (row, k-chunk); 64 x 8 chunks for A, 128 x 8 for B
+MOE_DEV void load_tile(const uint16_t* __restrict__ src, int rows_valid, int ld, int k0, int nrows,
+                       uint16_t* __restrict__ lds, int tid, uint4* regs, int nreg) {
+    for (int q = 0; q < nreg; ++q) {
+        const int c = tid + q * 256;
+        const int row = c >> 3, kc = c & 7;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < nrows && row < rows_valid)
+            v = *reinterpret_cast<const uint4*>(src + (size_t)row * ld + k0 + kc * 8);
+        regs[q] = v;
+    }
+}
+
+MOE_DEV void store_tile(uint16_t* __restrict__ lds, int tid, const uint4* regs, int nreg) {
+    for (int q = 0; q < nreg; ++q) {
+        const int c = tid + q * 256;
+        const int row = c >> 3, kc = c & 7;
+        *reinterpret_cast<uint4*>(lds + row * PITCH + kc * 8) = regs[q];
+    }
+}
+
+}  // namespace
+
+// EPI_F32:    out f32 [M, N] = A B^T           (B = wa, N rows)
+// EPI_SWIGLU: out bf16 [M, N] = bf16(SwiGLU(A wa^T, A wb^T)); each workgroup takes
+//             64 rows of wa and the same 64 rows of wb as its 128 B rows
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A, int M,
+                                                        const uint16_t* __restrict__ wa,
+                                                        const uint16_t* __restrict__ wb, int N, int K,
+                                                        void* __restrict__ out, float limit) {
+    __shared__ __align__(16) uint16_t sA[2][BM * PITCH];
+    __shared__ __align__(16) uint16_t sB[2][BN * PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int m0 = blockIdx.y * BM;
+    const int rows_per_b = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    const int n0 = blockIdx.x * rows_per_b;
+    const int a_valid = M - m0;
+    // B rows: EPI_F32 -> wa rows n0..n0+127; EPI_SWIGLU -> wa rows n0..n0+63 then wb rows n0..n0+63
+    const uint16_t* Ab = A + (size_t)m0 * K;
+
+    uint4 ra[2], rb[4];
+    auto load_b = [&](int k0) {
+        if (EPI == EPI_SWIGLU) {
+            // chunks 0..511 -> wa rows, 512..1023 -> wb rows
+            for (int q = 0; q < 4; ++q) {
+                const int c = tid + q * 256;
+                const int row = c >> 3, kc = c & 7;
+                const uint16_t* base = row < 64 ? wa + (size_t)(n0 + row) * K : wb + (size_t)(n0 + row - 64) * K;
+                rb[q] = *reinterpret_cast<const uint4*>(base + k0 + kc * 8);
+            }
+        } else {
+            load_tile(wa + (size_t)n0 * K, N - n0, K, k0, BN, nullptr, tid, rb, 4);
+        }
+    };
+    load_tile(Ab, a_valid, K, 0, BM, nullptr, tid, ra, 2);
+    load_b(0);
+    store_tile(sA[0], tid, ra, 2);
+    store_tile(sB[0], tid, rb, 4);
+    __syncthreads();
+
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) {
+            load_tile(Ab, a_valid, K, (kt + 1) * BK, BM, nullptr, tid, ra, 2);
+            load_b((kt + 1) * BK);
+        }
+        const uint16_t* a_s = sA[cur];
+        const uint16_t* b_s = sB[cur];
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            bf16x8_t af[4], bfr[2];
+            const int koff = kk + 8 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + (16 * i + (lane & 15)) * PITCH + koff);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // wave wv owns B rows {16 j' + ...}: for SwiGLU, rows 16 wv.. of wa and the same of wb
+                const int brow = EPI == EPI_SWIGLU ? (j == 0 ? 16 * wv : 64 + 16 * wv) : 32 * wv + 16 * j;
+                bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + (brow + (lane & 15)) * PITCH + koff);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {
+            store_tile(sA[cur ^ 1], tid, ra, 2);
+            store_tile(sB[cur ^ 1], tid, rb, 4);
+        }
+        __syncthreads();
+    }
+
+    // C layout: lane holds column (B row) lane % 16 of the 16x16 tile, rows 4 (lane / 16) + r
+    const int col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + 16 * i + 4 * (lane >> 4) + r;
+            if (row >= M) continue;
+            if (EPI == EPI_SWIGLU) {
+                const int n = n0 + 16 * wv + col;
+                const float h = swiglu(acc[i][0][r], acc[i][1][r], limit);
+                reinterpret_cast<uint16_t*>(out)[(size_t)row * N + n] = (uint16_t)f32_to_bf16(h);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int n = n0 + 32 * wv + 16 * j + col;
+                    if (n < N) reinterpret_cast<float*>(out)[(size_t)row * N + n] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+// logits f32 [m, E] = x W_R^T
+hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
+                              hipStream_t st) {
+    dim3 grid((E + BN - 1) / BN, (m + BM - 1) / BM);
+    gemm_bf16_kernel<EPI_F32><<<grid, 256, 0, st>>>(x, m, wr, wr, E, D, logits, 0.f);
+    return hipGetLastError();
+}
+
+// h bf16 [m, I] = SwiGLU(x W1^T, x W3^T);  ys f32 [m, D] = h W2^T
+hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,
+                                   const uint16_t* w2, uint16_t* h, float* ys, float limit, hipStream_t st) {
+    dim3 g1(I / (BN / 2), (m + BM - 1) / BM);
+    gemm_bf16_kernel<EPI_SWIGLU><<<g1, 256, 0, st>>>(x, m, w1, w3, I, D, h, limit);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 g2(D / BN, (m + BM - 1) / BM);
+    gemm_bf16_kernel<EPI_F32><<<g2, 256, 0, st>>>(h, m, w2, w2, D, I, ys, 0.f);
+    return hipGetLastError();
+}
+
+}  // namespace moe

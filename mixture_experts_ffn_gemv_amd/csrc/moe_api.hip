@@ -37,6 +37,7 @@ struct moe_ctx {
     int device = 0;
     int n_cu = 256;          // compute units of the device
     bool stream_ok = false;  // the streaming GEMVs fit this shape
+    bool mmq_ok = false;     // the MMQ tiles fit this shape
     int max_pairs = 0;
     int max_chunks = 0;   // chunk-list capacity
     uint8_t* dev = nullptr;
@@ -47,6 +48,7 @@ struct moe_ctx {
     int8_t* xq = nullptr;
     float* xd = nullptr;
     int32_t* xs16 = nullptr;
+    float* xs16f = nullptr;
     int32_t* offsets = nullptr;
     int32_t* active = nullptr;
     int32_t* n_active = nullptr;
@@ -119,14 +121,15 @@ void layout_of(const moe_cfg& c, size_t& slot, size_t& o1, size_t& o3, size_t& o
     slot = 2 * n13 + n2;
 }
 
-// upper bound of routed GEMV chunks for m tokens: sum_e ceil(c_e / 8) <= (P + 7 * min(E, P)) / 8
-int routed_chunk_bound(const moe_cfg& c, int m) {
+// upper bound of routed chunks of at most `rows` token rows for m tokens:
+// sum_e ceil(c_e / rows) <= (P + (rows - 1) * min(E, P)) / rows
+int routed_chunk_bound(const moe_cfg& c, int m, int rows = GEMV_ROWS) {
     const int P = m * c.topk;
     const int act = std::min(c.n_routed, P);
-    return (P + (GEMV_ROWS - 1) * act) / GEMV_ROWS + 1;
+    return (P + (rows - 1) * act) / rows + 1;
 }
 
-int shared_chunk_count(int m) { return (m + GEMV_ROWS - 1) / GEMV_ROWS; }
+int shared_chunk_count(int m, int rows = GEMV_ROWS) { return (m + rows - 1) / rows; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -189,13 +192,14 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
     return MOE_OK;
 }
 
-// router logits (+ q8_1(x) when quant) and the top-k into (idx, gw)
-int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int32_t* idx, float* gw, bool quant,
-              hipStream_t st) {
+// router logits and the top-k into (idx, gw) (moe_route)
+int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int32_t* idx, float* gw, hipStream_t st) {
     const moe_cfg& c = ctx->cfg;
     int rc = timed(ctx, st, MOE_K_ROUTER, [&] {
-        return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits,
-                                   quant ? ctx->xq : nullptr, ctx->xd, ctx->xs16, st);
+        if (m <= ROUTE_SMALL_MAX_M)
+            return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, nullptr,
+                                       nullptr, nullptr, st);
+        return launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
     });
     if (rc != MOE_OK) return rc;
     return timed(ctx, st, MOE_K_TOPK, [&] {
@@ -246,6 +250,7 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
             ctx->n_cu = prop.multiProcessorCount;
     }
     ctx->stream_ok = stream_gemv_supported(c.dim, c.inter);
+    ctx->mmq_ok = mmq_supported(c.dim, c.inter);
     const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
     const size_t P = M * c.topk;
     ctx->max_pairs = (int)P;
@@ -259,6 +264,7 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     const size_t o_xq = cv.take<int8_t>(M * D);
     const size_t o_xd = cv.take<float>(M * D / QB);
     const size_t o_xs = cv.take<int32_t>(M * D / 16);
+    const size_t o_xsf = cv.take<float>(M * D / 16);
     const size_t o_off = cv.take<int32_t>(E + 1);
     const size_t o_act = cv.take<int32_t>(E);
     const size_t o_nact = cv.take<int32_t>(1);
@@ -290,6 +296,7 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     ctx->xq = (int8_t*)(b + o_xq);
     ctx->xd = (float*)(b + o_xd);
     ctx->xs16 = (int32_t*)(b + o_xs);
+    ctx->xs16f = (float*)(b + o_xsf);
     ctx->offsets = (int32_t*)(b + o_off);
     ctx->active = (int32_t*)(b + o_act);
     ctx->n_active = (int32_t*)(b + o_nact);
@@ -405,7 +412,7 @@ int moe_route(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m,
     if (m < 1 || m > ctx->cfg.max_tokens || !aligned(x_bf16, 16)) return MOE_EINVAL;
     int rc = check_weights(ctx, w);
     if (rc != MOE_OK) return rc;
-    return run_route(ctx, w, (const uint16_t*)x_bf16, m, idx_out, weights_out, false, (hipStream_t)stream);
+    return run_route(ctx, w, (const uint16_t*)x_bf16, m, idx_out, weights_out, (hipStream_t)stream);
 }
 
 int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
@@ -424,25 +431,36 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     rc = upload_table(ctx, st);
     if (rc != MOE_OK) return rc;
     const bool bf16_shared = w->shared_fmt == MOE_SHARED_BF16;
+    const bool small = m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS;
+    const bool use_mmq = !small && ctx->mmq_ok;
     if (bf16_shared) {
         // the shared expert needs only x: run it beside the routing and the routed experts
         if (hipEventRecord(ctx->ev_fork, st) != hipSuccess || hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0) != hipSuccess)
             return MOE_EHIP;
-        rc = timed(ctx, ctx->side, MOE_K_SHARED_GATEUP, [&] {
-            return launch_shared_bf16_gateup(x, m, c.dim, c.inter, (const uint16_t*)w->shared_w1,
-                                             (const uint16_t*)w->shared_w3, (uint16_t*)ctx->h_shared,
-                                             c.swiglu_limit, ctx->side);
-        });
-        if (rc != MOE_OK) return rc;
-        rc = timed(ctx, ctx->side, MOE_K_SHARED_DOWN, [&] {
-            return launch_shared_bf16_down((const uint16_t*)ctx->h_shared, m, c.dim, c.inter,
-                                           (const uint16_t*)w->shared_w2, ctx->ys, ctx->side);
-        });
+        if (small) {
+            rc = timed(ctx, ctx->side, MOE_K_SHARED_GATEUP, [&] {
+                return launch_shared_bf16_gateup(x, m, c.dim, c.inter, (const uint16_t*)w->shared_w1,
+                                                 (const uint16_t*)w->shared_w3, (uint16_t*)ctx->h_shared,
+                                                 c.swiglu_limit, ctx->side);
+            });
+            if (rc != MOE_OK) return rc;
+            rc = timed(ctx, ctx->side, MOE_K_SHARED_DOWN, [&] {
+                return launch_shared_bf16_down((const uint16_t*)ctx->h_shared, m, c.dim, c.inter,
+                                               (const uint16_t*)w->shared_w2, ctx->ys, ctx->side);
+            });
+        } else {
+            rc = timed(ctx, ctx->side, MOE_K_SHARED_GATEUP, [&] {
+                return launch_shared_bf16_gemm(x, m, c.dim, c.inter, (const uint16_t*)w->shared_w1,
+                                               (const uint16_t*)w->shared_w3, (const uint16_t*)w->shared_w2,
+                                               (uint16_t*)ctx->h_shared, ctx->ys, c.swiglu_limit, ctx->side);
+            });
+        }
         if (rc != MOE_OK) return rc;
         if (hipEventRecord(ctx->ev_join, ctx->side) != hipSuccess) return MOE_EHIP;
     }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
-    if (m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS) {
+    const int chunk_rows = use_mmq ? mmq_chunk_rows(m, c.topk, c.n_routed) : GEMV_ROWS;
+    if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
                                        ctx->xd, ctx->xs16, st);
@@ -456,10 +474,19 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         });
         if (rc != MOE_OK) return rc;
     } else {
-        rc = run_route(ctx, w, x, m, ctx->idx, ctx->gw, true, st);
+        rc = timed(ctx, st, MOE_K_ROUTER, [&] {
+            hipError_t e = launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
+            if (e != hipSuccess) return e;
+            return launch_quantize_rows(x, m, c.dim, ctx->xq, ctx->xd, ctx->xs16, ctx->xs16f, st);
+        });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_TOPK, [&] {
+            return launch_topk(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp, c.norm_topk_prob,
+                               c.route_scale, ctx->idx, ctx->gw, ctx->err, st);
+        });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_BUCKET, [&] {
-            return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, ctx->offsets, ctx->active,
+            return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, chunk_rows, ctx->offsets, ctx->active,
                                  ctx->n_active, ctx->perm, ctx->inv, ctx->chunks, ctx->n_chunks, st);
         });
         if (rc != MOE_OK) return rc;
@@ -482,6 +509,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.xq = ctx->xq;
     a.xd = ctx->xd;
     a.xs16 = ctx->xs16;
+    a.xs16f = ctx->xs16f;
     a.h_routed = ctx->h_routed;
     a.h_shared = ctx->h_shared;
     a.hq_routed = ctx->hq_routed;
@@ -496,18 +524,26 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.I = c.inter;
     a.limit = c.swiglu_limit;
     a.err = ctx->err;
-    const int rows_max = std::min(m, GEMV_ROWS);
-    const int chunks = routed_chunk_bound(c, m) + (kq ? shared_chunk_count(m) : 0);
-    const bool streaming = rows_max <= 1 && ctx->stream_ok;
-    rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, chunks, st); });
-    if (rc != MOE_OK) return rc;
-    rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
-    if (rc != MOE_OK) return rc;
-    rc = timed(ctx, st, MOE_K_DOWN, [&] {
-        return streaming ? launch_down_q3k_stream(a, ctx->n_cu * 2, st)
-                         : launch_down_q3k(a, rows_max, chunks, st);
-    });
-    if (rc != MOE_OK) return rc;
+    const int rows_max = std::min(m, chunk_rows);
+    const int chunks = routed_chunk_bound(c, m, chunk_rows) + (kq ? shared_chunk_count(m, chunk_rows) : 0);
+    if (use_mmq) {
+        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, rows_max, chunks, true, st); });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, rows_max, chunks, false, st); });
+        if (rc != MOE_OK) return rc;
+    } else {
+        const bool streaming = rows_max <= 1 && ctx->stream_ok;
+        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, chunks, st); });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
+        if (rc != MOE_OK) return rc;
+        rc = timed(ctx, st, MOE_K_DOWN, [&] {
+            return streaming ? launch_down_q3k_stream(a, ctx->n_cu * 2, st) : launch_down_q3k(a, rows_max, chunks, st);
+        });
+        if (rc != MOE_OK) return rc;
+    }
     if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
     const float* ys = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
     rc = timed(ctx, st, MOE_K_COMBINE, [&] {
@@ -531,7 +567,8 @@ int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t 
 int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_out, float* d_out, void* stream) {
     if (x_bf16 == nullptr || q_out == nullptr || d_out == nullptr || rows < 1 || cols < QB || cols % QB) return MOE_EINVAL;
     if (!aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(d_out, 4)) return MOE_EINVAL;
-    return hip_status(launch_quantize_rows((const uint16_t*)x_bf16, rows, cols, q_out, d_out, nullptr, (hipStream_t)stream));
+    return hip_status(
+        launch_quantize_rows((const uint16_t*)x_bf16, rows, cols, q_out, d_out, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int moe_check(moe_ctx* ctx, void* stream) {

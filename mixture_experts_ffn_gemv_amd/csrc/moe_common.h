@@ -44,6 +44,7 @@ struct ExpertArgs {
     const int8_t* xq;           // q8_1 of x: int8 [m, D], d f32 [m, D/32], 16-sums i32 [m, D/16]
     const float* xd;
     const int32_t* xs16;
+    const float* xs16f;         // fp16(d) * (sum of each 16 quants) of x, f32 [m, D/16] (MMQ min term)
     float* h_routed;            // f32 [pairs, I] in position order
     float* h_shared;            // f32 [m, I]
     int8_t* hq_routed;          // q8_1 of h_routed: int8 [pairs, I], d f32 [pairs, I/32], 16-sums i32 [pairs, I/16]

@@ -22,7 +22,7 @@ namespace moe {
 // fp16(d) as f32, and the two 16-value sums of the quants used by the Q2_K
 // min term): d = amax / 127, q = round-half-away(x / d).
 MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* __restrict__ xq,
-                                 float* __restrict__ xd, int32_t* __restrict__ xs16) {
+                                 float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f = nullptr) {
     const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)b * QB);
     float v[32];
 #pragma unroll
@@ -44,6 +44,10 @@ MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* 
     if (xs16 != nullptr) {
         xs16[2 * b] = sl;
         xs16[2 * b + 1] = sh;
+    }
+    if (xs16f != nullptr) {   // exact: 11-bit scale times a sum of 16 quants
+        xs16f[2 * b] = d * (float)sl;
+        xs16f[2 * b + 1] = d * (float)sh;
     }
 }
 
@@ -98,9 +102,9 @@ __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __res
 // ---------------------------------------------------------------- q8_1 of rows
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int nblocks,
                                                             int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                            int32_t* __restrict__ xs16) {
+                                                            int32_t* __restrict__ xs16, float* __restrict__ xs16f) {
     const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b < nblocks) quantize_block_bf16(x, b, xq, xd, xs16);
+    if (b < nblocks) quantize_block_bf16(x, b, xq, xd, xs16, xs16f);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -259,7 +263,7 @@ MOE_DEV int block_exclusive_scan(int v, int* lds, int& total) {
 // experts with work, and the chunk list (GEMV_ROWS rows per chunk; the
 // K-quant shared expert's chunks follow the routed ones). One workgroup.
 __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __restrict__ idx, int P, int E,
-                                                            int m, int shared_chunks,
+                                                            int m, int shared_chunks, int rows_per_chunk,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ n_active,
@@ -281,23 +285,23 @@ __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __res
     const int aexcl = block_exclusive_scan((tid < E && v > 0) ? 1 : 0, scan_lds, nact);
     if (tid < E && v > 0) active[aexcl] = tid;
     if (tid == 0) *n_active = nact;
-    const int nc = tid < E ? (v + GEMV_ROWS - 1) / GEMV_ROWS : 0;
+    const int nc = tid < E ? (v + rows_per_chunk - 1) / rows_per_chunk : 0;
     int ntot;
     const int cexcl = block_exclusive_scan(nc, scan_lds, ntot);
     for (int q = 0; q < nc; ++q) {
         Chunk c;
         c.expert = tid;
-        c.row0 = excl + q * GEMV_ROWS;
-        c.nrows = min(GEMV_ROWS, v - q * GEMV_ROWS);
+        c.row0 = excl + q * rows_per_chunk;
+        c.nrows = min(rows_per_chunk, v - q * rows_per_chunk);
         c.pad = 0;
         chunks[cexcl + q] = c;
     }
-    const int nsh = shared_chunks ? (m + GEMV_ROWS - 1) / GEMV_ROWS : 0;
+    const int nsh = shared_chunks ? (m + rows_per_chunk - 1) / rows_per_chunk : 0;
     for (int q = tid; q < nsh; q += 1024) {
         Chunk c;
         c.expert = -1;
-        c.row0 = q * GEMV_ROWS;
-        c.nrows = min(GEMV_ROWS, m - q * GEMV_ROWS);
+        c.row0 = q * rows_per_chunk;
+        c.nrows = min(rows_per_chunk, m - q * rows_per_chunk);
         c.pad = 0;
         chunks[ntot + q] = c;
     }
@@ -456,9 +460,9 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
-                                hipStream_t st) {
+                                float* xs16f, hipStream_t st) {
     const int nb = m * (D / QB);
-    quantize_rows_kernel<<<(nb + 255) / 256, 256, 0, st>>>(x, nb, xq, xd, xs16);
+    quantize_rows_kernel<<<(nb + 255) / 256, 256, 0, st>>>(x, nb, xq, xd, xs16, xs16f);
     return hipGetLastError();
 }
 
@@ -478,12 +482,12 @@ hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int
     return hipGetLastError();
 }
 
-hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, int32_t* offsets,
-                         int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv, Chunk* chunks,
-                         int32_t* n_chunks, hipStream_t st) {
+hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, int rows_per_chunk,
+                         int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
+                         Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
     const int P = m * k;
-    bucket_count_kernel<<<1, 1024, 0, st>>>(idx, P, E, m, shared_chunks, offsets, active, n_active, chunks,
-                                            n_chunks);
+    bucket_count_kernel<<<1, 1024, 0, st>>>(idx, P, E, m, shared_chunks, rows_per_chunk, offsets, active, n_active,
+                                            chunks, n_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bucket_place_kernel<<<E, 256, 0, st>>>(idx, P, offsets, perm, inv);

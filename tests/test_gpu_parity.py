@@ -77,12 +77,27 @@ TINY_VARIANTS = {
 
 
 @pytest.mark.parametrize("variant", list(TINY_VARIANTS))
-@pytest.mark.parametrize("m", [1, 4, 13])
+@pytest.mark.parametrize("m", [1, 4, 13, 70])
 def test_tiny_layer(variant, m):
-    layer = Layer(S.TINY, 0, max_tokens=16, **TINY_VARIANTS[variant])
+    layer = Layer(S.TINY, 0, max_tokens=80, **TINY_VARIANTS[variant])
     try:
         x = S.make_tokens(m, S.TINY.dim, 0, index=m)
         check_layer(layer, x, f"tiny {variant}")
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("shared", ["bf16", "kquant"])
+@pytest.mark.parametrize("m", [150, 330])
+def test_tiny_hot_expert_spans_chunks(shared, m):
+    # every token picks expert 3 first: its group has all m rows, several MMQ chunks
+    # (m=150: 32-row chunks, two sub-tiles; m=330: 64-row chunks, four sub-tiles)
+    layer = Layer(S.TINY, 2, max_tokens=m, shared_fmt=shared)
+    try:
+        layer.bias[3] = 100.0
+        layer.d_bias.copy_(layer.bias.to(layer.dev))
+        rows = sorted({0, 31, 32, 63, 64, 127, 128, m - 1})
+        check_layer(layer, S.make_tokens(m, 256, 2), f"hot expert m={m} {shared}", sample_rows=rows)
     finally:
         layer.close()
 
