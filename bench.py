@@ -3,27 +3,62 @@
 
 Workloads (seeded synthetic inputs at the pages' DeepSeek-V4.1 layer shape:
 dim 5120, inter 2304, 384 routed experts, top-6, Q2_K gate/up and Q3_K down
-blocks, bf16 shared expert):
-  decode  (default): m = 1 token per step; the step cycles a pool of 256 tokens
-          and 4 layers' router + shared expert over one 384-expert pool, so no
-          step finds its weights in the 256 MB last-level cache from the step
-          before (the routed experts differ per token anyway).
-  prefill: m = 512 tokens per step, uniform routing (zero bias).
+blocks; router weights ~N(0, 0.02); expert weights ~N(0, 0.02) before
+quantisation; tokens ~N(0, 1) in bf16):
+  decode       m = 1 per step, bf16 shared expert, bias ~U(-0.05, 0.05). The
+               step cycles a pool of 256 tokens and 4 layers' router + shared
+               expert over one 384-expert pool, so no step finds its weights in
+               the 256 MB last-level cache from the step before (the routed
+               experts differ per token anyway). The headline line.
+  small        m = 8 independent tokens per step, K-quant shared expert.
+  prefill      m = 512 tokens per step, uniform routing (zero bias).
+  prefill_hot  m = 512 with bias +100 on six fixed experts: every token picks
+               them, six groups of 512 rows, the shape where int8 MFMA binds.
 A step is one moe_forward call (every kernel of the layer). Prints one JSON
-line; progress goes to stderr.
+line for the chosen workload; with the decode headline the other three are
+summarised under "workloads" (unless --no-extra). Progress goes to stderr.
+
+--traffic-from FETCH.csv WRITE.csv turns two rocprofv3 --pmc counter files
+(FETCH_SIZE, then WRITE_SIZE, of a run with --copy-calibration) into HBM bytes
+per launch of the workload's dominant kernel and stores them in
+profiles/traffic.json; no GPU is used for that.
 """
 import argparse
+import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+I8_PEAK_OPS = 5.0e15            # MI355X dense int8 MFMA
 METRIC = "MoE layer tokens/s (m=1 GEMV, m=512 MMQ) + expert-weight HBM GB/s vs peak"
+COPY_BYTES = 1 << 30            # the calibration copy reads and writes 1 GiB
+HOT_EXPERTS = (5, 77, 140, 203, 266, 329)
+
+WORKLOADS = {
+    "decode": dict(m=1, layers=4, bias=(-0.05, 0.05), shared="bf16", pool=256,
+                   desc="decode m=1 (GEMV path), bf16 shared expert"),
+    "small": dict(m=8, layers=4, bias=(-0.05, 0.05), shared="kquant", pool=256,
+                  desc="small batch m=8 (GEMV path), K-quant shared expert"),
+    "prefill": dict(m=512, layers=1, bias=None, shared="bf16", pool=512,
+                    desc="prefill m=512 (MMQ path), uniform routing, bf16 shared expert"),
+    "prefill_hot": dict(m=512, layers=1, bias="hot", shared="bf16", pool=512,
+                        desc="prefill m=512 (MMQ path), 6 hot experts take every token, bf16 shared expert"),
+}
+# the kernel each workload's roofline object describes, and its name in rocprofv3
+DOMINANT = {
+    "decode": ("gateup", r"^void moe::gateup_q2k_kernel<1>"),
+    "small": ("gateup", r"^void moe::gateup_q2k_kernel<"),
+    "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
+    "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
+}
+COPY_KERNEL = r"neg_kernel"
 
 
 def log(msg):
@@ -40,22 +75,72 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload, kernel):
-    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
-    on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from rocprofv3 counters, if
+    they were taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(path) as f:
-        rec = json.load(f)
-    ent = rec.get(workload, {}).get(kernel)
+    with open(TRAFFIC_JSON) as f:
+        ent = json.load(f).get(workload)
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(layers, tokens, experts, shape, sample):
-    """The oracle, as it stands, on `sample` steps of the same workload."""
+def traffic_from(fetch_csv, write_csv, workload):
+    """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant
+    kernel by what the same counters read for the 1 GiB calibration copy."""
+    kname = re.compile(DOMINANT[workload][1])
+    copy = re.compile(COPY_KERNEL)
+
+    def per_dispatch(path, counter):
+        ker, cal = {}, {}
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        # the calibration copy: the largest grid among the copy kernel's dispatches
+        copy_grid = max(int(r["Grid_Size"]) for r in rows if copy.search(r["Kernel_Name"]))
+        for row in rows:
+            v = float(row["Counter_Value"])
+            key = row["Dispatch_Id"]
+            if kname.search(row["Kernel_Name"]):
+                ker[key] = ker.get(key, 0.0) + v
+            elif copy.search(row["Kernel_Name"]) and int(row["Grid_Size"]) == copy_grid:
+                cal[key] = cal.get(key, 0.0) + v
+        if not ker or not cal:
+            raise SystemExit(f"{path}: no {counter} rows for the kernel ({len(ker)}) or the copy ({len(cal)})")
+        return sum(ker.values()) / len(ker), sum(cal.values()) / len(cal), len(ker)
+
+    f_k, f_c, n_f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w_k, w_c, n_w = per_dispatch(write_csv, "WRITE_SIZE")
+    copy_kib = COPY_BYTES / 1024.0
+    f_scale, w_scale = copy_kib / f_c, copy_kib / w_c
+    fetch_b = f_k * 1024.0 * f_scale
+    write_b = w_k * 1024.0 * w_scale
+    rec = {}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f)
+    rec[workload] = {
+        "kernel": DOMINANT[workload][1],
+        "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1),
+        "dispatches": [n_f, n_w],
+        "copy_fetch_kib": round(f_c, 1), "copy_write_kib": round(w_c, 1),
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "bytes_per_launch": int(fetch_b + write_b),
+        "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+        "source_hash": kernel_source_hash(),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec[workload]))
+
+
+def cpu_baseline(lay, tokens, experts, shape, sample):
+    """The oracle, as it stands, on `sample` decode steps of the same workload."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -67,13 +152,6 @@ def cpu_baseline(layers, tokens, experts, shape, sample):
 
     cfg = oracle.MoeCfg(shape.dim, shape.inter, shape.n_routed, shape.topk)
     cache = {}
-
-    def expert_bytes(e):
-        if e not in cache:
-            cache[e] = experts[e].cpu().numpy()
-        return cache[e]
-
-    lay = layers[0]
     shared = {"fmt": "bf16", **{k: bits(lay["shared"][k]) for k in ("w1", "w3", "w2")}}
     wr = bits(lay["wr"])
     bias = lay["bias"].cpu().numpy()
@@ -82,15 +160,193 @@ def cpu_baseline(layers, tokens, experts, shape, sample):
     for x in xs:
         idx = oracle.route(cfg, oracle.bf16_bits_to_f64(x), oracle.bf16_bits_to_f64(wr), bias)[0]
         for e in np.unique(idx):
-            expert_bytes(int(e))
+            if int(e) not in cache:
+                cache[int(e)] = experts[int(e)].cpu().numpy()
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for x in xs:
             oracle.moe_layer(cfg, x, wr, bias, lambda e: cache[e], shared)
         dt = time.perf_counter() - t0
     return {"value": sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample} decode tokens (m=1) of layer 0: float64 numpy oracle incl. decoding the "
-                      f"6 picked experts' blocks per token; {dt:.1f} s on one host core"}
+            "sample": f"{sample} decode tokens (m=1) of the first layer: the float64 numpy oracle including "
+                      f"decoding the 6 picked experts' blocks per token; {dt:.1f} s on one host core "
+                      f"(BLAS limited to one thread); host has {os.cpu_count()} logical CPUs"}
+
+
+class Bench:
+    def __init__(self, shape):
+        import torch
+
+        import mixture_experts_ffn_gemv_amd as moe
+        import synthetic as S
+        self.torch, self.moe, self.S = torch, moe, S
+        self.shape = shape
+        self.dev = torch.device("cuda:0")
+        t0 = time.time()
+        self.experts = S.make_experts(shape, 1, device=self.dev)
+        torch.cuda.synchronize()
+        log(f"experts drawn in {time.time() - t0:.1f}s ({self.experts.numel() / 1e9:.2f} GB)")
+        self.slot_bytes = self.experts.shape[1]
+
+    def layers(self, wl):
+        torch, moe, S, shape = self.torch, self.moe, self.S, self.shape
+        spec = WORKLOADS[wl]
+        out = []
+        for li in range(spec["layers"]):
+            seed = 1 if li == 0 else 1000 + li
+            if spec["bias"] == "hot":
+                b = torch.zeros(shape.n_routed, dtype=torch.float32)
+                b[list(HOT_EXPERTS)] = 100.0
+                wr, bias = S.make_router(shape, seed, 0.02, b)
+            else:
+                wr, bias = S.make_router(shape, seed, 0.02, spec["bias"])
+            sh = S.make_shared(shape, seed, spec["shared"])
+            lay = {"wr": wr, "bias": bias, "shared": sh, "d_wr": wr.to(self.dev), "d_bias": bias.to(self.dev)}
+            if spec["shared"] == "bf16":
+                lay["d_sh"] = {k: sh[k].to(self.dev) for k in ("w1", "w3", "w2")}
+                lay["w"] = moe.make_weights(lay["d_wr"], lay["d_bias"], moe.MOE_SHARED_BF16, lay["d_sh"]["w1"],
+                                            lay["d_sh"]["w3"], lay["d_sh"]["w2"])
+            else:
+                slot = sh["slot"].to(self.dev)
+                _, o1, o3, o2 = S.expert_layout(shape)
+                lay["d_sh"] = {"slot": slot}
+                lay["w"] = moe.make_weights(lay["d_wr"], lay["d_bias"], moe.MOE_SHARED_KQUANT, slot[o1:],
+                                            slot[o3:], slot[o2:])
+            out.append(lay)
+        return out
+
+    def run(self, wl, steps, warmup, copy_calibration=False):
+        torch, moe, S, shape = self.torch, self.moe, self.S, self.shape
+        spec = WORKLOADS[wl]
+        m, pool_n = spec["m"], spec["pool"]
+        layers = self.layers(wl)
+        n_layers = len(layers)
+        tokens = S.make_tokens(pool_n, shape.dim, 1, index={"decode": 0, "small": 3}.get(wl, 2))
+        d_tokens = tokens.to(self.dev)
+        cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8))
+        ctx = moe.moe_create(cfg)
+        moe.moe_set_slots(ctx, self.experts, shape.n_routed)
+        for e in range(shape.n_routed):
+            moe.moe_slot_bind(ctx, e, e)
+        out = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
+        idx = torch.empty((m, shape.topk), dtype=torch.int32, device=self.dev)
+        stream = torch.cuda.current_stream()
+        if copy_calibration:
+            # a plain elementwise copy (negation) of known size, for scaling the
+            # HBM byte counters of rocprofv3 --pmc runs
+            src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=self.dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+            del src, dst
+
+        def xs(i):
+            if m == pool_n:
+                return d_tokens
+            j = (i * m) % pool_n
+            return d_tokens[j:j + m]
+
+        def step(i, with_idx=False):
+            lay = layers[i % n_layers]
+            if with_idx:
+                moe.moe_forward_ex(ctx, lay["w"], xs(i), m, out, None, idx, stream)
+            else:
+                moe.moe_forward(ctx, lay["w"], xs(i), m, out, stream)
+
+        for i in range(warmup):
+            step(i)
+        rc = moe.moe_check(ctx)
+        if rc != moe.MOE_OK:
+            raise RuntimeError(f"{wl} warmup: {moe.strerror(rc)}")
+
+        # timed region: K steps bracketed by events on the launch stream
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(steps):
+            step(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_total = ev0.elapsed_time(ev1)
+        rc = moe.moe_check(ctx)
+        if rc != moe.MOE_OK:
+            raise RuntimeError(f"{wl} timed region: {moe.strerror(rc)}")
+
+        # the same K steps again with every kernel launch bracketed by HIP events on
+        # its own stream (the library records them): per-kernel durations
+        moe.moe_set_profiling(ctx, True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            step(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_profiled = ev0.elapsed_time(ev1)
+        ktimes = moe.moe_kernel_times(ctx)
+        moe.moe_set_profiling(ctx, False)
+
+        # distinct experts per step (the algorithmic bytes follow the routing), untimed
+        distinct = []
+        for i in range(min(steps, 64)):
+            step(warmup + i, with_idx=True)
+            distinct.append(len(torch.unique(idx)))
+        torch.cuda.synchronize()
+        moe.moe_destroy(ctx)
+
+        def avg_ms(k):
+            s, n = ktimes[k]
+            return s / n if n else 0.0
+
+        ms_step = ms_total / steps
+        expert_b = self.slot_bytes
+        n_exp = sum(distinct) / len(distinct)
+        q2k_matrix = shape.inter * (shape.dim // 256) * 84
+        shared_b = 3 * shape.dim * shape.inter * 2 if spec["shared"] == "bf16" else expert_b
+        routed_b = n_exp * expert_b
+        expert_bytes = routed_b + shared_b
+        router_b = shape.n_routed * shape.dim * 2
+        expert_ms = sum(avg_ms(k) for k in ("gateup", "down", "shared_gateup", "shared_down"))
+        gateup_bytes = n_exp * 2 * q2k_matrix + (2 * q2k_matrix if spec["shared"] == "kquant" else 0)
+        ga = avg_ms("gateup")
+        res = {
+            "workload": wl,
+            "config": spec["desc"],
+            "m": m,
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": round(ms_step, 5),
+            "tokens_per_s": round(m * steps / (ms_total / 1e3), 2),
+            "layers_in_rotation": n_layers,
+            "token_pool": pool_n,
+            "experts_per_step": n_exp,
+            "expert_weight_bytes_per_step": int(expert_bytes),
+            "expert_kernels_summed_ms": round(expert_ms, 5),
+            "expert_kernels_GB_per_s": round(expert_bytes / (expert_ms / 1e3) / 1e9, 1),
+            "expert_kernels_frac_of_hbm_peak": round(expert_bytes / (expert_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "layer_expert_GB_per_s": round(expert_bytes / (ms_step / 1e3) / 1e9, 1),
+            "layer_all_GB_per_s": round((expert_bytes + router_b) / (ms_step / 1e3) / 1e9, 1),
+            "layer_frac_of_hbm_peak": round(expert_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_step_with_kernel_events": round(ms_profiled / steps, 5),
+            "kernel_avg_ms": {k: round(avg_ms(k), 5) for k in ktimes if ktimes[k][1]},
+            "gateup_bytes_per_launch": int(gateup_bytes),
+            "gateup_avg_launch_ms": round(ga, 5),
+            "gateup_GB_per_s": round(gateup_bytes / (ga / 1e3) / 1e9, 1),
+        }
+        if m > 8:
+            # useful int8 products of the routed experts: 2 ops per multiply-add,
+            # gate + up (2 I D) and down (D I) per pick
+            ops = 2.0 * m * shape.topk * 3 * shape.dim * shape.inter
+            mmq_ms = avg_ms("gateup") + avg_ms("down")
+            res["routed_int8_ops_per_step"] = ops
+            res["mmq_ms"] = round(mmq_ms, 5)
+            res["mmq_i8_TOPS"] = round(ops / (mmq_ms / 1e3) / 1e12, 1)
+            res["mmq_i8_mfma_util"] = round(ops / (mmq_ms / 1e3) / I8_PEAK_OPS, 4)
+            res["mmq_routed_GB_per_s"] = round(routed_b / (mmq_ms / 1e3) / 1e9, 1)
+            res["mmq_frac_of_hbm_peak"] = round(routed_b / (mmq_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+        res["_layers"] = layers
+        res["_tokens"] = tokens
+        return res
 
 
 def main():
@@ -98,170 +354,98 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
-    ap.add_argument("--layers", type=int, default=4, help="layers (router + shared) in rotation (decode)")
-    ap.add_argument("--cpu-sample", type=int, default=2, help="oracle steps for cpu_baseline (0: skip)")
+    ap.add_argument("--workload", choices=tuple(WORKLOADS), default="decode")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' summaries")
+    ap.add_argument("--cpu-sample", type=int, default=4, help="oracle decode steps for cpu_baseline (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB elementwise copy first (for scaling --pmc byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (no sharding, no "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path (no sharding, no "
               "collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
-    import mixture_experts_ffn_gemv_amd as moe
     import synthetic as S
 
     torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    shape = S.REAL
-    decode = args.workload == "decode"
-    m = 1 if decode else 512
-    n_layers = args.layers if decode else 1
+    b = Bench(S.REAL)
+    wl = args.workload
+    log(f"{wl}: {args.warmup} warmup + {args.steps} timed steps")
+    head = b.run(wl, args.steps, args.warmup, copy_calibration=args.copy_calibration)
+    layers, tokens = head.pop("_layers"), head.pop("_tokens")
+    extra = {}
+    if wl == "decode" and not args.no_extra:
+        for other in ("small", "prefill", "prefill_hot"):
+            st = 100 if WORKLOADS[other]["m"] <= 8 else 10
+            log(f"{other}: 5 warmup + {st} timed steps")
+            r = b.run(other, st, 5)
+            r.pop("_layers"), r.pop("_tokens")
+            extra[other] = r
 
-    t0 = time.time()
-    experts = S.make_experts(shape, 1, device=dev)
-    torch.cuda.synchronize()
-    log(f"experts drawn in {time.time() - t0:.1f}s ({experts.numel() / 1e9:.2f} GB)")
-    layers = []
-    for li in range(n_layers):
-        seed = 1 if li == 0 else 1000 + li
-        wr, bias = S.make_router(shape, seed, 0.02, (-0.05, 0.05) if decode else None)
-        sh = S.make_shared(shape, seed, "bf16")
-        lay = {"wr": wr, "bias": bias, "shared": sh,
-               "d_wr": wr.to(dev), "d_bias": bias.to(dev), "d_sh": {k: sh[k].to(dev) for k in ("w1", "w3", "w2")}}
-        lay["w"] = moe.make_weights(lay["d_wr"], lay["d_bias"], moe.MOE_SHARED_BF16, lay["d_sh"]["w1"],
-                                    lay["d_sh"]["w3"], lay["d_sh"]["w2"])
-        layers.append(lay)
-    pool_n = 256 if decode else 512
-    tokens = S.make_tokens(pool_n, shape.dim, 1, index=0 if decode else 2)
-    d_tokens = tokens.to(dev)
-    cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8))
-    ctx = moe.moe_create(cfg)
-    moe.moe_set_slots(ctx, experts, shape.n_routed)
-    for e in range(shape.n_routed):
-        moe.moe_slot_bind(ctx, e, e)
-    out = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=dev)
-    idx = torch.empty((m, shape.topk), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i, with_idx=False):
-        lay = layers[i % n_layers]
-        x = d_tokens[i % pool_n:i % pool_n + 1] if decode else d_tokens
-        if with_idx:
-            moe.moe_forward_ex(ctx, lay["w"], x, m, out, None, idx, stream)
-        else:
-            moe.moe_forward(ctx, lay["w"], x, m, out, stream)
-
-    for i in range(args.warmup):
-        step(i)
-    rc = moe.moe_check(ctx)
-    if rc != moe.MOE_OK:
-        raise RuntimeError(f"warmup: {moe.strerror(rc)}")
-
-    # distinct experts per step (prefill: algorithmic bytes depend on the routing)
-    distinct = []
-    if not decode:
-        for i in range(min(args.steps, 4)):
-            step(i, with_idx=True)
-            distinct.append(len(torch.unique(idx)))
-        torch.cuda.synchronize()
-
-    # timed region: K steps bracketed by events on the launch stream
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    rc = moe.moe_check(ctx)
-    if rc != moe.MOE_OK:
-        raise RuntimeError(f"timed region: {moe.strerror(rc)}")
-
-    # the same K steps again with every kernel launch bracketed by HIP events on
-    # its own stream (the library records them): per-kernel durations
-    moe.moe_set_profiling(ctx, True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_profiled = ev0.elapsed_time(ev1)
-    ktimes = moe.moe_kernel_times(ctx)
-    moe.moe_set_profiling(ctx, False)
-
-    ms_step = ms_total / args.steps
-    value = m * args.steps / (ms_total / 1e3)
-
-    q2k_matrix = shape.inter * (shape.dim // 256) * 84
-    q3k_matrix = shape.dim * (shape.inter // 256) * 110
-    n_exp = shape.topk if decode else sum(distinct) / len(distinct)
-    gateup_bytes = n_exp * 2 * q2k_matrix
-    down_bytes = n_exp * q3k_matrix
-    shared_bytes = 3 * shape.dim * shape.inter * 2
-
-    def avg_ms(k):
-        s, n = ktimes[k]
-        return s / n if n else float("nan")
-
-    ga = avg_ms("gateup")
-    achieved = gateup_bytes / (ga / 1e3) / 1e9
-    traffic = stored_traffic(args.workload, "gateup")
-    expert_ms = sum(avg_ms(k) for k in ("gateup", "down", "shared_gateup", "shared_down"))
-    expert_bytes = gateup_bytes + down_bytes + shared_bytes
+    kname, _ = DOMINANT[wl]
+    ga = head["gateup_avg_launch_ms"]
+    achieved = head["gateup_GB_per_s"]
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": ("decode m=1" if decode else "prefill m=512")
-            + ": dim 5120, inter 2304, 384 routed experts top-6 (Q2_K gate/up, Q3_K down) x q8_1, bf16 shared",
-            "m": m,
-            "layers_in_rotation": n_layers,
-            "token_pool": pool_n,
-            "experts_per_step": n_exp,
+            "workload": head["config"] + ": dim 5120, inter 2304, 384 routed experts top-6 "
+                                         "(Q2_K gate/up, Q3_K down) x q8_1 activations",
+            "m": head["m"],
+            "layers_in_rotation": head["layers_in_rotation"],
+            "token_pool": head["token_pool"],
+            "experts_per_step": head["experts_per_step"],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gateup_q2k (routed gate/up GEMV + SwiGLU)",
-            "achieved": round(achieved, 1),
+            "kernel": ("gateup_q2k" if head["m"] <= 8 else "mmq_gateup_q2k") + " (routed gate/up + SwiGLU)",
+            "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "bytes_per_launch": int(gateup_bytes),
-            "avg_launch_ms": round(ga, 5),
+            "traffic": stored_traffic(wl),
+            "bytes_per_launch": head["gateup_bytes_per_launch"],
+            "avg_launch_ms": ga,
         },
         "expert_kernels": {
-            "bytes_per_step": int(expert_bytes),
-            "summed_ms": round(expert_ms, 5),
-            "GB_per_s": round(expert_bytes / (expert_ms / 1e3) / 1e9, 1),
-            "frac_of_hbm_peak": round(expert_bytes / (expert_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_step": head["expert_weight_bytes_per_step"],
+            "summed_ms": head["expert_kernels_summed_ms"],
+            "GB_per_s": head["expert_kernels_GB_per_s"],
+            "frac_of_hbm_peak": head["expert_kernels_frac_of_hbm_peak"],
         },
-        "layer_GB_per_s": round(expert_bytes / (ms_step / 1e3) / 1e9, 1),
-        "ms_per_step_with_kernel_events": round(ms_profiled / args.steps, 5),
+        "layer_GB_per_s": head["layer_expert_GB_per_s"],
+        "layer_frac_of_hbm_peak": head["layer_frac_of_hbm_peak"],
+        "ms_per_step_with_kernel_events": head["ms_per_step_with_kernel_events"],
         "kernel_timing": "per-kernel HIP events (recorded by the library on each launch's stream) over a "
                          "replay of the same steps right after the timed region",
-        "kernel_avg_ms": {k: round(avg_ms(k), 5) for k in ktimes if ktimes[k][1]},
+        "kernel_avg_ms": head["kernel_avg_ms"],
     }
-    if args.cpu_sample > 0 and decode:
+    for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak"):
+        if k in head:
+            result[k] = head[k]
+    if extra:
+        result["workloads"] = extra
+    if args.cpu_sample > 0 and wl == "decode":
         log("cpu baseline: running the oracle")
-        result["cpu_baseline"] = cpu_baseline(layers, tokens, experts, shape, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(layers[0], tokens, b.experts, b.shape, args.cpu_sample)
     else:
         result["cpu_baseline"] = None
-    moe.moe_destroy(ctx)
     print(json.dumps(result), flush=True)
 
 

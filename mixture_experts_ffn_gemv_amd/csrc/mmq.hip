@@ -3,7 +3,8 @@
 // module documentation: "by default MMQ above" eight rows; kernel table of
 // moe_v41.rs: mmq_q2k_* / mmq_q3k_*).
 //
-// A chunk is one expert with up to MMQ_ROWS token rows. One workgroup computes
+// A chunk is one expert with up to MMQ_ROWS token rows (in three size classes,
+// each launched with the sub-tile count it needs). One workgroup computes
 // 64 output rows of one chunk: gate/up for 64 rows of W1 and the same rows of
 // W3 (then the clamped SwiGLU), or down for 64 rows of W2. Tokens form the A
 // operand (16-row sub-tiles of q8_1 quants), weights the B operand
@@ -327,11 +328,18 @@ static hipError_t launch_mmq_ns(const ExpertArgs& a, int max_chunks, bool gateup
     return hipGetLastError();
 }
 
-hipError_t launch_mmq(const ExpertArgs& a, int rows_max, int max_chunks, bool gateup, hipStream_t st) {
-    if (max_chunks <= 0) return hipSuccess;
-    if (rows_max <= 16) return launch_mmq_ns<1>(a, max_chunks, gateup, st);
-    if (rows_max <= 32) return launch_mmq_ns<2>(a, max_chunks, gateup, st);
-    return launch_mmq_ns<4>(a, max_chunks, gateup, st);
+hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st) {
+    for (int c = 0; c < MMQ_CLASSES; ++c) {
+        if (plan.cap[c] <= 0) continue;
+        ExpertArgs ac = a;
+        ac.chunks = a.chunks + plan.base[c];
+        ac.n_chunks = a.n_chunks + c;
+        const hipError_t e = c == 0   ? launch_mmq_ns<1>(ac, plan.cap[c], gateup, st)
+                             : c == 1 ? launch_mmq_ns<2>(ac, plan.cap[c], gateup, st)
+                                      : launch_mmq_ns<4>(ac, plan.cap[c], gateup, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace moe

@@ -254,7 +254,9 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
     const size_t P = M * c.topk;
     ctx->max_pairs = (int)P;
-    ctx->max_chunks = routed_chunk_bound(c, (int)M) + shared_chunk_count((int)M) + 1;
+    // room for the GEMV list and for the MMQ plan of any m <= max_tokens (both grow with m)
+    ctx->max_chunks = std::max(routed_chunk_bound(c, (int)M) + shared_chunk_count((int)M) + 1,
+                               mmq_chunk_plan((int)M, c.topk, c.n_routed, true).total());
     layout_of(c, ctx->slot_bytes, ctx->off_w1, ctx->off_w3, ctx->off_w2);
 
     Carver cv;
@@ -268,7 +270,7 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     const size_t o_off = cv.take<int32_t>(E + 1);
     const size_t o_act = cv.take<int32_t>(E);
     const size_t o_nact = cv.take<int32_t>(1);
-    const size_t o_nch = cv.take<int32_t>(1);
+    const size_t o_nch = cv.take<int32_t>(MMQ_CLASSES);
     const size_t o_perm = cv.take<int32_t>(P);
     const size_t o_inv = cv.take<int32_t>(P);
     const size_t o_ch = cv.take<Chunk>(ctx->max_chunks);
@@ -459,7 +461,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (hipEventRecord(ctx->ev_join, ctx->side) != hipSuccess) return MOE_EHIP;
     }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
-    const int chunk_rows = use_mmq ? mmq_chunk_rows(m, c.topk, c.n_routed) : GEMV_ROWS;
+    const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq);
     if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
@@ -486,7 +488,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_BUCKET, [&] {
-            return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, chunk_rows, ctx->offsets, ctx->active,
+            return launch_bucket(ctx->idx, m, c.topk, c.n_routed, kq ? 1 : 0, use_mmq ? &plan : nullptr, ctx->offsets, ctx->active,
                                  ctx->n_active, ctx->perm, ctx->inv, ctx->chunks, ctx->n_chunks, st);
         });
         if (rc != MOE_OK) return rc;
@@ -524,14 +526,14 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.I = c.inter;
     a.limit = c.swiglu_limit;
     a.err = ctx->err;
-    const int rows_max = std::min(m, chunk_rows);
-    const int chunks = routed_chunk_bound(c, m, chunk_rows) + (kq ? shared_chunk_count(m, chunk_rows) : 0);
+    const int rows_max = std::min(m, GEMV_ROWS);
+    const int chunks = routed_chunk_bound(c, m) + (kq ? shared_chunk_count(m) : 0);
     if (use_mmq) {
-        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, rows_max, chunks, true, st); });
+        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, plan, true, st); });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
         if (rc != MOE_OK) return rc;
-        rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, rows_max, chunks, false, st); });
+        rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, plan, false, st); });
         if (rc != MOE_OK) return rc;
     } else {
         const bool streaming = rows_max <= 1 && ctx->stream_ok;

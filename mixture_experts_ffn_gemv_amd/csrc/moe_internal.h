@@ -20,6 +20,33 @@ struct GemvGeom {
 GemvGeom gateup_geom(int D, int I);
 GemvGeom down_geom(int D, int I);
 
+constexpr int MMQ_ROWS = 64;   // the most token rows one MMQ chunk holds (four 16-row sub-tiles)
+// MMQ chunk classes by expert-group size: a group of <= 16 rows is one chunk of
+// class 0 (one sub-tile), 17..32 rows one chunk of class 1 (two sub-tiles),
+// more rows are 64-row chunks of class 2 (four sub-tiles, the last one
+// ragged). Each class is launched with its own kernel instance, so chunks of
+// lightly used experts do not carry the registers of four sub-tiles.
+constexpr int MMQ_CLASSES = 3;
+constexpr int MMQ_CLASS_MAX[MMQ_CLASSES] = {16, 32, MMQ_ROWS};
+struct ChunkPlan {
+    int base[MMQ_CLASSES];   // first slot of each class in the chunk array
+    int cap[MMQ_CLASSES];    // slots reserved (an upper bound of the class's chunks)
+    int total() const { return base[MMQ_CLASSES - 1] + cap[MMQ_CLASSES - 1]; }
+};
+// P = m * k picks over E experts; `shared` adds the K-quant shared expert's m rows
+inline ChunkPlan mmq_chunk_plan(int m, int k, int E, bool shared) {
+    const int P = m * k, act = P < E ? P : E;
+    ChunkPlan pl;
+    pl.cap[0] = act + (shared && m <= 16 ? 1 : 0);
+    pl.cap[1] = P / 17 + (shared && m > 16 && m <= 32 ? 1 : 0);
+    // groups of v > 32 rows: sum ceil(v / 64) <= P / 64 + (number of such groups) <= P / 64 + P / 33
+    pl.cap[2] = P / MMQ_ROWS + P / 33 + 1 + (shared && m > 32 ? (m + MMQ_ROWS - 1) / MMQ_ROWS : 0);
+    pl.base[0] = 0;
+    pl.base[1] = pl.cap[0];
+    pl.base[2] = pl.cap[0] + pl.cap[1];
+    return pl;
+}
+
 // router logits for m tokens, plus q8_1 of x in the same launch when xq != NULL
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                                int8_t* xq, float* xd, int32_t* xs16, hipStream_t st);
@@ -34,20 +61,14 @@ hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, flo
                                 float* xs16f, hipStream_t st);
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp, int norm,
                        float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st);
-// chunks of at most rows_per_chunk token rows (GEMV_ROWS for the GEMVs, MMQ_ROWS for the MMQ)
-hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, int rows_per_chunk,
+// plan == nullptr: one chunk list of at most GEMV_ROWS rows per chunk (n_chunks[0]);
+// otherwise the three MMQ classes at plan->base[c], counts in n_chunks[c]
+hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st);
-constexpr int MMQ_ROWS = 64;   // the most token rows one MMQ chunk holds (four 16-row sub-tiles)
-// MMQ chunk height for a batch: the 16-row sub-tile count per chunk follows the
-// mean rows per expert, so that chunks of lightly used experts do not carry the
-// registers of four sub-tiles (a heavy expert is split into several chunks)
-inline int mmq_chunk_rows(int m, int k, int E) {
-    const long mean = ((long)m * k + E - 1) / E;
-    return mean <= 16 ? 16 : mean <= 40 ? 32 : MMQ_ROWS;
-}
 bool mmq_supported(int D, int I);
-hipError_t launch_mmq(const ExpertArgs& a, int rows_max, int max_chunks, bool gateup, hipStream_t st);
+// one launch per class with reserved slots; a.chunks / a.n_chunks point at class 0
+hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st);
 hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                               hipStream_t st);
 hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,

@@ -260,11 +260,14 @@ MOE_DEV int block_exclusive_scan(int v, int* lds, int& total) {
 }
 
 // Counts per expert, the exclusive scan into offsets, the ascending list of
-// experts with work, and the chunk list (GEMV_ROWS rows per chunk; the
-// K-quant shared expert's chunks follow the routed ones). One workgroup.
+// experts with work, and the chunk list(s); the K-quant shared expert's chunks
+// follow the routed ones of their list. classes == 0: one list of
+// GEMV_ROWS-row chunks. classes == 1: the three MMQ size classes (a group of
+// <= 16 rows, of 17..32 rows, or 64-row chunks of a larger group), class c at
+// chunks + base_c. One workgroup.
 __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __restrict__ idx, int P, int E,
-                                                            int m, int shared_chunks, int rows_per_chunk,
-                                                            int32_t* __restrict__ offsets,
+                                                            int m, int shared_chunks, int classes, int base1,
+                                                            int base2, int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ n_active,
                                                             Chunk* __restrict__ chunks,
@@ -285,27 +288,40 @@ __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __res
     const int aexcl = block_exclusive_scan((tid < E && v > 0) ? 1 : 0, scan_lds, nact);
     if (tid < E && v > 0) active[aexcl] = tid;
     if (tid == 0) *n_active = nact;
-    const int nc = tid < E ? (v + rows_per_chunk - 1) / rows_per_chunk : 0;
-    int ntot;
-    const int cexcl = block_exclusive_scan(nc, scan_lds, ntot);
-    for (int q = 0; q < nc; ++q) {
-        Chunk c;
-        c.expert = tid;
-        c.row0 = excl + q * rows_per_chunk;
-        c.nrows = min(rows_per_chunk, v - q * rows_per_chunk);
-        c.pad = 0;
-        chunks[cexcl + q] = c;
+    // a group of n rows: class and chunk height
+    auto cls_of = [&](int n) { return classes == 0 ? 0 : n <= MMQ_CLASS_MAX[0] ? 0 : n <= MMQ_CLASS_MAX[1] ? 1 : 2; };
+    auto rows_of = [&](int c) { return classes == 0 ? GEMV_ROWS : MMQ_CLASS_MAX[c]; };
+    const int base[3] = {0, base1, base2};
+    const int ncls = classes == 0 ? 1 : MMQ_CLASSES;
+    const int my_cls = cls_of(v);
+    const int my_rows = rows_of(my_cls);
+    const int nc = (tid < E && v > 0) ? (v + my_rows - 1) / my_rows : 0;
+    const int sh_cls = cls_of(m), sh_rows = rows_of(sh_cls);
+    const int nsh = shared_chunks ? (m + sh_rows - 1) / sh_rows : 0;
+    for (int c = 0; c < ncls; ++c) {
+        int ntot;
+        const int cexcl = block_exclusive_scan(my_cls == c ? nc : 0, scan_lds, ntot);
+        if (my_cls == c) {
+            for (int q = 0; q < nc; ++q) {
+                Chunk ch;
+                ch.expert = tid;
+                ch.row0 = excl + q * my_rows;
+                ch.nrows = min(my_rows, v - q * my_rows);
+                ch.pad = 0;
+                chunks[base[c] + cexcl + q] = ch;
+            }
+        }
+        const int nsh_c = sh_cls == c ? nsh : 0;
+        for (int q = tid; q < nsh_c; q += 1024) {
+            Chunk ch;
+            ch.expert = -1;
+            ch.row0 = q * sh_rows;
+            ch.nrows = min(sh_rows, m - q * sh_rows);
+            ch.pad = 0;
+            chunks[base[c] + ntot + q] = ch;
+        }
+        if (tid == 0) n_chunks[c] = ntot + nsh_c;
     }
-    const int nsh = shared_chunks ? (m + rows_per_chunk - 1) / rows_per_chunk : 0;
-    for (int q = tid; q < nsh; q += 1024) {
-        Chunk c;
-        c.expert = -1;
-        c.row0 = q * rows_per_chunk;
-        c.nrows = min(rows_per_chunk, m - q * rows_per_chunk);
-        c.pad = 0;
-        chunks[ntot + q] = c;
-    }
-    if (tid == 0) *n_chunks = ntot + nsh;
 }
 
 // Stable placement: workgroup e lists the pairs that picked expert e in pair
@@ -482,12 +498,12 @@ hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int
     return hipGetLastError();
 }
 
-hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, int rows_per_chunk,
+hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
     const int P = m * k;
-    bucket_count_kernel<<<1, 1024, 0, st>>>(idx, P, E, m, shared_chunks, rows_per_chunk, offsets, active, n_active,
-                                            chunks, n_chunks);
+    bucket_count_kernel<<<1, 1024, 0, st>>>(idx, P, E, m, shared_chunks, plan ? 1 : 0, plan ? plan->base[1] : 0,
+                                            plan ? plan->base[2] : 0, offsets, active, n_active, chunks, n_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bucket_place_kernel<<<E, 256, 0, st>>>(idx, P, offsets, perm, inv);

@@ -88,16 +88,16 @@ def test_tiny_layer(variant, m):
 
 
 @pytest.mark.parametrize("shared", ["bf16", "kquant"])
-@pytest.mark.parametrize("m", [150, 330])
+@pytest.mark.parametrize("m", [24, 40, 150, 330])
 def test_tiny_hot_expert_spans_chunks(shared, m):
-    # every token picks expert 3 first: its group has all m rows, several MMQ chunks
-    # (m=150: 32-row chunks, two sub-tiles; m=330: 64-row chunks, four sub-tiles)
+    # every token picks expert 3 first, so its group holds all m rows: one chunk of
+    # the 17..32-row class (m=24), one ragged 64-row chunk (m=40), or several 64-row
+    # chunks (m=150, 330); the other experts' groups fall in the smaller classes
     layer = Layer(S.TINY, 2, max_tokens=m, shared_fmt=shared)
     try:
         layer.bias[3] = 100.0
         layer.d_bias.copy_(layer.bias.to(layer.dev))
-        rows = sorted({0, 31, 32, 63, 64, 127, 128, m - 1})
-        check_layer(layer, S.make_tokens(m, 256, 2), f"hot expert m={m} {shared}", sample_rows=rows)
+        check_layer(layer, S.make_tokens(m, 256, 2), f"hot expert m={m} {shared}")
     finally:
         layer.close()
 
