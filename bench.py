@@ -432,8 +432,9 @@ def main():
         "layer_GB_per_s": head["layer_expert_GB_per_s"],
         "layer_frac_of_hbm_peak": head["layer_frac_of_hbm_peak"],
         "ms_per_step_with_kernel_events": head["ms_per_step_with_kernel_events"],
-        "kernel_timing": "per-kernel HIP events (recorded by the library on each launch's stream) over a "
-                         "replay of the same steps right after the timed region",
+        "kernel_timing": "per-kernel start/stop HIP events carried by each launch (hipExtLaunchKernel: the "
+                         "kernel's own begin/end timestamps) over a replay of the same steps right after "
+                         "the timed region",
         "kernel_avg_ms": head["kernel_avg_ms"],
     }
     for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak"):

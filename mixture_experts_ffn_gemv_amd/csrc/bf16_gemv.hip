@@ -132,7 +132,7 @@ static hipError_t launch_rows(const uint16_t* act, int m, int K, const uint16_t*
     const size_t lds = (size_t)R * NM * (L / RG) * T * sizeof(float);
     const int tiles = N / R;
     const int tchunks = (m + GEMV_ROWS - 1) / GEMV_ROWS;
-    bf16_rows_kernel<NM, T><<<tiles * tchunks, lanes * P, lds, st>>>(act, m, K, wa, wb, N, R, P, RG, out, limit);
+    launch_kernel(bf16_rows_kernel<NM, T>, tiles * tchunks, lanes * P, lds, st, act, m, K, wa, wb, N, R, P, RG, out, limit);
     return hipGetLastError();
 }
 

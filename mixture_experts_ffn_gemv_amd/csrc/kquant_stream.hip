@@ -464,13 +464,13 @@ bool stream_gemv_supported(int D, int I) {
 // one token row per chunk (the decode arm; wider chunks use the general GEMVs)
 hipError_t launch_gateup_q2k_stream(const ExpertArgs& a, int n_wg, hipStream_t st) {
     const StreamGeom g = gateup_stream_geom(a.D, a.I, 1);
-    gateup_q2k_stream_kernel<1><<<n_wg, g.threads, g.lds, st>>>(a, g.R, g.P, g.RG);
+    launch_kernel(gateup_q2k_stream_kernel<1>, n_wg, g.threads, g.lds, st, a, g.R, g.P, g.RG);
     return hipGetLastError();
 }
 
 hipError_t launch_down_q3k_stream(const ExpertArgs& a, int n_wg, hipStream_t st) {
     const StreamGeom g = down_stream_geom(a.D, a.I, 1);
-    down_q3k_stream_kernel<1><<<n_wg, g.threads, g.lds, st>>>(a, g.R, g.P, g.RG);
+    launch_kernel(down_q3k_stream_kernel<1>, n_wg, g.threads, g.lds, st, a, g.R, g.P, g.RG);
     return hipGetLastError();
 }
 

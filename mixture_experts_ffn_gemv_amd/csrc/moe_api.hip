@@ -15,6 +15,8 @@
 
 using namespace moe;
 
+thread_local LaunchTimer* moe::g_launch_timer = nullptr;
+
 namespace {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -144,21 +146,30 @@ hipEvent_t prof_event(moe_ctx* ctx) {
     return ctx->ev_pool[ctx->ev_next++];
 }
 
-// launch through `fn` (returns hipError_t), bracketed by events when profiling
+// with profiling on, the kernels `fn` launches (it returns hipError_t) carry
+// start/stop events recorded as kernel class `kind`
+struct ClassTimer final : LaunchTimer {
+    moe_ctx* ctx;
+    int kind;
+    bool next_pair(hipEvent_t* start, hipEvent_t* stop) override {
+        *start = prof_event(ctx);
+        *stop = prof_event(ctx);
+        if (*start == nullptr || *stop == nullptr) return false;
+        ctx->marks.push_back({kind, *start, *stop});
+        return true;
+    }
+};
+
 template <typename F>
-int timed(moe_ctx* ctx, hipStream_t st, int kind, F fn) {
-    hipEvent_t a = nullptr, b = nullptr;
-    if (ctx->prof) {
-        a = prof_event(ctx);
-        b = prof_event(ctx);
-        if (a == nullptr || b == nullptr || hipEventRecord(a, st) != hipSuccess) return MOE_EHIP;
-    }
-    if (fn() != hipSuccess) return MOE_EHIP;
-    if (ctx->prof) {
-        if (hipEventRecord(b, st) != hipSuccess) return MOE_EHIP;
-        ctx->marks.push_back({kind, a, b});
-    }
-    return MOE_OK;
+int timed(moe_ctx* ctx, hipStream_t, int kind, F fn) {
+    if (!ctx->prof) return fn() == hipSuccess ? MOE_OK : MOE_EHIP;
+    ClassTimer t;
+    t.ctx = ctx;
+    t.kind = kind;
+    g_launch_timer = &t;
+    const hipError_t e = fn();
+    g_launch_timer = nullptr;
+    return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 int upload_table(moe_ctx* ctx, hipStream_t st) {

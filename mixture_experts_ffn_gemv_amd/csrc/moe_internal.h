@@ -1,12 +1,34 @@
 // Launchers shared between the kernel translation units and the host library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "moe_common.h"
 
 namespace moe {
+
+// Per-kernel timing. While a sink is installed on the calling thread, every
+// launch below carries a start and a stop event that take the kernel's own
+// begin and end timestamps (hipExtLaunchKernel), the interval a kernel trace
+// reports; the sink supplies the events and remembers them.
+struct LaunchTimer {
+    virtual bool next_pair(hipEvent_t* start, hipEvent_t* stop) = 0;
+};
+extern thread_local LaunchTimer* g_launch_timer;
+
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
+    if (g_launch_timer != nullptr) {
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (!g_launch_timer->next_pair(&e0, &e1)) return hipErrorOutOfMemory;
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, static_cast<P>(args)...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, static_cast<P>(args)...);
+    }
+    return hipGetLastError();
+}
 
 struct GemvGeom {
     int P;          // rows processed in parallel

@@ -463,14 +463,14 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
     if (m <= 2) {
         const int ntg = (m + 1) / 2;
         if (m == 1)
-            router_quant_kernel<1><<<E + nq, 256, 0, st>>>(x, m, wr, D, E, 1, logits, xq, xd, xs16);
+            launch_kernel(router_quant_kernel<1>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
         else
-            router_quant_kernel<2><<<E * ntg + nq, 256, 0, st>>>(x, m, wr, D, E, ntg, logits, xq, xd, xs16);
+            launch_kernel(router_quant_kernel<2>, E * ntg + nq, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd, xs16);
     } else if (m <= 4) {
-        router_quant_kernel<4><<<E + nq, 256, 0, st>>>(x, m, wr, D, E, 1, logits, xq, xd, xs16);
+        launch_kernel(router_quant_kernel<4>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
     } else {
         const int ntg = (m + 7) / 8;
-        router_quant_kernel<8><<<E * ntg + nq, 256, 0, st>>>(x, m, wr, D, E, ntg, logits, xq, xd, xs16);
+        launch_kernel(router_quant_kernel<8>, E * ntg + nq, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd, xs16);
     }
     return hipGetLastError();
 }
@@ -478,7 +478,7 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
                                 float* xs16f, hipStream_t st) {
     const int nb = m * (D / QB);
-    quantize_rows_kernel<<<(nb + 255) / 256, 256, 0, st>>>(x, nb, xq, xd, xs16, xs16f);
+    launch_kernel(quantize_rows_kernel, (nb + 255) / 256, 256, 0, st, x, nb, xq, xd, xs16, xs16f);
     return hipGetLastError();
 }
 
@@ -486,7 +486,7 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                               Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
-    route_small_kernel<<<1, 1024, 0, st>>>(logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
+    launch_kernel(route_small_kernel, 1, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
                                            shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks);
     return hipGetLastError();
 }
@@ -494,7 +494,7 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                        int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st) {
     const int threads = (E + 63) / 64 * 64;
-    topk_rank_kernel<<<m, threads, 0, st>>>(logits, bias, E, k, gate_temp, norm, route_scale, idx, gw, err);
+    launch_kernel(topk_rank_kernel, m, threads, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, idx, gw, err);
     return hipGetLastError();
 }
 
@@ -502,11 +502,11 @@ hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chu
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
     const int P = m * k;
-    bucket_count_kernel<<<1, 1024, 0, st>>>(idx, P, E, m, shared_chunks, plan ? 1 : 0, plan ? plan->base[1] : 0,
+    launch_kernel(bucket_count_kernel, 1, 1024, 0, st, idx, P, E, m, shared_chunks, plan ? 1 : 0, plan ? plan->base[1] : 0,
                                             plan ? plan->base[2] : 0, offsets, active, n_active, chunks, n_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    bucket_place_kernel<<<E, 256, 0, st>>>(idx, P, offsets, perm, inv);
+    launch_kernel(bucket_place_kernel, E, 256, 0, st, idx, P, offsets, perm, inv);
     return hipGetLastError();
 }
 
