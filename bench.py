@@ -294,9 +294,9 @@ class Bench:
         torch.cuda.synchronize()
         moe.moe_destroy(ctx)
 
-        def avg_ms(k):
+        def avg_ms(k):   # per step: a class may launch several kernels per call
             s, n = ktimes[k]
-            return s / n if n else 0.0
+            return s / steps if n else 0.0
 
         ms_step = ms_total / steps
         expert_b = self.slot_bytes

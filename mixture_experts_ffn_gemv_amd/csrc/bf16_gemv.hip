@@ -132,8 +132,7 @@ static hipError_t launch_rows(const uint16_t* act, int m, int K, const uint16_t*
     const size_t lds = (size_t)R * NM * (L / RG) * T * sizeof(float);
     const int tiles = N / R;
     const int tchunks = (m + GEMV_ROWS - 1) / GEMV_ROWS;
-    launch_kernel(bf16_rows_kernel<NM, T>, tiles * tchunks, lanes * P, lds, st, act, m, K, wa, wb, N, R, P, RG, out, limit);
-    return hipGetLastError();
+    return launch_kernel(bf16_rows_kernel<NM, T>, tiles * tchunks, lanes * P, lds, st, act, m, K, wa, wb, N, R, P, RG, out, limit);
 }
 
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int m, int D, int I, const uint16_t* w1,

@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* e_rows, const float* ys, const float* gw, const int32_t* inv, int m,
                           int k, int D, uint16_t* out, hipStream_t st) {
     const int n4 = D / 4;
-    launch_kernel(combine_kernel, dim3((n4 + 255) / 256, m), 256, 0, st, e_rows, ys, gw, inv, k, D, out);
-    return hipGetLastError();
+    return launch_kernel(combine_kernel, dim3((n4 + 255) / 256, m), 256, 0, st, e_rows, ys, gw, inv, k, D, out);
 }
 
 }  // namespace moe

@@ -152,20 +152,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                               hipStream_t st) {
     dim3 grid((E + BN - 1) / BN, (m + BM - 1) / BM);
-    launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, 0, st, x, m, wr, wr, E, D, logits, 0.f);
-    return hipGetLastError();
+    return launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, 0, st, x, m, wr, wr, E, D, logits, 0.f);
 }
 
 // h bf16 [m, I] = SwiGLU(x W1^T, x W3^T);  ys f32 [m, D] = h W2^T
 hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,
                                    const uint16_t* w2, uint16_t* h, float* ys, float limit, hipStream_t st) {
     dim3 g1(I / (BN / 2), (m + BM - 1) / BM);
-    launch_kernel(gemm_bf16_kernel<EPI_SWIGLU>, g1, 256, 0, st, x, m, w1, w3, I, D, h, limit);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(gemm_bf16_kernel<EPI_SWIGLU>, g1, 256, 0, st, x, m, w1, w3, I, D, h, limit);
     if (e != hipSuccess) return e;
     dim3 g2(D / BN, (m + BM - 1) / BM);
-    launch_kernel(gemm_bf16_kernel<EPI_F32>, g2, 256, 0, st, h, m, w2, w2, D, I, ys, 0.f);
-    return hipGetLastError();
+    return launch_kernel(gemm_bf16_kernel<EPI_F32>, g2, 256, 0, st, h, m, w2, w2, D, I, ys, 0.f);
 }
 
 }  // namespace moe

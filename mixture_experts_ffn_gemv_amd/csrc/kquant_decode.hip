@@ -1,0 +1,361 @@
+// Expert kernels of the decode path (m <= 8 tokens). Every chunk is a single
+// row: one (token, pick) pair of a routed expert, or one token of a K-quant
+// shared expert, with its slot, token and routing weight resolved when the
+// routing made it. The arithmetic is the GEMV of the pages (GGUF Q2_K / Q3_K
+// superblocks read directly against q8_1 activations; metrale moe_v41 module
+// documentation; kernel table of moe_v41.rs: mmvq_q2k_experts /
+// mmvq_q3k_experts for all selected experts in one launch per projection,
+// swiglu_q8 for the SwiGLU and the q8_1 rows of its output in one launch,
+// accumulate / finish for the weighted sum).
+//
+//  gateup_q8_kernel:   one workgroup = one chunk x 32 rows of the inter
+//      dimension, W1 and W3, streamed as four 8-row sub-tiles through LDS;
+//      the epilogue applies the clamped SwiGLU and writes the q8_1 block the
+//      32 values of h form (no f32 h in memory).
+//  down_combine_kernel: one workgroup = 8 rows of the output dimension for
+//      every chunk. It streams the chunks' Q3_K rows and q8_1(h) records in
+//      groups, accumulates G * E per token in a fixed order (the chunks'
+//      order, then the shared expert's f32 output), and stores bf16.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int GU_TILE = 32;   // rows of I per gate/up workgroup: one q8_1 block of h
+constexpr int GU_SUB = 8;     // rows per sub-tile
+constexpr int DC_ROWS = 8;    // output rows per down workgroup
+constexpr int DC_GROUP = 2;   // chunks streamed together by the down workgroup
+constexpr int DC_NPF = 3;     // 16-byte loads per thread per group
+
+// bytes of one q8_1 record of an h row: quants, then the f32 scales, then the
+// 16-value sums
+MOE_DEV int rec_bytes(int I) { return I + (I / QB) * 4 + (I / 16) * 4; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ Q2_K gate/up -> q8_1(h)
+// One workgroup = one chunk x 32 rows of the inter dimension (one q8_1 block
+// of h), W1 and W3, as four 8-row sub-tiles staged through LDS with coalesced
+// 16-byte loads; the next sub-tile's loads are in flight while the current
+// one is computed. (Requesting all four sub-tiles at once was measured
+// slower: every workgroup then starts its arithmetic late.)
+// Lanes: tid = mtx * L + kb (L = D / 32; mtx 0 = W1, 1 = W3): lane kb holds
+// q8_1 block kb of x (plane j = kb & 3 of half hh of superblock s) in
+// registers and, per row, dots it with that plane's 32 two-bit weights.
+__global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int routed_rows) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int D = a.D, I = a.I;
+    const int L = D / QB;
+    const int nsb = D / QK;
+    const int rowbytes = nsb * Q2K_BYTES;
+    const int tiles = I / GU_TILE;
+    const int c = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int nch = *a.n_chunks;
+    if (c >= nch) return;
+    const Chunk ch = a.chunks[c];
+    const bool shared = ch.expert < 0;
+    const int r0 = tile * GU_TILE;
+    const int rec = rec_bytes(I);
+    uint8_t* out = a.hrec + (size_t)(shared ? routed_rows + ch.row0 : ch.row0) * rec;
+    const int tid = threadIdx.x, bd = blockDim.x;
+    const uint8_t *w1, *w3;
+    if (shared) {
+        w1 = a.sh_w1;
+        w3 = a.sh_w3;
+    } else {
+        if (ch.slot < 0) {   // not resident: flag it, and this block of h is zero
+            if (tid == 0 && tile == 0) atomicOr(a.err, ERR_NOTRESIDENT);
+            if (tid < GU_TILE / 4) reinterpret_cast<uint32_t*>(out + r0)[tid] = 0u;
+            if (tid == 0) {
+                reinterpret_cast<float*>(out + I)[tile] = 0.f;
+                reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile] = 0;
+                reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile + 1] = 0;
+            }
+            return;
+        }
+        const uint8_t* base = a.arena + (size_t)ch.slot * a.slot_bytes;
+        w1 = base + a.off_w1;
+        w3 = base + a.off_w3;
+    }
+    // sub-tile i = rows [r0 + 8 i, r0 + 8 i + 8) of W1, then the same rows of W3:
+    // 2 * n16 chunks of 16 bytes, six per thread in named registers, the next
+    // sub-tile's loads in flight while the current one is computed
+    const int n16 = GU_SUB * rowbytes / 16;
+    uint4 p0, p1, p2, p3, p4, p5;
+#define GU_LD(i, u, dst)                                                                                      \
+    dst = (tid + (u) * bd) < n16                                                                              \
+        ? reinterpret_cast<const uint4*>(w1 + (size_t)(r0 + GU_SUB * (i)) * rowbytes)[tid + (u) * bd]        \
+        : reinterpret_cast<const uint4*>(w3 + (size_t)(r0 + GU_SUB * (i)) * rowbytes)[min(tid + (u) * bd, 2 * n16 - 1) - n16];
+#define GU_LD_SUB(i) { GU_LD(i, 0, p0) GU_LD(i, 1, p1) GU_LD(i, 2, p2) GU_LD(i, 3, p3) GU_LD(i, 4, p4) GU_LD(i, 5, p5) }
+    GU_LD_SUB(0)
+
+    const int mtx = tid / L, kb = tid % L;
+    const bool live = tid < 2 * L;
+    const int s = kb >> 3, hh = (kb >> 2) & 1, j = kb & 3;
+    // the lane's activation block; plane j's mask leaves j < 3 weights times 4^j
+    // (folded into the block scale), plane 3 is shifted down by 2 (times 16)
+    uint32_t av[8];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(a.xq + (size_t)ch.token * D + kb * QB);
+        const uint4 u0 = src[0], u1 = src[1];
+        av[0] = u0.x; av[1] = u0.y; av[2] = u0.z; av[3] = u0.w;
+        av[4] = u1.x; av[5] = u1.y; av[6] = u1.z; av[7] = u1.w;
+    }
+    const float dxs = a.xd[(size_t)ch.token * L + kb] * (j == 0 ? 1.f : j == 1 ? 0.25f : 0.0625f);
+    const float dxm = a.xd[(size_t)ch.token * L + kb];
+    const int slo = a.xs16[(size_t)ch.token * 2 * L + 2 * kb];
+    const int shi = a.xs16[(size_t)ch.token * 2 * L + 2 * kb + 1];
+    const uint32_t wmask = j == 3 ? 0x30303030u : (0x03030303u << (2 * j));
+    const uint32_t wshift = j == 3 ? 2u : 0u;
+
+    uint4* tw = reinterpret_cast<uint4*>(smem);                                 // [2 * n16]
+    float* red = reinterpret_cast<float*>(smem + 2 * GU_SUB * rowbytes);         // [32][2][nsb]
+    float* hv = red + GU_TILE * 2 * nsb;                                          // [32]
+    const uint32_t* tw32 = reinterpret_cast<const uint32_t*>(smem);
+    for (int i = 0; i < GU_TILE / GU_SUB; ++i) {
+        if (i > 0) __syncthreads();   // every lane is done with the previous sub-tile
+        if (tid < 2 * n16) tw[tid] = p0;
+        if (tid + bd < 2 * n16) tw[tid + bd] = p1;
+        if (tid + 2 * bd < 2 * n16) tw[tid + 2 * bd] = p2;
+        if (tid + 3 * bd < 2 * n16) tw[tid + 3 * bd] = p3;
+        if (tid + 4 * bd < 2 * n16) tw[tid + 4 * bd] = p4;
+        if (tid + 5 * bd < 2 * n16) tw[tid + 5 * bd] = p5;
+        __syncthreads();
+        if (i + 1 < GU_TILE / GU_SUB) GU_LD_SUB(i + 1)
+        if (!live) continue;
+#pragma unroll 2
+        for (int r = 0; r < GU_SUB; ++r) {
+            const int sb = ((mtx * GU_SUB + r) * rowbytes + s * Q2K_BYTES) >> 2;   // dword index
+            const int qo = sb + 4 + 8 * hh;
+            int il = 0, ih = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) il = sdot4((tw32[qo + q] >> wshift) & wmask, av[q], il);
+#pragma unroll
+            for (int q = 4; q < 8; ++q) ih = sdot4((tw32[qo + q] >> wshift) & wmask, av[q], ih);
+            const uint32_t scw = tw32[sb + 2 * hh + (j >> 1)] >> (16 * (j & 1));
+            const uint32_t dd = tw32[sb + 20];
+            const int isum = __mul24((int)(scw & 15u), il) + __mul24((int)((scw >> 8) & 15u), ih);
+            const int msum = __mul24((int)((scw >> 4) & 15u), slo) + __mul24((int)((scw >> 12) & 15u), shi);
+            const float d = half_bits_to_f32(dd & 0xFFFFu), dmin = half_bits_to_f32(dd >> 16);
+            float part = fmaf(dxs * d, (float)isum, -(dxm * dmin) * (float)msum);
+            part = group8_sum(part);
+            if ((kb & 7) == 7) red[((GU_SUB * i + r) * 2 + mtx) * nsb + s] = part;
+        }
+    }
+#undef GU_LD_SUB
+#undef GU_LD
+    __syncthreads();
+    if (tid < GU_TILE) {
+        const float* rg = red + (size_t)(tid * 2 + 0) * nsb;
+        const float* ru = red + (size_t)(tid * 2 + 1) * nsb;
+        float gs = 0.f, us = 0.f;
+        for (int q = 0; q < nsb; ++q) {
+            gs += rg[q];
+            us += ru[q];
+        }
+        hv[tid] = swiglu(gs, us, a.limit);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float v[QB];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) v[q] = hv[q];
+        uint32_t qv[8];
+        float d16;
+        int sl, sh;
+        q8_1_block(v, qv, d16, sl, sh);
+        uint4* dst = reinterpret_cast<uint4*>(out + r0);
+        dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+        dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
+        reinterpret_cast<float*>(out + I)[tile] = d16;
+        int32_t* ss = reinterpret_cast<int32_t*>(out + I + (I / QB) * 4);
+        ss[2 * tile] = sl;
+        ss[2 * tile + 1] = sh;
+    }
+}
+
+// ------------------------------------------------------------------ Q3_K down + combine
+// Lanes: tid = pr * L + kb (L = I / 32; pr = output row of the tile, 8 rows).
+// LDS: per group of DC_GROUP chunks, each chunk's 8 W2 rows then its q8_1(h)
+// record; the per-row partial sums; the per-token accumulators.
+__global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int routed_rows, int m, int max_chunks,
+                                                            const float* __restrict__ ys, uint16_t* __restrict__ out) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int D = a.D, I = a.I;
+    const int L = I / QB;
+    const int nsb = I / QK;
+    const int rowbytes = nsb * Q3K_BYTES;
+    const int r0 = blockIdx.x * DC_ROWS;
+    const int tid = threadIdx.x, bd = blockDim.x;
+    const int rec = rec_bytes(I);
+    const int tile_bytes = DC_ROWS * rowbytes;   // a multiple of 16 (8 * 110 * nsb)
+    const int unit = tile_bytes + rec;           // LDS bytes per chunk
+    const int unit16 = unit / 16, tile16 = tile_bytes / 16;
+
+    // the chunk list (records read once, kept in LDS)
+    int* c_slot = reinterpret_cast<int*>(smem + DC_GROUP * unit + 16);
+    int* c_row = c_slot + max_chunks;
+    int* c_tok = c_row + max_chunks;
+    float* c_w = reinterpret_cast<float*>(c_tok + max_chunks);
+    float* red = c_w + max_chunks;                 // [DC_GROUP][DC_ROWS][nsb]
+    float* acc = red + DC_GROUP * DC_ROWS * nsb;   // [m][DC_ROWS]
+    const int nch = min(*a.n_chunks, max_chunks);
+    for (int q = tid; q < nch; q += bd) {
+        const Chunk ch = a.chunks[q];
+        const bool sh = ch.expert < 0;
+        c_slot[q] = sh ? -2 : ch.slot;
+        c_row[q] = sh ? routed_rows + ch.row0 : ch.row0;
+        c_tok[q] = ch.token;
+        c_w[q] = ch.weight;
+    }
+    for (int q = tid; q < m * DC_ROWS; q += bd) acc[q] = 0.f;
+    __syncthreads();
+
+    // group loads: DC_GROUP units of [tile | record]; chunks past the end repeat the last one
+    uint4 pf0, pf1, pf2;   // named registers (an array here was placed in scratch memory)
+    static_assert(DC_NPF == 3, "the prefetch registers below");
+#define DC_LOAD_ONE(g0, u, dst)                                                                              \
+    {                                                                                                        \
+        const int q = min(tid + (u) * bd, DC_GROUP * unit16 - 1);                                            \
+        const int cc = q / unit16, o = q % unit16;                                                           \
+        const int cidx = min((g0) + cc, nch - 1);                                                            \
+        const int slot = c_slot[cidx];                                                                       \
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);                                                                \
+        if (o < tile16) {                                                                                    \
+            if (slot != -1) {                                                                                \
+                const uint8_t* w2 = slot == -2 ? a.sh_w2 : a.arena + (size_t)slot * a.slot_bytes + a.off_w2;  \
+                v = reinterpret_cast<const uint4*>(w2 + (size_t)r0 * rowbytes)[o];                          \
+            }                                                                                                \
+        } else {                                                                                             \
+            v = reinterpret_cast<const uint4*>(a.hrec + (size_t)c_row[cidx] * rec)[o - tile16];              \
+        }                                                                                                    \
+        dst = v;                                                                                             \
+    }
+#define DC_LOAD_GROUP(g0) { DC_LOAD_ONE(g0, 0, pf0) DC_LOAD_ONE(g0, 1, pf1) DC_LOAD_ONE(g0, 2, pf2) }
+    if (nch > 0) DC_LOAD_GROUP(0)
+
+    const int pr = tid / L, kb = tid % L;
+    const bool lane_live = pr < DC_ROWS;
+    const int s = kb >> 3, hh = (kb >> 2) & 1, j = kb & 3;
+    // per-lane constants for the two 6-bit scales of sub-blocks n = 8hh + 2j + {0,1}
+    const int n_lo = 8 * hh + 2 * j;
+    const int lo_byte0 = 2 * j, lo_shift = 4 * hh;
+    const int hi_byte0 = 8 + (n_lo & 3), hi_byte1 = 8 + ((n_lo + 1) & 3);
+    const int hi_shift = 2 * (n_lo >> 2);
+    uint4* lds16 = reinterpret_cast<uint4*>(smem);
+    const uint32_t* lds32 = reinterpret_cast<const uint32_t*>(smem);
+    for (int g0 = 0; g0 < nch; g0 += DC_GROUP) {
+        if (g0 > 0) __syncthreads();   // the previous group's units and partials are consumed
+#define DC_STORE_ONE(u, src) \
+    if (tid + (u) * bd < DC_GROUP * unit16) lds16[tid + (u) * bd] = src;
+        DC_STORE_ONE(0, pf0) DC_STORE_ONE(1, pf1) DC_STORE_ONE(2, pf2)
+#undef DC_STORE_ONE
+        __syncthreads();
+        if (g0 + DC_GROUP < nch) DC_LOAD_GROUP(g0 + DC_GROUP)
+        const int ng = min(DC_GROUP, nch - g0);
+        if (lane_live) {
+            for (int cc = 0; cc < ng; ++cc) {
+                const int ubase = cc * unit;
+                const uint32_t* hq32 = lds32 + (ubase + tile_bytes) / 4;
+                uint32_t av[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) av[q] = hq32[kb * 8 + q];
+                const float dx = reinterpret_cast<const float*>(hq32 + I / 4)[kb];
+                const int* hs = reinterpret_cast<const int*>(hq32 + I / 4 + L);
+                const int slo = hs[2 * kb], shi = hs[2 * kb + 1];
+                const int sb = ubase + pr * rowbytes + s * Q3K_BYTES;   // 2-byte aligned
+                const int A = sb >> 2;
+                const uint32_t sh = (uint32_t)(sb & 3) * 8u;              // 0 or 16
+                uint32_t V[8];
+                {
+                    const int qo = A + 8 + 8 * hh;                           // qs[32 hh ..] at byte 32 + 32 hh
+                    uint32_t prev = lds32[qo];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint32_t next = lds32[qo + q + 1];
+                        const uint32_t qs = funnel(next, prev, sh);
+                        const uint32_t hm = funnel(lds32[A + q + 1], lds32[A + q], sh);
+                        prev = next;
+                        const uint32_t lo = (qs >> (2 * j)) & 0x03030303u;
+                        const uint32_t hb = (hm >> (4 * hh + j)) & 0x01010101u;
+                        V[q] = lo | (hb << 2);                               // q3 + 4, 0..7
+                    }
+                }
+                const uint32_t s0 = funnel(lds32[A + 25], lds32[A + 24], sh);   // scale bytes 0..3
+                const uint32_t s1 = funnel(lds32[A + 26], lds32[A + 25], sh);   // 4..7
+                const uint32_t s2 = funnel(lds32[A + 27], lds32[A + 26], sh);   // 8..11
+                const uint32_t dbits = (lds32[A + 27] >> sh) & 0xFFFFu;          // d at byte 108
+                const uint32_t lo_word = (lo_byte0 < 4) ? s0 : s1;
+                const int lsh = 8 * (lo_byte0 & 3);
+                const int low4_lo = (lo_word >> (lsh + lo_shift)) & 15;
+                const int low4_hi = (lo_word >> (lsh + 8 + lo_shift)) & 15;
+                const int hi2_lo = (s2 >> (8 * (hi_byte0 - 8) + hi_shift)) & 3;
+                const int hi2_hi = (s2 >> (8 * (hi_byte1 - 8) + hi_shift)) & 3;
+                const int s6_lo = (low4_lo | (hi2_lo << 4)) - 32;
+                const int s6_hi = (low4_hi | (hi2_hi << 4)) - 32;
+                const float d = half_bits_to_f32(dbits);
+                int il = 0, ih = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) il = sdot4(V[q], av[q], il);
+#pragma unroll
+                for (int q = 4; q < 8; ++q) ih = sdot4(V[q], av[q], ih);
+                il -= 4 * slo;
+                ih -= 4 * shi;
+                float part = dx * (d * (float)(__mul24(s6_lo, il) + __mul24(s6_hi, ih)));
+                part = group8_sum(part);
+                if ((kb & 7) == 7) red[(cc * DC_ROWS + pr) * nsb + s] = part;
+            }
+        }
+        __syncthreads();
+        if (tid < DC_ROWS) {   // row tid: this group's chunks in order
+            for (int cc = 0; cc < ng; ++cc) {
+                const float* re = red + (cc * DC_ROWS + tid) * nsb;
+                float e = 0.f;
+                for (int q = 0; q < nsb; ++q) e += re[q];
+                const int c = g0 + cc;
+                acc[c_tok[c] * DC_ROWS + tid] += c_slot[c] == -1 ? 0.f : c_w[c] * e;
+            }
+        }
+    }
+#undef DC_LOAD_GROUP
+#undef DC_LOAD_ONE
+    __syncthreads();
+    for (int q = tid; q < m * DC_ROWS; q += bd) {
+        const int t = q / DC_ROWS, r = q % DC_ROWS;
+        float v = acc[q];
+        if (ys != nullptr) v += ys[(size_t)t * D + r0 + r];
+        out[(size_t)t * D + r0 + r] = (uint16_t)f32_to_bf16(v);
+    }
+}
+
+// ------------------------------------------------------------------ launch
+bool decode_supported(int D, int I) {
+    // lanes: 2 * D / 32 for gate/up and 8 * I / 32 for down, within one workgroup
+    return D % QK == 0 && I % QK == 0 && D / 16 <= 1024 && I / 4 <= 1024 && D % DC_ROWS == 0;
+}
+
+static int round64(int v) { return (v + 63) / 64 * 64; }
+
+size_t decode_rec_bytes(int I) { return (size_t)I + (size_t)(I / QB) * 4 + (size_t)(I / 16) * 4; }
+
+hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st) {
+    if (max_chunks <= 0) return hipSuccess;
+    const int threads = round64(2 * (a.D / QB));
+    const int nsb = a.D / QK;
+    const size_t lds = (size_t)2 * GU_SUB * nsb * Q2K_BYTES + (size_t)GU_TILE * 2 * nsb * 4 + GU_TILE * 4;
+    return launch_kernel(gateup_q8_kernel, max_chunks * (a.I / GU_TILE), threads, lds, st, a, routed_rows);
+}
+
+hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
+                               uint16_t* out, hipStream_t st) {
+    const int threads = round64(DC_ROWS * (a.I / QB));
+    const int nsb = a.I / QK;
+    const size_t unit = (size_t)DC_ROWS * nsb * Q3K_BYTES + decode_rec_bytes(a.I);
+    const size_t lds = DC_GROUP * unit + 16 + (size_t)max_chunks * 16 + (size_t)DC_GROUP * DC_ROWS * nsb * 4 +
+                       (size_t)m * DC_ROWS * 4;
+    return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, ys, out);
+}
+
+}  // namespace moe

@@ -370,8 +370,7 @@ __global__ __launch_bounds__(256) void quantize_h_kernel(ExpertArgs a, int route
 hipError_t launch_quantize_h(const ExpertArgs& a, int routed_rows, int shared_rows, hipStream_t st) {
     const int total = (routed_rows + shared_rows) * (a.I / QB);
     if (total == 0) return hipSuccess;
-    launch_kernel(quantize_h_kernel, (total + 255) / 256, 256, 0, st, a, routed_rows, shared_rows);
-    return hipGetLastError();
+    return launch_kernel(quantize_h_kernel, (total + 255) / 256, 256, 0, st, a, routed_rows, shared_rows);
 }
 
 // ------------------------------------------------------------------ launch geometry
@@ -412,8 +411,7 @@ template <int T>
 static hipError_t launch_pair(const ExpertArgs& a, int max_chunks, hipStream_t st) {
     const GemvGeom gu = gateup_geom(a.D, a.I);
     const size_t lds1 = gu.lds_base + (size_t)gu.lds_per_t * T;
-    launch_kernel(gateup_q2k_kernel<T>, max_chunks * gu.tiles, gu.threads, lds1, st, a, gu.R, gu.P);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(gateup_q2k_kernel<T>, max_chunks * gu.tiles, gu.threads, lds1, st, a, gu.R, gu.P);
     if (e != hipSuccess) return e;
     return hipSuccess;
 }
@@ -422,8 +420,7 @@ template <int T>
 static hipError_t launch_down(const ExpertArgs& a, int max_chunks, hipStream_t st) {
     const GemvGeom dg = down_geom(a.D, a.I);
     const size_t lds2 = dg.lds_base + (size_t)dg.lds_per_t * T;
-    launch_kernel(down_q3k_kernel<T>, max_chunks * dg.tiles, dg.threads, lds2, st, a, dg.R, dg.P);
-    return hipGetLastError();
+    return launch_kernel(down_q3k_kernel<T>, max_chunks * dg.tiles, dg.threads, lds2, st, a, dg.R, dg.P);
 }
 
 hipError_t launch_gateup_q2k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st) {

@@ -320,12 +320,10 @@ static hipError_t launch_mmq_ns(const ExpertArgs& a, int max_chunks, bool gateup
     if (gateup) {
         const int KS = 4;
         const size_t lds = (size_t)128 * KS * Q2K_BYTES;
-        launch_kernel(mmq_gateup_q2k_kernel<NS>, max_chunks * (a.I / TILE_ROWS), 256, lds, st, a, KS);
-    } else {
-        const size_t lds = (size_t)TILE_ROWS * (a.I / QK) * Q3K_BYTES + 16 + 64 * 8;
-        launch_kernel(mmq_down_q3k_kernel<NS>, max_chunks * (a.D / TILE_ROWS), 256, lds, st, a);
+        return launch_kernel(mmq_gateup_q2k_kernel<NS>, max_chunks * (a.I / TILE_ROWS), 256, lds, st, a, KS);
     }
-    return hipGetLastError();
+    const size_t lds = (size_t)TILE_ROWS * (a.I / QK) * Q3K_BYTES + 16 + 64 * 8;
+    return launch_kernel(mmq_down_q3k_kernel<NS>, max_chunks * (a.D / TILE_ROWS), 256, lds, st, a);
 }
 
 hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st) {

@@ -38,7 +38,7 @@ struct moe_ctx {
     moe_cfg cfg;
     int device = 0;
     int n_cu = 256;          // compute units of the device
-    bool stream_ok = false;  // the streaming GEMVs fit this shape
+    bool decode_ok = false;  // the decode-path kernels fit this shape
     bool mmq_ok = false;     // the MMQ tiles fit this shape
     int max_pairs = 0;
     int max_chunks = 0;   // chunk-list capacity
@@ -59,6 +59,8 @@ struct moe_ctx {
     int32_t* inv = nullptr;
     Chunk* chunks = nullptr;
     float* h_routed = nullptr;
+    uint8_t* hrec = nullptr;
+    float* h_dec = nullptr;
     float* h_shared = nullptr;
     int8_t* hq_routed = nullptr;
     float* hd_routed = nullptr;
@@ -260,14 +262,17 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
         if (hipGetDeviceProperties(&prop, ctx->device) == hipSuccess && prop.multiProcessorCount > 0)
             ctx->n_cu = prop.multiProcessorCount;
     }
-    ctx->stream_ok = stream_gemv_supported(c.dim, c.inter);
+    ctx->decode_ok = decode_supported(c.dim, c.inter);
     ctx->mmq_ok = mmq_supported(c.dim, c.inter);
     const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
     const size_t P = M * c.topk;
     ctx->max_pairs = (int)P;
-    // room for the GEMV list and for the MMQ plan of any m <= max_tokens (both grow with m)
+    // room for the GEMV list, the MMQ plan of any m <= max_tokens (both grow with
+    // m) and the single-row chunks of the small-batch routing
+    const int m_small = (int)std::min<size_t>(M, ROUTE_SMALL_MAX_M);
     ctx->max_chunks = std::max(routed_chunk_bound(c, (int)M) + shared_chunk_count((int)M) + 1,
                                mmq_chunk_plan((int)M, c.topk, c.n_routed, true).total());
+    ctx->max_chunks = std::max(ctx->max_chunks, m_small * (c.topk + 1) + 1);
     layout_of(c, ctx->slot_bytes, ctx->off_w1, ctx->off_w3, ctx->off_w2);
 
     Carver cv;
@@ -295,6 +300,8 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     const size_t o_hss = cv.take<int32_t>(M * I / 16);
     const size_t o_er = cv.take<float>(P * D);
     const size_t o_ys = cv.take<float>(M * D);
+    const size_t o_rec = cv.take<uint8_t>((size_t)m_small * (c.topk + 1) * decode_rec_bytes((int)I));
+    const size_t o_hdec = cv.take<float>((size_t)m_small * (c.topk + 1) * I);
     const size_t o_err = cv.take<int32_t>(1);
     const size_t o_tab = cv.take<int32_t>(E);
     const size_t total = align_up(cv.off, 256);
@@ -326,6 +333,8 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     ctx->hd_shared = (float*)(b + o_hds);
     ctx->hs_shared = (int32_t*)(b + o_hss);
     ctx->e_rows = (float*)(b + o_er);
+    ctx->hrec = b + o_rec;
+    ctx->h_dec = (float*)(b + o_hdec);
     ctx->ys = (float*)(b + o_ys);
     ctx->err = (int32_t*)(b + o_err);
     ctx->slot_table_dev = (int32_t*)(b + o_tab);
@@ -428,6 +437,18 @@ int moe_route(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m,
     return run_route(ctx, w, (const uint16_t*)x_bf16, m, idx_out, weights_out, (hipStream_t)stream);
 }
 
+// the routing copies of moe_forward_ex and the call count
+static int finish_call(moe_ctx* ctx, float* weights_out, int32_t* idx_out, int P, hipStream_t st) {
+    if (weights_out != nullptr &&
+        hipMemcpyAsync(weights_out, ctx->gw, sizeof(float) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return MOE_EHIP;
+    if (idx_out != nullptr &&
+        hipMemcpyAsync(idx_out, ctx->idx, sizeof(int32_t) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return MOE_EHIP;
+    ctx->stats.calls++;
+    return MOE_OK;
+}
+
 int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
                    float* weights_out, int32_t* idx_out, void* stream) {
     if (ctx == nullptr || x_bf16 == nullptr || out_bf16 == nullptr) return MOE_EINVAL;
@@ -483,7 +504,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
             return launch_route_small(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp,
                                       c.norm_topk_prob, c.route_scale, ctx->idx, ctx->gw, ctx->err, kq ? 1 : 0,
                                       ctx->offsets, ctx->active, ctx->n_active, ctx->perm, ctx->inv, ctx->chunks,
-                                      ctx->n_chunks, st);
+                                      ctx->n_chunks, ctx->slot_table_dev, st);
         });
         if (rc != MOE_OK) return rc;
     } else {
@@ -524,6 +545,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.xs16 = ctx->xs16;
     a.xs16f = ctx->xs16f;
     a.h_routed = ctx->h_routed;
+    a.hrec = ctx->hrec;
+    a.h_dec = ctx->h_dec;
     a.h_shared = ctx->h_shared;
     a.hq_routed = ctx->hq_routed;
     a.hd_routed = ctx->hd_routed;
@@ -537,8 +560,23 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.I = c.inter;
     a.limit = c.swiglu_limit;
     a.err = ctx->err;
-    const int rows_max = std::min(m, GEMV_ROWS);
     const int chunks = routed_chunk_bound(c, m) + (kq ? shared_chunk_count(m) : 0);
+    const float* ys = w->shared_fmt == MOE_SHARED_BF16 ? ctx->ys : nullptr;
+    if (small && ctx->decode_ok) {
+        // one single-row chunk per pick (and per token of a K-quant shared expert):
+        // gate/up writes q8_1(h) records, down accumulates G E per token and stores bf16
+        const int nch = P + (kq ? m : 0);
+        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q8(a, P, nch, st); });
+        if (rc != MOE_OK) return rc;
+        if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
+        rc = timed(ctx, st, MOE_K_DOWN, [&] {
+            return launch_down_combine(a, P, m, nch, ys, (uint16_t*)out_bf16, st);
+        });
+        if (rc != MOE_OK) return rc;
+        return finish_call(ctx, weights_out, idx_out, P, st);
+    }
+    // chunks of at most GEMV_ROWS rows, or single rows on the small-batch routing
+    const int rows_max = small ? 1 : std::min(m, GEMV_ROWS);
     if (use_mmq) {
         rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, plan, true, st); });
         if (rc != MOE_OK) return rc;
@@ -547,30 +585,21 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, plan, false, st); });
         if (rc != MOE_OK) return rc;
     } else {
-        const bool streaming = rows_max <= 1 && ctx->stream_ok;
-        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, chunks, st); });
+        const int nch = small ? P + (kq ? m : 0) : chunks;
+        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, nch, st); });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
         if (rc != MOE_OK) return rc;
-        rc = timed(ctx, st, MOE_K_DOWN, [&] {
-            return streaming ? launch_down_q3k_stream(a, ctx->n_cu * 2, st) : launch_down_q3k(a, rows_max, chunks, st);
-        });
+        rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, nch, st); });
         if (rc != MOE_OK) return rc;
     }
     if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
-    const float* ys = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
+    const float* ys_all = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
     rc = timed(ctx, st, MOE_K_COMBINE, [&] {
-        return launch_combine(ctx->e_rows, ys, ctx->gw, ctx->inv, m, c.topk, c.dim, (uint16_t*)out_bf16, st);
+        return launch_combine(ctx->e_rows, ys_all, ctx->gw, ctx->inv, m, c.topk, c.dim, (uint16_t*)out_bf16, st);
     });
     if (rc != MOE_OK) return rc;
-    if (weights_out != nullptr &&
-        hipMemcpyAsync(weights_out, ctx->gw, sizeof(float) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
-        return MOE_EHIP;
-    if (idx_out != nullptr &&
-        hipMemcpyAsync(idx_out, ctx->idx, sizeof(int32_t) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
-        return MOE_EHIP;
-    ctx->stats.calls++;
-    return MOE_OK;
+    return finish_call(ctx, weights_out, idx_out, P, st);
 }
 
 int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16, void* stream) {

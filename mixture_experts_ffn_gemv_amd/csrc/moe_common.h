@@ -23,10 +23,13 @@ constexpr int ERR_NOTRESIDENT = 2;
 // expert >= 0: routed expert; row0 is a position in the expert-sorted pair list.
 // expert == -1: the shared expert; row0 is a token index.
 struct Chunk {
-    int32_t expert;
-    int32_t row0;
+    int32_t expert;   // routed expert id, or -1 for the K-quant shared expert
+    int32_t row0;     // first position (routed: in expert-sorted pick order; shared: token)
     int32_t nrows;
-    int32_t pad;
+    int32_t slot;     // decode chunks: the expert's slot when the chunk was made (-1: not resident)
+    int32_t token;    // decode chunks (one row each): the row's token
+    float weight;     // decode chunks: the row's routing weight (1 for the shared expert)
+    int32_t pad0, pad1;
 };
 
 // Everything the expert kernels read and write.
@@ -55,6 +58,8 @@ struct ExpertArgs {
     int32_t* hs_shared;
     float* e_rows;              // f32 [pairs, D] in position order
     float* ys;                  // f32 [m, D]
+    float* h_dec;               // decode path: f32 h rows (routed positions, then shared-expert tokens)
+    uint8_t* hrec;              // decode path: q8_1 record of each h row, [quants I | d f32 I/32 | 16-sums i32 I/16]
     int32_t D, I;
     float limit;
     int32_t* err;

@@ -78,7 +78,7 @@ constexpr int ROUTE_SMALL_MAX_PAIRS = 512;
 hipError_t launch_route_small(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
-                              Chunk* chunks, int32_t* n_chunks, hipStream_t st);
+                              Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st);
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
                                 float* xs16f, hipStream_t st);
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp, int norm,
@@ -98,10 +98,13 @@ hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const
 hipError_t launch_gateup_q2k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
 hipError_t launch_quantize_h(const ExpertArgs& a, int routed_rows, int shared_rows, hipStream_t st);
 hipError_t launch_down_q3k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
-// streaming (persistent, software-pipelined) GEMVs for chunks of one row
-bool stream_gemv_supported(int D, int I);
-hipError_t launch_gateup_q2k_stream(const ExpertArgs& a, int n_wg, hipStream_t st);
-hipError_t launch_down_q3k_stream(const ExpertArgs& a, int n_wg, hipStream_t st);
+// decode path (single-row chunks from the small-batch routing)
+bool decode_supported(int D, int I);
+size_t decode_rec_bytes(int I);
+// gate/up writing the q8_1 records of h
+hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st);
+hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
+                               uint16_t* out, hipStream_t st);
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int m, int D, int I, const uint16_t* w1,
                                      const uint16_t* w3, uint16_t* h_bf16, float limit, hipStream_t st);
 hipError_t launch_shared_bf16_down(const uint16_t* h_bf16, int m, int D, int I, const uint16_t* w2, float* ys,

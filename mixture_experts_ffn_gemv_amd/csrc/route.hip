@@ -307,7 +307,10 @@ __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __res
                 ch.expert = tid;
                 ch.row0 = excl + q * my_rows;
                 ch.nrows = min(my_rows, v - q * my_rows);
-                ch.pad = 0;
+                ch.slot = -1;
+                ch.token = -1;
+                ch.weight = 0.f;
+                ch.pad0 = ch.pad1 = 0;
                 chunks[base[c] + cexcl + q] = ch;
             }
         }
@@ -317,7 +320,10 @@ __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __res
             ch.expert = -1;
             ch.row0 = q * sh_rows;
             ch.nrows = min(sh_rows, m - q * sh_rows);
-            ch.pad = 0;
+            ch.slot = -1;
+            ch.token = -1;
+            ch.weight = 0.f;
+            ch.pad0 = ch.pad1 = 0;
             chunks[base[c] + ntot + q] = ch;
         }
         if (tid == 0) n_chunks[c] = ntot + nsh_c;
@@ -362,8 +368,9 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __rest
 // ---------------------------------------------------------------- small batches: top-k + bucketing
 // One workgroup of 1024 threads for m <= 8 tokens: the rank selection for
 // floor(1024 / E') tokens at a time (E' = E rounded up to 64), then the
-// bucketing of the m * k picks (counts, offsets, active experts, chunk list,
-// stable placement) without leaving the workgroup.
+// bucketing of the m * k picks (counts, offsets, active experts, stable
+// placement, and one single-row chunk per pick, then one per token for a
+// K-quant shared expert) without leaving the workgroup.
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ bias, int m, int E, int k,
                                                            float gate_temp, int norm, float route_scale,
@@ -374,7 +381,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                            int32_t* __restrict__ n_active,
                                                            int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                                            Chunk* __restrict__ chunks,
-                                                           int32_t* __restrict__ n_chunks) {
+                                                           int32_t* __restrict__ n_chunks,
+                                                           const int32_t* __restrict__ slot_table) {
     __shared__ __align__(16) float keys[1024];
     __shared__ float cand_key[1024], cand_s[1024];
     __shared__ int cand_id[1024];
@@ -423,29 +431,11 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     const int aexcl = block_exclusive_scan((tid < E && v > 0) ? 1 : 0, scan_lds, nact);
     if (tid < E && v > 0) active[aexcl] = tid;
     if (tid == 0) *n_active = nact;
-    const int nc = tid < E ? (v + GEMV_ROWS - 1) / GEMV_ROWS : 0;
-    int ntot;
-    const int cexcl = block_exclusive_scan(nc, scan_lds, ntot);
-    for (int q = 0; q < nc; ++q) {
-        Chunk c;
-        c.expert = tid;
-        c.row0 = excl + q * GEMV_ROWS;
-        c.nrows = min(GEMV_ROWS, v - q * GEMV_ROWS);
-        c.pad = 0;
-        chunks[cexcl + q] = c;
-    }
-    const int nsh = shared_chunks ? (m + GEMV_ROWS - 1) / GEMV_ROWS : 0;
-    if (tid < nsh) {
-        Chunk c;
-        c.expert = -1;
-        c.row0 = tid * GEMV_ROWS;
-        c.nrows = min(GEMV_ROWS, m - tid * GEMV_ROWS);
-        c.pad = 0;
-        chunks[ntot + tid] = c;
-    }
-    if (tid == 0) *n_chunks = ntot + nsh;
+    if (tid == 0) *n_chunks = total + (shared_chunks ? m : 0);
     __syncthreads();
-    // stable placement: position = offset of the expert + earlier pairs that picked it
+    // stable placement: position = offset of the expert + earlier pairs that picked
+    // it; one chunk per position (a single row), carrying what the decode kernels
+    // need without further lookups: the expert's slot, the token and the weight
     for (int p = tid; p < P; p += 1024) {
         const int pe = pick_e[p];
         int before = 0;
@@ -453,6 +443,26 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
         const int pos = offs[pe] + before;
         perm[pos] = p;
         inv[p] = pos;
+        Chunk c;
+        c.expert = pe;
+        c.row0 = pos;
+        c.nrows = 1;
+        c.slot = slot_table[pe];
+        c.token = p / k;
+        c.weight = pick_weight(pick_s + (p / k) * k, p % k, k, norm, route_scale);
+        c.pad0 = c.pad1 = 0;
+        chunks[pos] = c;
+    }
+    if (shared_chunks && tid < m) {
+        Chunk c;
+        c.expert = -1;
+        c.row0 = tid;
+        c.nrows = 1;
+        c.slot = 0;
+        c.token = tid;
+        c.weight = 1.f;
+        c.pad0 = c.pad1 = 0;
+        chunks[total + tid] = c;
     }
 }
 
@@ -460,54 +470,41 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                                int8_t* xq, float* xd, int32_t* xs16, hipStream_t st) {
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
-    if (m <= 2) {
-        const int ntg = (m + 1) / 2;
-        if (m == 1)
-            launch_kernel(router_quant_kernel<1>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
-        else
-            launch_kernel(router_quant_kernel<2>, E * ntg + nq, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd, xs16);
-    } else if (m <= 4) {
-        launch_kernel(router_quant_kernel<4>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
-    } else {
-        const int ntg = (m + 7) / 8;
-        launch_kernel(router_quant_kernel<8>, E * ntg + nq, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd, xs16);
-    }
-    return hipGetLastError();
+    if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
+    if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
+    if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
+    const int ntg = (m + 7) / 8;
+    return launch_kernel(router_quant_kernel<8>, E * ntg + nq, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd, xs16);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
                                 float* xs16f, hipStream_t st) {
     const int nb = m * (D / QB);
-    launch_kernel(quantize_rows_kernel, (nb + 255) / 256, 256, 0, st, x, nb, xq, xd, xs16, xs16f);
-    return hipGetLastError();
+    return launch_kernel(quantize_rows_kernel, (nb + 255) / 256, 256, 0, st, x, nb, xq, xd, xs16, xs16f);
 }
 
 hipError_t launch_route_small(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
-                              Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
-    launch_kernel(route_small_kernel, 1, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
-                                           shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks);
-    return hipGetLastError();
+                              Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st) {
+    return launch_kernel(route_small_kernel, 1, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
+                  shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
 }
 
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                        int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st) {
     const int threads = (E + 63) / 64 * 64;
-    launch_kernel(topk_rank_kernel, m, threads, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, idx, gw, err);
-    return hipGetLastError();
+    return launch_kernel(topk_rank_kernel, m, threads, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, idx, gw, err);
 }
 
 hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
     const int P = m * k;
-    launch_kernel(bucket_count_kernel, 1, 1024, 0, st, idx, P, E, m, shared_chunks, plan ? 1 : 0, plan ? plan->base[1] : 0,
+    hipError_t e = launch_kernel(bucket_count_kernel, 1, 1024, 0, st, idx, P, E, m, shared_chunks, plan ? 1 : 0, plan ? plan->base[1] : 0,
                                             plan ? plan->base[2] : 0, offsets, active, n_active, chunks, n_chunks);
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_kernel(bucket_place_kernel, E, 256, 0, st, idx, P, offsets, perm, inv);
-    return hipGetLastError();
+    return launch_kernel(bucket_place_kernel, E, 256, 0, st, idx, P, offsets, perm, inv);
 }
 
 }  // namespace moe
