@@ -14,6 +14,12 @@ quantisation; tokens ~N(0, 1) in bf16):
   prefill      m = 512 tokens per step, uniform routing (zero bias).
   prefill_hot  m = 512 with bias +100 on six fixed experts: every token picks
                them, six groups of 512 rows, the shape where int8 MFMA binds.
+  skewed       m = 2048 with a Zipf(1.1)-shaped bias (calibrated so the 38
+               most loaded experts take half of the assignments), only 96
+               device slots, every expert in a page-locked host arena: each
+               call streams its missing experts in over the host link (least
+               recently used slots reused, waves when the picks outnumber the
+               slots). The LRU is warmed with 3 untimed calls.
 A step is one moe_forward call (every kernel of the layer). Prints one JSON
 line for the chosen workload; with the decode headline the other three are
 summarised under "workloads" (unless --no-extra). Progress goes to stderr.
@@ -50,6 +56,9 @@ WORKLOADS = {
                     desc="prefill m=512 (MMQ path), uniform routing, bf16 shared expert"),
     "prefill_hot": dict(m=512, layers=1, bias="hot", shared="bf16", pool=512,
                         desc="prefill m=512 (MMQ path), 6 hot experts take every token, bf16 shared expert"),
+    "skewed": dict(m=2048, layers=1, bias="skewed", shared="bf16", pool=2048, slots=96,
+                   desc="skewed prefill m=2048 (MMQ path), 96 device slots, misses streamed from a pinned host "
+                        "arena, bf16 shared expert"),
 }
 # the kernel each workload's roofline object describes, and its name in rocprofv3
 DOMINANT = {
@@ -57,6 +66,7 @@ DOMINANT = {
     "small": ("gateup", r"^void moe::gateup_q2k_kernel<"),
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
+    "skewed": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),
 }
 COPY_KERNEL = r"neg_kernel"
 
@@ -198,6 +208,8 @@ class Bench:
                 b = torch.zeros(shape.n_routed, dtype=torch.float32)
                 b[list(HOT_EXPERTS)] = 100.0
                 wr, bias = S.make_router(shape, seed, 0.02, b)
+            elif spec["bias"] == "skewed":
+                wr, bias = S.make_router(shape, seed, 0.02, S.skewed_bias(shape, 4, S.C4_BIAS_SCALE))
             else:
                 wr, bias = S.make_router(shape, seed, 0.02, spec["bias"])
             sh = S.make_shared(shape, seed, spec["shared"])
@@ -221,13 +233,24 @@ class Bench:
         m, pool_n = spec["m"], spec["pool"]
         layers = self.layers(wl)
         n_layers = len(layers)
-        tokens = S.make_tokens(pool_n, shape.dim, 1, index={"decode": 0, "small": 3}.get(wl, 2))
+        if wl == "skewed":
+            tokens = S.make_tokens(pool_n, shape.dim, 4, index=0)
+        else:
+            tokens = S.make_tokens(pool_n, shape.dim, 1, index={"decode": 0, "small": 3}.get(wl, 2))
         d_tokens = tokens.to(self.dev)
         cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8))
         ctx = moe.moe_create(cfg)
-        moe.moe_set_slots(ctx, self.experts, shape.n_routed)
-        for e in range(shape.n_routed):
-            moe.moe_slot_bind(ctx, e, e)
+        streamed = "slots" in spec
+        if streamed:
+            # a small device arena; every expert in page-locked host memory
+            slot_arena = torch.empty((spec["slots"], self.slot_bytes), dtype=torch.uint8, device=self.dev)
+            host = self.pinned_experts()
+            moe.moe_set_slots(ctx, slot_arena, spec["slots"])
+            moe.moe_set_host_arena(ctx, host, self.slot_bytes)
+        else:
+            moe.moe_set_slots(ctx, self.experts, shape.n_routed)
+            for e in range(shape.n_routed):
+                moe.moe_slot_bind(ctx, e, e)
         out = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
         idx = torch.empty((m, shape.topk), dtype=torch.int32, device=self.dev)
         stream = torch.cuda.current_stream()
@@ -259,6 +282,7 @@ class Bench:
         rc = moe.moe_check(ctx)
         if rc != moe.MOE_OK:
             raise RuntimeError(f"{wl} warmup: {moe.strerror(rc)}")
+        moe.moe_reset_stats(ctx)
 
         # timed region: K steps bracketed by events on the launch stream
         torch.cuda.synchronize()
@@ -272,6 +296,7 @@ class Bench:
         rc = moe.moe_check(ctx)
         if rc != moe.MOE_OK:
             raise RuntimeError(f"{wl} timed region: {moe.strerror(rc)}")
+        stats = moe.moe_get_stats(ctx)
 
         # the same K steps again with every kernel launch bracketed by HIP events on
         # its own stream (the library records them): per-kernel durations
@@ -344,9 +369,47 @@ class Bench:
             res["mmq_i8_mfma_util"] = round(ops / (mmq_ms / 1e3) / I8_PEAK_OPS, 4)
             res["mmq_routed_GB_per_s"] = round(routed_b / (mmq_ms / 1e3) / 1e9, 1)
             res["mmq_frac_of_hbm_peak"] = round(routed_b / (mmq_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+        if streamed:
+            calls = max(1, stats["calls"])
+            link = stats["bytes_copied"] / (ms_total / 1e3) / 1e9
+            res["streaming"] = {
+                "device_slots": spec["slots"],
+                "hits_per_call": stats["hits"] / calls,
+                "misses_per_call": stats["misses"] / calls,
+                "waves_per_call": stats["waves"] / calls,
+                "bytes_copied_per_call": stats["bytes_copied"] / calls,
+                "route_readback_ms_per_call": round(stats["route_ms"] / calls, 4),
+                "copy_ms_per_call": round(stats["fetch_ms"] / calls, 4),
+                "link_GB_per_s": round(link, 2),
+                "pinned_copy_peak_GB_per_s": round(self.pinned_copy_peak(), 2),
+            }
+            res["streaming"]["link_frac_of_pinned_peak"] = round(link / res["streaming"]["pinned_copy_peak_GB_per_s"], 4)
         res["_layers"] = layers
         res["_tokens"] = tokens
         return res
+
+    def pinned_experts(self):
+        """Every expert's slice in page-locked host memory (a new pinned tensor)."""
+        if getattr(self, "_host", None) is None:
+            self._host = self.torch.empty(tuple(self.experts.shape), dtype=self.torch.uint8, pin_memory=True)
+            self._host.copy_(self.experts)
+        return self._host
+
+    def pinned_copy_peak(self):
+        """Host-to-device rate of one 1 GiB copy from page-locked memory."""
+        torch = self.torch
+        src = self.pinned_experts().view(-1)[:1 << 30]
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = 0.0
+        for _ in range(3):
+            ev0.record()
+            dst.copy_(src, non_blocking=True)
+            ev1.record()
+            torch.cuda.synchronize()
+            best = max(best, (1 << 30) / (ev0.elapsed_time(ev1) / 1e3) / 1e9)
+        del dst
+        return best
 
 
 def main():
@@ -381,10 +444,11 @@ def main():
     layers, tokens = head.pop("_layers"), head.pop("_tokens")
     extra = {}
     if wl == "decode" and not args.no_extra:
-        for other in ("small", "prefill", "prefill_hot"):
-            st = 100 if WORKLOADS[other]["m"] <= 8 else 10
-            log(f"{other}: 5 warmup + {st} timed steps")
-            r = b.run(other, st, 5)
+        for other in ("small", "prefill", "prefill_hot", "skewed"):
+            st = 100 if WORKLOADS[other]["m"] <= 8 else 5 if other == "skewed" else 10
+            wu = 3 if other == "skewed" else 5
+            log(f"{other}: {wu} warmup + {st} timed steps")
+            r = b.run(other, st, wu)
             r.pop("_layers"), r.pop("_tokens")
             extra[other] = r
 

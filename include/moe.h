@@ -81,16 +81,17 @@ typedef struct moe_weights {
 } moe_weights;
 
 /* Counters of the calls since creation or moe_reset_stats (metrale's MoeV41Timing:
- * hits, misses and bytes_read; host-clock milliseconds of the routing read-back
- * and of the miss copies; only calls that stream misses read routing back). */
+ * hits, misses and bytes_read; the time of the routing read-back and of the
+ * miss copies). Only calls made with a host arena read the routing back and
+ * stream; moe_get_stats / moe_reset_stats wait for the copies still queued. */
 typedef struct moe_stats {
     uint64_t calls;         /* moe_forward / moe_forward_ex calls */
-    uint64_t hits;          /* picked experts found resident, per streamed call */
+    uint64_t hits;          /* distinct picked experts already resident at a streamed call's start */
     uint64_t misses;        /* picked experts copied from the host arena */
     uint64_t bytes_copied;  /* host-to-device bytes of those copies */
     uint64_t waves;         /* slot waves run by streamed calls */
-    double route_ms;        /* host time waiting for the routing read-back */
-    double fetch_ms;        /* host time spent issuing and waiting on miss copies */
+    double route_ms;        /* host time waiting for the routing read-back (includes the queued work before it) */
+    double fetch_ms;        /* device time of the miss copies (events on the copy stream) */
 } moe_stats;
 
 typedef struct moe_ctx moe_ctx;
@@ -127,10 +128,16 @@ int moe_slot_of(const moe_ctx* ctx, int32_t expert, int32_t* slot);
 
 /* Optional page-locked host arena holding every routed expert's slice,
  * expert e at host + e * expert_stride (expert_stride >= slot_bytes). With it,
- * moe_forward streams the experts it needs that are not resident into the
- * device slots (least-recently-used eviction, hipMemcpyAsync on a side stream,
- * fenced by events), in waves of at most n_slots experts. NULL disables it.
- * The memory must come from hipHostMalloc (or equivalent pinned allocation). */
+ * every moe_forward reads its picks back (one host wait), copies the picked
+ * experts that are not resident into device slots (least recently used slots
+ * reused, hipMemcpyAsync on the context's copy stream, fenced by events) and
+ * rebinds the slot table. When the distinct picks outnumber the slots the
+ * experts run in waves of half the slots each (one wave's copies overlap the
+ * previous wave's kernels). The memory must be page-locked (hipHostMalloc or
+ * an equivalent pinned allocation); NULL disables streaming. Slots the caller
+ * bound stay usable and become part of the LRU. MOE_EINVAL for a stride below
+ * slot_bytes; MOE_ENOMEM / MOE_EHIP when the copy stream or its pinned
+ * buffers cannot be made. */
 int moe_set_host_arena(moe_ctx* ctx, const void* pinned_host, size_t expert_stride);
 
 /* Routing only (metrale's route / route_launch, with the selection on the

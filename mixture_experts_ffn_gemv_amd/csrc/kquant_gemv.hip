@@ -93,6 +93,7 @@ __global__ __launch_bounds__(512) void gateup_q2k_kernel(ExpertArgs a, int R, in
         w1 = a.sh_w1;
         w3 = a.sh_w3;
     } else {
+        if (a.slot_table[ch.expert] == SLOT_SKIP) return;   // computed in another slot wave
         const uint8_t* base = expert_base(a, ch.expert);
         if (base == nullptr) {
             if (threadIdx.x == 0 && tile == 0) atomicOr(a.err, ERR_NOTRESIDENT);
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(640) void down_q3k_kernel(ExpertArgs a, int R, int 
     if (cr.shared) {
         w2 = a.sh_w2;
     } else {
+        if (a.slot_table[ch.expert] == SLOT_SKIP) return;   // computed in another slot wave
         const uint8_t* base = expert_base(a, ch.expert);
         if (base == nullptr) {
             for (int q = threadIdx.x; q < R * cr.nrows; q += blockDim.x)

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int K
         w3 = a.sh_w3;
     } else {
         const int slot = a.slot_table[ch.expert];
+        if (slot == SLOT_SKIP) return;   // computed in another slot wave
         if (slot < 0) {
             if (tid == 0 && rt == 0) atomicOr(a.err, ERR_NOTRESIDENT);
             for (int q = tid; q < TILE_ROWS * ch.nrows; q += 256)
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a) {
         w2 = a.sh_w2;
     } else {
         const int slot = a.slot_table[ch.expert];
+        if (slot == SLOT_SKIP) return;   // computed in another slot wave
         if (slot < 0) {
             for (int q = tid; q < TILE_ROWS * ch.nrows; q += 256)
                 eout[(size_t)(q / TILE_ROWS) * D + r0 + q % TILE_ROWS] = 0.f;

@@ -85,10 +85,17 @@ struct moe_ctx {
     bool table_dirty = true;
     hipEvent_t table_ev = nullptr;
     bool table_ev_pending = false;
-    // host arena
+    // host arena and the miss streaming (copies on their own stream, fenced by events)
     const uint8_t* host_arena = nullptr;
     size_t host_stride = 0;
-    moe_stats stats;
+    hipStream_t copy = nullptr;
+    int32_t* idx_host = nullptr;    // pinned read-back of the picks
+    int32_t* view_host = nullptr;   // pinned per-wave slot tables, [E][E]
+    std::vector<uint64_t> slot_tick; // slot -> last call that used it (least recently used goes first)
+    uint64_t tick = 0;
+    std::vector<hipEvent_t> ev_copy, ev_wave, ev_c0, ev_c1;   // per wave
+    mutable std::vector<std::pair<hipEvent_t, hipEvent_t>> fetch_pending;
+    mutable moe_stats stats;
     // per-kernel timing
     bool prof = false;
     std::vector<hipEvent_t> ev_pool;
@@ -366,6 +373,11 @@ int moe_destroy(moe_ctx* ctx) {
     if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
     if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
     if (ctx->side) (void)hipStreamDestroy(ctx->side);
+    if (ctx->copy) (void)hipStreamDestroy(ctx->copy);
+    for (auto* v : {&ctx->ev_copy, &ctx->ev_wave, &ctx->ev_c0, &ctx->ev_c1})
+        for (hipEvent_t e : *v) (void)hipEventDestroy(e);
+    if (ctx->idx_host) (void)hipHostFree(ctx->idx_host);
+    if (ctx->view_host) (void)hipHostFree(ctx->view_host);
     for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
     if (ctx->slot_host) (void)hipHostFree(ctx->slot_host);
     if (ctx->dev) (void)hipFree(ctx->dev);
@@ -380,6 +392,7 @@ int moe_set_slots(moe_ctx* ctx, void* arena_dev, int32_t n_slots) {
     ctx->arena = (uint8_t*)arena_dev;
     ctx->n_slots = n_slots;
     ctx->slot_owner.assign(n_slots, -1);
+    ctx->slot_tick.assign(n_slots, 0);
     for (int e = 0; e < ctx->cfg.n_routed; ++e) ctx->slot_host[e] = -1;
     ctx->table_dirty = true;
     return MOE_OK;
@@ -423,6 +436,13 @@ int moe_slot_of(const moe_ctx* ctx, int32_t expert, int32_t* slot) {
 int moe_set_host_arena(moe_ctx* ctx, const void* pinned_host, size_t expert_stride) {
     if (ctx == nullptr) return MOE_EINVAL;
     if (pinned_host != nullptr && expert_stride < ctx->slot_bytes) return MOE_EINVAL;
+    if (pinned_host != nullptr && ctx->copy == nullptr) {
+        const size_t E = ctx->cfg.n_routed;
+        if (hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking) != hipSuccess) return MOE_EHIP;
+        if (hipHostMalloc((void**)&ctx->idx_host, sizeof(int32_t) * ctx->max_pairs, hipHostMallocDefault) != hipSuccess ||
+            hipHostMalloc((void**)&ctx->view_host, sizeof(int32_t) * E * E, hipHostMallocDefault) != hipSuccess)
+            return MOE_ENOMEM;
+    }
     ctx->host_arena = (const uint8_t*)pinned_host;
     ctx->host_stride = expert_stride;
     return MOE_OK;
@@ -446,6 +466,121 @@ static int finish_call(moe_ctx* ctx, float* weights_out, int32_t* idx_out, int P
         hipMemcpyAsync(idx_out, ctx->idx, sizeof(int32_t) * P, hipMemcpyDeviceToDevice, st) != hipSuccess)
         return MOE_EHIP;
     ctx->stats.calls++;
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- miss streaming
+// (metrale's ExpertLru and forward: route, read the picks back, gather the
+// picked experts' slices into device slots, misses copied from the host arena
+// on a side stream; MoeV41 struct documentation, forward / arena_of)
+
+static hipEvent_t wave_event(std::vector<hipEvent_t>& pool, size_t w, bool timing) {
+    while (pool.size() <= w) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, timing ? hipEventDefault : hipEventDisableTiming) != hipSuccess) return nullptr;
+        pool.push_back(e);
+    }
+    return pool[w];
+}
+
+static void collect_fetch_times(const moe_ctx* ctx) {
+    for (const auto& pr : ctx->fetch_pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(pr.second) == hipSuccess && hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess)
+            ctx->stats.fetch_ms += ms;
+    }
+    ctx->fetch_pending.clear();
+}
+
+// Read the picks back (the one host wait of a streamed call) and split the
+// distinct experts into waves that fit the slots: resident ones first, so no
+// wave evicts an expert a later wave still finds resident; several waves take
+// half the slots each, so one wave's copies never overwrite the slots the
+// wave before it is still computing with.
+static int plan_waves(moe_ctx* ctx, int P, hipStream_t st, std::vector<std::vector<int>>& waves) {
+    waves.clear();
+    const auto t0 = std::chrono::steady_clock::now();
+    if (hipMemcpyAsync(ctx->idx_host, ctx->idx, sizeof(int32_t) * P, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return MOE_EHIP;
+    ctx->stats.route_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    collect_fetch_times(ctx);
+    std::vector<char> seen(ctx->cfg.n_routed, 0);
+    std::vector<int> hits, misses;
+    for (int p = 0; p < P; ++p) {
+        const int e = ctx->idx_host[p];
+        if (e < 0 || e >= ctx->cfg.n_routed || seen[e]) continue;
+        seen[e] = 1;
+    }
+    for (int e = 0; e < ctx->cfg.n_routed; ++e)
+        if (seen[e]) (ctx->slot_host[e] >= 0 ? hits : misses).push_back(e);
+    ctx->stats.hits += hits.size();
+    std::vector<int> order(hits);
+    order.insert(order.end(), misses.begin(), misses.end());
+    const int n = (int)order.size();
+    const int cap = n <= ctx->n_slots ? ctx->n_slots : std::max(1, ctx->n_slots / 2);
+    for (int i = 0; i < n; i += cap)
+        waves.emplace_back(order.begin() + i, order.begin() + std::min(n, i + cap));
+    return MOE_OK;
+}
+
+// Make wave w resident (least recently used slots outside this wave and the one
+// before it are reused), then point the device table at it: the wave's experts
+// at their slots, the experts of the other waves at SLOT_SKIP.
+static int run_wave(moe_ctx* ctx, const std::vector<std::vector<int>>& waves, size_t w, hipStream_t st) {
+    int rc = table_mutable(ctx);
+    if (rc != MOE_OK) return rc;
+    const int E = ctx->cfg.n_routed;
+    std::vector<char> keep(ctx->n_slots, 0);
+    for (size_t v = (w > 0 ? w - 1 : 0); v <= w; ++v)
+        for (int e : waves[v])
+            if (ctx->slot_host[e] >= 0) keep[ctx->slot_host[e]] = 1;
+    ++ctx->tick;
+    hipEvent_t c0 = wave_event(ctx->ev_c0, w, true), c1 = wave_event(ctx->ev_c1, w, true);
+    hipEvent_t ec = wave_event(ctx->ev_copy, w, false);
+    if (c0 == nullptr || c1 == nullptr || ec == nullptr) return MOE_EHIP;
+    // the slots of wave w - 2 may be overwritten: wait until that wave's kernels are done
+    if (w >= 2 && hipStreamWaitEvent(ctx->copy, ctx->ev_wave[w - 2], 0) != hipSuccess) return MOE_EHIP;
+    bool copied = false;
+    for (int e : waves[w]) {
+        if (ctx->slot_host[e] < 0) {
+            int victim = -1;
+            for (int sl = 0; sl < ctx->n_slots; ++sl) {
+                if (keep[sl]) continue;
+                if (victim < 0 || (ctx->slot_owner[sl] < 0 && ctx->slot_owner[victim] >= 0) ||
+                    ((ctx->slot_owner[sl] < 0) == (ctx->slot_owner[victim] < 0) && ctx->slot_tick[sl] < ctx->slot_tick[victim]))
+                    victim = sl;
+            }
+            if (victim < 0) return MOE_ESTATE;   // cannot happen: a wave takes at most half the slots
+            if (!copied && hipEventRecord(c0, ctx->copy) != hipSuccess) return MOE_EHIP;
+            copied = true;
+            if (ctx->slot_owner[victim] >= 0) ctx->slot_host[ctx->slot_owner[victim]] = SLOT_NONE;
+            if (hipMemcpyAsync(ctx->arena + (size_t)victim * ctx->slot_bytes, ctx->host_arena + (size_t)e * ctx->host_stride,
+                               ctx->slot_bytes, hipMemcpyHostToDevice, ctx->copy) != hipSuccess)
+                return MOE_EHIP;
+            ctx->slot_owner[victim] = e;
+            ctx->slot_host[e] = victim;
+            ctx->stats.misses++;
+            ctx->stats.bytes_copied += ctx->slot_bytes;
+        }
+        keep[ctx->slot_host[e]] = 1;
+        ctx->slot_tick[ctx->slot_host[e]] = ctx->tick;
+    }
+    if (copied) {
+        if (hipEventRecord(c1, ctx->copy) != hipSuccess || hipEventRecord(ec, ctx->copy) != hipSuccess ||
+            hipStreamWaitEvent(st, ec, 0) != hipSuccess)
+            return MOE_EHIP;
+        ctx->fetch_pending.emplace_back(c0, c1);
+    }
+    int32_t* view = ctx->view_host + w * (size_t)E;
+    for (int e = 0; e < E; ++e) view[e] = ctx->slot_host[e];
+    for (size_t v = 0; v < waves.size(); ++v)
+        if (v != w)
+            for (int e : waves[v]) view[e] = SLOT_SKIP;
+    if (hipMemcpyAsync(ctx->slot_table_dev, view, sizeof(int32_t) * E, hipMemcpyHostToDevice, st) != hipSuccess)
+        return MOE_EHIP;
+    ctx->table_dirty = true;   // the next call uploads the residency table again
+    ctx->stats.waves++;
     return MOE_OK;
 }
 
@@ -562,7 +697,20 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.err = ctx->err;
     const int chunks = routed_chunk_bound(c, m) + (kq ? shared_chunk_count(m) : 0);
     const float* ys = w->shared_fmt == MOE_SHARED_BF16 ? ctx->ys : nullptr;
-    if (small && ctx->decode_ok) {
+
+    // with a host arena: read the picks back and stream the missing experts in
+    std::vector<std::vector<int>> waves;
+    if (ctx->host_arena != nullptr) {
+        rc = plan_waves(ctx, P, st, waves);
+        if (rc != MOE_OK) return rc;
+        if (waves.size() == 1) {
+            rc = run_wave(ctx, waves, 0, st);
+            if (rc != MOE_OK) return rc;
+            if (small && hip_status(launch_refresh_slots(ctx->chunks, ctx->n_chunks, ctx->slot_table_dev, st)) != MOE_OK)
+                return MOE_EHIP;
+        }
+    }
+    if (small && ctx->decode_ok && waves.size() <= 1) {
         // one single-row chunk per pick (and per token of a K-quant shared expert):
         // gate/up writes q8_1(h) records, down accumulates G E per token and stores bf16
         const int nch = P + (kq ? m : 0);
@@ -575,23 +723,35 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (rc != MOE_OK) return rc;
         return finish_call(ctx, weights_out, idx_out, P, st);
     }
-    // chunks of at most GEMV_ROWS rows, or single rows on the small-batch routing
+    // chunks of at most GEMV_ROWS rows, or single rows on the small-batch routing;
+    // with several slot waves the kernels run once per wave and skip the other waves' experts
     const int rows_max = small ? 1 : std::min(m, GEMV_ROWS);
-    if (use_mmq) {
-        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, plan, true, st); });
-        if (rc != MOE_OK) return rc;
-        rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
-        if (rc != MOE_OK) return rc;
-        rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, plan, false, st); });
-        if (rc != MOE_OK) return rc;
-    } else {
-        const int nch = small ? P + (kq ? m : 0) : chunks;
-        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, nch, st); });
-        if (rc != MOE_OK) return rc;
-        rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
-        if (rc != MOE_OK) return rc;
-        rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, nch, st); });
-        if (rc != MOE_OK) return rc;
+    const int nch = small ? P + (kq ? m : 0) : chunks;
+    const size_t n_runs = std::max<size_t>(1, waves.size());
+    for (size_t wv = 0; wv < n_runs; ++wv) {
+        if (waves.size() > 1) {
+            rc = run_wave(ctx, waves, wv, st);
+            if (rc != MOE_OK) return rc;
+        }
+        if (use_mmq) {
+            rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, plan, true, st); });
+            if (rc != MOE_OK) return rc;
+            rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
+            if (rc != MOE_OK) return rc;
+            rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, plan, false, st); });
+            if (rc != MOE_OK) return rc;
+        } else {
+            rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, nch, st); });
+            if (rc != MOE_OK) return rc;
+            rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
+            if (rc != MOE_OK) return rc;
+            rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, nch, st); });
+            if (rc != MOE_OK) return rc;
+        }
+        if (waves.size() > 1) {
+            hipEvent_t ew = wave_event(ctx->ev_wave, wv, false);
+            if (ew == nullptr || hipEventRecord(ew, st) != hipSuccess) return MOE_EHIP;
+        }
     }
     if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
     const float* ys_all = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
@@ -663,12 +823,14 @@ int moe_kernel_times(moe_ctx* ctx, double* ms_sum, int64_t* launches, int32_t n)
 
 int moe_get_stats(const moe_ctx* ctx, moe_stats* out) {
     if (ctx == nullptr || out == nullptr) return MOE_EINVAL;
+    collect_fetch_times(ctx);
     *out = ctx->stats;
     return MOE_OK;
 }
 
 int moe_reset_stats(moe_ctx* ctx) {
     if (ctx == nullptr) return MOE_EINVAL;
+    collect_fetch_times(ctx);
     std::memset(&ctx->stats, 0, sizeof(ctx->stats));
     return MOE_OK;
 }

@@ -18,6 +18,10 @@ constexpr int GEMV_ROWS = 8;     // token rows per GEMV chunk
 // device error word bits
 constexpr int ERR_NONFINITE = 1;
 constexpr int ERR_NOTRESIDENT = 2;
+// slot-table entries: >= 0 a slot; -1 not resident (an error when picked);
+// SLOT_SKIP: picked, but computed in another slot wave of this call (the kernels skip it)
+constexpr int SLOT_NONE = -1;
+constexpr int SLOT_SKIP = -2;
 
 // One unit of expert work: up to GEMV_ROWS token rows of one expert.
 // expert >= 0: routed expert; row0 is a position in the expert-sorted pair list.

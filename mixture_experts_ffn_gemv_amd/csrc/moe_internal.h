@@ -88,6 +88,8 @@ hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int
 hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st);
+// the small-batch chunks re-read their experts' slots (after miss streaming)
+hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, hipStream_t st);
 bool mmq_supported(int D, int I);
 // one launch per class with reserved slots; a.chunks / a.n_chunks point at class 0
 hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st);

@@ -466,7 +466,23 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     }
 }
 
+// After experts were streamed into slots: the single-row chunks of the small-batch
+// routing take their experts' slots again from the table.
+__global__ __launch_bounds__(256) void refresh_slots_kernel(Chunk* __restrict__ chunks,
+                                                            const int32_t* __restrict__ n_chunks,
+                                                            const int32_t* __restrict__ slot_table) {
+    const int n = *n_chunks;
+    for (int c = threadIdx.x; c < n; c += 256) {
+        const int e = chunks[c].expert;
+        if (e >= 0) chunks[c].slot = slot_table[e];
+    }
+}
+
 // ---------------------------------------------------------------- launchers
+hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, hipStream_t st) {
+    return launch_kernel(refresh_slots_kernel, 1, 256, 0, st, chunks, n_chunks, slot_table);
+}
+
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                                int8_t* xq, float* xd, int32_t* xs16, hipStream_t st) {
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;

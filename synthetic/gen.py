@@ -43,7 +43,7 @@ REAL = LayerShape(dim=5120, inter=2304, n_routed=384, topk=6)
 # 2048-token skewed prefill on the real layer (seed 1). Calibrated so the 38 most
 # loaded experts take 50 +- 1 % of the assignments; tests/golden/make_c4_bias.py
 # wrote it and tests/test_synthetic.py checks it with the oracle's router.
-C4_BIAS_SCALE = 0.0
+C4_BIAS_SCALE = 0.143256
 
 
 def stream_seed(seed, tag, index=0, matrix=0):

@@ -22,7 +22,7 @@ def bits(t):
 class Layer:
     def __init__(self, shape, seed, *, shared_fmt="bf16", bias=(-0.1, 0.1), router_std=0.05, max_tokens=8,
                  expert_device="cpu", gate_temp=1.0, norm=True, route_scale=1.5, limit=10.0, bind_all=True,
-                 n_slots=None, experts=None, verbose=False):
+                 n_slots=None, experts=None, host_arena=False, verbose=False):
         self.shape = shape
         self.dev = torch.device("cuda")
         t0 = time.time()
@@ -44,6 +44,12 @@ class Layer:
         if bind_all and self.n_slots == shape.n_routed:
             for e in range(shape.n_routed):
                 moe.moe_slot_bind(self.ctx, e, e)
+        self.host = None
+        if host_arena:
+            # every expert in page-locked host memory (a new pinned tensor, not a registered one)
+            self.host = torch.empty(self.arena_src.shape, dtype=torch.uint8, pin_memory=True)
+            self.host.copy_(self.arena_src)
+            moe.moe_set_host_arena(self.ctx, self.host, self.arena_src.shape[1])
         self.d_wr = self.wr.to(self.dev)
         self.d_bias = self.bias.to(self.dev)
         self.d_shared = None
