@@ -31,21 +31,46 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
     return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (i32x4_t){0, 0, 0, 0}, 0, 0, 0);
 }
 
-MOE_DEV int chunk_token_mmq(const ExpertArgs& a, const Chunk& ch, int i) {
-    return ch.expert < 0 ? ch.row0 + i : a.perm[ch.row0 + i] / a.topk;
-}
 
 }  // namespace
 
+// Workgroups are spread over the 8 XCDs round-robin by id; the tiles of one
+// chunk are given consecutive logical ids on one XCD so that their shared
+// activation rows are fetched into one L2 (nb_pad is a multiple of 8).
+MOE_DEV int xcd_logical_block(int b, int nb_pad) { return (b & 7) * (nb_pad >> 3) + (b >> 3); }
+
 // ------------------------------------------------------------------ Q2_K gate/up
-// LDS: raw blocks of 64 W1 rows then 64 W3 rows, KS superblocks at a time.
+// Rounds of KS = 2 superblocks. Per round the workgroup stages, through
+// registers into LDS (the next round's loads in flight while the current
+// round is computed): the raw blocks of its 64 W1 and 64 W3 rows, the q8_1
+// quants of its token rows, their block scales and their per-16 sums (both
+// transposed to [k][row] so a lane reads its four C rows at once).
+namespace {
+constexpr int GKS = 2;                        // superblocks per round
+constexpr int GW_DW = GKS * Q2K_BYTES / 4;    // 42 dwords of one row per round
+constexpr int GA_STRIDE = GKS * QK + 16;      // bytes per token row in LDS (padded against bank conflicts)
+
 template <int NS>
-__global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int KS) {
+struct GateupLds {
+    static constexpr int rows = NS * 16;
+    static constexpr int w_bytes = 128 * GW_DW * 4;
+    static constexpr int a_off = w_bytes;
+    static constexpr int dx_off = a_off + rows * GA_STRIDE;        // [GKS * 8][rows] f32
+    static constexpr int x16_off = dx_off + GKS * 8 * rows * 4;    // [GKS * 16][rows] f32
+    static constexpr int bytes = x16_off + GKS * 16 * rows * 4;
+};
+}  // namespace
+
+template <int NS>
+__global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int nb) {
     extern __shared__ __align__(16) uint8_t smem[];
+    using LL = GateupLds<NS>;
     const int D = a.D, I = a.I;
     const int nsb = D / QK;
     const int tiles = I / TILE_ROWS;
-    const int c = blockIdx.x / tiles, rt = blockIdx.x % tiles;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (lb >= nb) return;
+    const int c = lb / tiles, rt = lb % tiles;
     if (c >= *a.n_chunks) return;
     const Chunk ch = a.chunks[c];
     const bool shared = ch.expert < 0;
@@ -70,45 +95,129 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int K
         w3 = base + a.off_w3;
     }
     const size_t rowbytes = (size_t)nsb * Q2K_BYTES;
-    const int seg_dw = KS * Q2K_BYTES / 4;              // dwords per row segment
-    uint32_t* lds = reinterpret_cast<uint32_t*>(smem);   // [128 rows][seg_dw]
+    const int rounds = (nsb + GKS - 1) / GKS;
+
+    // --- staging assignments (fixed over the rounds; the last round may hold one superblock)
+    // weights: dword q = tid + 256 u of the [128 rows][ks * 21] segment
+    // activations: 16-byte chunk q = tid + 256 u of the [rows][ks * 16] quants
+    constexpr int NW = 128 * GW_DW / 256;          // 21
+    constexpr int NA = (LL::rows * GKS * 16 + 255) / 256;
+    uint32_t wr[NW];
+    uint4 ar[NA];
+    uint4 dxr, x16r0, x16r1;
+    auto token_of = [&](int i) { return i < ch.nrows ? (shared ? ch.row0 + i : a.perm[ch.row0 + i] / a.topk) : -1; };
+    auto stage_load = [&](int rd) {
+        const int sb0 = rd * GKS, ks = min(GKS, nsb - sb0), seg = ks * 21;
+        // weights: row = q / seg (magic multipliers, exact for q < 128 * 42)
+#pragma unroll
+        for (int u = 0; u < NW; ++u) {
+            const int q = tid + 256 * u;
+            const int row = ks == 2 ? (int)(((uint32_t)q * 24967u) >> 20) : (int)(((uint32_t)q * 49933u) >> 20);
+            const int dw = q - row * seg;
+            wr[u] = 0u;
+            if (row < 128) {
+                const uint8_t* src = (row < 64 ? w1 + (size_t)(r0 + row) * rowbytes
+                                               : w3 + (size_t)(r0 + row - 64) * rowbytes) + (size_t)sb0 * Q2K_BYTES;
+                wr[u] = reinterpret_cast<const uint32_t*>(src)[dw];
+            }
+        }
+        const int cpr = ks * 16;   // 16-byte chunks of quants per token row
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int q = tid + 256 * u;
+            const int row = q / cpr, col = q % cpr;
+            ar[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < LL::rows) {
+                const int t = token_of(row);
+                if (t >= 0) ar[u] = reinterpret_cast<const uint4*>(a.xq + (size_t)t * D + sb0 * QK)[col];
+            }
+        }
+        // scales: row = tid / (2 ks), 4 consecutive blocks; 16-sums: row = tid / (4 ks)
+        dxr = make_uint4(0u, 0u, 0u, 0u);
+        {
+            const int row = tid / (2 * ks), col = tid % (2 * ks);
+            if (row < LL::rows) {
+                const int t = token_of(row);
+                if (t >= 0) dxr = reinterpret_cast<const uint4*>(a.xd + (size_t)t * (D / QB) + sb0 * 8)[col];
+            }
+        }
+        x16r0 = x16r1 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = tid + 256 * u;
+            const int row = q / (4 * ks), col = q % (4 * ks);
+            if (row < LL::rows) {
+                const int t = token_of(row);
+                if (t >= 0) {
+                    const uint4 v = reinterpret_cast<const uint4*>(a.xs16f + (size_t)t * (D / 16) + sb0 * 16)[col];
+                    if (u == 0) x16r0 = v; else x16r1 = v;
+                }
+            }
+        }
+    };
+    auto stage_store = [&](int rd) {
+        const int sb0 = rd * GKS, ks = min(GKS, nsb - sb0), seg = ks * 21;
+        uint32_t* wl = reinterpret_cast<uint32_t*>(smem);
+#pragma unroll
+        for (int u = 0; u < NW; ++u) {
+            const int q = tid + 256 * u;
+            const int row = ks == 2 ? (int)(((uint32_t)q * 24967u) >> 20) : (int)(((uint32_t)q * 49933u) >> 20);
+            if (row < 128) wl[row * GW_DW + (q - row * seg)] = wr[u];
+        }
+        const int cpr = ks * 16;
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int q = tid + 256 * u;
+            const int row = q / cpr, col = q % cpr;
+            if (row < LL::rows) *reinterpret_cast<uint4*>(smem + LL::a_off + row * GA_STRIDE + col * 16) = ar[u];
+        }
+        float* dxl = reinterpret_cast<float*>(smem + LL::dx_off);
+        {
+            const int row = tid / (2 * ks), col = tid % (2 * ks);
+            if (row < LL::rows) {
+                dxl[(4 * col + 0) * LL::rows + row] = __uint_as_float(dxr.x);
+                dxl[(4 * col + 1) * LL::rows + row] = __uint_as_float(dxr.y);
+                dxl[(4 * col + 2) * LL::rows + row] = __uint_as_float(dxr.z);
+                dxl[(4 * col + 3) * LL::rows + row] = __uint_as_float(dxr.w);
+            }
+        }
+        float* xl = reinterpret_cast<float*>(smem + LL::x16_off);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = tid + 256 * u;
+            const int row = q / (4 * ks), col = q % (4 * ks);
+            const uint4 v = u == 0 ? x16r0 : x16r1;
+            if (row < LL::rows) {
+                xl[(4 * col + 0) * LL::rows + row] = __uint_as_float(v.x);
+                xl[(4 * col + 1) * LL::rows + row] = __uint_as_float(v.y);
+                xl[(4 * col + 2) * LL::rows + row] = __uint_as_float(v.z);
+                xl[(4 * col + 3) * LL::rows + row] = __uint_as_float(v.w);
+            }
+        }
+    };
 
     // A rows: token of sub-tile s, row lane % 16; C rows: tokens 4 (lane / 16) + r
     const int g = lane >> 4, l16 = lane & 15;
-    int tokA[NS], tokC[NS][4];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int ia = 16 * s + l16;
-        tokA[s] = ia < ch.nrows ? chunk_token_mmq(a, ch, ia) : -1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ic = 16 * s + 4 * g + r;
-            tokC[s][r] = ic < ch.nrows ? chunk_token_mmq(a, ch, ic) : -1;
-        }
-    }
     typedef float f4 __attribute__((ext_vector_type(4)));
     f4 accg[NS], accu[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) accg[s] = accu[s] = (f4){0.f, 0.f, 0.f, 0.f};
     const int ns = min(NS, (ch.nrows + 15) / 16);   // sub-tiles holding tokens
+    const int wrow = 16 * wv + l16;                   // this lane's weight row (B column) in the tile
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(smem);
+    const float* dxl = reinterpret_cast<const float*>(smem + LL::dx_off);
+    const float* xl = reinterpret_cast<const float*>(smem + LL::x16_off);
 
-    const int wrow = 16 * wv + l16;   // this lane's weight row (B column) in the tile
-    for (int sb0 = 0; sb0 < nsb; sb0 += KS) {
-        const int ks = min(KS, nsb - sb0);
-        const int sdw = ks * Q2K_BYTES / 4;
-        // stage rows [r0, r0+64) of W1 and W3, superblocks [sb0, sb0+ks)
-        for (int q = tid; q < 128 * sdw; q += 256) {
-            const int row = q / sdw, dw = q % sdw;
-            const uint8_t* src = (row < 64 ? w1 + (size_t)(r0 + row) * rowbytes
-                                            : w3 + (size_t)(r0 + row - 64) * rowbytes) +
-                                 (size_t)sb0 * Q2K_BYTES;
-            lds[row * seg_dw + dw] = reinterpret_cast<const uint32_t*>(src)[dw];
-        }
+    stage_load(0);
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rd > 0) __syncthreads();   // the previous round is consumed
+        stage_store(rd);
         __syncthreads();
+        if (rd + 1 < rounds) stage_load(rd + 1);   // in flight during this round's products
+        const int ks = min(GKS, nsb - rd * GKS);
         for (int sbi = 0; sbi < ks; ++sbi) {
-            const int sb = sb0 + sbi;
-            const uint32_t* bg = lds + wrow * seg_dw + sbi * (Q2K_BYTES / 4);
-            const uint32_t* bu = lds + (64 + wrow) * seg_dw + sbi * (Q2K_BYTES / 4);
+            const uint32_t* bg = wl + wrow * GW_DW + sbi * 21;
+            const uint32_t* bu = wl + (64 + wrow) * GW_DW + sbi * 21;
             const uint32_t ddg = bg[20], ddu = bu[20];
             const float dg = half_bits_to_f32(ddg & 0xFFFFu), dming = half_bits_to_f32(ddg >> 16);
             const float du = half_bits_to_f32(ddu & 0xFFFFu), dminu = half_bits_to_f32(ddu >> 16);
@@ -129,19 +238,19 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int K
                 const uint32_t bu1 = ((bu[qd + 1] >> (2 * j)) & 0x03030303u) * scu;
                 const int64_t Bg = (int64_t)(((uint64_t)bg1 << 32) | bg0);
                 const int64_t Bu = (int64_t)(((uint64_t)bu1 << 32) | bu0);
-                const int kbg = sb * 8 + kb8;
+                const int kk = sbi * 8 + kb8;   // block within the round
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     if (s >= ns) break;
-                    int64_t A = 0;
-                    if (tokA[s] >= 0) A = *reinterpret_cast<const int64_t*>(a.xq + (size_t)tokA[s] * D + kbg * QB + 8 * g);
+                    const int64_t A = *reinterpret_cast<const int64_t*>(smem + LL::a_off + (16 * s + l16) * GA_STRIDE +
+                                                                        kk * QB + 8 * g);
                     const i32x4_t cg = mfma_i8(A, Bg);
                     const i32x4_t cu = mfma_i8(A, Bu);
+                    const f4 dx = *reinterpret_cast<const f4*>(dxl + kk * LL::rows + 16 * s + 4 * g);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float dx = tokC[s][r] >= 0 ? a.xd[(size_t)tokC[s][r] * (D / QB) + kbg] : 0.f;
-                        sg[s][r] = fmaf((float)cg[r], dx, sg[s][r]);
-                        su[s][r] = fmaf((float)cu[r], dx, su[s][r]);
+                        sg[s][r] = fmaf((float)cg[r], dx[r], sg[s][r]);
+                        su[s][r] = fmaf((float)cu[r], dx[r], su[s][r]);
                     }
                 }
             }
@@ -165,13 +274,12 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int K
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float x16 = tokA[s] >= 0 ? a.xs16f[(size_t)tokA[s] * (D / 16) + sb * 16 + 4 * q + g] : 0.f;
+                    const float x16 = xl[(sbi * 16 + 4 * q + g) * LL::rows + 16 * s + l16];
                     accg[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(x16, bmg[q], accg[s], 0, 0, 0);
                     accu[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(x16, bmu[q], accu[s], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -184,16 +292,34 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int K
 }
 
 // ------------------------------------------------------------------ Q3_K down
-// LDS: the raw blocks of 64 whole W2 rows (contiguous), then the 64-entry byte
-// lookup table (32 - sc6) * (v - 4) for v = 0..7, indexed by sc6.
+// LDS: the raw blocks of the 64 whole W2 rows (contiguous, staged once), the
+// 64-entry byte lookup table (32 - sc6) * (v - 4) for v = 0..7 indexed by sc6,
+// then per superblock the q8_1 quants of the chunk's h rows and their block
+// scales ([k][row]), staged through registers one superblock ahead.
+namespace {
+constexpr int DA_STRIDE = QK + 16;  // bytes per h row in LDS (padded against bank conflicts)
 template <int NS>
-__global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a) {
+struct DownLds {
+    static constexpr int rows = NS * 16;
+    __host__ __device__ static int w_bytes(int I) { return TILE_ROWS * (I / QK) * Q3K_BYTES; }   // multiple of 16
+    __host__ __device__ static int lut_off(int I) { return w_bytes(I) + 16; }
+    __host__ __device__ static int a_off(int I) { return lut_off(I) + 64 * 8; }
+    __host__ __device__ static int dx_off(int I) { return a_off(I) + rows * DA_STRIDE; }   // [8][rows] f32
+    __host__ __device__ static int bytes(int I) { return dx_off(I) + 8 * rows * 4; }
+};
+}  // namespace
+
+template <int NS>
+__global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb) {
     extern __shared__ __align__(16) uint8_t smem[];
+    using LL = DownLds<NS>;
     const int D = a.D, I = a.I;
     const int nsb = I / QK;
     const int rowbytes = nsb * Q3K_BYTES;
     const int tiles = D / TILE_ROWS;
-    const int c = blockIdx.x / tiles, rt = blockIdx.x % tiles;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (lb >= nb) return;
+    const int c = lb / tiles, rt = lb % tiles;
     if (c >= *a.n_chunks) return;
     const Chunk ch = a.chunks[c];
     const bool shared = ch.expert < 0;
@@ -213,13 +339,60 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a) {
         }
         w2 = a.arena + (size_t)slot * a.slot_bytes + a.off_w2;
     }
+    const int8_t* hq = shared ? a.hq_shared : a.hq_routed;
+    const float* hd = shared ? a.hd_shared : a.hd_routed;
+    const int rows_valid = ch.nrows;
+    // per superblock: 16-byte chunk q = tid + 256 u of [rows][16] quants; scales: row = tid / 2
+    constexpr int NA = (LL::rows * 16 + 255) / 256;
+    uint4 ar[NA];
+    uint4 dxr;
+    auto stage_load = [&](int sb) {
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int q = tid + 256 * u;
+            const int row = q >> 4, col = q & 15;
+            ar[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (row < rows_valid && row < LL::rows)
+                ar[u] = reinterpret_cast<const uint4*>(hq + (size_t)(ch.row0 + row) * I + sb * QK)[col];
+        }
+        dxr = make_uint4(0u, 0u, 0u, 0u);
+        const int row = tid >> 1, col = tid & 1;
+        if (row < rows_valid && row < LL::rows)
+            dxr = reinterpret_cast<const uint4*>(hd + (size_t)(ch.row0 + row) * (I / QB) + sb * 8)[col];
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int q = tid + 256 * u;
+            const int row = q >> 4, col = q & 15;
+            if (row < LL::rows) *reinterpret_cast<uint4*>(smem + LL::a_off(I) + row * DA_STRIDE + col * 16) = ar[u];
+        }
+        float* dxl = reinterpret_cast<float*>(smem + LL::dx_off(I));
+        const int row = tid >> 1, col = tid & 1;
+        if (row < LL::rows) {
+            dxl[(4 * col + 0) * LL::rows + row] = __uint_as_float(dxr.x);
+            dxl[(4 * col + 1) * LL::rows + row] = __uint_as_float(dxr.y);
+            dxl[(4 * col + 2) * LL::rows + row] = __uint_as_float(dxr.z);
+            dxl[(4 * col + 3) * LL::rows + row] = __uint_as_float(dxr.w);
+        }
+    };
+    stage_load(0);
     uint32_t* lds = reinterpret_cast<uint32_t*>(smem);
-    const int tile_bytes = TILE_ROWS * rowbytes;                 // multiple of 16 (64 * 110 * nsb)
-    uint2* lut = reinterpret_cast<uint2*>(smem + tile_bytes + 16);   // [64]
+    const int tile_bytes = LL::w_bytes(I);
+    uint2* lut = reinterpret_cast<uint2*>(smem + LL::lut_off(I));   // [64]
     {
         const uint4* src = reinterpret_cast<const uint4*>(w2 + (size_t)r0 * rowbytes);
         uint4* dst = reinterpret_cast<uint4*>(smem);
-        for (int q = tid; q < tile_bytes / 16; q += 256) dst[q] = src[q];
+        const int n16 = tile_bytes / 16;
+        int q = tid;
+        for (; q + 3 * 256 < n16; q += 4 * 256) {   // four loads in flight per step
+            const uint4 v0 = src[q], v1 = src[q + 256], v2 = src[q + 512], v3 = src[q + 768];
+            dst[q] = v0;
+            dst[q + 256] = v1;
+            dst[q + 512] = v2;
+            dst[q + 768] = v3;
+        }
+        for (; q < n16; q += 256) dst[q] = src[q];
         if (tid < 64) {
             const int sneg = 32 - tid;   // -(sc6 - 32)
             uint32_t lo = 0, hi = 0;
@@ -228,30 +401,20 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a) {
             lut[tid] = make_uint2(lo, hi);
         }
     }
-    __syncthreads();
 
-    const int hq_ld = I;
-    const int8_t* hq = shared ? a.hq_shared : a.hq_routed;
-    const float* hd = shared ? a.hd_shared : a.hd_routed;
     const int g = lane >> 4, l16 = lane & 15;
-    int rowA[NS], rowC[NS][4];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int ia = 16 * s + l16;
-        rowA[s] = ia < ch.nrows ? ch.row0 + ia : -1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ic = 16 * s + 4 * g + r;
-            rowC[s][r] = ic < ch.nrows ? ch.row0 + ic : -1;
-        }
-    }
     typedef float f4 __attribute__((ext_vector_type(4)));
     f4 acc[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[s] = (f4){0.f, 0.f, 0.f, 0.f};
     const int ns = min(NS, (ch.nrows + 15) / 16);
     const int wrow = 16 * wv + l16;
+    const float* dxl = reinterpret_cast<const float*>(smem + LL::dx_off(I));
     for (int sb = 0; sb < nsb; ++sb) {
+        if (sb > 0) __syncthreads();   // the previous superblock's activations are consumed
+        stage_store();
+        __syncthreads();
+        if (sb + 1 < nsb) stage_load(sb + 1);
         const int off = wrow * rowbytes + sb * Q3K_BYTES;   // 2-byte aligned
         const int A0 = off >> 2;
         const uint32_t sh = (uint32_t)(off & 3) * 8u;
@@ -281,18 +444,15 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a) {
             const uint32_t b0 = __builtin_amdgcn_perm(L.y, L.x, v0);
             const uint32_t b1 = __builtin_amdgcn_perm(L.y, L.x, v1);
             const int64_t B = (int64_t)(((uint64_t)b1 << 32) | b0);
-            const int kbg = sb * 8 + kb8;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
-                int64_t A = 0;
-                if (rowA[s] >= 0) A = *reinterpret_cast<const int64_t*>(hq + (size_t)rowA[s] * hq_ld + kbg * QB + 8 * g);
+                const int64_t A = *reinterpret_cast<const int64_t*>(smem + LL::a_off(I) + (16 * s + l16) * DA_STRIDE +
+                                                                    kb8 * QB + 8 * g);
                 const i32x4_t cc = mfma_i8(A, B);
+                const f4 dx = *reinterpret_cast<const f4*>(dxl + kb8 * LL::rows + 16 * s + 4 * g);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float dx = rowC[s][r] >= 0 ? hd[(size_t)rowC[s][r] * (I / QB) + kbg] : 0.f;
-                    ss[s][r] = fmaf((float)cc[r], dx, ss[s][r]);
-                }
+                for (int r = 0; r < 4; ++r) ss[s][r] = fmaf((float)cc[r], dx[r], ss[s][r]);
             }
         }
 #pragma unroll
@@ -312,20 +472,18 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a) {
 
 // ------------------------------------------------------------------ launch
 bool mmq_supported(int D, int I) {
-    // whole 64-row tiles, and the W2 tile plus its lookup table within LDS
-    return I % TILE_ROWS == 0 && D % TILE_ROWS == 0 &&
-           (size_t)TILE_ROWS * (I / QK) * Q3K_BYTES + 16 + 64 * 8 <= 160 * 1024;
+    // whole 64-row tiles, and the W2 tile, its lookup table and the widest
+    // class's activation rows within LDS
+    return I % TILE_ROWS == 0 && D % TILE_ROWS == 0 && DownLds<4>::bytes(I) <= 160 * 1024;
 }
 
 template <int NS>
 static hipError_t launch_mmq_ns(const ExpertArgs& a, int max_chunks, bool gateup, hipStream_t st) {
-    if (gateup) {
-        const int KS = 4;
-        const size_t lds = (size_t)128 * KS * Q2K_BYTES;
-        return launch_kernel(mmq_gateup_q2k_kernel<NS>, max_chunks * (a.I / TILE_ROWS), 256, lds, st, a, KS);
-    }
-    const size_t lds = (size_t)TILE_ROWS * (a.I / QK) * Q3K_BYTES + 16 + 64 * 8;
-    return launch_kernel(mmq_down_q3k_kernel<NS>, max_chunks * (a.D / TILE_ROWS), 256, lds, st, a);
+    const int nb = max_chunks * (gateup ? a.I / TILE_ROWS : a.D / TILE_ROWS);
+    const int nb_pad = (nb + 7) / 8 * 8;
+    if (gateup)
+        return launch_kernel(mmq_gateup_q2k_kernel<NS>, nb_pad, 256, (size_t)GateupLds<NS>::bytes, st, a, nb);
+    return launch_kernel(mmq_down_q3k_kernel<NS>, nb_pad, 256, (size_t)DownLds<NS>::bytes(a.I), st, a, nb);
 }
 
 hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st) {
