@@ -298,6 +298,38 @@ class Bench:
             raise RuntimeError(f"{wl} timed region: {moe.strerror(rc)}")
         stats = moe.moe_get_stats(ctx)
 
+        # decode: the same steps replayed from HIP graphs (one per layer, captured
+        # with a fixed input buffer that each step's token is copied into first)
+        graph_ms = None
+        if m <= 8 and not streamed:
+            x_static = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
+            out_static = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
+            x_static.copy_(xs(0))
+            graphs = []
+            for lay in layers:
+                moe.moe_forward(ctx, lay["w"], x_static, m, out_static)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    moe.moe_forward(ctx, lay["w"], x_static, m, out_static)
+                graphs.append(g)
+            for i in range(warmup):
+                x_static.copy_(xs(i))
+                graphs[i % n_layers].replay()
+            torch.cuda.synchronize()
+            gs = torch.cuda.current_stream()
+            ev0.record(gs)
+            for i in range(steps):
+                x_static.copy_(xs(warmup + i))
+                graphs[(warmup + i) % n_layers].replay()
+            ev1.record(gs)
+            torch.cuda.synchronize()
+            graph_ms = ev0.elapsed_time(ev1) / steps
+            rc = moe.moe_check(ctx)
+            if rc != moe.MOE_OK:
+                raise RuntimeError(f"{wl} graph replay: {moe.strerror(rc)}")
+            del graphs
+
         # the same K steps again with every kernel launch bracketed by HIP events on
         # its own stream (the library records them): per-kernel durations
         moe.moe_set_profiling(ctx, True)
@@ -358,6 +390,14 @@ class Bench:
             "gateup_avg_launch_ms": round(ga, 5),
             "gateup_GB_per_s": round(gateup_bytes / (ga / 1e3) / 1e9, 1),
         }
+        if graph_ms is not None:
+            res["graph_replay"] = {
+                "ms_per_step": round(graph_ms, 5),
+                "tokens_per_s": round(m / (graph_ms / 1e3), 2),
+                "layer_expert_GB_per_s": round(expert_bytes / (graph_ms / 1e3) / 1e9, 1),
+                "note": "one HIP graph per layer, each step copies its tokens into the graph's input buffer "
+                        "(copy included in the time)",
+            }
         if m > 8:
             # useful int8 products of the routed experts: 2 ops per multiply-add,
             # gate + up (2 I D) and down (D I) per pick
@@ -501,7 +541,7 @@ def main():
                          "the timed region",
         "kernel_avg_ms": head["kernel_avg_ms"],
     }
-    for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak"):
+    for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak", "graph_replay"):
         if k in head:
             result[k] = head[k]
     if extra:

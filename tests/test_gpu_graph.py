@@ -1,0 +1,59 @@
+"""GPU: the decode step captured in a HIP graph replays bit for bit like the
+eager call (the pages' compute_m1: no per-token host arguments, so one graph
+of it replays for any token written into its input buffer).
+
+Every replay is checked against an eager call of the same token, with the
+eager work and a synchronisation between replays.
+"""
+import pytest
+import torch
+
+import mixture_experts_ffn_gemv_amd as moe
+import synthetic as S
+from layer_fixture import Layer
+from test_gpu_parity import real_experts  # noqa: F401 (module fixture)
+
+pytestmark = pytest.mark.gpu
+
+
+def capture_and_compare(layer, tokens, label):
+    dev = layer.dev
+    m = 1
+    x_static = torch.zeros((m, layer.shape.dim), dtype=torch.bfloat16, device=dev)
+    out_static = torch.empty((m, layer.shape.dim), dtype=torch.bfloat16, device=dev)
+    x_static.copy_(tokens[0:1].to(dev))
+    moe.moe_forward(layer.ctx, layer.w, x_static, m, out_static)   # uploads the slot table before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_forward(layer.ctx, layer.w, x_static, m, out_static)
+    torch.cuda.synchronize()
+    for t in range(tokens.shape[0]):
+        x = tokens[t:t + 1].to(dev)
+        x_static.copy_(x)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out_static.clone()
+        ref = torch.empty_like(out_static)
+        moe.moe_forward(layer.ctx, layer.w, x, m, ref)   # eager work between replays
+        torch.cuda.synchronize()
+        assert layer.check() == moe.MOE_OK
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"{label}: token {t} differs"
+    print(f"[{label}] {tokens.shape[0]} replays bit-identical to eager", flush=True)
+
+
+@pytest.mark.parametrize("shared", ["bf16", "kquant", "none"])
+def test_tiny_decode_graph(shared):
+    layer = Layer(S.TINY, 0, max_tokens=8, shared_fmt=shared)
+    try:
+        capture_and_compare(layer, S.make_tokens(6, S.TINY.dim, 0, index=50), f"tiny graph {shared}")
+    finally:
+        layer.close()
+
+
+def test_real_decode_graph(real_experts):
+    layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=8, experts=real_experts)
+    try:
+        capture_and_compare(layer, S.make_tokens(4, S.REAL.dim, 1, index=0), "real decode graph")
+    finally:
+        layer.close()
