@@ -62,8 +62,8 @@ WORKLOADS = {
 }
 # the kernel each workload's roofline object describes, and its name in rocprofv3
 DOMINANT = {
-    "decode": ("gateup", r"^void moe::gateup_q2k_kernel<1>"),
-    "small": ("gateup", r"^void moe::gateup_q2k_kernel<"),
+    "decode": ("gateup", r"^moe::gateup_q8_kernel"),
+    "small": ("gateup", r"^moe::gateup_q8_kernel"),
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
     "skewed": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),
@@ -518,7 +518,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("gateup_q2k" if head["m"] <= 8 else "mmq_gateup_q2k") + " (routed gate/up + SwiGLU)",
+            "kernel": ("gateup_q8 (routed gate/up + SwiGLU + q8_1 of h)" if head["m"] <= 8
+                       else "mmq_gateup_q2k (routed gate/up + SwiGLU)"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
