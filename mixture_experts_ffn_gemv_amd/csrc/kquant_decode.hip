@@ -259,12 +259,14 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
             for (int cc = 0; cc < ng; ++cc) {
                 const int ubase = cc * unit;
                 const uint32_t* hq32 = lds32 + (ubase + tile_bytes) / 4;
-                uint32_t av[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) av[q] = hq32[kb * 8 + q];
+                // the lane's q8_1 block of h: two 16-byte reads (dword reads at a
+                // 32-byte lane stride conflicted on the LDS banks)
+                const uint4 h0 = reinterpret_cast<const uint4*>(hq32)[2 * kb];
+                const uint4 h1 = reinterpret_cast<const uint4*>(hq32)[2 * kb + 1];
+                const uint32_t av[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
                 const float dx = reinterpret_cast<const float*>(hq32 + I / 4)[kb];
-                const int* hs = reinterpret_cast<const int*>(hq32 + I / 4 + L);
-                const int slo = hs[2 * kb], shi = hs[2 * kb + 1];
+                const int2 hs = reinterpret_cast<const int2*>(hq32 + I / 4 + L)[kb];
+                const int slo = hs.x, shi = hs.y;
                 const int sb = ubase + pr * rowbytes + s * Q3K_BYTES;   // 2-byte aligned
                 const int A = sb >> 2;
                 const uint32_t sh = (uint32_t)(sb & 3) * 8u;              // 0 or 16

@@ -466,6 +466,136 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     }
 }
 
+// One token (decode): every thread scores one expert, then the first
+// wavefront selects, weighs and lists the picks without further barriers.
+// Its lane l holds experts l, l + 64, ...; each of the k rounds takes the
+// largest remaining key across the wavefront (ties to the lower expert id,
+// NaN keys last as on the general path). The winner of a round is
+// wavefront-uniform, so the picks stay in registers (lane r holds pick r).
+constexpr int M1_MAX_KEYS = 16;   // keys per lane: E <= 1024
+
+// wavefront-wide max / min, the result in every lane: DPP inside each 16-lane
+// row (quad swaps, then rotations by 4 and 8), then the four rows' values
+template <int CTRL>
+MOE_DEV int dpp_mov(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+MOE_DEV float wave_max_f32(float v) {
+    v = fmaxf(v, __int_as_float(dpp_mov<0xB1>(__float_as_int(v))));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, __int_as_float(dpp_mov<0x4E>(__float_as_int(v))));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, __int_as_float(dpp_mov<0x124>(__float_as_int(v))));   // row_ror:4
+    v = fmaxf(v, __int_as_float(dpp_mov<0x128>(__float_as_int(v))));   // row_ror:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+MOE_DEV int wave_min_i32(int v) {
+    v = min(v, dpp_mov<0xB1>(v));
+    v = min(v, dpp_mov<0x4E>(v));
+    v = min(v, dpp_mov<0x124>(v));
+    v = min(v, dpp_mov<0x128>(v));
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return min(min(r0, r1), min(r2, r3));
+}
+
+__global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                                                        int E, int k, float gate_temp, int norm, float route_scale,
+                                                        int32_t* __restrict__ idx, float* __restrict__ gw,
+                                                        int32_t* __restrict__ err, int shared_chunks,
+                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+                                                        int32_t* __restrict__ n_active, int32_t* __restrict__ perm,
+                                                        int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
+                                                        int32_t* __restrict__ n_chunks,
+                                                        const int32_t* __restrict__ slot_table) {
+    __shared__ float keys[64 * M1_MAX_KEYS], scores[64 * M1_MAX_KEYS];
+    const int tid = threadIdx.x;
+    {
+        float sv, kv;
+        bool bad;
+        score_key(logits, bias, tid, E, gate_temp, sv, kv, bad);
+        keys[tid] = kv;
+        scores[tid] = sv;
+        if (__any(bad) && (tid & 63) == 0) atomicOr(err, ERR_NONFINITE);
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    const int lane = tid;
+    float key[M1_MAX_KEYS];
+#pragma unroll
+    for (int i = 0; i < M1_MAX_KEYS; ++i) key[i] = lane + 64 * i < E ? keys[lane + 64 * i] : -INFINITY;
+    unsigned used = 0u;   // bit i: key i of this lane already picked
+    int my_e = 0;
+    float my_s = 0.f;
+    for (int r = 0; r < k; ++r) {
+        // the lane's best remaining key (lowest id among equal keys: ids grow with i)
+        float bk = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < M1_MAX_KEYS; ++i) {
+            const int id = lane + 64 * i;
+            if (id < E && !((used >> i) & 1u) && (key[i] > bk || (key[i] == bk && id < bi))) {
+                bk = key[i];
+                bi = id;
+            }
+        }
+        // across the wavefront: the largest key, then the lowest id holding it
+        const float kmax = wave_max_f32(bk);
+        const int win = wave_min_i32(bk == kmax ? bi : 0x7fffffff);
+        if ((win & 63) == lane) used |= 1u << (win >> 6);
+        if (lane == r) {
+            my_e = win;
+            my_s = scores[win];
+        }
+    }
+    // weights (the normaliser summed in pick order), and the picks sorted by
+    // expert id (all distinct): position = rank of the id
+    float sum = 0.f;
+    for (int q = 0; q < k; ++q) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), q));
+    const float wgt = (norm && k > 1 ? my_s / (sum + 1e-20f) : my_s) * route_scale;
+    int pos = 0;
+    for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(my_e, q) < my_e ? 1 : 0;
+    if (lane < k) {
+        idx[lane] = my_e;
+        gw[lane] = wgt;
+        perm[pos] = lane;
+        inv[lane] = pos;
+        active[pos] = my_e;
+        Chunk c;
+        c.expert = my_e;
+        c.row0 = pos;
+        c.nrows = 1;
+        c.slot = slot_table[my_e];
+        c.token = 0;
+        c.weight = wgt;
+        c.pad0 = c.pad1 = 0;
+        chunks[pos] = c;
+    }
+    if (shared_chunks && lane == 0) {
+        Chunk c;
+        c.expert = -1;
+        c.row0 = 0;
+        c.nrows = 1;
+        c.slot = 0;
+        c.token = 0;
+        c.weight = 1.f;
+        c.pad0 = c.pad1 = 0;
+        chunks[k] = c;
+    }
+    // offsets[e] = picks with a smaller id
+    for (int e = lane; e <= E; e += 64) {
+        int cnt = 0;
+        for (int q = 0; q < k; ++q) cnt += __builtin_amdgcn_readlane(my_e, q) < e ? 1 : 0;
+        offsets[e] = cnt;
+    }
+    if (lane == 0) {
+        *n_active = k;
+        *n_chunks = k + (shared_chunks ? 1 : 0);
+    }
+}
+
 // After experts were streamed into slots: the single-row chunks of the small-batch
 // routing take their experts' slots again from the table.
 __global__ __launch_bounds__(256) void refresh_slots_kernel(Chunk* __restrict__ chunks,
@@ -503,6 +633,9 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                               Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st) {
+    if (m == 1 && E <= 64 * M1_MAX_KEYS && k <= 64)
+        return launch_kernel(route_m1_kernel, 1, (E + 63) / 64 * 64, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, idx, gw,
+                             err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
     return launch_kernel(route_small_kernel, 1, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
                   shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
 }

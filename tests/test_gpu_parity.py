@@ -145,13 +145,29 @@ def test_route_only_matches_forward():
         layer.close()
 
 
-def test_nan_key_reported():
-    layer = Layer(S.TINY, 0, max_tokens=4)
+@pytest.mark.parametrize("m", [1, 2, 12])
+def test_nan_key_reported(m):
+    layer = Layer(S.TINY, 0, max_tokens=16)
     try:
         layer.d_bias[3] = float("nan")
-        layer.forward(S.make_tokens(2, 256, 1).cuda())
+        layer.forward(S.make_tokens(m, 256, 1).cuda())
         assert layer.check() == moe.MOE_ENONFINITE
         assert layer.check() == moe.MOE_OK          # the word is cleared by the read
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("m", [1, 3, 12])
+def test_tied_keys_pick_lowest_ids(m):
+    # a zero router and zero bias: every key is sqrt(ln 2), so each token picks
+    # experts 0..k-1 in that order (ties go to the lower id)
+    layer = Layer(S.TINY, 0, max_tokens=16, router_std=0.0, bias=None)
+    try:
+        _, gw, idx = layer.forward(S.make_tokens(m, 256, 6).cuda())
+        assert layer.check() == moe.MOE_OK
+        k = S.TINY.topk
+        assert idx.cpu().tolist() == [list(range(k))] * m
+        assert torch.allclose(gw.cpu(), torch.full((m, k), 1.5 / k))
     finally:
         layer.close()
 
