@@ -501,28 +501,13 @@ MOE_DEV int wave_min_i32(int v) {
     return min(min(r0, r1), min(r2, r3));
 }
 
-__global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
-                                                        int E, int k, float gate_temp, int norm, float route_scale,
-                                                        int32_t* __restrict__ idx, float* __restrict__ gw,
-                                                        int32_t* __restrict__ err, int shared_chunks,
-                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ active,
-                                                        int32_t* __restrict__ n_active, int32_t* __restrict__ perm,
-                                                        int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
-                                                        int32_t* __restrict__ n_chunks,
-                                                        const int32_t* __restrict__ slot_table) {
-    __shared__ float keys[64 * M1_MAX_KEYS], scores[64 * M1_MAX_KEYS];
-    const int tid = threadIdx.x;
-    {
-        float sv, kv;
-        bool bad;
-        score_key(logits, bias, tid, E, gate_temp, sv, kv, bad);
-        keys[tid] = kv;
-        scores[tid] = sv;
-        if (__any(bad) && (tid & 63) == 0) atomicOr(err, ERR_NONFINITE);
-    }
-    __syncthreads();
-    if (tid >= 64) return;
-    const int lane = tid;
+// The selection by the first wavefront, from all E keys and scores in LDS.
+MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int norm, float route_scale,
+                       int32_t* __restrict__ idx, float* __restrict__ gw, int shared_chunks,
+                       int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                       int32_t* __restrict__ perm, int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
+                       int32_t* __restrict__ n_chunks, const int32_t* __restrict__ slot_table) {
+    const int lane = threadIdx.x;
     float key[M1_MAX_KEYS];
 #pragma unroll
     for (int i = 0; i < M1_MAX_KEYS; ++i) key[i] = lane + 64 * i < E ? keys[lane + 64 * i] : -INFINITY;
@@ -594,6 +579,31 @@ __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict_
         *n_active = k;
         *n_chunks = k + (shared_chunks ? 1 : 0);
     }
+}
+
+__global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                                                        int E, int k, float gate_temp, int norm, float route_scale,
+                                                        int32_t* __restrict__ idx, float* __restrict__ gw,
+                                                        int32_t* __restrict__ err, int shared_chunks,
+                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+                                                        int32_t* __restrict__ n_active, int32_t* __restrict__ perm,
+                                                        int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
+                                                        int32_t* __restrict__ n_chunks,
+                                                        const int32_t* __restrict__ slot_table) {
+    __shared__ float keys[64 * M1_MAX_KEYS], scores[64 * M1_MAX_KEYS];
+    const int tid = threadIdx.x;
+    {
+        float sv, kv;
+        bool bad;
+        score_key(logits, bias, tid, E, gate_temp, sv, kv, bad);
+        keys[tid] = kv;
+        scores[tid] = sv;
+        if (__any(bad) && (tid & 63) == 0) atomicOr(err, ERR_NONFINITE);
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    select_m1(keys, scores, E, k, norm, route_scale, idx, gw, shared_chunks, offsets, active, n_active, perm, inv,
+              chunks, n_chunks, slot_table);
 }
 
 // After experts were streamed into slots: the single-row chunks of the small-batch
