@@ -25,6 +25,8 @@ namespace {
 
 constexpr int GU_TILE = 32;   // rows of I per gate/up workgroup: one q8_1 block of h
 constexpr int GU_SUB = 8;     // rows per sub-tile
+constexpr int GU_NU = 6;      // 16-byte loads into LDS per thread per sub-tile (2 * 8 * 84 * nsb bytes over 16 * nsb lanes)
+constexpr int GU_MAX_THREADS = 512;
 constexpr int DC_ROWS = 8;    // output rows per down workgroup
 constexpr int DC_GROUP = 2;   // chunks streamed together by the down workgroup
 constexpr int DC_NPF = 3;     // 16-byte loads per thread per group
@@ -37,14 +39,17 @@ MOE_DEV int rec_bytes(int I) { return I + (I / QB) * 4 + (I / 16) * 4; }
 
 // ------------------------------------------------------------------ Q2_K gate/up -> q8_1(h)
 // One workgroup = one chunk x 32 rows of the inter dimension (one q8_1 block
-// of h), W1 and W3, as four 8-row sub-tiles staged through LDS with coalesced
-// 16-byte loads; the next sub-tile's loads are in flight while the current
-// one is computed. (Requesting all four sub-tiles at once was measured
-// slower: every workgroup then starts its arithmetic late.)
-// Lanes: tid = mtx * L + kb (L = D / 32; mtx 0 = W1, 1 = W3): lane kb holds
-// q8_1 block kb of x (plane j = kb & 3 of half hh of superblock s) in
-// registers and, per row, dots it with that plane's 32 two-bit weights.
-__global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int routed_rows) {
+// of h), W1 and W3. The 32 rows stream through LDS as four sub-tiles of 8 rows
+// of each matrix, loaded straight from global memory into LDS (no register
+// staging) into two LDS slots: sub-tile i + 1 is in flight while sub-tile i is
+// computed, and sub-tile i + 2 is requested as soon as slot i & 1 is free.
+// Lanes: tid = 16 * s + r: superblock column s of local row r of the sub-tile
+// (rows 0..7 are W1, 8..15 are W3). A lane keeps the q8_1 block data of
+// superblock s of x in registers for the whole tile and does every weight of
+// one (row, superblock) per sub-tile: the four 2-bit planes of each qs dword
+// are masked in place (planes 1 and 3 land at 4x, folded into the activation
+// block scale), and the sub-block scales and mins are applied per 16 weights.
+__global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a, int routed_rows) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
     const int L = D / QB;
@@ -52,14 +57,41 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
     const int rowbytes = nsb * Q2K_BYTES;
     const int tiles = I / GU_TILE;
     const int c = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int tid = threadIdx.x, bd = blockDim.x;
+    const int slot_bytes = GU_NU * bd * 16;
     const int nch = *a.n_chunks;
     if (c >= nch) return;
     const Chunk ch = a.chunks[c];
+    const int token = ch.token;
+
+    // the lane's superblock of x: 256 quants, the eight block scales and the
+    // 16-value sums (requested before the weights, used once the first sub-tile is in)
+    const int r = tid & 15, s = tid >> 4;
+    const bool live = s < nsb;
+    const int sx = live ? s : 0;
+    uint32_t xv[64];
+    float4 d0, d1;
+    int4 s16v[4];
+    {
+        const uint4* xs = reinterpret_cast<const uint4*>(a.xq + (size_t)token * D + (size_t)sx * QK);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint4 v = xs[q];
+            xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+        }
+        const float4* dp = reinterpret_cast<const float4*>(a.xd + (size_t)token * L + (size_t)sx * 8);
+        d0 = dp[0];
+        d1 = dp[1];
+        const int4* sp = reinterpret_cast<const int4*>(a.xs16 + (size_t)token * 2 * L + (size_t)sx * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s16v[q] = sp[q];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // these loads stay ahead of the sub-tile requests
+
     const bool shared = ch.expert < 0;
     const int r0 = tile * GU_TILE;
     const int rec = rec_bytes(I);
     uint8_t* out = a.hrec + (size_t)(shared ? routed_rows + ch.row0 : ch.row0) * rec;
-    const int tid = threadIdx.x, bd = blockDim.x;
     const uint8_t *w1, *w3;
     if (shared) {
         w1 = a.sh_w1;
@@ -79,100 +111,117 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
         w1 = base + a.off_w1;
         w3 = base + a.off_w3;
     }
-    // sub-tile i = rows [r0 + 8 i, r0 + 8 i + 8) of W1, then the same rows of W3:
-    // 2 * n16 chunks of 16 bytes, six per thread in named registers, the next
-    // sub-tile's loads in flight while the current one is computed
+    // Sub-tile i = W1 rows [r0 + 8 i, r0 + 8 i + 8) then the same rows of W3:
+    // 2 * n16 16-byte units, unit f of thread tid's u-th load being u * bd + tid.
+    // Each wave's load writes 64 consecutive units of the slot; units past the
+    // end re-read the last one into the slot's padding, so every wave issues
+    // exactly GU_NU loads per sub-tile (the waits below count them).
     const int n16 = GU_SUB * rowbytes / 16;
-    uint4 p0, p1, p2, p3, p4, p5;
-#define GU_LD(i, u, dst)                                                                                      \
-    dst = (tid + (u) * bd) < n16                                                                              \
-        ? reinterpret_cast<const uint4*>(w1 + (size_t)(r0 + GU_SUB * (i)) * rowbytes)[tid + (u) * bd]        \
-        : reinterpret_cast<const uint4*>(w3 + (size_t)(r0 + GU_SUB * (i)) * rowbytes)[min(tid + (u) * bd, 2 * n16 - 1) - n16];
-#define GU_LD_SUB(i) { GU_LD(i, 0, p0) GU_LD(i, 1, p1) GU_LD(i, 2, p2) GU_LD(i, 3, p3) GU_LD(i, 4, p4) GU_LD(i, 5, p5) }
-    GU_LD_SUB(0)
-
-    const int mtx = tid / L, kb = tid % L;
-    const bool live = tid < 2 * L;
-    const int s = kb >> 3, hh = (kb >> 2) & 1, j = kb & 3;
-    // the lane's activation block; plane j's mask leaves j < 3 weights times 4^j
-    // (folded into the block scale), plane 3 is shifted down by 2 (times 16)
-    uint32_t av[8];
+    const int wave_unit = tid & ~63;
+    auto issue = [&](int i) {
+        uint8_t* dst = smem + (i & 1) * slot_bytes;
+        const uint8_t* g1 = w1 + (size_t)(r0 + GU_SUB * i) * rowbytes;
+        const uint8_t* g3 = w3 + (size_t)(r0 + GU_SUB * i) * rowbytes;
+#pragma unroll
+        for (int u = 0; u < GU_NU; ++u) {
+            const int f = min(u * bd + tid, 2 * n16 - 1);
+            const uint8_t* src = f < n16 ? g1 + (size_t)f * 16 : g3 + (size_t)(f - n16) * 16;
+            load_lds16(src, dst + (size_t)(u * bd + wave_unit) * 16);
+        }
+    };
+    issue(0);
+    issue(1);
+    float dxs[8], m16[16];
     {
-        const uint4* src = reinterpret_cast<const uint4*>(a.xq + (size_t)ch.token * D + kb * QB);
-        const uint4 u0 = src[0], u1 = src[1];
-        av[0] = u0.x; av[1] = u0.y; av[2] = u0.z; av[3] = u0.w;
-        av[4] = u1.x; av[5] = u1.y; av[6] = u1.z; av[7] = u1.w;
+        const float dx[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            m16[4 * q + 0] = dx[2 * q] * (float)s16v[q].x;
+            m16[4 * q + 1] = dx[2 * q] * (float)s16v[q].y;
+            m16[4 * q + 2] = dx[2 * q + 1] * (float)s16v[q].z;
+            m16[4 * q + 3] = dx[2 * q + 1] * (float)s16v[q].w;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dxs[t] = (t & 1) ? 0.25f * dx[t] : dx[t];
     }
-    const float dxs = a.xd[(size_t)ch.token * L + kb] * (j == 0 ? 1.f : j == 1 ? 0.25f : 0.0625f);
-    const float dxm = a.xd[(size_t)ch.token * L + kb];
-    const int slo = a.xs16[(size_t)ch.token * 2 * L + 2 * kb];
-    const int shi = a.xs16[(size_t)ch.token * 2 * L + 2 * kb + 1];
-    const uint32_t wmask = j == 3 ? 0x30303030u : (0x03030303u << (2 * j));
-    const uint32_t wshift = j == 3 ? 2u : 0u;
 
-    uint4* tw = reinterpret_cast<uint4*>(smem);                                 // [2 * n16]
-    float* red = reinterpret_cast<float*>(smem + 2 * GU_SUB * rowbytes);         // [32][2][nsb]
-    float* hv = red + GU_TILE * 2 * nsb;                                          // [32]
-    const uint32_t* tw32 = reinterpret_cast<const uint32_t*>(smem);
+    float* red = reinterpret_cast<float*>(smem + 2 * slot_bytes);   // [4 sub-tiles][16 rows][nsb]
     for (int i = 0; i < GU_TILE / GU_SUB; ++i) {
-        if (i > 0) __syncthreads();   // every lane is done with the previous sub-tile
-        if (tid < 2 * n16) tw[tid] = p0;
-        if (tid + bd < 2 * n16) tw[tid + bd] = p1;
-        if (tid + 2 * bd < 2 * n16) tw[tid + 2 * bd] = p2;
-        if (tid + 3 * bd < 2 * n16) tw[tid + 3 * bd] = p3;
-        if (tid + 4 * bd < 2 * n16) tw[tid + 4 * bd] = p4;
-        if (tid + 5 * bd < 2 * n16) tw[tid + 5 * bd] = p5;
-        __syncthreads();
-        if (i + 1 < GU_TILE / GU_SUB) GU_LD_SUB(i + 1)
-        if (!live) continue;
-#pragma unroll 2
-        for (int r = 0; r < GU_SUB; ++r) {
-            const int sb = ((mtx * GU_SUB + r) * rowbytes + s * Q2K_BYTES) >> 2;   // dword index
-            const int qo = sb + 4 + 8 * hh;
-            int il = 0, ih = 0;
+        if (i + 1 < GU_TILE / GU_SUB) wait_vm_loads<GU_NU>();   // sub-tile i is in LDS (i + 1 may not be)
+        else wait_vm_loads<0>();
+        barrier_lds();
+        if (live) {
+            const uint32_t* wp = reinterpret_cast<const uint32_t*>(smem + (i & 1) * slot_bytes + r * rowbytes +
+                                                                   s * Q2K_BYTES);
+            uint32_t sc[4], qw[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) il = sdot4((tw32[qo + q] >> wshift) & wmask, av[q], il);
+            for (int q = 0; q < 4; ++q) sc[q] = wp[q];
 #pragma unroll
-            for (int q = 4; q < 8; ++q) ih = sdot4((tw32[qo + q] >> wshift) & wmask, av[q], ih);
-            const uint32_t scw = tw32[sb + 2 * hh + (j >> 1)] >> (16 * (j & 1));
-            const uint32_t dd = tw32[sb + 20];
-            const int isum = __mul24((int)(scw & 15u), il) + __mul24((int)((scw >> 8) & 15u), ih);
-            const int msum = __mul24((int)((scw >> 4) & 15u), slo) + __mul24((int)((scw >> 12) & 15u), shi);
+            for (int q = 0; q < 16; ++q) qw[q] = wp[4 + q];
+            const uint32_t dd = wp[20];
+            // qs byte b of half hh holds weight 128 hh + 32 j + b in bits 2j..2j+1
+            // (sub-block 8 hh + 2 j + b / 16, activation block 4 hh + j); the first
+            // product of each sub-block starts its sum
+            int in[16];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) {
+                    const uint32_t w = qw[8 * hh + cc], w4 = w >> 4;
+                    const int nb = 8 * hh + (cc >> 2);
+                    const bool first = (cc & 3) == 0;
+                    in[nb + 0] = sdot4(w & 0x03030303u, xv[(4 * hh + 0) * 8 + cc], first ? 0 : in[nb + 0]);
+                    in[nb + 2] = sdot4(w & 0x0C0C0C0Cu, xv[(4 * hh + 1) * 8 + cc], first ? 0 : in[nb + 2]);
+                    in[nb + 4] = sdot4(w4 & 0x03030303u, xv[(4 * hh + 2) * 8 + cc], first ? 0 : in[nb + 4]);
+                    in[nb + 6] = sdot4(w4 & 0x0C0C0C0Cu, xv[(4 * hh + 3) * 8 + cc], first ? 0 : in[nb + 6]);
+                }
+            }
+            // scale bytes 4q .. 4q + 3 = sub-blocks 4q .. 4q + 3 (activation blocks 2q, 2q + 1):
+            // low nibbles the scales, high nibbles the mins
+            float fs = 0.f, ms = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t sq = sc[q] & 0x0F0F0F0Fu, mq = (sc[q] >> 4) & 0x0F0F0F0Fu;
+                const int is0 = __mul24((int)(sq & 0xFFu), in[4 * q]) + __mul24((int)((sq >> 8) & 0xFFu), in[4 * q + 1]);
+                const int is1 = __mul24((int)((sq >> 16) & 0xFFu), in[4 * q + 2]) + __mul24((int)(sq >> 24), in[4 * q + 3]);
+                fs = fmaf(dxs[2 * q], (float)is0, fs);
+                fs = fmaf(dxs[2 * q + 1], (float)is1, fs);
+                ms = fmaf((float)(mq & 0xFFu), m16[4 * q], ms);
+                ms = fmaf((float)((mq >> 8) & 0xFFu), m16[4 * q + 1], ms);
+                ms = fmaf((float)((mq >> 16) & 0xFFu), m16[4 * q + 2], ms);
+                ms = fmaf((float)(mq >> 24), m16[4 * q + 3], ms);
+            }
             const float d = half_bits_to_f32(dd & 0xFFFFu), dmin = half_bits_to_f32(dd >> 16);
-            float part = fmaf(dxs * d, (float)isum, -(dxm * dmin) * (float)msum);
-            part = group8_sum(part);
-            if ((kb & 7) == 7) red[((GU_SUB * i + r) * 2 + mtx) * nsb + s] = part;
+            red[(i * 16 + r) * nsb + s] = fmaf(d, fs, -dmin * ms);
+        }
+        if (i + 2 < GU_TILE / GU_SUB) {
+            barrier_lds();   // every lane is done with slot i & 1
+            issue(i + 2);
         }
     }
-#undef GU_LD_SUB
-#undef GU_LD
-    __syncthreads();
+    barrier_lds();
+    // row t of the tile: W1 and W3 partials of sub-tile t / 8, local rows t % 8 and 8 + t % 8;
+    // then the q8_1 block of the 32 values of h across lanes 0..31
     if (tid < GU_TILE) {
-        const float* rg = red + (size_t)(tid * 2 + 0) * nsb;
-        const float* ru = red + (size_t)(tid * 2 + 1) * nsb;
+        const float* rg = red + ((tid >> 3) * 16 + (tid & 7)) * nsb;
+        const float* ru = rg + 8 * nsb;
         float gs = 0.f, us = 0.f;
         for (int q = 0; q < nsb; ++q) {
             gs += rg[q];
             us += ru[q];
         }
-        hv[tid] = swiglu(gs, us, a.limit);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float v[QB];
+        const float h = swiglu(gs, us, a.limit);
+        float amax = fabsf(h);
 #pragma unroll
-        for (int q = 0; q < QB; ++q) v[q] = hv[q];
-        uint32_t qv[8];
-        float d16;
-        int sl, sh;
-        q8_1_block(v, qv, d16, sl, sh);
-        uint4* dst = reinterpret_cast<uint4*>(out + r0);
-        dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
-        dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
-        reinterpret_cast<float*>(out + I)[tile] = d16;
-        int32_t* ss = reinterpret_cast<int32_t*>(out + I + (I / QB) * 4);
-        ss[2 * tile] = sl;
-        ss[2 * tile + 1] = sh;
+        for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+        const float d = amax / 127.0f;
+        const int qi = (d == 0.f) ? 0 : (int)roundf(h / d);
+        reinterpret_cast<int8_t*>(out + r0)[tid] = (int8_t)qi;
+        int qs = qi;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) qs += __shfl_xor(qs, off, 16);
+        if (tid == 0) reinterpret_cast<float*>(out + I)[tile] = round_to_fp16(d);
+        if ((tid & 15) == 0) reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile + (tid >> 4)] = qs;
     }
 }
 
@@ -334,8 +383,8 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
 
 // ------------------------------------------------------------------ launch
 bool decode_supported(int D, int I) {
-    // lanes: 2 * D / 32 for gate/up and 8 * I / 32 for down, within one workgroup
-    return D % QK == 0 && I % QK == 0 && D / 16 <= 1024 && I / 4 <= 1024 && D % DC_ROWS == 0;
+    // lanes: 16 per superblock of D for gate/up and 8 * I / 32 for down, within one workgroup
+    return D % QK == 0 && I % QK == 0 && 16 * (D / QK) <= GU_MAX_THREADS && I / 4 <= 1024 && D % DC_ROWS == 0;
 }
 
 static int round64(int v) { return (v + 63) / 64 * 64; }
@@ -344,9 +393,9 @@ size_t decode_rec_bytes(int I) { return (size_t)I + (size_t)(I / QB) * 4 + (size
 
 hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st) {
     if (max_chunks <= 0) return hipSuccess;
-    const int threads = round64(2 * (a.D / QB));
     const int nsb = a.D / QK;
-    const size_t lds = (size_t)2 * GU_SUB * nsb * Q2K_BYTES + (size_t)GU_TILE * 2 * nsb * 4 + GU_TILE * 4;
+    const int threads = round64(16 * nsb);
+    const size_t lds = (size_t)2 * GU_NU * threads * 16 + (size_t)(GU_TILE / GU_SUB) * 16 * nsb * 4;
     return launch_kernel(gateup_q8_kernel, max_chunks * (a.I / GU_TILE), threads, lds, st, a, routed_rows);
 }
 

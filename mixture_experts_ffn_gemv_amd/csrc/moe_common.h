@@ -165,6 +165,32 @@ MOE_DEV int wave_inclusive_scan(int v) {
     return v;
 }
 
+// 16 bytes per lane from global memory straight into LDS (gfx950 global_load_lds_dwordx4).
+// `lds` must be the same in every lane of the wave: lane l writes lds + 16 l.
+// The load counts as a vector-memory load of the issuing wave (vmcnt).
+MOE_DEV void load_lds16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order); a compiler fence keeps LDS reads after it.
+template <int N>
+MOE_DEV void wait_vm_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// leaves global loads (including loads into LDS) in flight.
+MOE_DEV void barrier_lds() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt not waited
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 MOE_DEV float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);

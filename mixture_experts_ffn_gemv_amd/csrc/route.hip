@@ -10,6 +10,7 @@
 // instead of the pages' host round trip.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "route_select.h"
 
 namespace moe {
 
@@ -108,26 +109,6 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- top-k
-// Scores and keys: v = z / gate_temp; softplus(v) = v above 20, else ln(1 + e^v);
-// s = sqrt(softplus); key = s + bias. A NaN key raises the error bit and is
-// ordered as -inf, so k picks always exist.
-MOE_DEV void score_key(const float* __restrict__ logits_row, const float* __restrict__ bias, int e, int E,
-                       float gate_temp, float& s, float& key, bool& bad) {
-    key = -INFINITY;
-    s = 0.f;
-    bad = false;
-    if (e < E) {
-        const float v = logits_row[e] / gate_temp;
-        const float sp = v > 20.f ? v : log1pf(expf(v));
-        s = sqrtf(sp);
-        key = s + bias[e];
-        if (key != key) {
-            bad = true;
-            key = -INFINITY;
-        }
-    }
-}
-
 // rank_e = #{f : key_f > key_e or (key_f == key_e and f < e)} over n (multiple of
 // 16) keys in LDS; the picks are the experts of rank < k, in rank order.
 MOE_DEV int key_rank(const float* keys, int n, float key, int e) {
@@ -467,79 +448,23 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
 }
 
 // One token (decode): every thread scores one expert, then the first
-// wavefront selects, weighs and lists the picks without further barriers.
-// Its lane l holds experts l, l + 64, ...; each of the k rounds takes the
-// largest remaining key across the wavefront (ties to the lower expert id,
-// NaN keys last as on the general path). The winner of a round is
-// wavefront-uniform, so the picks stay in registers (lane r holds pick r).
+// wavefront selects (wave_topk: ties to the lower expert id, NaN keys last as
+// on the general path), weighs and lists the picks without further barriers.
 constexpr int M1_MAX_KEYS = 16;   // keys per lane: E <= 1024
 
-// wavefront-wide max / min, the result in every lane: DPP inside each 16-lane
-// row (quad swaps, then rotations by 4 and 8), then the four rows' values
-template <int CTRL>
-MOE_DEV int dpp_mov(int v) {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
-}
-MOE_DEV float wave_max_f32(float v) {
-    v = fmaxf(v, __int_as_float(dpp_mov<0xB1>(__float_as_int(v))));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, __int_as_float(dpp_mov<0x4E>(__float_as_int(v))));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, __int_as_float(dpp_mov<0x124>(__float_as_int(v))));   // row_ror:4
-    v = fmaxf(v, __int_as_float(dpp_mov<0x128>(__float_as_int(v))));   // row_ror:8
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-MOE_DEV int wave_min_i32(int v) {
-    v = min(v, dpp_mov<0xB1>(v));
-    v = min(v, dpp_mov<0x4E>(v));
-    v = min(v, dpp_mov<0x124>(v));
-    v = min(v, dpp_mov<0x128>(v));
-    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    return min(min(r0, r1), min(r2, r3));
-}
-
 // The selection by the first wavefront, from all E keys and scores in LDS.
+template <int KPL>
 MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int norm, float route_scale,
                        int32_t* __restrict__ idx, float* __restrict__ gw, int shared_chunks,
                        int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                        int32_t* __restrict__ perm, int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
                        int32_t* __restrict__ n_chunks, const int32_t* __restrict__ slot_table) {
     const int lane = threadIdx.x;
-    float key[M1_MAX_KEYS];
-#pragma unroll
-    for (int i = 0; i < M1_MAX_KEYS; ++i) key[i] = lane + 64 * i < E ? keys[lane + 64 * i] : -INFINITY;
-    unsigned used = 0u;   // bit i: key i of this lane already picked
-    int my_e = 0;
-    float my_s = 0.f;
-    for (int r = 0; r < k; ++r) {
-        // the lane's best remaining key (lowest id among equal keys: ids grow with i)
-        float bk = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < M1_MAX_KEYS; ++i) {
-            const int id = lane + 64 * i;
-            if (id < E && !((used >> i) & 1u) && (key[i] > bk || (key[i] == bk && id < bi))) {
-                bk = key[i];
-                bi = id;
-            }
-        }
-        // across the wavefront: the largest key, then the lowest id holding it
-        const float kmax = wave_max_f32(bk);
-        const int win = wave_min_i32(bk == kmax ? bi : 0x7fffffff);
-        if ((win & 63) == lane) used |= 1u << (win >> 6);
-        if (lane == r) {
-            my_e = win;
-            my_s = scores[win];
-        }
-    }
-    // weights (the normaliser summed in pick order), and the picks sorted by
-    // expert id (all distinct): position = rank of the id
-    float sum = 0.f;
-    for (int q = 0; q < k; ++q) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), q));
-    const float wgt = (norm && k > 1 ? my_s / (sum + 1e-20f) : my_s) * route_scale;
+    int my_e;
+    float my_s;
+    wave_topk<KPL>(keys, scores, E, k, my_e, my_s);
+    const float wgt = wave_pick_weight(my_s, k, norm, route_scale);
+    // the picks sorted by expert id (all distinct): position = rank of the id
     int pos = 0;
     for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(my_e, q) < my_e ? 1 : 0;
     if (lane < k) {
@@ -581,6 +506,7 @@ MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int
     }
 }
 
+template <int KPL>
 __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
                                                         int E, int k, float gate_temp, int norm, float route_scale,
                                                         int32_t* __restrict__ idx, float* __restrict__ gw,
@@ -602,7 +528,7 @@ __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict_
     }
     __syncthreads();
     if (tid >= 64) return;
-    select_m1(keys, scores, E, k, norm, route_scale, idx, gw, shared_chunks, offsets, active, n_active, perm, inv,
+    select_m1<KPL>(keys, scores, E, k, norm, route_scale, idx, gw, shared_chunks, offsets, active, n_active, perm, inv,
               chunks, n_chunks, slot_table);
 }
 
@@ -643,9 +569,15 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                               Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st) {
-    if (m == 1 && E <= 64 * M1_MAX_KEYS && k <= 64)
-        return launch_kernel(route_m1_kernel, 1, (E + 63) / 64 * 64, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, idx, gw,
-                             err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
+    if (m == 1 && E <= 64 * M1_MAX_KEYS && k <= 64) {
+        const int th = (E + 63) / 64 * 64;
+#define ROUTE_M1(KPL) launch_kernel(route_m1_kernel<KPL>, 1, th, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, \
+                                    idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table)
+        const int kpl = topk_kpl(E);
+        const hipError_t e = kpl == 2 ? ROUTE_M1(2) : kpl == 6 ? ROUTE_M1(6) : ROUTE_M1(16);
+#undef ROUTE_M1
+        return e;
+    }
     return launch_kernel(route_small_kernel, 1, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
                   shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
 }
