@@ -27,6 +27,8 @@ CFLAGS = [
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs (no accumulator-register copies)
+    "-mllvm", "--amdgpu-mfma-vgpr-form=true",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

@@ -40,24 +40,45 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 MOE_DEV int xcd_logical_block(int b, int nb_pad) { return (b & 7) * (nb_pad >> 3) + (b >> 3); }
 
 // ------------------------------------------------------------------ Q2_K gate/up
-// Rounds of KS = 2 superblocks. Per round the workgroup stages, through
-// registers into LDS (the next round's loads in flight while the current
-// round is computed): the raw blocks of its 64 W1 and 64 W3 rows, the q8_1
-// quants of its token rows, their block scales and their per-16 sums (both
-// transposed to [k][row] so a lane reads its four C rows at once).
+// Weights are the A operand (16 rows of W1 and the same 16 rows of W3 per
+// wavefront, 64 per workgroup), the chunk's token rows the B operand (NS
+// sub-tiles of 16 columns): C[row][token] = v_mfma_i32_16x16x32_i8 over one
+// q8_1 block, rescaled by the token's block scale (C column = lane % 16, so
+// one scalar per lane and block).
+//  * Per superblock the workgroup's 2 x 64 weight rows (84 bytes each) and
+//    the activations of its token rows (quants, block scales, per-16 sums
+//    times the block scale) go from global memory straight into LDS with
+//    wavefront-wide loads: the weight rows three at a time (63 lanes x 4
+//    bytes, groups padded to 65 dwords so the 16 rows a wavefront reads lie
+//    in distinct banks), the activations transposed to [16-byte chunk][token]
+//    / [block][token]. NBUF superblocks are in LDS: one is computed while the
+//    next NBUF - 1 are in flight.
+//  * A lane (row = lane % 16, g = lane / 16) takes from its row's superblock
+//    the sixteen scale bytes, d / dmin and the qs bytes 8g..8g+7 of both
+//    halves, which hold its eight K values of all four planes. The A bytes
+//    sc_n * q come from a byte lookup (v_perm_b32 on [3 sc, 2 sc, sc, 0]
+//    indexed by 3 - q).
+//  * The min part -dmin * m_n * X16_n (X16 = block scale times the sum of 16
+//    quants) is four f32 16x16x4 products per matrix and superblock (K = the
+//    16 sub-blocks).
 namespace {
-constexpr int GKS = 2;                        // superblocks per round
-constexpr int GW_DW = GKS * Q2K_BYTES / 4;    // 42 dwords of one row per round
-constexpr int GA_STRIDE = GKS * QK + 16;      // bytes per token row in LDS (padded against bank conflicts)
+constexpr int GW_GROUPS = 22;        // groups of three rows per matrix (66 >= 64)
+constexpr int GW_GSTRIDE = 65;       // dwords per group in LDS
+constexpr int GW_LOADS = 2 * GW_GROUPS / 4;   // weight loads into LDS per thread and superblock (11)
 
 template <int NS>
 struct GateupLds {
-    static constexpr int rows = NS * 16;
-    static constexpr int w_bytes = 128 * GW_DW * 4;
-    static constexpr int a_off = w_bytes;
-    static constexpr int dx_off = a_off + rows * GA_STRIDE;        // [GKS * 8][rows] f32
-    static constexpr int x16_off = dx_off + GKS * 8 * rows * 4;    // [GKS * 16][rows] f32
-    static constexpr int bytes = x16_off + GKS * 16 * rows * 4;
+    static constexpr int R = NS * 16;                        // token rows
+    static constexpr int nbuf = 2;                           // superblocks in LDS: one computed, one in flight
+    static constexpr int w_off = 0;                          // [44 groups][65] dwords
+    static constexpr int q_off = w_off + 2 * GW_GROUPS * GW_GSTRIDE * 4;   // [16 chunks][R] x 16 B
+    static constexpr int ndx = (8 * R + 255) / 256;          // dword loads per thread for the block scales
+    static constexpr int dx_off = q_off + 16 * R * 16;       // [8 blocks][R] f32 (+ padding to ndx * 256)
+    static constexpr int x16_off = dx_off + ndx * 256 * 4;   // [16 sub-blocks][R] f32
+    static constexpr int buf_bytes = (x16_off + 16 * R * 4 + 15) / 16 * 16;
+    static constexpr int ndma = GW_LOADS + NS + ndx + NS;    // loads into LDS per thread and superblock
+    static constexpr int xch_off = nbuf * buf_bytes;         // [4 waves][2 matrices][16 rows] f32: d of each row
+    static constexpr int bytes = xch_off + 4 * 2 * 16 * 4;
 };
 }  // namespace
 
@@ -65,6 +86,7 @@ template <int NS>
 __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int nb) {
     extern __shared__ __align__(16) uint8_t smem[];
     using LL = GateupLds<NS>;
+    constexpr int R = LL::R;
     const int D = a.D, I = a.I;
     const int nsb = D / QK;
     const int tiles = I / TILE_ROWS;
@@ -75,6 +97,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     const Chunk ch = a.chunks[c];
     const bool shared = ch.expert < 0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
     const int r0 = rt * TILE_ROWS;
     float* hout = (shared ? a.h_shared : a.h_routed) + (size_t)ch.row0 * I;
     const uint8_t *w1, *w3;
@@ -95,217 +118,187 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         w3 = base + a.off_w3;
     }
     const size_t rowbytes = (size_t)nsb * Q2K_BYTES;
-    const int rounds = (nsb + GKS - 1) / GKS;
 
-    // --- staging assignments (fixed over the rounds; the last round may hold one superblock)
-    // weights: dword q = tid + 256 u of the [128 rows][ks * 21] segment
-    // activations: 16-byte chunk q = tid + 256 u of the [rows][ks * 16] quants
-    constexpr int NW = 128 * GW_DW / 256;          // 21
-    constexpr int NA = (LL::rows * GKS * 16 + 255) / 256;
-    uint32_t wr[NW];
-    uint4 ar[NA];
-    uint4 dxr, x16r0, x16r1;
-    auto token_of = [&](int i) { return i < ch.nrows ? (shared ? ch.row0 + i : a.perm[ch.row0 + i] / a.topk) : -1; };
-    auto stage_load = [&](int rd) {
-        const int sb0 = rd * GKS, ks = min(GKS, nsb - sb0), seg = ks * 21;
-        // weights: row = q / seg (magic multipliers, exact for q < 128 * 42)
+    // staging of one superblock into buffer bi (every thread issues LL::ndma loads)
+    const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));   // rows past the chunk repeat its last row
+    const int stok = shared ? ch.row0 + srow : a.perm[ch.row0 + srow] / a.topk;
+    const int8_t* xq_row = a.xq + (size_t)stok * D;
+    const float* xd_row = a.xd + (size_t)stok * (D / QB);
+    const float* xf_row = a.xs16f + (size_t)stok * (D / 16);
+    const int gl_row = min(lane / 21, 2), gl_dw = lane == 63 ? 0 : lane % 21;   // lane 63 repeats a dword into the pad
+    auto stage = [&](int sb, int bi) {
+        uint8_t* buf = smem + bi * LL::buf_bytes;
 #pragma unroll
-        for (int u = 0; u < NW; ++u) {
-            const int q = tid + 256 * u;
-            const int row = ks == 2 ? (int)(((uint32_t)q * 24967u) >> 20) : (int)(((uint32_t)q * 49933u) >> 20);
-            const int dw = q - row * seg;
-            wr[u] = 0u;
-            if (row < 128) {
-                const uint8_t* src = (row < 64 ? w1 + (size_t)(r0 + row) * rowbytes
-                                               : w3 + (size_t)(r0 + row - 64) * rowbytes) + (size_t)sb0 * Q2K_BYTES;
-                wr[u] = reinterpret_cast<const uint32_t*>(src)[dw];
-            }
+        for (int u = 0; u < GW_LOADS; ++u) {   // group q = 4u + wave: rows 3 gi .. 3 gi + 2 of matrix q / 22
+            const int q = 4 * u + wv, m = q / GW_GROUPS, gi = q % GW_GROUPS;
+            const int row = min(3 * gi + gl_row, TILE_ROWS - 1);
+            const uint8_t* src = (m ? w3 : w1) + (size_t)(r0 + row) * rowbytes + (size_t)sb * Q2K_BYTES + gl_dw * 4;
+            load_lds4(src, buf + LL::w_off + q * GW_GSTRIDE * 4);
         }
-        const int cpr = ks * 16;   // 16-byte chunks of quants per token row
 #pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            const int q = tid + 256 * u;
-            const int row = q / cpr, col = q % cpr;
-            ar[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (row < LL::rows) {
-                const int t = token_of(row);
-                if (t >= 0) ar[u] = reinterpret_cast<const uint4*>(a.xq + (size_t)t * D + sb0 * QK)[col];
-            }
+        for (int u = 0; u < NS; ++u) {   // unit p = u * 256 + tid: 16-byte chunk p / R of row p % R
+            const int kc = (u * 256 + tid) / R;
+            load_lds16(xq_row + (size_t)sb * QK + kc * 16, buf + LL::q_off + (u * 256 + wv * 64) * 16);
         }
-        // scales: row = tid / (2 ks), 4 consecutive blocks; 16-sums: row = tid / (4 ks)
-        dxr = make_uint4(0u, 0u, 0u, 0u);
-        {
-            const int row = tid / (2 * ks), col = tid % (2 * ks);
-            if (row < LL::rows) {
-                const int t = token_of(row);
-                if (t >= 0) dxr = reinterpret_cast<const uint4*>(a.xd + (size_t)t * (D / QB) + sb0 * 8)[col];
-            }
-        }
-        x16r0 = x16r1 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = tid + 256 * u;
-            const int row = q / (4 * ks), col = q % (4 * ks);
-            if (row < LL::rows) {
-                const int t = token_of(row);
-                if (t >= 0) {
-                    const uint4 v = reinterpret_cast<const uint4*>(a.xs16f + (size_t)t * (D / 16) + sb0 * 16)[col];
-                    if (u == 0) x16r0 = v; else x16r1 = v;
-                }
-            }
+        for (int u = 0; u < LL::ndx; ++u) {
+            const int kb = min((u * 256 + tid) / R, 7);
+            load_lds4(xd_row + (size_t)sb * 8 + kb, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
         }
-    };
-    auto stage_store = [&](int rd) {
-        const int sb0 = rd * GKS, ks = min(GKS, nsb - sb0), seg = ks * 21;
-        uint32_t* wl = reinterpret_cast<uint32_t*>(smem);
 #pragma unroll
-        for (int u = 0; u < NW; ++u) {
-            const int q = tid + 256 * u;
-            const int row = ks == 2 ? (int)(((uint32_t)q * 24967u) >> 20) : (int)(((uint32_t)q * 49933u) >> 20);
-            if (row < 128) wl[row * GW_DW + (q - row * seg)] = wr[u];
-        }
-        const int cpr = ks * 16;
-#pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            const int q = tid + 256 * u;
-            const int row = q / cpr, col = q % cpr;
-            if (row < LL::rows) *reinterpret_cast<uint4*>(smem + LL::a_off + row * GA_STRIDE + col * 16) = ar[u];
-        }
-        float* dxl = reinterpret_cast<float*>(smem + LL::dx_off);
-        {
-            const int row = tid / (2 * ks), col = tid % (2 * ks);
-            if (row < LL::rows) {
-                dxl[(4 * col + 0) * LL::rows + row] = __uint_as_float(dxr.x);
-                dxl[(4 * col + 1) * LL::rows + row] = __uint_as_float(dxr.y);
-                dxl[(4 * col + 2) * LL::rows + row] = __uint_as_float(dxr.z);
-                dxl[(4 * col + 3) * LL::rows + row] = __uint_as_float(dxr.w);
-            }
-        }
-        float* xl = reinterpret_cast<float*>(smem + LL::x16_off);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = tid + 256 * u;
-            const int row = q / (4 * ks), col = q % (4 * ks);
-            const uint4 v = u == 0 ? x16r0 : x16r1;
-            if (row < LL::rows) {
-                xl[(4 * col + 0) * LL::rows + row] = __uint_as_float(v.x);
-                xl[(4 * col + 1) * LL::rows + row] = __uint_as_float(v.y);
-                xl[(4 * col + 2) * LL::rows + row] = __uint_as_float(v.z);
-                xl[(4 * col + 3) * LL::rows + row] = __uint_as_float(v.w);
-            }
+        for (int u = 0; u < NS; ++u) {
+            const int n = (u * 256 + tid) / R;
+            load_lds4(xf_row + (size_t)sb * 16 + n, buf + LL::x16_off + (u * 256 + wv * 64) * 4);
         }
     };
 
-    // A rows: token of sub-tile s, row lane % 16; C rows: tokens 4 (lane / 16) + r
-    const int g = lane >> 4, l16 = lane & 15;
+    // this lane's weight rows in LDS (dword offsets), W1 and W3
+    const int wr = 16 * wv + l16;
+    const int wo1 = (wr / 3) * GW_GSTRIDE + (wr % 3) * 21;
+    const int wo3 = wo1 + GW_GROUPS * GW_GSTRIDE;
+
     typedef float f4 __attribute__((ext_vector_type(4)));
     f4 accg[NS], accu[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) accg[s] = accu[s] = (f4){0.f, 0.f, 0.f, 0.f};
     const int ns = min(NS, (ch.nrows + 15) / 16);   // sub-tiles holding tokens
-    const int wrow = 16 * wv + l16;                   // this lane's weight row (B column) in the tile
-    const uint32_t* wl = reinterpret_cast<const uint32_t*>(smem);
-    const float* dxl = reinterpret_cast<const float*>(smem + LL::dx_off);
-    const float* xl = reinterpret_cast<const float*>(smem + LL::x16_off);
+    float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 32;
 
-    stage_load(0);
-    for (int rd = 0; rd < rounds; ++rd) {
-        if (rd > 0) __syncthreads();   // the previous round is consumed
-        stage_store(rd);
-        __syncthreads();
-        if (rd + 1 < rounds) stage_load(rd + 1);   // in flight during this round's products
-        const int ks = min(GKS, nsb - rd * GKS);
-        for (int sbi = 0; sbi < ks; ++sbi) {
-            const uint32_t* bg = wl + wrow * GW_DW + sbi * 21;
-            const uint32_t* bu = wl + (64 + wrow) * GW_DW + sbi * 21;
-            const uint32_t ddg = bg[20], ddu = bu[20];
-            const float dg = half_bits_to_f32(ddg & 0xFFFFu), dming = half_bits_to_f32(ddg >> 16);
-            const float du = half_bits_to_f32(ddu & 0xFFFFu), dminu = half_bits_to_f32(ddu >> 16);
-            f4 sg[NS], su[NS];
+    // superblocks 0 .. nbuf - 2 in flight before the first round
 #pragma unroll
-            for (int s = 0; s < NS; ++s) sg[s] = su[s] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int kb8 = 0; kb8 < 8; ++kb8) {
-                const int hh = kb8 >> 2, j = kb8 & 3;
-                // B: 8 weights at positions 8g..8g+7 of plane j, half hh; one sub-block
-                const int n = 8 * hh + 2 * j + (g >> 1);
-                const int qd = 4 + 8 * hh + 2 * g;   // dword of qs[32 hh + 8 g]
-                const uint32_t scg = (bg[n >> 2] >> (8 * (n & 3))) & 15;
-                const uint32_t scu = (bu[n >> 2] >> (8 * (n & 3))) & 15;
-                const uint32_t bg0 = ((bg[qd] >> (2 * j)) & 0x03030303u) * scg;
-                const uint32_t bg1 = ((bg[qd + 1] >> (2 * j)) & 0x03030303u) * scg;
-                const uint32_t bu0 = ((bu[qd] >> (2 * j)) & 0x03030303u) * scu;
-                const uint32_t bu1 = ((bu[qd + 1] >> (2 * j)) & 0x03030303u) * scu;
-                const int64_t Bg = (int64_t)(((uint64_t)bg1 << 32) | bg0);
-                const int64_t Bu = (int64_t)(((uint64_t)bu1 << 32) | bu0);
-                const int kk = sbi * 8 + kb8;   // block within the round
+    for (int i = 0; i < LL::nbuf - 1; ++i) stage(min(i, nsb - 1), i);
+    int bcur = 0;   // buffer of superblock sb
+    for (int sb = 0; sb < nsb; ++sb) {
+        // superblock sb is in LDS once at most the later superblocks' loads are outstanding
+        wait_vm_loads<(LL::nbuf - 2) * LL::ndma>();
+        barrier_lds();   // ... for every wave; the buffer of superblock sb - 1 is free
+        const int bnext = bcur == 0 ? LL::nbuf - 1 : bcur - 1;   // (sb + nbuf - 1) % nbuf
+        stage(min(sb + LL::nbuf - 1, nsb - 1), bnext);           // past the end: a repeat, so the counts hold
+        const uint8_t* buf = smem + bcur * LL::buf_bytes;
+        const uint32_t* wl = reinterpret_cast<const uint32_t*>(buf + LL::w_off);
+        const float* dxl = reinterpret_cast<const float*>(buf + LL::dx_off);
+        const float* xl = reinterpret_cast<const float*>(buf + LL::x16_off);
+        uint32_t cw[2][9];   // scales, qs 8g.. (2 dwords), qs 32 + 8g.. (2), d | dmin
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    if (s >= ns) break;
-                    const int64_t A = *reinterpret_cast<const int64_t*>(smem + LL::a_off + (16 * s + l16) * GA_STRIDE +
-                                                                        kk * QB + 8 * g);
-                    const i32x4_t cg = mfma_i8(A, Bg);
-                    const i32x4_t cu = mfma_i8(A, Bu);
-                    const f4 dx = *reinterpret_cast<const f4*>(dxl + kk * LL::rows + 16 * s + 4 * g);
+        for (int m = 0; m < 2; ++m) {
+            const uint32_t* p = wl + (m ? wo3 : wo1);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        sg[s][r] = fmaf((float)cg[r], dx[r], sg[s][r]);
-                        su[s][r] = fmaf((float)cu[r], dx[r], su[s][r]);
-                    }
-                }
-            }
-            // min part, -dmin * sum_n m_n * X16_n with X16_n = fp16(d of the q8_1 block)
-            // times the sum of the sub-block's 16 quants: four f32 16x16x4 matrix-core
-            // products per matrix (K = the 16 sub-blocks), accumulated straight into acc
-            float bmg[4], bmu[4];
+            for (int q = 0; q < 4; ++q) cw[m][q] = p[q];
+            cw[m][4] = p[4 + 2 * g];
+            cw[m][5] = p[5 + 2 * g];
+            cw[m][6] = p[12 + 2 * g];
+            cw[m][7] = p[13 + 2 * g];
+            cw[m][8] = p[20];
+        }
+        f4 sg[NS], su[NS];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = 4 * q + g;
-                bmg[q] = -dming * (float)((bg[n >> 2] >> (8 * (n & 3) + 4)) & 15);
-                bmu[q] = -dminu * (float)((bu[n >> 2] >> (8 * (n & 3) + 4)) & 15);
+        for (int s = 0; s < NS; ++s) sg[s] = su[s] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb8 = 0; kb8 < 8; ++kb8) {
+            const int hh = kb8 >> 2, j = kb8 & 3;
+            // this lane's 8 weights: positions 8g..8g+7 of plane j, half hh (sub-block 8hh + 2j + g / 2)
+            const int nsh = 8 * ((2 * j + (g >> 1)) & 3);
+            int64_t Aw[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                // lookup bytes 3 sc, 2 sc, sc, 0, indexed by 3 - q (the inverted 2-bit field)
+                const uint32_t sc = (cw[m][2 * hh + (j >> 1)] >> nsh) & 15u;
+                const uint32_t lut = __umul24(sc, 0x010203u);
+                const uint32_t s0 = ((cw[m][4 + 2 * hh] >> (2 * j)) & 0x03030303u) ^ 0x03030303u;
+                const uint32_t s1 = ((cw[m][5 + 2 * hh] >> (2 * j)) & 0x03030303u) ^ 0x03030303u;
+                const uint32_t b0 = __builtin_amdgcn_perm(lut, lut, s0);
+                const uint32_t b1 = __builtin_amdgcn_perm(lut, lut, s1);
+                Aw[m] = (int64_t)(((uint64_t)b1 << 32) | b0);
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
+                const int64_t B = *reinterpret_cast<const int64_t*>(
+                    buf + LL::q_off + ((2 * kb8 + (g >> 1)) * R + 16 * s + l16) * 16 + 8 * (g & 1));
+                const float dx = dxl[kb8 * R + 16 * s + l16];
+                const i32x4_t cg = mfma_i8(Aw[0], B);
+                const i32x4_t cu = mfma_i8(Aw[1], B);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    accg[s][r] = fmaf(dg, sg[s][r], accg[s][r]);
-                    accu[s][r] = fmaf(du, su[s][r], accu[s][r]);
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float x16 = xl[(sbi * 16 + 4 * q + g) * LL::rows + 16 * s + l16];
-                    accg[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(x16, bmg[q], accg[s], 0, 0, 0);
-                    accu[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(x16, bmu[q], accu[s], 0, 0, 0);
+                    sg[s][r] = fmaf(dx, (float)cg[r], sg[s][r]);
+                    su[s][r] = fmaf(dx, (float)cu[r], su[s][r]);
                 }
             }
         }
+        // d of the four C rows 4g..4g+3 (held by the lanes of those rows)
+        const float dg = half_bits_to_f32(cw[0][8] & 0xFFFFu), du = half_bits_to_f32(cw[1][8] & 0xFFFFu);
+        if (g == 0) {
+            xch[l16] = dg;
+            xch[16 + l16] = du;
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const f4 dG = *reinterpret_cast<const f4*>(xch + 4 * g);
+        const f4 dU = *reinterpret_cast<const f4*>(xch + 16 + 4 * g);
+        // min part: A = -dmin * m_n of this lane's row for sub-block n = 4q + g
+        const float nmg = -half_bits_to_f32(cw[0][8] >> 16), nmu = -half_bits_to_f32(cw[1][8] >> 16);
+        float bmg[4], bmu[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bmg[q] = nmg * (float)((cw[0][q] >> (8 * g + 4)) & 15u);
+            bmu[q] = nmu * (float)((cw[1][q] >> (8 * g + 4)) & 15u);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (s >= ns) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                accg[s][r] = fmaf(dG[r], sg[s][r], accg[s][r]);
+                accu[s][r] = fmaf(dU[r], su[s][r], accu[s][r]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x16 = xl[(4 * q + g) * R + 16 * s + l16];
+                accg[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(bmg[q], x16, accg[s], 0, 0, 0);
+                accu[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(bmu[q], x16, accu[s], 0, 0, 0);
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the d exchange slots are reused next superblock
+        bcur = bcur == LL::nbuf - 1 ? 0 : bcur + 1;
     }
+    wait_vm_loads<0>();   // no load into LDS outlives the workgroup
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
+        const int t = 16 * s + l16;
+        if (t < ch.nrows) {
+            f4 h;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * s + 4 * g + r;
-            if (i < ch.nrows) hout[(size_t)i * I + r0 + wrow] = swiglu(accg[s][r], accu[s][r], a.limit);
+            for (int r = 0; r < 4; ++r) h[r] = swiglu(accg[s][r], accu[s][r], a.limit);
+            *reinterpret_cast<f4*>(hout + (size_t)t * I + r0 + 16 * wv + 4 * g) = h;
         }
     }
 }
 
 // ------------------------------------------------------------------ Q3_K down
-// LDS: the raw blocks of the 64 whole W2 rows (contiguous, staged once), the
-// 64-entry byte lookup table (32 - sc6) * (v - 4) for v = 0..7 indexed by sc6,
-// then per superblock the q8_1 quants of the chunk's h rows and their block
-// scales ([k][row]), staged through registers one superblock ahead.
+// W2 rows are the A operand (16 per wavefront, 64 per workgroup), the chunk's
+// q8_1 rows of h the B operand: C[row][token] per q8_1 block, rescaled by the
+// token's block scale, times -d of the row per superblock.
+//  * The 64 whole W2 rows (contiguous in memory) go into LDS with
+//    wavefront-wide 16-byte loads once; the h quants and block scales of each
+//    superblock follow transposed to [16-byte chunk][token] / [block][token]
+//    (the next superblock in flight while one is computed when LDS allows).
+//  * A lane (row = lane % 16, g = lane / 16) realigns once per superblock the
+//    hmask bytes 8g..8g+7, the qs bytes 8g.. of both halves and the scales
+//    (superblocks are 110 bytes, so half of them start at 2 bytes past a dword).
+//  * B bytes: (32 - sc6) * (q3 + 4 - 4), from a 64-entry lookup of the 8 values
+//    per six-bit scale (v_perm_b32 on q3 + 4); the sign goes into d.
 namespace {
-constexpr int DA_STRIDE = QK + 16;  // bytes per h row in LDS (padded against bank conflicts)
 template <int NS>
 struct DownLds {
-    static constexpr int rows = NS * 16;
+    static constexpr int R = NS * 16;
+    static constexpr int nbuf = NS == 1 ? 2 : 1;
     __host__ __device__ static int w_bytes(int I) { return TILE_ROWS * (I / QK) * Q3K_BYTES; }   // multiple of 16
-    __host__ __device__ static int lut_off(int I) { return w_bytes(I) + 16; }
-    __host__ __device__ static int a_off(int I) { return lut_off(I) + 64 * 8; }
-    __host__ __device__ static int dx_off(int I) { return a_off(I) + rows * DA_STRIDE; }   // [8][rows] f32
-    __host__ __device__ static int bytes(int I) { return dx_off(I) + 8 * rows * 4; }
+    __host__ __device__ static int lut_off(int I) { return w_bytes(I) + 1024; }   // past the last loads' overrun
+    __host__ __device__ static int act_off(int I) { return lut_off(I) + 64 * 8; }
+    static constexpr int ndx = (8 * R + 255) / 256;
+    static constexpr int q_bytes = 16 * R * 16;
+    static constexpr int buf_bytes = q_bytes + ndx * 256 * 4;
+    __host__ __device__ static int xch_off(int I) { return act_off(I) + nbuf * buf_bytes; }
+    __host__ __device__ static int bytes(int I) { return xch_off(I) + 4 * 16 * 4; }
 };
 }  // namespace
 
@@ -313,6 +306,7 @@ template <int NS>
 __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb) {
     extern __shared__ __align__(16) uint8_t smem[];
     using LL = DownLds<NS>;
+    constexpr int R = LL::R;
     const int D = a.D, I = a.I;
     const int nsb = I / QK;
     const int rowbytes = nsb * Q3K_BYTES;
@@ -324,6 +318,7 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     const Chunk ch = a.chunks[c];
     const bool shared = ch.expert < 0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, l16 = lane & 15, gh = g >> 1;
     const int r0 = rt * TILE_ROWS;
     float* eout = (shared ? a.ys : a.e_rows) + (size_t)ch.row0 * D;
     const uint8_t* w2;
@@ -341,132 +336,131 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     }
     const int8_t* hq = shared ? a.hq_shared : a.hq_routed;
     const float* hd = shared ? a.hd_shared : a.hd_routed;
-    const int rows_valid = ch.nrows;
-    // per superblock: 16-byte chunk q = tid + 256 u of [rows][16] quants; scales: row = tid / 2
-    constexpr int NA = (LL::rows * 16 + 255) / 256;
-    uint4 ar[NA];
-    uint4 dxr;
-    auto stage_load = [&](int sb) {
-#pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            const int q = tid + 256 * u;
-            const int row = q >> 4, col = q & 15;
-            ar[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (row < rows_valid && row < LL::rows)
-                ar[u] = reinterpret_cast<const uint4*>(hq + (size_t)(ch.row0 + row) * I + sb * QK)[col];
-        }
-        dxr = make_uint4(0u, 0u, 0u, 0u);
-        const int row = tid >> 1, col = tid & 1;
-        if (row < rows_valid && row < LL::rows)
-            dxr = reinterpret_cast<const uint4*>(hd + (size_t)(ch.row0 + row) * (I / QB) + sb * 8)[col];
-    };
-    auto stage_store = [&]() {
-#pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            const int q = tid + 256 * u;
-            const int row = q >> 4, col = q & 15;
-            if (row < LL::rows) *reinterpret_cast<uint4*>(smem + LL::a_off(I) + row * DA_STRIDE + col * 16) = ar[u];
-        }
-        float* dxl = reinterpret_cast<float*>(smem + LL::dx_off(I));
-        const int row = tid >> 1, col = tid & 1;
-        if (row < LL::rows) {
-            dxl[(4 * col + 0) * LL::rows + row] = __uint_as_float(dxr.x);
-            dxl[(4 * col + 1) * LL::rows + row] = __uint_as_float(dxr.y);
-            dxl[(4 * col + 2) * LL::rows + row] = __uint_as_float(dxr.z);
-            dxl[(4 * col + 3) * LL::rows + row] = __uint_as_float(dxr.w);
-        }
-    };
-    stage_load(0);
-    uint32_t* lds = reinterpret_cast<uint32_t*>(smem);
-    const int tile_bytes = LL::w_bytes(I);
-    uint2* lut = reinterpret_cast<uint2*>(smem + LL::lut_off(I));   // [64]
+
+    // the W2 tile: 16-byte unit f = 256 u + tid; waves wholly past the end skip the load
     {
-        const uint4* src = reinterpret_cast<const uint4*>(w2 + (size_t)r0 * rowbytes);
-        uint4* dst = reinterpret_cast<uint4*>(smem);
-        const int n16 = tile_bytes / 16;
-        int q = tid;
-        for (; q + 3 * 256 < n16; q += 4 * 256) {   // four loads in flight per step
-            const uint4 v0 = src[q], v1 = src[q + 256], v2 = src[q + 512], v3 = src[q + 768];
-            dst[q] = v0;
-            dst[q + 256] = v1;
-            dst[q + 512] = v2;
-            dst[q + 768] = v3;
-        }
-        for (; q < n16; q += 256) dst[q] = src[q];
-        if (tid < 64) {
-            const int sneg = 32 - tid;   // -(sc6 - 32)
-            uint32_t lo = 0, hi = 0;
-            for (int v = 0; v < 4; ++v) lo |= ((uint32_t)((sneg * (v - 4)) & 0xFF)) << (8 * v);
-            for (int v = 4; v < 8; ++v) hi |= ((uint32_t)((sneg * (v - 4)) & 0xFF)) << (8 * (v - 4));
-            lut[tid] = make_uint2(lo, hi);
+        const int n16 = LL::w_bytes(I) / 16;
+        const uint8_t* src = w2 + (size_t)r0 * rowbytes;
+        for (int u = 0; 256 * u < n16; ++u) {
+            if (256 * u + 64 * wv < n16) {
+                const int f = min(256 * u + tid, n16 - 1);
+                load_lds16(src + (size_t)f * 16, smem + (size_t)(256 * u + 64 * wv) * 16);
+            }
         }
     }
+    // h rows of the chunk (rows past it repeat its last row; their products are never stored)
+    const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));
+    const int8_t* hq_row = hq + (size_t)(ch.row0 + srow) * I;
+    const float* hd_row = hd + (size_t)(ch.row0 + srow) * (I / QB);
+    auto stage = [&](int sb, int bi) {
+        uint8_t* buf = smem + LL::act_off(I) + bi * LL::buf_bytes;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int kc = (u * 256 + tid) / R;
+            load_lds16(hq_row + (size_t)sb * QK + kc * 16, buf + (u * 256 + wv * 64) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < LL::ndx; ++u) {
+            const int kb = min((u * 256 + tid) / R, 7);
+            load_lds4(hd_row + (size_t)sb * 8 + kb, buf + LL::q_bytes + (u * 256 + wv * 64) * 4);
+        }
+    };
+    stage(0, 0);
+    // lookup: entry sc6 holds (32 - sc6) * (v - 4) for v = 0..7 (bytes; lies in [-128, 124])
+    uint2* lut = reinterpret_cast<uint2*>(smem + LL::lut_off(I));
+    if (tid < 64) {
+        const int sneg = 32 - tid;
+        uint32_t lo = 0, hi = 0;
+        for (int v = 0; v < 4; ++v) lo |= ((uint32_t)((sneg * (v - 4)) & 0xFF)) << (8 * v);
+        for (int v = 4; v < 8; ++v) hi |= ((uint32_t)((sneg * (v - 4)) & 0xFF)) << (8 * (v - 4));
+        lut[tid] = make_uint2(lo, hi);
+    }
 
-    const int g = lane >> 4, l16 = lane & 15;
     typedef float f4 __attribute__((ext_vector_type(4)));
     f4 acc[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[s] = (f4){0.f, 0.f, 0.f, 0.f};
     const int ns = min(NS, (ch.nrows + 15) / 16);
     const int wrow = 16 * wv + l16;
-    const float* dxl = reinterpret_cast<const float*>(smem + LL::dx_off(I));
+    const uint32_t* lds = reinterpret_cast<const uint32_t*>(smem);
+    float* xch = reinterpret_cast<float*>(smem + LL::xch_off(I)) + wv * 16;
+
     for (int sb = 0; sb < nsb; ++sb) {
-        if (sb > 0) __syncthreads();   // the previous superblock's activations are consumed
-        stage_store();
-        __syncthreads();
-        if (sb + 1 < nsb) stage_load(sb + 1);
+        wait_vm_loads<0>();   // the tile (first round) and superblock sb's h rows
+        barrier_lds();
+        const int bi = LL::nbuf == 2 ? (sb & 1) : 0;
+        if (LL::nbuf == 2) stage(min(sb + 1, nsb - 1), bi ^ 1);
+        const uint8_t* buf = smem + LL::act_off(I) + bi * LL::buf_bytes;
+        const float* dxl = reinterpret_cast<const float*>(buf + LL::q_bytes);
+
         const int off = wrow * rowbytes + sb * Q3K_BYTES;   // 2-byte aligned
         const int A0 = off >> 2;
-        const uint32_t sh = (uint32_t)(off & 3) * 8u;
-        const uint32_t s0 = funnel(lds[A0 + 25], lds[A0 + 24], sh);
-        const uint32_t s1 = funnel(lds[A0 + 26], lds[A0 + 25], sh);
-        const uint32_t s2 = funnel(lds[A0 + 27], lds[A0 + 26], sh);
-        const float dneg = -half_bits_to_f32((lds[A0 + 27] >> sh) & 0xFFFFu);
+        const uint32_t sh = (uint32_t)(off & 3) * 8u;        // 0 or 16
+        uint32_t hm[2], q0[2], q1[2];
+        {
+            const uint32_t h0 = lds[A0 + 2 * g], h1 = lds[A0 + 2 * g + 1], h2 = lds[A0 + 2 * g + 2];
+            hm[0] = funnel(h1, h0, sh);
+            hm[1] = funnel(h2, h1, sh);
+            const uint32_t a0 = lds[A0 + 8 + 2 * g], a1 = lds[A0 + 9 + 2 * g], a2 = lds[A0 + 10 + 2 * g];
+            q0[0] = funnel(a1, a0, sh);
+            q0[1] = funnel(a2, a1, sh);
+            const uint32_t b0 = lds[A0 + 16 + 2 * g], b1 = lds[A0 + 17 + 2 * g], b2 = lds[A0 + 18 + 2 * g];
+            q1[0] = funnel(b1, b0, sh);
+            q1[1] = funnel(b2, b1, sh);
+        }
+        const uint32_t t24 = lds[A0 + 24], t25 = lds[A0 + 25], t26 = lds[A0 + 26], t27 = lds[A0 + 27];
+        const uint32_t S0 = funnel(t25, t24, sh), S1 = funnel(t26, t25, sh), S2 = funnel(t27, t26, sh);
+        const float dneg = -half_bits_to_f32((t27 >> sh) & 0xFFFFu);
+
         f4 ss[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) ss[s] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll
         for (int kb8 = 0; kb8 < 8; ++kb8) {
             const int hh = kb8 >> 2, j = kb8 & 3;
-            const int n = 8 * hh + 2 * j + (g >> 1);
-            // six-bit scale of sub-block n
-            const uint32_t low4 = (((n & 7) < 4 ? s0 : s1) >> (8 * (n & 3) + 4 * (n >> 3))) & 15;
-            const uint32_t hi2 = (s2 >> (8 * (n & 3) + 2 * (n >> 2))) & 3;
+            // six-bit scale of sub-block n = 8 hh + 2 j + g / 2: low nibble of byte
+            // (2j + g/2) (high nibble for hh = 1), two high bits from byte 8 + n % 4
+            const int nb4 = (2 * j + gh) & 3;
+            const uint32_t low4 = ((j < 2 ? S0 : S1) >> (8 * nb4 + 4 * hh)) & 15u;
+            const uint32_t hi2 = (S2 >> (8 * nb4 + 2 * (2 * hh + (j >> 1)))) & 3u;
             const uint2 L = lut[low4 | (hi2 << 4)];
             // q3 + 4 for positions 8g..8g+7 of plane j, half hh
-            const int qdw = A0 + 8 + 8 * hh + 2 * g;   // qs[32 hh + 8 g] (before the realignment)
-            const int hdw = A0 + 2 * g;                // hmask[8 g]
-            const uint32_t q0 = funnel(lds[qdw + 1], lds[qdw], sh), q1 = funnel(lds[qdw + 2], lds[qdw + 1], sh);
-            const uint32_t m0 = funnel(lds[hdw + 1], lds[hdw], sh), m1 = funnel(lds[hdw + 2], lds[hdw + 1], sh);
+            const uint32_t* qh = hh ? q1 : q0;
             const int hbit = 4 * hh + j;
-            const uint32_t v0 = ((q0 >> (2 * j)) & 0x03030303u) | (((m0 >> hbit) & 0x01010101u) << 2);
-            const uint32_t v1 = ((q1 >> (2 * j)) & 0x03030303u) | (((m1 >> hbit) & 0x01010101u) << 2);
-            const uint32_t b0 = __builtin_amdgcn_perm(L.y, L.x, v0);
-            const uint32_t b1 = __builtin_amdgcn_perm(L.y, L.x, v1);
-            const int64_t B = (int64_t)(((uint64_t)b1 << 32) | b0);
+            const uint32_t v0 = ((qh[0] >> (2 * j)) & 0x03030303u) | (((hm[0] >> hbit) & 0x01010101u) << 2);
+            const uint32_t v1 = ((qh[1] >> (2 * j)) & 0x03030303u) | (((hm[1] >> hbit) & 0x01010101u) << 2);
+            const int64_t Aw = (int64_t)(((uint64_t)__builtin_amdgcn_perm(L.y, L.x, v1) << 32) |
+                                         __builtin_amdgcn_perm(L.y, L.x, v0));
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
-                const int64_t A = *reinterpret_cast<const int64_t*>(smem + LL::a_off(I) + (16 * s + l16) * DA_STRIDE +
-                                                                    kb8 * QB + 8 * g);
-                const i32x4_t cc = mfma_i8(A, B);
-                const f4 dx = *reinterpret_cast<const f4*>(dxl + kb8 * LL::rows + 16 * s + 4 * g);
+                const int64_t B = *reinterpret_cast<const int64_t*>(
+                    buf + ((2 * kb8 + gh) * R + 16 * s + l16) * 16 + 8 * (g & 1));
+                const float dx = dxl[kb8 * R + 16 * s + l16];
+                const i32x4_t cc = mfma_i8(Aw, B);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ss[s][r] = fmaf((float)cc[r], dx[r], ss[s][r]);
+                for (int r = 0; r < 4; ++r) ss[s][r] = fmaf(dx, (float)cc[r], ss[s][r]);
             }
         }
+        // -d of the four C rows 4g..4g+3 (held by the lanes of those rows)
+        if (g == 0) xch[l16] = dneg;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const f4 dn = *reinterpret_cast<const f4*>(xch + 4 * g);
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(dneg, ss[s][r], acc[s][r]);
+            for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(dn[r], ss[s][r], acc[s][r]);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (LL::nbuf == 1 && sb + 1 < nsb) {
+            barrier_lds();   // everyone is done with the buffer
+            stage(sb + 1, 0);
+        }
     }
+    wait_vm_loads<0>();   // no load into LDS outlives the workgroup
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * s + 4 * g + r;
-            if (i < ch.nrows) eout[(size_t)i * D + r0 + wrow] = acc[s][r];
-        }
+        const int t = 16 * s + l16;
+        if (t < ch.nrows) *reinterpret_cast<f4*>(eout + (size_t)t * D + r0 + 16 * wv + 4 * g) = acc[s];
     }
 }
 

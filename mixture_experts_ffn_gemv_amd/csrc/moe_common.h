@@ -172,6 +172,11 @@ MOE_DEV void load_lds16(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// 4 bytes per lane from global memory straight into LDS (lane l writes lds + 4 l).
+MOE_DEV void load_lds4(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (they complete in issue order); a compiler fence keeps LDS reads after it.
 template <int N>
