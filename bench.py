@@ -193,7 +193,9 @@ class Bench:
         self.shape = shape
         self.dev = torch.device("cuda:0")
         t0 = time.time()
-        self.experts = S.make_experts(shape, 1, device=self.dev)
+        self.experts = S.make_experts(shape, 1, device=self.dev)   # plain GGUF row order (the oracle's view)
+        self.cfg0 = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk)
+        self.packed = moe.pack_experts(self.cfg0, self.experts)      # the library's slot layout
         torch.cuda.synchronize()
         log(f"experts drawn in {time.time() - t0:.1f}s ({self.experts.numel() / 1e9:.2f} GB)")
         self.slot_bytes = self.experts.shape[1]
@@ -219,7 +221,8 @@ class Bench:
                 lay["w"] = moe.make_weights(lay["d_wr"], lay["d_bias"], moe.MOE_SHARED_BF16, lay["d_sh"]["w1"],
                                             lay["d_sh"]["w3"], lay["d_sh"]["w2"])
             else:
-                slot = sh["slot"].to(self.dev)
+                slot = torch.empty_like(sh["slot"], device=self.dev)
+                moe.moe_pack_expert(self.cfg0, sh["slot"].to(self.dev), slot)
                 _, o1, o3, o2 = S.expert_layout(shape)
                 lay["d_sh"] = {"slot": slot}
                 lay["w"] = moe.make_weights(lay["d_wr"], lay["d_bias"], moe.MOE_SHARED_KQUANT, slot[o1:],
@@ -248,7 +251,7 @@ class Bench:
             moe.moe_set_slots(ctx, slot_arena, spec["slots"])
             moe.moe_set_host_arena(ctx, host, self.slot_bytes)
         else:
-            moe.moe_set_slots(ctx, self.experts, shape.n_routed)
+            moe.moe_set_slots(ctx, self.packed, shape.n_routed)
             for e in range(shape.n_routed):
                 moe.moe_slot_bind(ctx, e, e)
         out = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
@@ -431,8 +434,8 @@ class Bench:
     def pinned_experts(self):
         """Every expert's slice in page-locked host memory (a new pinned tensor)."""
         if getattr(self, "_host", None) is None:
-            self._host = self.torch.empty(tuple(self.experts.shape), dtype=self.torch.uint8, pin_memory=True)
-            self._host.copy_(self.experts)
+            self._host = self.torch.empty(tuple(self.packed.shape), dtype=self.torch.uint8, pin_memory=True)
+            self._host.copy_(self.packed)
         return self._host
 
     def pinned_copy_peak(self):

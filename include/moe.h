@@ -54,7 +54,8 @@ extern "C" {
 /* shared expert formats */
 #define MOE_SHARED_NONE 0
 #define MOE_SHARED_BF16 1      /* w1/w3 bf16 [inter, dim], w2 bf16 [dim, inter], row-major */
-#define MOE_SHARED_KQUANT 2    /* w1/w3 Q2_K blocks [inter][dim/256], w2 Q3_K blocks [dim][inter/256] */
+#define MOE_SHARED_KQUANT 2    /* w1/w3 Q2_K blocks [inter][dim/256], w2 Q3_K blocks [dim][inter/256],
+                                  each in the panel order of moe_expert_layout (moe_pack_expert) */
 
 /* Layer configuration (the fields of metrale's MoeV41Cfg). */
 typedef struct moe_cfg {
@@ -106,11 +107,27 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out);
 int moe_destroy(moe_ctx* ctx);
 
 /* Byte layout of one routed expert's slice (the analogue of metrale's
- * arena_of): [W1 Q2_K | W3 Q2_K | W2 Q3_K], raw GGUF block bytes, rows in
- * order; W1/W3 are [inter][dim/256] blocks of 84 B, W2 [dim][inter/256]
- * blocks of 110 B. All four outputs are required. MOE_EINVAL on a bad cfg. */
+ * arena_of): [W1 Q2_K | W3 Q2_K | W2 Q3_K]; W1/W3 hold inter rows of dim/256
+ * blocks of 84 B, W2 dim rows of inter/256 blocks of 110 B, the GGUF block
+ * bytes unchanged. Inside each matrix the blocks are in panel order: panels
+ * of 8 consecutive rows, each panel holding its rows' block 0, then their
+ * block 1, ... (block s of row r at ((r/8)*nsb + s)*8*B + (r%8)*B, nsb blocks
+ * per row of B bytes), so that every 8-row tile and every block column of a
+ * panel is one contiguous run. moe_pack_expert turns a slice in plain GGUF
+ * row order into this layout. All four outputs are required. MOE_EINVAL on a
+ * bad cfg. */
 int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, size_t* off_w3,
                       size_t* off_w2);
+
+/* Reorder one expert slice from plain GGUF row order (each matrix's rows one
+ * after another, a row's blocks consecutive) into the slot layout of
+ * moe_expert_layout. src and dst: device, slot_bytes each, 2-byte aligned, not
+ * overlapping; asynchronous on `stream`. Used for routed expert slots, host
+ * arena slices (pack on the device, then copy) and a K-quant shared expert.
+ * MOE_EINVAL for a bad cfg, NULL or overlapping buffers; MOE_EHIP on a launch
+ * error. (A layout step of this library: the blocks themselves are the
+ * pages' GGUF Q2_K / Q3_K blocks, untouched.) */
+int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream);
 
 /* Give the context a caller-owned device arena of n_slots slices of slot_bytes
  * (256-byte aligned base) and reset the slot table to "nothing resident".

@@ -27,7 +27,8 @@ MOE_SHARED_BF16 = 1
 MOE_SHARED_KQUANT = 2
 
 EXPORTED = (
-    "moe_create", "moe_destroy", "moe_expert_layout", "moe_set_slots", "moe_slot_bind", "moe_slot_evict",
+    "moe_create", "moe_destroy", "moe_expert_layout", "moe_pack_expert", "moe_set_slots", "moe_slot_bind",
+    "moe_slot_evict",
     "moe_slot_of", "moe_set_host_arena", "moe_route", "moe_forward", "moe_forward_ex", "moe_check",
     "moe_get_stats", "moe_reset_stats", "moe_strerror", "moe_quantize_q8_1", "moe_set_profiling",
     "moe_kernel_times",
@@ -96,6 +97,7 @@ def lib():
             "moe_create": [P(moe_cfg), P(vp)],
             "moe_destroy": [vp],
             "moe_expert_layout": [P(moe_cfg), P(sz), P(sz), P(sz), P(sz)],
+            "moe_pack_expert": [P(moe_cfg), vp, vp, vp],
             "moe_set_slots": [vp, vp, i32],
             "moe_slot_bind": [vp, i32, i32],
             "moe_slot_evict": [vp, i32],
@@ -176,6 +178,19 @@ def moe_expert_layout(cfg):
     out = [ctypes.c_size_t() for _ in range(4)]
     _check(lib().moe_expert_layout(ctypes.byref(cfg), *[ctypes.byref(o) for o in out]), "moe_expert_layout")
     return tuple(o.value for o in out)
+
+
+def moe_pack_expert(cfg, src, dst, stream=None):
+    return _check(lib().moe_pack_expert(ctypes.byref(cfg), _ptr(src), _ptr(dst), _stream(stream)), "moe_pack_expert")
+
+
+def pack_experts(cfg, arena, stream=None):
+    """Expert slices in plain GGUF row order, uint8 [n, slot_bytes] on the
+    device -> a new tensor of the same shape in the slot layout."""
+    out = torch.empty_like(arena)
+    for e in range(arena.shape[0]):
+        moe_pack_expert(cfg, arena[e], out[e], stream)
+    return out
 
 
 def moe_set_slots(ctx, arena, n_slots):

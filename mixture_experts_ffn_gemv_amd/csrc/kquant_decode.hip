@@ -151,8 +151,8 @@ __global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a,
         else wait_vm_loads<0>();
         barrier_lds();
         if (live) {
-            const uint32_t* wp = reinterpret_cast<const uint32_t*>(smem + (i & 1) * slot_bytes + r * rowbytes +
-                                                                   s * Q2K_BYTES);
+            const uint32_t* wp = reinterpret_cast<const uint32_t*>(smem + (i & 1) * slot_bytes +
+                                                                   panel_off(r, s, nsb, Q2K_BYTES));
             uint32_t sc[4], qw[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) sc[q] = wp[q];
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
                 const float dx = reinterpret_cast<const float*>(hq32 + I / 4)[kb];
                 const int2 hs = reinterpret_cast<const int2*>(hq32 + I / 4 + L)[kb];
                 const int slo = hs.x, shi = hs.y;
-                const int sb = ubase + pr * rowbytes + s * Q3K_BYTES;   // 2-byte aligned
+                const int sb = ubase + panel_off(pr, s, nsb, Q3K_BYTES);   // 2-byte aligned
                 const int A = sb >> 2;
                 const uint32_t sh = (uint32_t)(sb & 3) * 8u;              // 0 or 16
                 uint32_t V[8];

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(512) void gateup_q2k_kernel(ExpertArgs a, int R, in
 
     const uint32_t* tw32 = reinterpret_cast<const uint32_t*>(tw);
     for (int r = pr; r < R; r += P) {
-        const int sb = (mtx * R + r) * rowbytes + s * Q2K_BYTES;   // multiple of 4
+        const int sb = mtx * R * rowbytes + panel_off(r, s, nsb, Q2K_BYTES);   // multiple of 4
         uint32_t W[8];
         const int qoff = (sb + 16 + 32 * hh) >> 2;
 #pragma unroll
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(640) void down_q3k_kernel(ExpertArgs a, int R, int 
     const int hi_shift = 2 * (n_lo >> 2);
     const uint32_t* tw32 = reinterpret_cast<const uint32_t*>(tw);
     for (int r = pr; r < R; r += P) {
-        const int sb = r * rowbytes + s * Q3K_BYTES;    // 2-byte aligned
+        const int sb = panel_off(r, s, nsb, Q3K_BYTES);    // 2-byte aligned
         const int A = sb >> 2;
         const uint32_t sh = (uint32_t)(sb & 3) * 8u;     // 0 or 16
         uint32_t V[8];

@@ -45,14 +45,14 @@ MOE_DEV int xcd_logical_block(int b, int nb_pad) { return (b & 7) * (nb_pad >> 3
 // sub-tiles of 16 columns): C[row][token] = v_mfma_i32_16x16x32_i8 over one
 // q8_1 block, rescaled by the token's block scale (C column = lane % 16, so
 // one scalar per lane and block).
-//  * Per superblock the workgroup's 2 x 64 weight rows (84 bytes each) and
-//    the activations of its token rows (quants, block scales, per-16 sums
-//    times the block scale) go from global memory straight into LDS with
-//    wavefront-wide loads: the weight rows three at a time (63 lanes x 4
-//    bytes, groups padded to 65 dwords so the 16 rows a wavefront reads lie
-//    in distinct banks), the activations transposed to [16-byte chunk][token]
-//    / [block][token]. NBUF superblocks are in LDS: one is computed while the
-//    next NBUF - 1 are in flight.
+//  * Per superblock the workgroup's 2 x 64 weight rows (eight panels of each
+//    matrix: one contiguous 672-byte run per panel) and the activations of
+//    its token rows (quants, block scales, per-16 sums times the block scale)
+//    go from global memory straight into LDS with wavefront-wide loads; the
+//    weights land as [matrix][row][84 bytes] (a 21-dword row stride: the 16
+//    rows a wavefront reads lie in distinct banks), the activations transposed
+//    to [16-byte chunk][token] / [block][token]. Two superblocks are in LDS:
+//    one is computed while the next is in flight.
 //  * A lane (row = lane % 16, g = lane / 16) takes from its row's superblock
 //    the sixteen scale bytes, d / dmin and the qs bytes 8g..8g+7 of both
 //    halves, which hold its eight K values of all four planes. The A bytes
@@ -62,21 +62,19 @@ MOE_DEV int xcd_logical_block(int b, int nb_pad) { return (b & 7) * (nb_pad >> 3
 //    quants) is four f32 16x16x4 products per matrix and superblock (K = the
 //    16 sub-blocks).
 namespace {
-constexpr int GW_GROUPS = 22;        // groups of three rows per matrix (66 >= 64)
-constexpr int GW_GSTRIDE = 65;       // dwords per group in LDS
-constexpr int GW_LOADS = 2 * GW_GROUPS / 4;   // weight loads into LDS per thread and superblock (11)
+constexpr int GW_UNITS = 2 * TILE_ROWS * Q2K_BYTES / 16;   // 16-byte units of one superblock column (672)
+constexpr int GW_LOADS = (GW_UNITS + 255) / 256;           // per thread (3)
 
 template <int NS>
 struct GateupLds {
     static constexpr int R = NS * 16;                        // token rows
     static constexpr int nbuf = 2;                           // superblocks in LDS: one computed, one in flight
-    static constexpr int w_off = 0;                          // [44 groups][65] dwords
-    static constexpr int q_off = w_off + 2 * GW_GROUPS * GW_GSTRIDE * 4;   // [16 chunks][R] x 16 B
+    static constexpr int w_off = 0;                          // [2 matrices][64 rows][84 B] (+ overrun)
+    static constexpr int q_off = w_off + GW_LOADS * 256 * 16;   // [16 chunks][R] x 16 B
     static constexpr int ndx = (8 * R + 255) / 256;          // dword loads per thread for the block scales
     static constexpr int dx_off = q_off + 16 * R * 16;       // [8 blocks][R] f32 (+ padding to ndx * 256)
     static constexpr int x16_off = dx_off + ndx * 256 * 4;   // [16 sub-blocks][R] f32
     static constexpr int buf_bytes = (x16_off + 16 * R * 4 + 15) / 16 * 16;
-    static constexpr int ndma = GW_LOADS + NS + ndx + NS;    // loads into LDS per thread and superblock
     static constexpr int xch_off = nbuf * buf_bytes;         // [4 waves][2 matrices][16 rows] f32: d of each row
     static constexpr int bytes = xch_off + 4 * 2 * 16 * 4;
 };
@@ -125,16 +123,21 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     const int8_t* xq_row = a.xq + (size_t)stok * D;
     const float* xd_row = a.xd + (size_t)stok * (D / QB);
     const float* xf_row = a.xs16f + (size_t)stok * (D / 16);
-    const int gl_row = min(lane / 21, 2), gl_dw = lane == 63 ? 0 : lane % 21;   // lane 63 repeats a dword into the pad
+    // weight unit f = 256 u + tid of a superblock column: matrix f / 336, panel (f % 336) / 42,
+    // 16-byte piece f % 42 (units past the end repeat the last one into the overrun)
+    const uint8_t* wsrc[GW_LOADS];
+#pragma unroll
+    for (int u = 0; u < GW_LOADS; ++u) {
+        const int f = min(256 * u + tid, GW_UNITS - 1);
+        const int m = f / (GW_UNITS / 2), rem = f % (GW_UNITS / 2);
+        const int pp = rem / (PANEL * Q2K_BYTES / 16), k = rem % (PANEL * Q2K_BYTES / 16);
+        wsrc[u] = (m ? w3 : w1) + (size_t)(r0 + PANEL * pp) * rowbytes + k * 16;
+    }
     auto stage = [&](int sb, int bi) {
         uint8_t* buf = smem + bi * LL::buf_bytes;
 #pragma unroll
-        for (int u = 0; u < GW_LOADS; ++u) {   // group q = 4u + wave: rows 3 gi .. 3 gi + 2 of matrix q / 22
-            const int q = 4 * u + wv, m = q / GW_GROUPS, gi = q % GW_GROUPS;
-            const int row = min(3 * gi + gl_row, TILE_ROWS - 1);
-            const uint8_t* src = (m ? w3 : w1) + (size_t)(r0 + row) * rowbytes + (size_t)sb * Q2K_BYTES + gl_dw * 4;
-            load_lds4(src, buf + LL::w_off + q * GW_GSTRIDE * 4);
-        }
+        for (int u = 0; u < GW_LOADS; ++u)
+            load_lds16(wsrc[u] + (size_t)sb * (PANEL * Q2K_BYTES), buf + LL::w_off + (u * 256 + wv * 64) * 16);
 #pragma unroll
         for (int u = 0; u < NS; ++u) {   // unit p = u * 256 + tid: 16-byte chunk p / R of row p % R
             const int kc = (u * 256 + tid) / R;
@@ -154,8 +157,8 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
 
     // this lane's weight rows in LDS (dword offsets), W1 and W3
     const int wr = 16 * wv + l16;
-    const int wo1 = (wr / 3) * GW_GSTRIDE + (wr % 3) * 21;
-    const int wo3 = wo1 + GW_GROUPS * GW_GSTRIDE;
+    const int wo1 = wr * (Q2K_BYTES / 4);
+    const int wo3 = wo1 + TILE_ROWS * (Q2K_BYTES / 4);
 
     typedef float f4 __attribute__((ext_vector_type(4)));
     f4 accg[NS], accu[NS];
@@ -164,16 +167,12 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     const int ns = min(NS, (ch.nrows + 15) / 16);   // sub-tiles holding tokens
     float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 32;
 
-    // superblocks 0 .. nbuf - 2 in flight before the first round
-#pragma unroll
-    for (int i = 0; i < LL::nbuf - 1; ++i) stage(min(i, nsb - 1), i);
-    int bcur = 0;   // buffer of superblock sb
+    stage(0, 0);
     for (int sb = 0; sb < nsb; ++sb) {
-        // superblock sb is in LDS once at most the later superblocks' loads are outstanding
-        wait_vm_loads<(LL::nbuf - 2) * LL::ndma>();
-        barrier_lds();   // ... for every wave; the buffer of superblock sb - 1 is free
-        const int bnext = bcur == 0 ? LL::nbuf - 1 : bcur - 1;   // (sb + nbuf - 1) % nbuf
-        stage(min(sb + LL::nbuf - 1, nsb - 1), bnext);           // past the end: a repeat, so the counts hold
+        wait_vm_loads<0>();   // superblock sb is in LDS ...
+        barrier_lds();        // ... for every wave; the buffer of superblock sb - 1 is free
+        const int bcur = sb & 1;
+        if (sb + 1 < nsb) stage(sb + 1, bcur ^ 1);
         const uint8_t* buf = smem + bcur * LL::buf_bytes;
         const uint32_t* wl = reinterpret_cast<const uint32_t*>(buf + LL::w_off);
         const float* dxl = reinterpret_cast<const float*>(buf + LL::dx_off);
@@ -258,7 +257,6 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the d exchange slots are reused next superblock
-        bcur = bcur == LL::nbuf - 1 ? 0 : bcur + 1;
     }
     wait_vm_loads<0>();   // no load into LDS outlives the workgroup
 #pragma unroll
@@ -277,28 +275,31 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
 // W2 rows are the A operand (16 per wavefront, 64 per workgroup), the chunk's
 // q8_1 rows of h the B operand: C[row][token] per q8_1 block, rescaled by the
 // token's block scale, times -d of the row per superblock.
-//  * The 64 whole W2 rows (contiguous in memory) go into LDS with
-//    wavefront-wide 16-byte loads once; the h quants and block scales of each
-//    superblock follow transposed to [16-byte chunk][token] / [block][token]
-//    (the next superblock in flight while one is computed when LDS allows).
+//  * Per superblock the 64 rows' blocks (eight panels: one contiguous
+//    880-byte run each) and the h quants and block scales go into LDS with
+//    wavefront-wide loads, the weights as [row][110 bytes], the activations
+//    transposed to [16-byte chunk][token] / [block][token]; two superblocks are
+//    in LDS, one computed while the next is in flight.
 //  * A lane (row = lane % 16, g = lane / 16) realigns once per superblock the
 //    hmask bytes 8g..8g+7, the qs bytes 8g.. of both halves and the scales
 //    (superblocks are 110 bytes, so half of them start at 2 bytes past a dword).
 //  * B bytes: (32 - sc6) * (q3 + 4 - 4), from a 64-entry lookup of the 8 values
 //    per six-bit scale (v_perm_b32 on q3 + 4); the sign goes into d.
 namespace {
+constexpr int DW_UNITS = TILE_ROWS * Q3K_BYTES / 16;   // 16-byte units of one superblock column (440)
+constexpr int DW_LOADS = (DW_UNITS + 255) / 256;       // per thread (2)
+
 template <int NS>
 struct DownLds {
     static constexpr int R = NS * 16;
-    static constexpr int nbuf = NS == 1 ? 2 : 1;
-    __host__ __device__ static int w_bytes(int I) { return TILE_ROWS * (I / QK) * Q3K_BYTES; }   // multiple of 16
-    __host__ __device__ static int lut_off(int I) { return w_bytes(I) + 1024; }   // past the last loads' overrun
-    __host__ __device__ static int act_off(int I) { return lut_off(I) + 64 * 8; }
     static constexpr int ndx = (8 * R + 255) / 256;
-    static constexpr int q_bytes = 16 * R * 16;
-    static constexpr int buf_bytes = q_bytes + ndx * 256 * 4;
-    __host__ __device__ static int xch_off(int I) { return act_off(I) + nbuf * buf_bytes; }
-    __host__ __device__ static int bytes(int I) { return xch_off(I) + 4 * 16 * 4; }
+    static constexpr int w_bytes = DW_LOADS * 256 * 16;   // [64 rows][110 B] (+ overrun)
+    static constexpr int q_off = w_bytes;
+    static constexpr int dx_off = q_off + 16 * R * 16;
+    static constexpr int buf_bytes = dx_off + ndx * 256 * 4;
+    static constexpr int lut_off = 2 * buf_bytes;
+    static constexpr int xch_off = lut_off + 64 * 8;
+    __host__ __device__ static int bytes(int) { return xch_off + 4 * 16 * 4; }
 };
 }  // namespace
 
@@ -337,37 +338,37 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     const int8_t* hq = shared ? a.hq_shared : a.hq_routed;
     const float* hd = shared ? a.hd_shared : a.hd_routed;
 
-    // the W2 tile: 16-byte unit f = 256 u + tid; waves wholly past the end skip the load
-    {
-        const int n16 = LL::w_bytes(I) / 16;
-        const uint8_t* src = w2 + (size_t)r0 * rowbytes;
-        for (int u = 0; 256 * u < n16; ++u) {
-            if (256 * u + 64 * wv < n16) {
-                const int f = min(256 * u + tid, n16 - 1);
-                load_lds16(src + (size_t)f * 16, smem + (size_t)(256 * u + 64 * wv) * 16);
-            }
-        }
-    }
     // h rows of the chunk (rows past it repeat its last row; their products are never stored)
     const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));
     const int8_t* hq_row = hq + (size_t)(ch.row0 + srow) * I;
     const float* hd_row = hd + (size_t)(ch.row0 + srow) * (I / QB);
+    // weight unit f = 256 u + tid of a superblock column: panel f / 55, piece f % 55
+    const uint8_t* wsrc[DW_LOADS];
+#pragma unroll
+    for (int u = 0; u < DW_LOADS; ++u) {
+        const int f = min(256 * u + tid, DW_UNITS - 1);
+        const int pp = f / (PANEL * Q3K_BYTES / 16), k = f % (PANEL * Q3K_BYTES / 16);
+        wsrc[u] = w2 + (size_t)(r0 + PANEL * pp) * rowbytes + k * 16;
+    }
     auto stage = [&](int sb, int bi) {
-        uint8_t* buf = smem + LL::act_off(I) + bi * LL::buf_bytes;
+        uint8_t* buf = smem + bi * LL::buf_bytes;
+#pragma unroll
+        for (int u = 0; u < DW_LOADS; ++u)
+            load_lds16(wsrc[u] + (size_t)sb * (PANEL * Q3K_BYTES), buf + (u * 256 + wv * 64) * 16);
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int kc = (u * 256 + tid) / R;
-            load_lds16(hq_row + (size_t)sb * QK + kc * 16, buf + (u * 256 + wv * 64) * 16);
+            load_lds16(hq_row + (size_t)sb * QK + kc * 16, buf + LL::q_off + (u * 256 + wv * 64) * 16);
         }
 #pragma unroll
         for (int u = 0; u < LL::ndx; ++u) {
             const int kb = min((u * 256 + tid) / R, 7);
-            load_lds4(hd_row + (size_t)sb * 8 + kb, buf + LL::q_bytes + (u * 256 + wv * 64) * 4);
+            load_lds4(hd_row + (size_t)sb * 8 + kb, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
         }
     };
     stage(0, 0);
     // lookup: entry sc6 holds (32 - sc6) * (v - 4) for v = 0..7 (bytes; lies in [-128, 124])
-    uint2* lut = reinterpret_cast<uint2*>(smem + LL::lut_off(I));
+    uint2* lut = reinterpret_cast<uint2*>(smem + LL::lut_off);
     if (tid < 64) {
         const int sneg = 32 - tid;
         uint32_t lo = 0, hi = 0;
@@ -382,18 +383,18 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     for (int s = 0; s < NS; ++s) acc[s] = (f4){0.f, 0.f, 0.f, 0.f};
     const int ns = min(NS, (ch.nrows + 15) / 16);
     const int wrow = 16 * wv + l16;
-    const uint32_t* lds = reinterpret_cast<const uint32_t*>(smem);
-    float* xch = reinterpret_cast<float*>(smem + LL::xch_off(I)) + wv * 16;
+    float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 16;
 
     for (int sb = 0; sb < nsb; ++sb) {
-        wait_vm_loads<0>();   // the tile (first round) and superblock sb's h rows
-        barrier_lds();
-        const int bi = LL::nbuf == 2 ? (sb & 1) : 0;
-        if (LL::nbuf == 2) stage(min(sb + 1, nsb - 1), bi ^ 1);
-        const uint8_t* buf = smem + LL::act_off(I) + bi * LL::buf_bytes;
-        const float* dxl = reinterpret_cast<const float*>(buf + LL::q_bytes);
+        wait_vm_loads<0>();   // superblock sb is in LDS ...
+        barrier_lds();        // ... for every wave; the buffer of superblock sb - 1 is free
+        const int bi = sb & 1;
+        if (sb + 1 < nsb) stage(sb + 1, bi ^ 1);
+        const uint8_t* buf = smem + bi * LL::buf_bytes;
+        const uint32_t* lds = reinterpret_cast<const uint32_t*>(buf);
+        const float* dxl = reinterpret_cast<const float*>(buf + LL::dx_off);
 
-        const int off = wrow * rowbytes + sb * Q3K_BYTES;   // 2-byte aligned
+        const int off = wrow * Q3K_BYTES;   // 2-byte aligned
         const int A0 = off >> 2;
         const uint32_t sh = (uint32_t)(off & 3) * 8u;        // 0 or 16
         uint32_t hm[2], q0[2], q1[2];
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
                 const int64_t B = *reinterpret_cast<const int64_t*>(
-                    buf + ((2 * kb8 + gh) * R + 16 * s + l16) * 16 + 8 * (g & 1));
+                    buf + LL::q_off + ((2 * kb8 + gh) * R + 16 * s + l16) * 16 + 8 * (g & 1));
                 const float dx = dxl[kb8 * R + 16 * s + l16];
                 const i32x4_t cc = mfma_i8(Aw, B);
 #pragma unroll
@@ -451,10 +452,6 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(dn[r], ss[s][r], acc[s][r]);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (LL::nbuf == 1 && sb + 1 < nsb) {
-            barrier_lds();   // everyone is done with the buffer
-            stage(sb + 1, 0);
-        }
     }
     wait_vm_loads<0>();   // no load into LDS outlives the workgroup
 #pragma unroll

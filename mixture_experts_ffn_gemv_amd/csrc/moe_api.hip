@@ -251,6 +251,39 @@ int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, si
     return MOE_OK;
 }
 
+// One thread per block of a rows x nsb matrix of B-byte blocks (B even): block
+// (r, s) moves from plain row order to the panel order of the slot layout.
+__global__ __launch_bounds__(256) void pack_matrix_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          int rows, int nsb, int B) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)rows * nsb) return;
+    const int r = (int)(q / nsb), s = (int)(q % nsb);
+    const uint16_t* in = reinterpret_cast<const uint16_t*>(src + q * B);
+    uint16_t* out = reinterpret_cast<uint16_t*>(dst + panel_off(r, s, nsb, B));
+    for (int i = 0; i < B / 2; ++i) out[i] = in[i];
+}
+
+int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream) {
+    if (check_cfg(cfg) != MOE_OK || src == nullptr || dst == nullptr) return MOE_EINVAL;
+    if (((uintptr_t)src | (uintptr_t)dst) & 1) return MOE_EINVAL;
+    size_t bytes, o1, o3, o2;
+    layout_of(*cfg, bytes, o1, o3, o2);
+    const uint8_t* s8 = (const uint8_t*)src;
+    uint8_t* d8 = (uint8_t*)dst;
+    if (s8 < d8 + bytes && d8 < s8 + bytes) return MOE_EINVAL;
+    const hipStream_t st = (hipStream_t)stream;
+    const int D = cfg->dim, I = cfg->inter;
+    struct M { size_t off; int rows, nsb, B; } mats[3] = {
+        {o1, I, D / QK, Q2K_BYTES}, {o3, I, D / QK, Q2K_BYTES}, {o2, D, I / QK, Q3K_BYTES}};
+    for (const M& m : mats) {
+        const int64_t n = (int64_t)m.rows * m.nsb;
+        if (hip_status(launch_kernel(pack_matrix_kernel, (int)((n + 255) / 256), 256, 0, st, s8 + m.off, d8 + m.off,
+                                     m.rows, m.nsb, m.B)) != MOE_OK)
+            return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
 int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     if (out == nullptr) return MOE_EINVAL;
     const int rc = check_cfg(cfg);

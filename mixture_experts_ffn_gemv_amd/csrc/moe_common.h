@@ -15,6 +15,19 @@ constexpr int Q3K_BYTES = 110;   // hmask[32] | qs[64] | scales[12] | d
 constexpr int QB = 32;           // values per q8_1 block
 constexpr int GEMV_ROWS = 8;     // token rows per GEMV chunk
 
+// Slot layout of a K-quant matrix (rows x nsb superblocks of B bytes): panels of
+// PANEL consecutive rows; a panel holds its rows' superblock 0, then their
+// superblock 1, and so on. A tile of whole panels is one contiguous byte
+// range (as in plain row order), and each superblock column of a panel is one
+// contiguous run of PANEL * B bytes.
+constexpr int PANEL = 8;
+
+// Byte offset of superblock s of row r from the start of r's panel group
+// (r counted from a panel boundary).
+MOE_DEV __host__ int panel_off(int r, int s, int nsb, int B) {
+    return ((r / PANEL) * nsb + s) * PANEL * B + (r % PANEL) * B;
+}
+
 // device error word bits
 constexpr int ERR_NONFINITE = 1;
 constexpr int ERR_NOTRESIDENT = 2;

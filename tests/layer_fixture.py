@@ -36,8 +36,10 @@ class Layer:
                             swiglu_limit=limit)
         self.ctx = moe.moe_create(self.cfg)
         self.n_slots = n_slots or shape.n_routed
+        # the library reads slots in its panel layout; the oracle reads arena_src (plain GGUF rows)
+        packed = moe.pack_experts(self.cfg, self.arena_src.to(self.dev))
         if self.n_slots == shape.n_routed:
-            self.arena = self.arena_src.to(self.dev)
+            self.arena = packed
         else:
             self.arena = torch.zeros((self.n_slots, self.arena_src.shape[1]), dtype=torch.uint8, device=self.dev)
         moe.moe_set_slots(self.ctx, self.arena, self.n_slots)
@@ -48,7 +50,7 @@ class Layer:
         if host_arena:
             # every expert in page-locked host memory (a new pinned tensor, not a registered one)
             self.host = torch.empty(self.arena_src.shape, dtype=torch.uint8, pin_memory=True)
-            self.host.copy_(self.arena_src)
+            self.host.copy_(packed)
             moe.moe_set_host_arena(self.ctx, self.host, self.arena_src.shape[1])
         self.d_wr = self.wr.to(self.dev)
         self.d_bias = self.bias.to(self.dev)
@@ -59,7 +61,8 @@ class Layer:
                 self.d_shared = {k: self.shared[k].to(self.dev) for k in ("w1", "w3", "w2")}
                 fmt = moe.MOE_SHARED_BF16
             else:
-                slot = self.shared["slot"].to(self.dev)
+                slot = torch.empty(self.shared["slot"].shape, dtype=torch.uint8, device=self.dev)
+                moe.moe_pack_expert(self.cfg, self.shared["slot"].to(self.dev), slot)
                 _, o1, o3, o2 = S.expert_layout(shape)
                 self.d_shared = {"slot": slot, "w1": slot[o1:o3], "w3": slot[o3:o2], "w2": slot[o2:]}
                 fmt = moe.MOE_SHARED_KQUANT
@@ -72,6 +75,7 @@ class Layer:
         if self.ctx is not None:
             moe.moe_destroy(self.ctx)
             self.ctx = None
+        self.arena = None   # the packed copy (the caller may hold the plain one)
 
     def forward(self, x, m=None, stream=None):
         m = x.shape[0] if m is None else m
