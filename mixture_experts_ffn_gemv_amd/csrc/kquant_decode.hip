@@ -16,6 +16,8 @@
 //      every chunk. It streams the chunks' Q3_K rows and q8_1(h) records in
 //      groups, accumulates G * E per token in a fixed order (the chunks'
 //      order, then the shared expert's f32 output), and stores bf16.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -27,9 +29,7 @@ constexpr int GU_TILE = 32;   // rows of I per gate/up workgroup: one q8_1 block
 constexpr int GU_SUB = 8;     // rows per sub-tile
 constexpr int GU_NU = 6;      // 16-byte loads into LDS per thread per sub-tile (2 * 8 * 84 * nsb bytes over 16 * nsb lanes)
 constexpr int GU_MAX_THREADS = 512;
-constexpr int DC_ROWS = 8;    // output rows per down workgroup
-constexpr int DC_GROUP = 2;   // chunks streamed together by the down workgroup
-constexpr int DC_NPF = 3;     // 16-byte loads per thread per group
+constexpr int DC_ROWS = 8;    // output rows per down workgroup: one panel
 
 // bytes of one q8_1 record of an h row: quants, then the f32 scales, then the
 // 16-value sums
@@ -226,30 +226,34 @@ __global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a,
 }
 
 // ------------------------------------------------------------------ Q3_K down + combine
-// Lanes: tid = pr * L + kb (L = I / 32; pr = output row of the tile, 8 rows).
-// LDS: per group of DC_GROUP chunks, each chunk's 8 W2 rows then its q8_1(h)
-// record; the per-row partial sums; the per-token accumulators.
+// One workgroup = one panel of 8 output rows for every chunk; a pass takes G
+// chunks at once. Lanes: tid = r + 8 (s + nsb cl): row r of the panel,
+// superblock s, chunk cl of the pass. A lane loads its 110-byte block straight
+// from global memory into registers (the 8 rows of a superblock column are one
+// contiguous run, so a wavefront reads whole runs), realigns it (blocks start
+// on 2-byte boundaries) and dots all 256 weights against the chunk's q8_1 h,
+// whose records the pass loads into LDS. The per-(row, chunk) sums over the
+// superblocks and the weighted sum over the chunks of each token run in a
+// fixed order (chunks in list order, then the shared expert's f32 output).
 __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int routed_rows, int m, int max_chunks,
-                                                            const float* __restrict__ ys, uint16_t* __restrict__ out) {
+                                                            int G, const float* __restrict__ ys,
+                                                            uint16_t* __restrict__ out) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
-    const int L = I / QB;
     const int nsb = I / QK;
     const int rowbytes = nsb * Q3K_BYTES;
     const int r0 = blockIdx.x * DC_ROWS;
-    const int tid = threadIdx.x, bd = blockDim.x;
+    const int tid = threadIdx.x, bd = blockDim.x, wv = tid >> 6;
     const int rec = rec_bytes(I);
-    const int tile_bytes = DC_ROWS * rowbytes;   // a multiple of 16 (8 * 110 * nsb)
-    const int unit = tile_bytes + rec;           // LDS bytes per chunk
-    const int unit16 = unit / 16, tile16 = tile_bytes / 16;
-
-    // the chunk list (records read once, kept in LDS)
-    int* c_slot = reinterpret_cast<int*>(smem + DC_GROUP * unit + 16);
+    const int rec16 = rec / 16;                          // a multiple of 16 bytes (I a multiple of 256)
+    const int nu = (G * rec16 + bd - 1) / bd;            // record loads per thread and pass
+    uint8_t* hrec = smem;                                // [G][rec] (+ the last loads' overrun)
+    int* c_slot = reinterpret_cast<int*>(smem + (size_t)nu * bd * 16);
     int* c_row = c_slot + max_chunks;
     int* c_tok = c_row + max_chunks;
     float* c_w = reinterpret_cast<float*>(c_tok + max_chunks);
-    float* red = c_w + max_chunks;                 // [DC_GROUP][DC_ROWS][nsb]
-    float* acc = red + DC_GROUP * DC_ROWS * nsb;   // [m][DC_ROWS]
+    float* part = c_w + max_chunks;                      // [G][8][nsb]
+    float* acc = part + G * DC_ROWS * nsb;               // [m][8]
     const int nch = min(*a.n_chunks, max_chunks);
     for (int q = tid; q < nch; q += bd) {
         const Chunk ch = a.chunks[q];
@@ -262,129 +266,104 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     for (int q = tid; q < m * DC_ROWS; q += bd) acc[q] = 0.f;
     __syncthreads();
 
-    // group loads: DC_GROUP units of [tile | record]; chunks past the end repeat the last one
-    uint4 pf0, pf1, pf2;   // named registers (an array here was placed in scratch memory)
-    static_assert(DC_NPF == 3, "the prefetch registers below");
-#define DC_LOAD_ONE(g0, u, dst)                                                                              \
-    {                                                                                                        \
-        const int q = min(tid + (u) * bd, DC_GROUP * unit16 - 1);                                            \
-        const int cc = q / unit16, o = q % unit16;                                                           \
-        const int cidx = min((g0) + cc, nch - 1);                                                            \
-        const int slot = c_slot[cidx];                                                                       \
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);                                                                \
-        if (o < tile16) {                                                                                    \
-            if (slot != -1) {                                                                                \
-                const uint8_t* w2 = slot == -2 ? a.sh_w2 : a.arena + (size_t)slot * a.slot_bytes + a.off_w2;  \
-                v = reinterpret_cast<const uint4*>(w2 + (size_t)r0 * rowbytes)[o];                          \
-            }                                                                                                \
-        } else {                                                                                             \
-            v = reinterpret_cast<const uint4*>(a.hrec + (size_t)c_row[cidx] * rec)[o - tile16];              \
-        }                                                                                                    \
-        dst = v;                                                                                             \
-    }
-#define DC_LOAD_GROUP(g0) { DC_LOAD_ONE(g0, 0, pf0) DC_LOAD_ONE(g0, 1, pf1) DC_LOAD_ONE(g0, 2, pf2) }
-    if (nch > 0) DC_LOAD_GROUP(0)
-
-    const int pr = tid / L, kb = tid % L;
-    const bool lane_live = pr < DC_ROWS;
-    const int s = kb >> 3, hh = (kb >> 2) & 1, j = kb & 3;
-    // per-lane constants for the two 6-bit scales of sub-blocks n = 8hh + 2j + {0,1}
-    const int n_lo = 8 * hh + 2 * j;
-    const int lo_byte0 = 2 * j, lo_shift = 4 * hh;
-    const int hi_byte0 = 8 + (n_lo & 3), hi_byte1 = 8 + ((n_lo + 1) & 3);
-    const int hi_shift = 2 * (n_lo >> 2);
-    uint4* lds16 = reinterpret_cast<uint4*>(smem);
-    const uint32_t* lds32 = reinterpret_cast<const uint32_t*>(smem);
-    for (int g0 = 0; g0 < nch; g0 += DC_GROUP) {
-        if (g0 > 0) __syncthreads();   // the previous group's units and partials are consumed
-#define DC_STORE_ONE(u, src) \
-    if (tid + (u) * bd < DC_GROUP * unit16) lds16[tid + (u) * bd] = src;
-        DC_STORE_ONE(0, pf0) DC_STORE_ONE(1, pf1) DC_STORE_ONE(2, pf2)
-#undef DC_STORE_ONE
-        __syncthreads();
-        if (g0 + DC_GROUP < nch) DC_LOAD_GROUP(g0 + DC_GROUP)
-        const int ng = min(DC_GROUP, nch - g0);
-        if (lane_live) {
-            for (int cc = 0; cc < ng; ++cc) {
-                const int ubase = cc * unit;
-                const uint32_t* hq32 = lds32 + (ubase + tile_bytes) / 4;
-                // the lane's q8_1 block of h: two 16-byte reads (dword reads at a
-                // 32-byte lane stride conflicted on the LDS banks)
-                const uint4 h0 = reinterpret_cast<const uint4*>(hq32)[2 * kb];
-                const uint4 h1 = reinterpret_cast<const uint4*>(hq32)[2 * kb + 1];
-                const uint32_t av[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-                const float dx = reinterpret_cast<const float*>(hq32 + I / 4)[kb];
-                const int2 hs = reinterpret_cast<const int2*>(hq32 + I / 4 + L)[kb];
-                const int slo = hs.x, shi = hs.y;
-                const int sb = ubase + panel_off(pr, s, nsb, Q3K_BYTES);   // 2-byte aligned
-                const int A = sb >> 2;
-                const uint32_t sh = (uint32_t)(sb & 3) * 8u;              // 0 or 16
-                uint32_t V[8];
-                {
-                    const int qo = A + 8 + 8 * hh;                           // qs[32 hh ..] at byte 32 + 32 hh
-                    uint32_t prev = lds32[qo];
+    const int r = tid & 7, sc = tid >> 3, s = sc % nsb, cl = sc / nsb;
+    const uint32_t* h32 = reinterpret_cast<const uint32_t*>(hrec) + (size_t)cl * (rec / 4);
+    for (int g0 = 0; g0 < nch; g0 += G) {
+        const int ng = min(G, nch - g0);
+        // this pass's h records into LDS (units past the end repeat the last one)
+        for (int u = 0; u < nu; ++u) {
+            const int f = min(u * bd + tid, ng * rec16 - 1);
+            const int q = f / rec16, k = f % rec16;
+            load_lds16(a.hrec + (size_t)c_row[g0 + q] * rec + k * 16, hrec + (size_t)(u * bd + wv * 64) * 16);
+        }
+        // this lane's block: 28 dwords from the dword below its start (in bounds: a block
+        // that starts on a dword ends 2 bytes before the next block of its column run)
+        const bool act = cl < ng;
+        const int slot = act ? c_slot[g0 + cl] : -1;
+        uint32_t W[28];
+        uint32_t sh = 0;
+        if (slot != -1) {
+            const uint8_t* w2 = slot == -2 ? a.sh_w2 : a.arena + (size_t)slot * a.slot_bytes + a.off_w2;
+            const uint8_t* blk = w2 + (size_t)r0 * rowbytes + (size_t)(s * DC_ROWS + r) * Q3K_BYTES;
+            sh = (uint32_t)((uintptr_t)blk & 3) * 8u;
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(blk) & ~(uintptr_t)3);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const uint32_t next = lds32[qo + q + 1];
-                        const uint32_t qs = funnel(next, prev, sh);
-                        const uint32_t hm = funnel(lds32[A + q + 1], lds32[A + q], sh);
-                        prev = next;
-                        const uint32_t lo = (qs >> (2 * j)) & 0x03030303u;
-                        const uint32_t hb = (hm >> (4 * hh + j)) & 0x01010101u;
-                        V[q] = lo | (hb << 2);                               // q3 + 4, 0..7
-                    }
-                }
-                const uint32_t s0 = funnel(lds32[A + 25], lds32[A + 24], sh);   // scale bytes 0..3
-                const uint32_t s1 = funnel(lds32[A + 26], lds32[A + 25], sh);   // 4..7
-                const uint32_t s2 = funnel(lds32[A + 27], lds32[A + 26], sh);   // 8..11
-                const uint32_t dbits = (lds32[A + 27] >> sh) & 0xFFFFu;          // d at byte 108
-                const uint32_t lo_word = (lo_byte0 < 4) ? s0 : s1;
-                const int lsh = 8 * (lo_byte0 & 3);
-                const int low4_lo = (lo_word >> (lsh + lo_shift)) & 15;
-                const int low4_hi = (lo_word >> (lsh + 8 + lo_shift)) & 15;
-                const int hi2_lo = (s2 >> (8 * (hi_byte0 - 8) + hi_shift)) & 3;
-                const int hi2_hi = (s2 >> (8 * (hi_byte1 - 8) + hi_shift)) & 3;
-                const int s6_lo = (low4_lo | (hi2_lo << 4)) - 32;
-                const int s6_hi = (low4_hi | (hi2_hi << 4)) - 32;
-                const float d = half_bits_to_f32(dbits);
+            for (int q = 0; q < 28; ++q) W[q] = p[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 28; ++q) W[q] = 0u;
+        }
+        wait_vm_loads<0>();
+        barrier_lds();
+        if (act) {
+            // realigned block: hmask dwords 0..7, qs 8..23, scales 24..26, d in 27
+            uint32_t B[28];
+#pragma unroll
+            for (int q = 0; q < 27; ++q) B[q] = funnel(W[q + 1], W[q], sh);
+            B[27] = W[27] >> sh;
+            const uint32_t* hq = h32 + s * (QK / 4);
+            const float* hd = reinterpret_cast<const float*>(h32 + I / 4) + s * 8;
+            const int* hs = reinterpret_cast<const int*>(h32 + I / 4 + I / QB) + s * 16;
+            float fs = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {   // q8_1 block t of h: plane j = t % 4 of half hh = t / 4
+                const int hh = t >> 2, j = t & 3;
+                const uint4 x0 = reinterpret_cast<const uint4*>(hq + 8 * t)[0];
+                const uint4 x1 = reinterpret_cast<const uint4*>(hq + 8 * t)[1];
+                const uint32_t xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
                 int il = 0, ih = 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) il = sdot4(V[q], av[q], il);
-#pragma unroll
-                for (int q = 4; q < 8; ++q) ih = sdot4(V[q], av[q], ih);
-                il -= 4 * slo;
-                ih -= 4 * shi;
-                float part = dx * (d * (float)(__mul24(s6_lo, il) + __mul24(s6_hi, ih)));
-                part = group8_sum(part);
-                if ((kb & 7) == 7) red[(cc * DC_ROWS + pr) * nsb + s] = part;
+                for (int cc = 0; cc < 8; ++cc) {
+                    // q3 + 4 = low two bits | high bit << 2, for 4 weights
+                    const uint32_t v = ((B[8 + 8 * hh + cc] >> (2 * j)) & 0x03030303u) |
+                                       (((B[cc] >> (4 * hh + j)) & 0x01010101u) << 2);
+                    if (cc < 4) il = sdot4(v, xv[cc], il);
+                    else ih = sdot4(v, xv[cc], ih);
+                }
+                const int2 s16 = reinterpret_cast<const int2*>(hs)[t];
+                il -= 4 * s16.x;
+                ih -= 4 * s16.y;
+                // six-bit scales of sub-blocks n = 2t, 2t + 1: low nibble of byte n % 8
+                // (high nibble for n >= 8), two high bits of byte 8 + n % 4 at 2 (n / 4)
+                const int n0 = 2 * t, n1 = 2 * t + 1;
+                const int lo0 = (B[24 + ((n0 & 7) >> 2)] >> (8 * (n0 & 3) + 4 * hh)) & 15;
+                const int lo1 = (B[24 + ((n1 & 7) >> 2)] >> (8 * (n1 & 3) + 4 * hh)) & 15;
+                const int hi0 = (B[26] >> (8 * (n0 & 3) + 2 * (n0 >> 2))) & 3;
+                const int hi1 = (B[26] >> (8 * (n1 & 3) + 2 * (n1 >> 2))) & 3;
+                const int isum = __mul24((lo0 | (hi0 << 4)) - 32, il) + __mul24((lo1 | (hi1 << 4)) - 32, ih);
+                fs = fmaf(hd[t], (float)isum, fs);
             }
+            part[(cl * DC_ROWS + r) * nsb + s] = half_bits_to_f32(B[27] & 0xFFFFu) * fs;
         }
-        __syncthreads();
-        if (tid < DC_ROWS) {   // row tid: this group's chunks in order
-            for (int cc = 0; cc < ng; ++cc) {
-                const float* re = red + (cc * DC_ROWS + tid) * nsb;
+        barrier_lds();
+        if (tid < m * DC_ROWS) {   // token tid / 8, row tid % 8: this pass's chunks in order
+            const int t = tid >> 3, rr = tid & 7;
+            float v = acc[tid];
+            for (int q = 0; q < ng; ++q) {
+                const int c = g0 + q;
+                if (c_tok[c] != t || c_slot[c] == -1) continue;
+                const float* pe = part + (q * DC_ROWS + rr) * nsb;
                 float e = 0.f;
-                for (int q = 0; q < nsb; ++q) e += re[q];
-                const int c = g0 + cc;
-                acc[c_tok[c] * DC_ROWS + tid] += c_slot[c] == -1 ? 0.f : c_w[c] * e;
+                for (int k = 0; k < nsb; ++k) e += pe[k];
+                v = fmaf(c_w[c], e, v);
             }
+            acc[tid] = v;
         }
+        barrier_lds();   // the records and partials are reused by the next pass
     }
-#undef DC_LOAD_GROUP
-#undef DC_LOAD_ONE
-    __syncthreads();
     for (int q = tid; q < m * DC_ROWS; q += bd) {
-        const int t = q / DC_ROWS, r = q % DC_ROWS;
+        const int t = q / DC_ROWS, rr = q % DC_ROWS;
         float v = acc[q];
-        if (ys != nullptr) v += ys[(size_t)t * D + r0 + r];
-        out[(size_t)t * D + r0 + r] = (uint16_t)f32_to_bf16(v);
+        if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
+        out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v);
     }
 }
 
 // ------------------------------------------------------------------ launch
 bool decode_supported(int D, int I) {
     // lanes: 16 per superblock of D for gate/up and 8 * I / 32 for down, within one workgroup
-    return D % QK == 0 && I % QK == 0 && 16 * (D / QK) <= GU_MAX_THREADS && I / 4 <= 1024 && D % DC_ROWS == 0;
+    return D % QK == 0 && I % QK == 0 && 16 * (D / QK) <= GU_MAX_THREADS && DC_ROWS * (I / QK) <= 1024 &&
+           D % DC_ROWS == 0;
 }
 
 static int round64(int v) { return (v + 63) / 64 * 64; }
@@ -401,12 +380,16 @@ hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks
 
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
                                uint16_t* out, hipStream_t st) {
-    const int threads = round64(DC_ROWS * (a.I / QB));
     const int nsb = a.I / QK;
-    const size_t unit = (size_t)DC_ROWS * nsb * Q3K_BYTES + decode_rec_bytes(a.I);
-    const size_t lds = DC_GROUP * unit + 16 + (size_t)max_chunks * 16 + (size_t)DC_GROUP * DC_ROWS * nsb * 4 +
+    const int lanes = DC_ROWS * nsb;                      // per chunk
+    const int G = std::max(1, std::min(max_chunks, 1024 / lanes));
+    const int threads = round64(lanes * G);
+    const int rec16 = (int)(decode_rec_bytes(a.I) / 16);
+    const int nu = (G * rec16 + threads - 1) / threads;
+    const size_t lds = (size_t)nu * threads * 16 + (size_t)max_chunks * 16 + (size_t)G * DC_ROWS * nsb * 4 +
                        (size_t)m * DC_ROWS * 4;
-    return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, ys, out);
+    return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, G, ys,
+                         out);
 }
 
 }  // namespace moe
