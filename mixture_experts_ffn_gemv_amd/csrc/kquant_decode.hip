@@ -35,6 +35,12 @@ constexpr int DC_ROWS = 8;    // output rows per down workgroup: one panel
 // 16-value sums
 MOE_DEV int rec_bytes(int I) { return I + (I / QB) * 4 + (I / 16) * 4; }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ Q2_K gate/up -> q8_1(h)
@@ -237,6 +243,8 @@ __global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a,
 // fixed order (chunks in list order, then the shared expert's f32 output).
 __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int routed_rows, int m, int max_chunks,
                                                             int G, const float* __restrict__ ys,
+                                                            const uint16_t* __restrict__ sh_w2,
+                                                            const uint16_t* __restrict__ h_sh,
                                                             uint16_t* __restrict__ out) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
@@ -254,6 +262,7 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     float* c_w = reinterpret_cast<float*>(c_tok + max_chunks);
     float* part = c_w + max_chunks;                      // [G][8][nsb]
     float* acc = part + G * DC_ROWS * nsb;               // [m][8]
+    float* shp = acc + m * DC_ROWS;                      // [8][I / 32][m]: bf16 shared expert partials
     const int nch = min(*a.n_chunks, max_chunks);
     for (int q = tid; q < nch; q += bd) {
         const Chunk ch = a.chunks[q];
@@ -264,6 +273,28 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
         c_w[q] = ch.weight;
     }
     for (int q = tid; q < m * DC_ROWS; q += bd) acc[q] = 0.f;
+    // bf16 shared expert (when given): this panel's W2 rows against h (bf16 [m, I]),
+    // one (row, 32-element slice) per job, partials summed in slice order below
+    const int ns32 = I / 32;
+    if (sh_w2 != nullptr) {
+        for (int job = tid; job < DC_ROWS * ns32; job += bd) {
+            const int rr = job / ns32, ks = job % ns32;
+            const uint4* wp = reinterpret_cast<const uint4*>(sh_w2 + (size_t)(r0 + rr) * I + 32 * ks);
+            const uint4 w0 = wp[0], w1 = wp[1], w2 = wp[2], w3 = wp[3];
+            const uint32_t wv[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
+                                     w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
+            for (int t = 0; t < m; ++t) {
+                const uint4* hp = reinterpret_cast<const uint4*>(h_sh + (size_t)t * I + 32 * ks);
+                const uint4 h0 = hp[0], h1 = hp[1], h2 = hp[2], h3 = hp[3];
+                const uint32_t hv[16] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w,
+                                         h2.x, h2.y, h2.z, h2.w, h3.x, h3.y, h3.z, h3.w};
+                float v = 0.f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) v = dot2_bf16(wv[q], hv[q], v);
+                shp[(rr * ns32 + ks) * m + t] = v;
+            }
+        }
+    }
     __syncthreads();
 
     const int r = tid & 7, sc = tid >> 3, s = sc % nsb, cl = sc / nsb;
@@ -355,6 +386,11 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
         const int t = q / DC_ROWS, rr = q % DC_ROWS;
         float v = acc[q];
         if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
+        if (sh_w2 != nullptr) {
+            float e = 0.f;
+            for (int k = 0; k < ns32; ++k) e += shp[(rr * ns32 + k) * m + t];
+            v += e;
+        }
         out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v);
     }
 }
@@ -379,7 +415,7 @@ hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks
 }
 
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
-                               uint16_t* out, hipStream_t st) {
+                               const uint16_t* sh_w2_bf16, const uint16_t* h_sh_bf16, uint16_t* out, hipStream_t st) {
     const int nsb = a.I / QK;
     const int lanes = DC_ROWS * nsb;                      // per chunk
     const int G = std::max(1, std::min(max_chunks, 1024 / lanes));
@@ -387,9 +423,9 @@ hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int 
     const int rec16 = (int)(decode_rec_bytes(a.I) / 16);
     const int nu = (G * rec16 + threads - 1) / threads;
     const size_t lds = (size_t)nu * threads * 16 + (size_t)max_chunks * 16 + (size_t)G * DC_ROWS * nsb * 4 +
-                       (size_t)m * DC_ROWS * 4;
+                       (size_t)m * DC_ROWS * 4 + (sh_w2_bf16 ? (size_t)DC_ROWS * (a.I / 32) * m * 4 : 0);
     return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, G, ys,
-                         out);
+                         sh_w2_bf16, h_sh_bf16, out);
 }
 
 }  // namespace moe

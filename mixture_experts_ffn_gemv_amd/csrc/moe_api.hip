@@ -635,7 +635,27 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     const bool bf16_shared = w->shared_fmt == MOE_SHARED_BF16;
     const bool small = m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS;
     const bool use_mmq = !small && ctx->mmq_ok;
-    if (bf16_shared) {
+    // decode with every picked expert in its slot: the bf16 shared expert rides in
+    // the same launches (its gate/up rows as extra workgroups of the two routing
+    // kernels, its down inside the routed down kernel), no second stream
+    const bool shared_fused = bf16_shared && small && ctx->decode_ok && ctx->host_arena == nullptr;
+    SharedRows sr_a{}, sr_b{};
+    if (shared_fused) {
+        sr_a.w1 = (const uint16_t*)w->shared_w1;
+        sr_a.w3 = (const uint16_t*)w->shared_w3;
+        sr_a.x = x;
+        sr_a.h = (uint16_t*)ctx->h_shared;
+        sr_a.D = c.dim;
+        sr_a.I = c.inter;
+        sr_a.m = m;
+        sr_a.limit = c.swiglu_limit;
+        sr_b = sr_a;
+        sr_a.row0 = 0;
+        sr_a.rows = c.inter / 2;
+        sr_b.row0 = sr_a.rows;
+        sr_b.rows = c.inter - sr_a.rows;
+    }
+    if (bf16_shared && !shared_fused) {
         // the shared expert needs only x: run it beside the routing and the routed experts
         if (hipEventRecord(ctx->ev_fork, st) != hipSuccess || hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0) != hipSuccess)
             return MOE_EHIP;
@@ -665,14 +685,14 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
-                                       ctx->xd, ctx->xs16, st);
+                                       ctx->xd, ctx->xs16, st, shared_fused ? &sr_a : nullptr);
         });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_TOPK, [&] {
             return launch_route_small(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp,
                                       c.norm_topk_prob, c.route_scale, ctx->idx, ctx->gw, ctx->err, kq ? 1 : 0,
                                       ctx->offsets, ctx->active, ctx->n_active, ctx->perm, ctx->inv, ctx->chunks,
-                                      ctx->n_chunks, ctx->slot_table_dev, st);
+                                      ctx->n_chunks, ctx->slot_table_dev, st, shared_fused ? &sr_b : nullptr);
         });
         if (rc != MOE_OK) return rc;
     } else {
@@ -749,9 +769,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         const int nch = P + (kq ? m : 0);
         rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q8(a, P, nch, st); });
         if (rc != MOE_OK) return rc;
-        if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
+        if (bf16_shared && !shared_fused && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
         rc = timed(ctx, st, MOE_K_DOWN, [&] {
-            return launch_down_combine(a, P, m, nch, ys, (uint16_t*)out_bf16, st);
+            if (shared_fused)
+                return launch_down_combine(a, P, m, nch, nullptr, (const uint16_t*)w->shared_w2,
+                                           (const uint16_t*)ctx->h_shared, (uint16_t*)out_bf16, st);
+            return launch_down_combine(a, P, m, nch, ys, nullptr, nullptr, (uint16_t*)out_bf16, st);
         });
         if (rc != MOE_OK) return rc;
         return finish_call(ctx, weights_out, idx_out, P, st);
@@ -786,7 +809,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
             if (ew == nullptr || hipEventRecord(ew, st) != hipSuccess) return MOE_EHIP;
         }
     }
-    if (bf16_shared && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
+    if (bf16_shared && !shared_fused && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
     const float* ys_all = w->shared_fmt == MOE_SHARED_NONE ? nullptr : ctx->ys;
     rc = timed(ctx, st, MOE_K_COMBINE, [&] {
         return launch_combine(ctx->e_rows, ys_all, ctx->gw, ctx->inv, m, c.topk, c.dim, (uint16_t*)out_bf16, st);

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "moe_common.h"
+#include "shared_rows.h"
 
 namespace moe {
 
@@ -71,14 +72,15 @@ inline ChunkPlan mmq_chunk_plan(int m, int k, int E, bool shared) {
 
 // router logits for m tokens, plus q8_1 of x in the same launch when xq != NULL
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st);
+                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st, const SharedRows* sr = nullptr);
 // top-k and bucketing in one workgroup, for m * topk <= 512 and m <= 8
 constexpr int ROUTE_SMALL_MAX_M = 8;
 constexpr int ROUTE_SMALL_MAX_PAIRS = 512;
 hipError_t launch_route_small(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
-                              Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st);
+                              Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st,
+                              const SharedRows* sr = nullptr);
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
                                 float* xs16f, hipStream_t st);
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp, int norm,
@@ -105,8 +107,9 @@ bool decode_supported(int D, int I);
 size_t decode_rec_bytes(int I);
 // gate/up writing the q8_1 records of h
 hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st);
+// down + weighted combine; a bf16 shared expert's down (W2 bf16 [D, I], h bf16 [m, I]) rides along when given
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
-                               uint16_t* out, hipStream_t st);
+                               const uint16_t* sh_w2_bf16, const uint16_t* h_sh_bf16, uint16_t* out, hipStream_t st);
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int m, int D, int I, const uint16_t* w1,
                                      const uint16_t* w3, uint16_t* h_bf16, float limit, hipStream_t st);
 hipError_t launch_shared_bf16_down(const uint16_t* h_bf16, int m, int D, int I, const uint16_t* w2, float* ys,

@@ -8,9 +8,12 @@
 // times route_scale; and the Open Model Atlas router equations for
 // DeepSeek V4.1. The selection runs on the device (one wavefront per token)
 // instead of the pages' host round trip.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 #include "route_select.h"
+#include "shared_rows.h"
 
 namespace moe {
 
@@ -56,8 +59,14 @@ template <int TT>
 __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __restrict__ x, int m,
                                                            const uint16_t* __restrict__ wr, int D, int E, int ntg,
                                                            float* __restrict__ logits, int8_t* __restrict__ xq,
-                                                           float* __restrict__ xd, int32_t* __restrict__ xs16) {
+                                                           float* __restrict__ xd, int32_t* __restrict__ xs16,
+                                                           SharedRows sr) {
     const int nrouter = E * ntg;
+    const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
+    if ((int)blockIdx.x >= nrouter + nq) {   // the shared expert's rows
+        shared_gateup_block(sr, blockIdx.x - nrouter - nq);
+        return;
+    }
     if ((int)blockIdx.x >= nrouter) {
         const int b = (blockIdx.x - nrouter) * 256 + threadIdx.x;
         if (b < m * (D / QB)) quantize_block_bf16(x, b, xq, xd, xs16);
@@ -363,7 +372,11 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                            int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                                            Chunk* __restrict__ chunks,
                                                            int32_t* __restrict__ n_chunks,
-                                                           const int32_t* __restrict__ slot_table) {
+                                                           const int32_t* __restrict__ slot_table, SharedRows sr) {
+    if (blockIdx.x > 0) {   // the shared expert's rows
+        shared_gateup_block(sr, blockIdx.x - 1);
+        return;
+    }
     __shared__ __align__(16) float keys[1024];
     __shared__ float cand_key[1024], cand_s[1024];
     __shared__ int cand_id[1024];
@@ -515,7 +528,11 @@ __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict_
                                                         int32_t* __restrict__ n_active, int32_t* __restrict__ perm,
                                                         int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
                                                         int32_t* __restrict__ n_chunks,
-                                                        const int32_t* __restrict__ slot_table) {
+                                                        const int32_t* __restrict__ slot_table, SharedRows sr) {
+    if (blockIdx.x > 0) {   // the shared expert's rows
+        shared_gateup_block(sr, blockIdx.x - 1);
+        return;
+    }
     __shared__ float keys[64 * M1_MAX_KEYS], scores[64 * M1_MAX_KEYS];
     const int tid = threadIdx.x;
     {
@@ -550,13 +567,17 @@ hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const in
 }
 
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st) {
+                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st, const SharedRows* sr) {
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
-    if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
-    if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
-    if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16);
+    SharedRows none{};
+    const SharedRows& s = sr ? *sr : none;
+    const int nsh = sr ? shared_rows_blocks(sr->rows, 256) : 0;
+    if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
+    if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
+    if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
     const int ntg = (m + 7) / 8;
-    return launch_kernel(router_quant_kernel<8>, E * ntg + nq, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd, xs16);
+    return launch_kernel(router_quant_kernel<8>, E * ntg + nq + nsh, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd,
+                         xs16, s);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
@@ -568,18 +589,25 @@ hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, flo
 hipError_t launch_route_small(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
                               int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
-                              Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st) {
+                              Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st,
+                              const SharedRows* sr) {
+    SharedRows none{};
+    const SharedRows& s = sr ? *sr : none;
     if (m == 1 && E <= 64 * M1_MAX_KEYS && k <= 64) {
-        const int th = (E + 63) / 64 * 64;
-#define ROUTE_M1(KPL) launch_kernel(route_m1_kernel<KPL>, 1, th, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, \
-                                    idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table)
+        const int th = std::max(128, (E + 63) / 64 * 64);   // shared-expert rows take two wavefronts each
+        const int grid = 1 + (sr ? shared_rows_blocks(sr->rows, th) : 0);
+#define ROUTE_M1(KPL) launch_kernel(route_m1_kernel<KPL>, grid, th, 0, st, logits, bias, E, k, gate_temp, norm, \
+                                    route_scale, idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, \
+                                    chunks, n_chunks, slot_table, s)
         const int kpl = topk_kpl(E);
         const hipError_t e = kpl == 2 ? ROUTE_M1(2) : kpl == 6 ? ROUTE_M1(6) : ROUTE_M1(16);
 #undef ROUTE_M1
         return e;
     }
-    return launch_kernel(route_small_kernel, 1, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err,
-                  shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
+    const int grid = 1 + (sr ? shared_rows_blocks(sr->rows, 1024) : 0);
+    return launch_kernel(route_small_kernel, grid, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale,
+                         idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks,
+                         slot_table, s);
 }
 
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
