@@ -9,13 +9,13 @@
 // accumulate / finish for the weighted sum).
 //
 //  gateup_q8_kernel:   one workgroup = one chunk x 32 rows of the inter
-//      dimension, W1 and W3, streamed as four 8-row sub-tiles through LDS;
-//      the epilogue applies the clamped SwiGLU and writes the q8_1 block the
-//      32 values of h form (no f32 h in memory).
+//      dimension (four 8-row panels), W1 and W3, every block loaded straight
+//      into registers at the start; the epilogue applies the clamped SwiGLU and
+//      writes the q8_1 block the 32 values of h form (no f32 h in memory).
 //  down_combine_kernel: one workgroup = 8 rows of the output dimension for
-//      every chunk. It streams the chunks' Q3_K rows and q8_1(h) records in
-//      groups, accumulates G * E per token in a fixed order (the chunks'
-//      order, then the shared expert's f32 output), and stores bf16.
+//      every chunk. It loads the chunks' q8_1(h) records into LDS and each
+//      lane's Q3_K block into registers, accumulates G * E per token in a
+//      fixed order (the chunks' order, then the shared expert), and stores bf16.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -25,10 +25,7 @@ namespace moe {
 
 namespace {
 
-constexpr int GU_TILE = 32;   // rows of I per gate/up workgroup: one q8_1 block of h
-constexpr int GU_SUB = 8;     // rows per sub-tile
-constexpr int GU_NU = 6;      // 16-byte loads into LDS per thread per sub-tile (2 * 8 * 84 * nsb bytes over 16 * nsb lanes)
-constexpr int GU_MAX_THREADS = 512;
+constexpr int GU_TILE = 32;   // rows of I per gate/up workgroup: one q8_1 block of h (four panels)
 constexpr int DC_ROWS = 8;    // output rows per down workgroup: one panel
 
 // bytes of one q8_1 record of an h row: quants, then the f32 scales, then the
@@ -44,56 +41,32 @@ MOE_DEV float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }  // namespace
 
 // ------------------------------------------------------------------ Q2_K gate/up -> q8_1(h)
-// One workgroup = one chunk x 32 rows of the inter dimension (one q8_1 block
-// of h), W1 and W3. The 32 rows stream through LDS as four sub-tiles of 8 rows
-// of each matrix, loaded straight from global memory into LDS (no register
-// staging) into two LDS slots: sub-tile i + 1 is in flight while sub-tile i is
-// computed, and sub-tile i + 2 is requested as soon as slot i & 1 is free.
-// Lanes: tid = 16 * s + r: superblock column s of local row r of the sub-tile
-// (rows 0..7 are W1, 8..15 are W3). A lane keeps the q8_1 block data of
-// superblock s of x in registers for the whole tile and does every weight of
-// one (row, superblock) per sub-tile: the four 2-bit planes of each qs dword
+// One workgroup = one chunk x 32 rows of the inter dimension (four 8-row
+// panels: one q8_1 block of h), W1 and W3. Lanes: tid = r + 8 (sl + NSL (m + 2 p)):
+// row r of panel p of matrix m (0 = W1, 1 = W3), superblocks s = sl + NSL k,
+// k < SPL. A lane loads its SPL 84-byte blocks straight from global memory into
+// registers at the start: the 8 rows of a superblock column are one contiguous
+// run, so each wavefront load covers whole runs (5 KB contiguous), and every
+// weight of the tile is requested at once. The token's q8_1 activations come
+// into LDS by the DMA path. Per block the four 2-bit planes of each qs dword
 // are masked in place (planes 1 and 3 land at 4x, folded into the activation
-// block scale), and the sub-block scales and mins are applied per 16 weights.
-__global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a, int routed_rows) {
+// block scale) and the sub-block scales and mins applied per 16 weights; the
+// per-row sums over the superblocks run in order, then the clamped SwiGLU and
+// the q8_1 block of the 32 values of h across 32 lanes.
+template <int SPL>
+__global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int routed_rows) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
     const int L = D / QB;
     const int nsb = D / QK;
+    const int NSL = (nsb + SPL - 1) / SPL;
     const int rowbytes = nsb * Q2K_BYTES;
     const int tiles = I / GU_TILE;
     const int c = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-    const int tid = threadIdx.x, bd = blockDim.x;
-    const int slot_bytes = GU_NU * bd * 16;
+    const int tid = threadIdx.x, bd = blockDim.x, wv = tid >> 6;
     const int nch = *a.n_chunks;
     if (c >= nch) return;
     const Chunk ch = a.chunks[c];
-    const int token = ch.token;
-
-    // the lane's superblock of x: 256 quants, the eight block scales and the
-    // 16-value sums (requested before the weights, used once the first sub-tile is in)
-    const int r = tid & 15, s = tid >> 4;
-    const bool live = s < nsb;
-    const int sx = live ? s : 0;
-    uint32_t xv[64];
-    float4 d0, d1;
-    int4 s16v[4];
-    {
-        const uint4* xs = reinterpret_cast<const uint4*>(a.xq + (size_t)token * D + (size_t)sx * QK);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint4 v = xs[q];
-            xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-        }
-        const float4* dp = reinterpret_cast<const float4*>(a.xd + (size_t)token * L + (size_t)sx * 8);
-        d0 = dp[0];
-        d1 = dp[1];
-        const int4* sp = reinterpret_cast<const int4*>(a.xs16 + (size_t)token * 2 * L + (size_t)sx * 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s16v[q] = sp[q];
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // these loads stay ahead of the sub-tile requests
-
     const bool shared = ch.expert < 0;
     const int r0 = tile * GU_TILE;
     const int rec = rec_bytes(I);
@@ -108,8 +81,7 @@ __global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a,
             if (tid < GU_TILE / 4) reinterpret_cast<uint32_t*>(out + r0)[tid] = 0u;
             if (tid == 0) {
                 reinterpret_cast<float*>(out + I)[tile] = 0.f;
-                reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile] = 0;
-                reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile + 1] = 0;
+                reinterpret_cast<int2*>(out + I + (I / QB) * 4)[tile] = make_int2(0, 0);
             }
             return;
         }
@@ -117,100 +89,90 @@ __global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a,
         w1 = base + a.off_w1;
         w3 = base + a.off_w3;
     }
-    // Sub-tile i = W1 rows [r0 + 8 i, r0 + 8 i + 8) then the same rows of W3:
-    // 2 * n16 16-byte units, unit f of thread tid's u-th load being u * bd + tid.
-    // Each wave's load writes 64 consecutive units of the slot; units past the
-    // end re-read the last one into the slot's padding, so every wave issues
-    // exactly GU_NU loads per sub-tile (the waits below count them).
-    const int n16 = GU_SUB * rowbytes / 16;
-    const int wave_unit = tid & ~63;
-    auto issue = [&](int i) {
-        uint8_t* dst = smem + (i & 1) * slot_bytes;
-        const uint8_t* g1 = w1 + (size_t)(r0 + GU_SUB * i) * rowbytes;
-        const uint8_t* g3 = w3 + (size_t)(r0 + GU_SUB * i) * rowbytes;
-#pragma unroll
-        for (int u = 0; u < GU_NU; ++u) {
-            const int f = min(u * bd + tid, 2 * n16 - 1);
-            const uint8_t* src = f < n16 ? g1 + (size_t)f * 16 : g3 + (size_t)(f - n16) * 16;
-            load_lds16(src, dst + (size_t)(u * bd + wave_unit) * 16);
-        }
-    };
-    issue(0);
-    issue(1);
-    float dxs[8], m16[16];
+    // the token's q8_1 activations into LDS: quants (D bytes), block scales (L f32),
+    // 16-value sums (2L i32); whole wavefronts past the end skip the load
+    const int nx16 = (D + 4 * L + 8 * L) / 16;
     {
-        const float dx[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            m16[4 * q + 0] = dx[2 * q] * (float)s16v[q].x;
-            m16[4 * q + 1] = dx[2 * q] * (float)s16v[q].y;
-            m16[4 * q + 2] = dx[2 * q + 1] * (float)s16v[q].z;
-            m16[4 * q + 3] = dx[2 * q + 1] * (float)s16v[q].w;
+        const int wave_unit = tid & ~63;
+        const uint8_t* xq = reinterpret_cast<const uint8_t*>(a.xq + (size_t)ch.token * D);
+        const uint8_t* xd = reinterpret_cast<const uint8_t*>(a.xd + (size_t)ch.token * L);
+        const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.xs16 + (size_t)ch.token * 2 * L);
+        for (int u = 0; u * bd < nx16; ++u) {
+            if (u * bd + wave_unit < nx16) {
+                const int f = min(u * bd + tid, nx16 - 1);
+                const uint8_t* src = f < D / 16 ? xq + (size_t)f * 16
+                                   : f < D / 16 + L / 4 ? xd + (size_t)(f - D / 16) * 16
+                                                        : xs + (size_t)(f - D / 16 - L / 4) * 16;
+                load_lds16(src, smem + (size_t)(u * bd + wave_unit) * 16);
+            }
         }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) dxs[t] = (t & 1) ? 0.25f * dx[t] : dx[t];
     }
+    // this lane's blocks, straight into registers
+    const int r = tid & 7, rest = tid >> 3, sl = rest % NSL, mp = rest / NSL;
+    const int m = mp & 1, p = mp >> 1;
+    const bool live = p < GU_TILE / PANEL;
+    uint32_t wq[SPL][21];
+    {
+        const uint8_t* panel = (m ? w3 : w1) + (size_t)(r0 + PANEL * (live ? p : 0)) * rowbytes;
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) {
+            const int s = min(sl + NSL * k, nsb - 1);
+            const uint32_t* q = reinterpret_cast<const uint32_t*>(panel + (size_t)(s * PANEL + r) * Q2K_BYTES);
+#pragma unroll
+            for (int i = 0; i < 21; ++i) wq[k][i] = q[i];
+        }
+    }
+    wait_vm_loads<0>();
+    barrier_lds();
 
-    float* red = reinterpret_cast<float*>(smem + 2 * slot_bytes);   // [4 sub-tiles][16 rows][nsb]
-    for (int i = 0; i < GU_TILE / GU_SUB; ++i) {
-        if (i + 1 < GU_TILE / GU_SUB) wait_vm_loads<GU_NU>();   // sub-tile i is in LDS (i + 1 may not be)
-        else wait_vm_loads<0>();
-        barrier_lds();
-        if (live) {
-            const uint32_t* wp = reinterpret_cast<const uint32_t*>(smem + (i & 1) * slot_bytes +
-                                                                   panel_off(r, s, nsb, Q2K_BYTES));
-            uint32_t sc[4], qw[16];
+    const uint8_t* xl = smem;
+    float* red = reinterpret_cast<float*>(smem + (size_t)((nx16 + bd - 1) / bd) * bd * 16);   // [8 vectors x 4 panels... ][nsb]
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sc[q] = wp[q];
+    for (int k = 0; k < SPL; ++k) {
+        const int s = sl + NSL * k;
+        if (!live || s >= nsb) continue;
+        const uint32_t* sc = wq[k];
+        const uint32_t* qw = wq[k] + 4;
+        const uint32_t dd = wq[k][20];
+        const uint32_t* xq32 = reinterpret_cast<const uint32_t*>(xl) + s * (QK / 4);
+        const float* dxp = reinterpret_cast<const float*>(xl + D) + s * 8;
+        const int* s16p = reinterpret_cast<const int*>(xl + D + 4 * L) + s * 16;
+        float fs = 0.f, ms = 0.f;
+        // q8_1 block t = 4 hh + j of x meets plane j of qs half hh: qs byte b of half
+        // hh holds weight 128 hh + 32 j + b in bits 2j..2j+1 (sub-block 2t + b / 16)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) qw[q] = wp[4 + q];
-            const uint32_t dd = wp[20];
-            // qs byte b of half hh holds weight 128 hh + 32 j + b in bits 2j..2j+1
-            // (sub-block 8 hh + 2 j + b / 16, activation block 4 hh + j); the first
-            // product of each sub-block starts its sum
-            int in[16];
+        for (int t = 0; t < 8; ++t) {
+            const int hh = t >> 2, j = t & 3;
+            const uint4 x0 = reinterpret_cast<const uint4*>(xq32 + 8 * t)[0];
+            const uint4 x1 = reinterpret_cast<const uint4*>(xq32 + 8 * t)[1];
+            const uint32_t xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            int il = 0, ih = 0;
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const uint32_t w = qw[8 * hh + cc], w4 = w >> 4;
-                    const int nb = 8 * hh + (cc >> 2);
-                    const bool first = (cc & 3) == 0;
-                    in[nb + 0] = sdot4(w & 0x03030303u, xv[(4 * hh + 0) * 8 + cc], first ? 0 : in[nb + 0]);
-                    in[nb + 2] = sdot4(w & 0x0C0C0C0Cu, xv[(4 * hh + 1) * 8 + cc], first ? 0 : in[nb + 2]);
-                    in[nb + 4] = sdot4(w4 & 0x03030303u, xv[(4 * hh + 2) * 8 + cc], first ? 0 : in[nb + 4]);
-                    in[nb + 6] = sdot4(w4 & 0x0C0C0C0Cu, xv[(4 * hh + 3) * 8 + cc], first ? 0 : in[nb + 6]);
-                }
+            for (int cc = 0; cc < 8; ++cc) {
+                const uint32_t w = qw[8 * hh + cc];
+                const uint32_t pl = j == 0 ? (w & 0x03030303u) : j == 1 ? (w & 0x0C0C0C0Cu)
+                                  : j == 2 ? ((w >> 4) & 0x03030303u) : ((w >> 4) & 0x0C0C0C0Cu);
+                if (cc < 4) il = sdot4(pl, xv[cc], il);
+                else ih = sdot4(pl, xv[cc], ih);
             }
-            // scale bytes 4q .. 4q + 3 = sub-blocks 4q .. 4q + 3 (activation blocks 2q, 2q + 1):
-            // low nibbles the scales, high nibbles the mins
-            float fs = 0.f, ms = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t sq = sc[q] & 0x0F0F0F0Fu, mq = (sc[q] >> 4) & 0x0F0F0F0Fu;
-                const int is0 = __mul24((int)(sq & 0xFFu), in[4 * q]) + __mul24((int)((sq >> 8) & 0xFFu), in[4 * q + 1]);
-                const int is1 = __mul24((int)((sq >> 16) & 0xFFu), in[4 * q + 2]) + __mul24((int)(sq >> 24), in[4 * q + 3]);
-                fs = fmaf(dxs[2 * q], (float)is0, fs);
-                fs = fmaf(dxs[2 * q + 1], (float)is1, fs);
-                ms = fmaf((float)(mq & 0xFFu), m16[4 * q], ms);
-                ms = fmaf((float)((mq >> 8) & 0xFFu), m16[4 * q + 1], ms);
-                ms = fmaf((float)((mq >> 16) & 0xFFu), m16[4 * q + 2], ms);
-                ms = fmaf((float)(mq >> 24), m16[4 * q + 3], ms);
-            }
-            const float d = half_bits_to_f32(dd & 0xFFFFu), dmin = half_bits_to_f32(dd >> 16);
-            red[(i * 16 + r) * nsb + s] = fmaf(d, fs, -dmin * ms);
+            const uint32_t sw = sc[t >> 1] >> (16 * (t & 1));   // scale bytes 2t, 2t + 1
+            const int isum = __mul24((int)(sw & 15u), il) + __mul24((int)((sw >> 8) & 15u), ih);
+            const float dx = dxp[t];
+            const int2 s16 = reinterpret_cast<const int2*>(s16p)[t];
+            fs = fmaf((j & 1) ? 0.25f * dx : dx, (float)isum, fs);
+            ms = fmaf((float)((sw >> 4) & 15u), dx * (float)s16.x, ms);
+            ms = fmaf((float)((sw >> 12) & 15u), dx * (float)s16.y, ms);
         }
-        if (i + 2 < GU_TILE / GU_SUB) {
-            barrier_lds();   // every lane is done with slot i & 1
-            issue(i + 2);
-        }
+        const float d = half_bits_to_f32(dd & 0xFFFFu), dmin = half_bits_to_f32(dd >> 16);
+        red[((p * 2 + m) * PANEL + r) * nsb + s] = fmaf(d, fs, -dmin * ms);
     }
     barrier_lds();
-    // row t of the tile: W1 and W3 partials of sub-tile t / 8, local rows t % 8 and 8 + t % 8;
-    // then the q8_1 block of the 32 values of h across lanes 0..31
+    // row t of the tile (panel t / 8, row t % 8): the W1 and W3 sums, the clamped
+    // SwiGLU, then the q8_1 block of the 32 values across lanes 0..31
     if (tid < GU_TILE) {
-        const float* rg = red + ((tid >> 3) * 16 + (tid & 7)) * nsb;
-        const float* ru = rg + 8 * nsb;
+        const int pp = tid >> 3, rr = tid & 7;
+        const float* rg = red + ((pp * 2 + 0) * PANEL + rr) * nsb;
+        const float* ru = red + ((pp * 2 + 1) * PANEL + rr) * nsb;
         float gs = 0.f, us = 0.f;
         for (int q = 0; q < nsb; ++q) {
             gs += rg[q];
@@ -229,6 +191,7 @@ __global__ __launch_bounds__(GU_MAX_THREADS) void gateup_q8_kernel(ExpertArgs a,
         if (tid == 0) reinterpret_cast<float*>(out + I)[tile] = round_to_fp16(d);
         if ((tid & 15) == 0) reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile + (tid >> 4)] = qs;
     }
+    (void)wv;
 }
 
 // ------------------------------------------------------------------ Q3_K down + combine
@@ -397,9 +360,9 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
 
 // ------------------------------------------------------------------ launch
 bool decode_supported(int D, int I) {
-    // lanes: 16 per superblock of D for gate/up and 8 * I / 32 for down, within one workgroup
-    return D % QK == 0 && I % QK == 0 && 16 * (D / QK) <= GU_MAX_THREADS && DC_ROWS * (I / QK) <= 1024 &&
-           D % DC_ROWS == 0;
+    // lanes: 64 per superblock slot of D (at most two superblocks per lane) for gate/up,
+    // 8 per superblock of I for down, within one workgroup
+    return D % QK == 0 && I % QK == 0 && 32 * (D / QK) <= 1024 && DC_ROWS * (I / QK) <= 1024 && D % DC_ROWS == 0;
 }
 
 static int round64(int v) { return (v + 63) / 64 * 64; }
@@ -409,9 +372,13 @@ size_t decode_rec_bytes(int I) { return (size_t)I + (size_t)(I / QB) * 4 + (size
 hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st) {
     if (max_chunks <= 0) return hipSuccess;
     const int nsb = a.D / QK;
-    const int threads = round64(16 * nsb);
-    const size_t lds = (size_t)2 * GU_NU * threads * 16 + (size_t)(GU_TILE / GU_SUB) * 16 * nsb * 4;
-    return launch_kernel(gateup_q8_kernel, max_chunks * (a.I / GU_TILE), threads, lds, st, a, routed_rows);
+    const int spl = 64 * nsb <= 1024 ? 1 : 2;                 // superblocks per lane
+    const int threads = round64(64 * ((nsb + spl - 1) / spl));  // 8 rows x slots x 2 matrices x 4 panels
+    const int nx16 = (a.D + 12 * (a.D / QB)) / 16;
+    const size_t lds = (size_t)((nx16 + threads - 1) / threads) * threads * 16 + (size_t)64 * nsb * 4;
+    const int grid = max_chunks * (a.I / GU_TILE);
+    if (spl == 1) return launch_kernel(gateup_q8_kernel<1>, grid, threads, lds, st, a, routed_rows);
+    return launch_kernel(gateup_q8_kernel<2>, grid, threads, lds, st, a, routed_rows);
 }
 
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
