@@ -62,8 +62,8 @@ WORKLOADS = {
 }
 # the kernel each workload's roofline object describes, and its name in rocprofv3
 DOMINANT = {
-    "decode": ("gateup", r"^moe::gateup_q8_kernel"),
-    "small": ("gateup", r"^moe::gateup_q8_kernel"),
+    "decode": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
+    "small": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
     "skewed": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),
