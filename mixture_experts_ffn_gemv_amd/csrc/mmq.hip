@@ -6,16 +6,20 @@
 // A chunk is one expert with up to MMQ_ROWS token rows (in three size classes,
 // each launched with the sub-tile count it needs). One workgroup computes
 // 64 output rows of one chunk: gate/up for 64 rows of W1 and the same rows of
-// W3 (then the clamped SwiGLU), or down for 64 rows of W2. Tokens form the A
-// operand (16-row sub-tiles of q8_1 quants), weights the B operand
-// (v_mfma_i32_16x16x32_i8: K = 32 is exactly one q8_1 block, so each product is
-// rescaled by that block's activation scale).
-//  * Q2_K: the B bytes are sc_n * q (<= 45), so d * (B . A) covers the scale
-//    part of the weight; the min part -dmin * m_n * sum(A) is added per
+// W3 (then the clamped SwiGLU), or down for 64 rows of W2. Weights form the A
+// operand (16 rows per wavefront), the chunk's tokens the B operand (16-column
+// sub-tiles of q8_1 quants); v_mfma_i32_16x16x32_i8 has K = 32, exactly one
+// q8_1 block, so each product is rescaled by that block's activation scale,
+// one scalar per lane since a lane's accumulators share one token column.
+//  * Q2_K: the A bytes are sc_n * q (<= 45), so d * (A . B) covers the scale
+//    part of the weight; the min part -dmin * m_n * sum(B) is added per
 //    superblock from the per-16 sums of the activation quants.
-//  * Q3_K: the B bytes are (32 - sc6_n) * q3 = -(sc6_n - 32) q3, which lies in
+//  * Q3_K: the A bytes are (32 - sc6_n) * q3 = -(sc6_n - 32) q3, which lies in
 //    [-128, 124] (the unnegated product would reach +128), built with a
-//    v_perm_b32 byte lookup from q3 + 4; the sign goes into d.
+//    byte lookup from q3 + 4; the sign goes into d.
+// Weight tiles are whole 8-row panels (the slot layout stores a panel's rows
+// of one superblock column as one contiguous run), streamed through LDS by the
+// wavefront-wide global-to-LDS load path.
 #include "moe_common.h"
 #include "moe_internal.h"
 
