@@ -89,25 +89,30 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
         w1 = base + a.off_w1;
         w3 = base + a.off_w3;
     }
-    // the token's q8_1 activations into LDS: quants (D bytes), block scales (L f32),
-    // 16-value sums (2L i32); whole wavefronts past the end skip the load
+    // the token's q8_1 activations: quants (D bytes), block scales (L f32),
+    // 16-value sums (2L i32), requested first, through registers into LDS
     const int nx16 = (D + 4 * L + 8 * L) / 16;
+    const int nxu = (nx16 + bd - 1) / bd;
+    uint4 xv0 = make_uint4(0, 0, 0, 0);
     {
-        const int wave_unit = tid & ~63;
         const uint8_t* xq = reinterpret_cast<const uint8_t*>(a.xq + (size_t)ch.token * D);
         const uint8_t* xd = reinterpret_cast<const uint8_t*>(a.xd + (size_t)ch.token * L);
         const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.xs16 + (size_t)ch.token * 2 * L);
-        for (int u = 0; u * bd < nx16; ++u) {
-            if (u * bd + wave_unit < nx16) {
-                const int f = min(u * bd + tid, nx16 - 1);
+        for (int u = 0; u < nxu; ++u) {
+            const int f = u * bd + tid;
+            if (f < nx16) {
                 const uint8_t* src = f < D / 16 ? xq + (size_t)f * 16
                                    : f < D / 16 + L / 4 ? xd + (size_t)(f - D / 16) * 16
                                                         : xs + (size_t)(f - D / 16 - L / 4) * 16;
-                load_lds16(src, smem + (size_t)(u * bd + wave_unit) * 16);
+                const uint4 v = *reinterpret_cast<const uint4*>(src);
+                if (u == 0) xv0 = v;   // stored after the weight loads are issued
+                else reinterpret_cast<uint4*>(smem)[f] = v;
             }
         }
     }
-    // this lane's blocks, straight into registers
+    // this lane's blocks, straight into registers (the waits for them are the
+    // compiler's, placed at their first use, so the first block is computed
+    // while the later ones arrive)
     const int r = tid & 7, rest = tid >> 3, sl = rest % NSL, mp = rest / NSL;
     const int m = mp & 1, p = mp >> 1;
     const bool live = p < GU_TILE / PANEL;
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
             for (int i = 0; i < 21; ++i) wq[k][i] = q[i];
         }
     }
-    wait_vm_loads<0>();
+    if (tid < nx16) reinterpret_cast<uint4*>(smem)[tid] = xv0;
     barrier_lds();
 
     const uint8_t* xl = smem;
@@ -214,18 +219,20 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     const int nsb = I / QK;
     const int rowbytes = nsb * Q3K_BYTES;
     const int r0 = blockIdx.x * DC_ROWS;
-    const int tid = threadIdx.x, bd = blockDim.x, wv = tid >> 6;
+    const int tid = threadIdx.x, bd = blockDim.x;
     const int rec = rec_bytes(I);
     const int rec16 = rec / 16;                          // a multiple of 16 bytes (I a multiple of 256)
     const int nu = (G * rec16 + bd - 1) / bd;            // record loads per thread and pass
-    uint8_t* hrec = smem;                                // [G][rec] (+ the last loads' overrun)
-    int* c_slot = reinterpret_cast<int*>(smem + (size_t)nu * bd * 16);
+    constexpr int NR = 3;   // record units per thread held in registers; further ones load synchronously
+    uint8_t* hrec = smem;                                // [G][rec] (+ the last loads' overrun), >= NR bd units
+    int* c_slot = reinterpret_cast<int*>(smem + (size_t)max(nu, NR) * bd * 16);
     int* c_row = c_slot + max_chunks;
     int* c_tok = c_row + max_chunks;
     float* c_w = reinterpret_cast<float*>(c_tok + max_chunks);
     float* part = c_w + max_chunks;                      // [G][8][nsb]
     float* acc = part + G * DC_ROWS * nsb;               // [m][8]
-    float* shp = acc + m * DC_ROWS;                      // [8][I / 32][m]: bf16 shared expert partials
+    float* esum = acc + m * DC_ROWS;                     // [G][8]
+    float* shp = esum + G * DC_ROWS;                     // [8][I / 64][m]: bf16 shared expert partials
     const int nch = min(*a.n_chunks, max_chunks);
     for (int q = tid; q < nch; q += bd) {
         const Chunk ch = a.chunks[q];
@@ -237,24 +244,28 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     }
     for (int q = tid; q < m * DC_ROWS; q += bd) acc[q] = 0.f;
     // bf16 shared expert (when given): this panel's W2 rows against h (bf16 [m, I]),
-    // one (row, 32-element slice) per job, partials summed in slice order below
-    const int ns32 = I / 32;
+    // one (row, 64-element slice) per job (one job per thread at the decode shapes),
+    // partials summed in slice order below
+    const int nsj = I / 64;
     if (sh_w2 != nullptr) {
-        for (int job = tid; job < DC_ROWS * ns32; job += bd) {
-            const int rr = job / ns32, ks = job % ns32;
-            const uint4* wp = reinterpret_cast<const uint4*>(sh_w2 + (size_t)(r0 + rr) * I + 32 * ks);
-            const uint4 w0 = wp[0], w1 = wp[1], w2 = wp[2], w3 = wp[3];
-            const uint32_t wv[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
-                                     w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
+        for (int job = tid; job < DC_ROWS * nsj; job += bd) {
+            const int rr = job / nsj, ks = job % nsj;
+            const uint4* wp = reinterpret_cast<const uint4*>(sh_w2 + (size_t)(r0 + rr) * I + 64 * ks);
+            uint4 wv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) wv[q] = wp[q];
             for (int t = 0; t < m; ++t) {
-                const uint4* hp = reinterpret_cast<const uint4*>(h_sh + (size_t)t * I + 32 * ks);
-                const uint4 h0 = hp[0], h1 = hp[1], h2 = hp[2], h3 = hp[3];
-                const uint32_t hv[16] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w,
-                                         h2.x, h2.y, h2.z, h2.w, h3.x, h3.y, h3.z, h3.w};
+                const uint4* hp = reinterpret_cast<const uint4*>(h_sh + (size_t)t * I + 64 * ks);
                 float v = 0.f;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) v = dot2_bf16(wv[q], hv[q], v);
-                shp[(rr * ns32 + ks) * m + t] = v;
+                for (int q = 0; q < 8; ++q) {
+                    const uint4 hv = hp[q];
+                    v = dot2_bf16(wv[q].x, hv.x, v);
+                    v = dot2_bf16(wv[q].y, hv.y, v);
+                    v = dot2_bf16(wv[q].z, hv.z, v);
+                    v = dot2_bf16(wv[q].w, hv.w, v);
+                }
+                shp[(rr * nsj + ks) * m + t] = v;
             }
         }
     }
@@ -264,32 +275,36 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     const uint32_t* h32 = reinterpret_cast<const uint32_t*>(hrec) + (size_t)cl * (rec / 4);
     for (int g0 = 0; g0 < nch; g0 += G) {
         const int ng = min(G, nch - g0);
-        // this pass's h records into LDS (units past the end repeat the last one)
-        for (int u = 0; u < nu; ++u) {
+        // this pass's q8_1(h) records (units past the end repeat the last one) and this
+        // lane's block, 28 dwords from the dword below its start (in bounds: a block that
+        // starts on a dword ends 2 bytes before the next block of its column run), all
+        // requested in straight-line code (a lane without a block reads slot 0's), the
+        // records first; they go into LDS through registers, so that every wait is exact
+        // and a lane computes its block as soon as the block has arrived. Record units
+        // past NR per thread (other shapes) are staged first, synchronously.
+        auto rec_unit = [&](int u) {
             const int f = min(u * bd + tid, ng * rec16 - 1);
             const int q = f / rec16, k = f % rec16;
-            load_lds16(a.hrec + (size_t)c_row[g0 + q] * rec + k * 16, hrec + (size_t)(u * bd + wv * 64) * 16);
-        }
-        // this lane's block: 28 dwords from the dword below its start (in bounds: a block
-        // that starts on a dword ends 2 bytes before the next block of its column run)
+            return reinterpret_cast<const uint4*>(a.hrec + (size_t)c_row[g0 + q] * rec + k * 16);
+        };
+        for (int u = NR; u < nu; ++u) reinterpret_cast<uint4*>(hrec)[u * bd + tid] = *rec_unit(u);
+        uint4 R[NR];
+#pragma unroll
+        for (int u = 0; u < NR; ++u) R[u] = *rec_unit(u);
         const bool act = cl < ng;
         const int slot = act ? c_slot[g0 + cl] : -1;
+        const uint8_t* w2 = slot == -2 ? a.sh_w2 : a.arena + (size_t)max(slot, 0) * a.slot_bytes + a.off_w2;
+        const uint8_t* blk = w2 + (size_t)r0 * rowbytes + (size_t)(s * DC_ROWS + r) * Q3K_BYTES;
+        const uint32_t mis = (uint32_t)((uintptr_t)blk & 3);
+        const uint32_t sh = mis * 8u;
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(blk - mis);   // pointer arithmetic keeps it global
         uint32_t W[28];
-        uint32_t sh = 0;
-        if (slot != -1) {
-            const uint8_t* w2 = slot == -2 ? a.sh_w2 : a.arena + (size_t)slot * a.slot_bytes + a.off_w2;
-            const uint8_t* blk = w2 + (size_t)r0 * rowbytes + (size_t)(s * DC_ROWS + r) * Q3K_BYTES;
-            sh = (uint32_t)((uintptr_t)blk & 3) * 8u;
-            const uint32_t* p = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(blk) & ~(uintptr_t)3);
 #pragma unroll
-            for (int q = 0; q < 28; ++q) W[q] = p[q];
-        } else {
+        for (int q = 0; q < 28; ++q) W[q] = wp[q];
 #pragma unroll
-            for (int q = 0; q < 28; ++q) W[q] = 0u;
-        }
-        wait_vm_loads<0>();
+        for (int u = 0; u < NR; ++u) reinterpret_cast<uint4*>(hrec)[u * bd + tid] = R[u];
         barrier_lds();
-        if (act) {
+        if (slot != -1) {
             // realigned block: hmask dwords 0..7, qs 8..23, scales 24..26, d in 27
             uint32_t B[28];
 #pragma unroll
@@ -330,31 +345,42 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
             part[(cl * DC_ROWS + r) * nsb + s] = half_bits_to_f32(B[27] & 0xFFFFu) * fs;
         }
         barrier_lds();
+        // E of each (chunk, row): its superblock partials in order
+        for (int q = tid; q < ng * DC_ROWS; q += bd) {
+            const float* pe = part + q * nsb;
+            float e = 0.f;
+            for (int k = 0; k < nsb; ++k) e += pe[k];
+            esum[q] = e;
+        }
+        barrier_lds();
         if (tid < m * DC_ROWS) {   // token tid / 8, row tid % 8: this pass's chunks in order
             const int t = tid >> 3, rr = tid & 7;
             float v = acc[tid];
             for (int q = 0; q < ng; ++q) {
                 const int c = g0 + q;
-                if (c_tok[c] != t || c_slot[c] == -1) continue;
-                const float* pe = part + (q * DC_ROWS + rr) * nsb;
-                float e = 0.f;
-                for (int k = 0; k < nsb; ++k) e += pe[k];
-                v = fmaf(c_w[c], e, v);
+                if (c_tok[c] == t && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + rr], v);
             }
             acc[tid] = v;
         }
         barrier_lds();   // the records and partials are reused by the next pass
     }
-    for (int q = tid; q < m * DC_ROWS; q += bd) {
-        const int t = q / DC_ROWS, rr = q % DC_ROWS;
-        float v = acc[q];
-        if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
-        if (sh_w2 != nullptr) {
-            float e = 0.f;
-            for (int k = 0; k < ns32; ++k) e += shp[(rr * ns32 + k) * m + t];
-            v += e;
+    // output (token t, row rr) = q / 8: 8 threads per output, each summing every eighth
+    // shared-expert partial in order, then across the 8 (all threads run the same trips)
+    for (int q0 = 0; q0 < m * DC_ROWS * 8; q0 += bd) {
+        const int q = q0 + tid, o = q >> 3, j = q & 7;
+        const int t = o / DC_ROWS, rr = o % DC_ROWS;
+        const bool live = o < m * DC_ROWS;
+        float e = 0.f;
+        if (live && sh_w2 != nullptr)
+            for (int k = j; k < nsj; k += 8) e += shp[(rr * nsj + k) * m + t];
+        e += __shfl_xor(e, 1, 8);
+        e += __shfl_xor(e, 2, 8);
+        e += __shfl_xor(e, 4, 8);
+        if (live && j == 0) {
+            float v = acc[o];
+            if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
+            out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v + e);
         }
-        out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v);
     }
 }
 
@@ -389,8 +415,9 @@ hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int 
     const int threads = round64(lanes * G);
     const int rec16 = (int)(decode_rec_bytes(a.I) / 16);
     const int nu = (G * rec16 + threads - 1) / threads;
-    const size_t lds = (size_t)nu * threads * 16 + (size_t)max_chunks * 16 + (size_t)G * DC_ROWS * nsb * 4 +
-                       (size_t)m * DC_ROWS * 4 + (sh_w2_bf16 ? (size_t)DC_ROWS * (a.I / 32) * m * 4 : 0);
+    const size_t lds = (size_t)std::max(nu, 3) * threads * 16 + (size_t)max_chunks * 16 + (size_t)G * DC_ROWS * nsb * 4 +
+                       (size_t)m * DC_ROWS * 4 + (size_t)G * DC_ROWS * 4 +
+                       (sh_w2_bf16 ? (size_t)DC_ROWS * (a.I / 64) * m * 4 : 0);
     return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, G, ys,
                          sh_w2_bf16, h_sh_bf16, out);
 }

@@ -102,6 +102,19 @@ def test_tiny_hot_expert_spans_chunks(shared, m):
         layer.close()
 
 
+@pytest.mark.parametrize("m", [1, 2, 5, 8])
+def test_mid_decode_bf16_shared(m):
+    # dim 1024, inter 512, top-4: the decode kernels at a shape between the tiny one and
+    # the real one (256-thread gate/up workgroups, two K superblocks of W2 per row, the
+    # bf16 shared expert's rows split over the routing launches and the down kernel)
+    shape = S.LayerShape(1024, 512, 16, 4)
+    layer = Layer(shape, 5, max_tokens=8)
+    try:
+        check_layer(layer, S.make_tokens(m, 1024, 5, index=m), f"mid bf16 shared m={m}")
+    finally:
+        layer.close()
+
+
 def test_tiny_topk1():
     shape = S.LayerShape(256, 256, 16, 1)
     layer = Layer(shape, 3, max_tokens=8)
