@@ -54,6 +54,9 @@ WORKLOADS = {
                   desc="small batch m=8 (GEMV path), K-quant shared expert"),
     "prefill": dict(m=512, layers=1, bias=None, shared="bf16", pool=512,
                     desc="prefill m=512 (MMQ path), uniform routing, bf16 shared expert"),
+    "prefill_mixed": dict(m=512, layers=1, bias=None, shared="bf16", pool=512, dispatch="mixed",
+                          desc="prefill m=512 with groups of <= 8 rows on the GEMV kernels and larger ones on "
+                               "MMQ, uniform routing, bf16 shared expert"),
     "prefill_hot": dict(m=512, layers=1, bias="hot", shared="bf16", pool=512,
                         desc="prefill m=512 (MMQ path), 6 hot experts take every token, bf16 shared expert"),
     "skewed": dict(m=2048, layers=1, bias="skewed", shared="bf16", pool=2048, slots=96,
@@ -65,6 +68,7 @@ DOMINANT = {
     "decode": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "small": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
+    "prefill_mixed": ("gateup", r"^void moe::gateup_q2k_kernel<8>"),    # the groups of <= 8 rows
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
     "skewed": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),
 }
@@ -243,6 +247,8 @@ class Bench:
         d_tokens = tokens.to(self.dev)
         cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8))
         ctx = moe.moe_create(cfg)
+        if spec.get("dispatch") == "mixed":
+            moe.moe_set_dispatch(ctx, moe.MOE_DISPATCH_MIXED)
         streamed = "slots" in spec
         if streamed:
             # a small device arena; every expert in page-locked host memory
@@ -487,7 +493,7 @@ def main():
     layers, tokens = head.pop("_layers"), head.pop("_tokens")
     extra = {}
     if wl == "decode" and not args.no_extra:
-        for other in ("small", "prefill", "prefill_hot", "skewed"):
+        for other in ("small", "prefill", "prefill_mixed", "prefill_hot", "skewed"):
             st = 100 if WORKLOADS[other]["m"] <= 8 else 5 if other == "skewed" else 10
             wu = 3 if other == "skewed" else 5
             log(f"{other}: {wu} warmup + {st} timed steps")

@@ -177,6 +177,19 @@ int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t 
 int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
                    float* weights_out, int32_t* idx_out, void* stream);
 
+/* How a call of more than 8 tokens runs the routed experts, by group size (the
+ * rows that picked one expert). MOE_DISPATCH_MMQ (the default): every group on
+ * the int8 matrix-core (MMQ) kernels, the smallest in 16-row tiles.
+ * MOE_DISPATCH_MIXED: the rule of the metrale moe_v41 module documentation,
+ * GEMVs for groups of up to eight rows and MMQ above; on gfx950 the dot4 GEMV
+ * kernels stream such groups several times slower than the MMQ tiles, so it
+ * is not the default. Calls of up to 8 tokens always use the GEMV kernels.
+ * Takes effect for the calls queued after it. MOE_EINVAL for NULL or another
+ * value. */
+#define MOE_DISPATCH_MMQ 0
+#define MOE_DISPATCH_MIXED 1
+int moe_set_dispatch(moe_ctx* ctx, int32_t mode);
+
 /* The layer's activation quantiser alone (q8_1 of bf16 rows), exposed so its
  * output can be checked bit for bit: x_bf16 [rows, cols] (device, 16-byte
  * aligned, cols a multiple of 32); q_out int8 [rows, cols] and d_out f32

@@ -26,12 +26,15 @@ MOE_SHARED_NONE = 0
 MOE_SHARED_BF16 = 1
 MOE_SHARED_KQUANT = 2
 
+MOE_DISPATCH_MMQ = 0
+MOE_DISPATCH_MIXED = 1
+
 EXPORTED = (
     "moe_create", "moe_destroy", "moe_expert_layout", "moe_pack_expert", "moe_set_slots", "moe_slot_bind",
     "moe_slot_evict",
     "moe_slot_of", "moe_set_host_arena", "moe_route", "moe_forward", "moe_forward_ex", "moe_check",
     "moe_get_stats", "moe_reset_stats", "moe_strerror", "moe_quantize_q8_1", "moe_set_profiling",
-    "moe_kernel_times",
+    "moe_kernel_times", "moe_set_dispatch",
 )
 
 KERNEL_CLASSES = ("router", "quant_h", "topk", "bucket", "gateup", "shared_gateup", "down", "shared_down",
@@ -111,6 +114,7 @@ def lib():
             "moe_reset_stats": [vp],
             "moe_quantize_q8_1": [vp, i32, i32, vp, vp, vp],
             "moe_set_profiling": [vp, i32],
+            "moe_set_dispatch": [vp, i32],
             "moe_kernel_times": [vp, P(ctypes.c_double), P(ctypes.c_int64), i32],
         }
         for name, args in sigs.items():
@@ -237,6 +241,11 @@ def moe_quantize_q8_1(x, rows, cols, q_out, d_out, stream=None):
 def moe_check(ctx, stream=None):
     """Synchronise and return the device status code (does not raise)."""
     return lib().moe_check(ctx, _stream(stream))
+
+
+def moe_set_dispatch(ctx, mode):
+    """MOE_DISPATCH_MMQ (the default) or MOE_DISPATCH_MIXED (GEMVs for groups of <= 8 rows, MMQ above)."""
+    return _check(lib().moe_set_dispatch(ctx, int(mode)), "moe_set_dispatch")
 
 
 def moe_set_profiling(ctx, on):

@@ -40,6 +40,7 @@ struct moe_ctx {
     int n_cu = 256;          // compute units of the device
     bool decode_ok = false;  // the decode-path kernels fit this shape
     bool mmq_ok = false;     // the MMQ tiles fit this shape
+    bool mixed = false;      // groups of <= GEMV_ROWS rows on the GEMV kernels when the MMQ path runs
     int max_pairs = 0;
     int max_chunks = 0;   // chunk-list capacity
     uint8_t* dev = nullptr;
@@ -311,7 +312,8 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     // m) and the single-row chunks of the small-batch routing
     const int m_small = (int)std::min<size_t>(M, ROUTE_SMALL_MAX_M);
     ctx->max_chunks = std::max(routed_chunk_bound(c, (int)M) + shared_chunk_count((int)M) + 1,
-                               mmq_chunk_plan((int)M, c.topk, c.n_routed, true).total());
+                               std::max(mmq_chunk_plan((int)M, c.topk, c.n_routed, true, false).total(),
+                                        mmq_chunk_plan((int)M, c.topk, c.n_routed, true, true).total()));
     ctx->max_chunks = std::max(ctx->max_chunks, m_small * (c.topk + 1) + 1);
     layout_of(c, ctx->slot_bytes, ctx->off_w1, ctx->off_w3, ctx->off_w2);
 
@@ -326,7 +328,7 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     const size_t o_off = cv.take<int32_t>(E + 1);
     const size_t o_act = cv.take<int32_t>(E);
     const size_t o_nact = cv.take<int32_t>(1);
-    const size_t o_nch = cv.take<int32_t>(MMQ_CLASSES);
+    const size_t o_nch = cv.take<int32_t>(PLAN_LISTS);
     const size_t o_perm = cv.take<int32_t>(P);
     const size_t o_inv = cv.take<int32_t>(P);
     const size_t o_ch = cv.take<Chunk>(ctx->max_chunks);
@@ -681,7 +683,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (hipEventRecord(ctx->ev_join, ctx->side) != hipSuccess) return MOE_EHIP;
     }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
-    const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq);
+    const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq, ctx->mixed);
     if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
@@ -790,10 +792,24 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
             if (rc != MOE_OK) return rc;
         }
         if (use_mmq) {
+            // a mixed plan's small groups on the GEMV kernels, the rest on MMQ
+            ExpertArgs ag = a;
+            ag.chunks = a.chunks + plan.base[GEMV_LIST];
+            ag.n_chunks = a.n_chunks + GEMV_LIST;
+            if (plan.cap[GEMV_LIST] > 0) {
+                rc = timed(ctx, st, MOE_K_GATEUP,
+                           [&] { return launch_gateup_q2k(ag, GEMV_ROWS, plan.cap[GEMV_LIST], st); });
+                if (rc != MOE_OK) return rc;
+            }
             rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_mmq(a, plan, true, st); });
             if (rc != MOE_OK) return rc;
             rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
             if (rc != MOE_OK) return rc;
+            if (plan.cap[GEMV_LIST] > 0) {
+                rc = timed(ctx, st, MOE_K_DOWN,
+                           [&] { return launch_down_q3k(ag, GEMV_ROWS, plan.cap[GEMV_LIST], st); });
+                if (rc != MOE_OK) return rc;
+            }
             rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, plan, false, st); });
             if (rc != MOE_OK) return rc;
         } else {
@@ -838,6 +854,12 @@ int moe_check(moe_ctx* ctx, void* stream) {
     if (hipMemcpy(ctx->err, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return MOE_EHIP;
     if (word & ERR_NONFINITE) return MOE_ENONFINITE;
     if (word & ERR_NOTRESIDENT) return MOE_ENOTRESIDENT;
+    return MOE_OK;
+}
+
+int moe_set_dispatch(moe_ctx* ctx, int32_t mode) {
+    if (ctx == nullptr || (mode != MOE_DISPATCH_MIXED && mode != MOE_DISPATCH_MMQ)) return MOE_EINVAL;
+    ctx->mixed = mode == MOE_DISPATCH_MIXED;
     return MOE_OK;
 }
 

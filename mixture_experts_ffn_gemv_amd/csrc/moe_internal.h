@@ -51,22 +51,32 @@ constexpr int MMQ_ROWS = 64;   // the most token rows one MMQ chunk holds (four 
 // lightly used experts do not carry the registers of four sub-tiles.
 constexpr int MMQ_CLASSES = 3;
 constexpr int MMQ_CLASS_MAX[MMQ_CLASSES] = {16, 32, MMQ_ROWS};
+// A mixed plan (GEMVs for groups of up to GEMV_ROWS rows, MMQ above, as the
+// pages dispatch by group size) adds a fourth list of GEMV chunks; the MMQ
+// classes then hold groups of more than GEMV_ROWS rows only.
+constexpr int GEMV_LIST = MMQ_CLASSES;
+constexpr int PLAN_LISTS = MMQ_CLASSES + 1;
 struct ChunkPlan {
-    int base[MMQ_CLASSES];   // first slot of each class in the chunk array
-    int cap[MMQ_CLASSES];    // slots reserved (an upper bound of the class's chunks)
-    int total() const { return base[MMQ_CLASSES - 1] + cap[MMQ_CLASSES - 1]; }
+    int base[PLAN_LISTS];   // first slot of each list in the chunk array
+    int cap[PLAN_LISTS];    // slots reserved (an upper bound of the list's chunks)
+    bool mixed;
+    int total() const { return base[GEMV_LIST] + cap[GEMV_LIST]; }
 };
 // P = m * k picks over E experts; `shared` adds the K-quant shared expert's m rows
-inline ChunkPlan mmq_chunk_plan(int m, int k, int E, bool shared) {
+// (in the list its m rows fall in, like a routed group of m rows)
+inline ChunkPlan mmq_chunk_plan(int m, int k, int E, bool shared, bool mixed) {
     const int P = m * k, act = P < E ? P : E;
     ChunkPlan pl;
-    pl.cap[0] = act + (shared && m <= 16 ? 1 : 0);
+    pl.mixed = mixed;
+    const bool sh_gemv = shared && mixed && m <= GEMV_ROWS;
+    const int g0 = mixed ? (P / (GEMV_ROWS + 1) < act ? P / (GEMV_ROWS + 1) : act) : act;
+    pl.cap[0] = g0 + (shared && !sh_gemv && m <= 16 ? 1 : 0);
     pl.cap[1] = P / 17 + (shared && m > 16 && m <= 32 ? 1 : 0);
     // groups of v > 32 rows: sum ceil(v / 64) <= P / 64 + (number of such groups) <= P / 64 + P / 33
     pl.cap[2] = P / MMQ_ROWS + P / 33 + 1 + (shared && m > 32 ? (m + MMQ_ROWS - 1) / MMQ_ROWS : 0);
+    pl.cap[GEMV_LIST] = mixed ? act + (sh_gemv ? 1 : 0) : 0;
     pl.base[0] = 0;
-    pl.base[1] = pl.cap[0];
-    pl.base[2] = pl.cap[0] + pl.cap[1];
+    for (int c = 1; c < PLAN_LISTS; ++c) pl.base[c] = pl.base[c - 1] + pl.cap[c - 1];
     return pl;
 }
 
@@ -86,7 +96,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, flo
 hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp, int norm,
                        float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st);
 // plan == nullptr: one chunk list of at most GEMV_ROWS rows per chunk (n_chunks[0]);
-// otherwise the three MMQ classes at plan->base[c], counts in n_chunks[c]
+// otherwise the plan's lists (three MMQ classes, and the GEMV list of a mixed plan)
+// at plan->base[c], counts in n_chunks[c]
 hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st);

@@ -254,10 +254,11 @@ MOE_DEV int block_exclusive_scan(int v, int* lds, int& total) {
 // follow the routed ones of their list. classes == 0: one list of
 // GEMV_ROWS-row chunks. classes == 1: the three MMQ size classes (a group of
 // <= 16 rows, of 17..32 rows, or 64-row chunks of a larger group), class c at
-// chunks + base_c. One workgroup.
+// chunks + base_c. classes == 2: as 1, but a group of at most GEMV_ROWS rows is
+// one chunk of the GEMV list (list 3). One workgroup.
 __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __restrict__ idx, int P, int E,
                                                             int m, int shared_chunks, int classes, int base1,
-                                                            int base2, int32_t* __restrict__ offsets,
+                                                            int base2, int base3, int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ n_active,
                                                             Chunk* __restrict__ chunks,
@@ -279,10 +280,16 @@ __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __res
     if (tid < E && v > 0) active[aexcl] = tid;
     if (tid == 0) *n_active = nact;
     // a group of n rows: class and chunk height
-    auto cls_of = [&](int n) { return classes == 0 ? 0 : n <= MMQ_CLASS_MAX[0] ? 0 : n <= MMQ_CLASS_MAX[1] ? 1 : 2; };
-    auto rows_of = [&](int c) { return classes == 0 ? GEMV_ROWS : MMQ_CLASS_MAX[c]; };
-    const int base[3] = {0, base1, base2};
-    const int ncls = classes == 0 ? 1 : MMQ_CLASSES;
+    auto cls_of = [&](int n) {
+        return classes == 0                       ? 0
+               : classes == 2 && n <= GEMV_ROWS   ? GEMV_LIST
+               : n <= MMQ_CLASS_MAX[0]            ? 0
+               : n <= MMQ_CLASS_MAX[1]            ? 1
+                                                  : 2;
+    };
+    auto rows_of = [&](int c) { return classes == 0 || c == GEMV_LIST ? GEMV_ROWS : MMQ_CLASS_MAX[c]; };
+    const int base[PLAN_LISTS] = {0, base1, base2, base3};
+    const int ncls = classes == 0 ? 1 : classes == 1 ? MMQ_CLASSES : PLAN_LISTS;
     const int my_cls = cls_of(v);
     const int my_rows = rows_of(my_cls);
     const int nc = (tid < E && v > 0) ? (v + my_rows - 1) / my_rows : 0;
@@ -620,8 +627,10 @@ hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chu
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st) {
     const int P = m * k;
-    hipError_t e = launch_kernel(bucket_count_kernel, 1, 1024, 0, st, idx, P, E, m, shared_chunks, plan ? 1 : 0, plan ? plan->base[1] : 0,
-                                            plan ? plan->base[2] : 0, offsets, active, n_active, chunks, n_chunks);
+    const int classes = plan == nullptr ? 0 : plan->mixed ? 2 : 1;
+    hipError_t e = launch_kernel(bucket_count_kernel, 1, 1024, 0, st, idx, P, E, m, shared_chunks, classes,
+                                 plan ? plan->base[1] : 0, plan ? plan->base[2] : 0, plan ? plan->base[GEMV_LIST] : 0,
+                                 offsets, active, n_active, chunks, n_chunks);
     if (e != hipSuccess) return e;
     return launch_kernel(bucket_place_kernel, E, 256, 0, st, idx, P, offsets, perm, inv);
 }

@@ -22,7 +22,7 @@ def bits(t):
 class Layer:
     def __init__(self, shape, seed, *, shared_fmt="bf16", bias=(-0.1, 0.1), router_std=0.05, max_tokens=8,
                  expert_device="cpu", gate_temp=1.0, norm=True, route_scale=1.5, limit=10.0, bind_all=True,
-                 n_slots=None, experts=None, host_arena=False, verbose=False):
+                 n_slots=None, experts=None, host_arena=False, dispatch=None, verbose=False):
         self.shape = shape
         self.dev = torch.device("cuda")
         t0 = time.time()
@@ -35,6 +35,8 @@ class Layer:
         self.ocfg_kw = dict(gate_temp=gate_temp, norm_topk_prob=norm, route_scale=route_scale,
                             swiglu_limit=limit)
         self.ctx = moe.moe_create(self.cfg)
+        if dispatch is not None:
+            moe.moe_set_dispatch(self.ctx, dispatch)
         self.n_slots = n_slots or shape.n_routed
         # the library reads slots in its panel layout; the oracle reads arena_src (plain GGUF rows)
         packed = moe.pack_experts(self.cfg, self.arena_src.to(self.dev))

@@ -58,6 +58,7 @@ def test_strerror_and_null_handling(lib):
     assert moe.strerror(-99) == "unknown status"
     assert lib.moe_destroy(None) == moe.MOE_OK
     assert lib.moe_create(None, None) == moe.MOE_EINVAL
+    assert lib.moe_set_dispatch(None, moe.MOE_DISPATCH_MIXED) == moe.MOE_EINVAL
     assert lib.moe_check(None, None) == moe.MOE_EINVAL
     assert lib.moe_get_stats(None, None) == moe.MOE_EINVAL
     assert lib.moe_quantize_q8_1(None, 1, 32, None, None, None) == moe.MOE_EINVAL

@@ -87,17 +87,20 @@ def test_tiny_layer(variant, m):
         layer.close()
 
 
+@pytest.mark.parametrize("dispatch", ["mixed", "mmq"])
 @pytest.mark.parametrize("shared", ["bf16", "kquant"])
 @pytest.mark.parametrize("m", [24, 40, 150, 330])
-def test_tiny_hot_expert_spans_chunks(shared, m):
+def test_tiny_hot_expert_spans_chunks(shared, m, dispatch):
     # every token picks expert 3 first, so its group holds all m rows: one chunk of
     # the 17..32-row class (m=24), one ragged 64-row chunk (m=40), or several 64-row
-    # chunks (m=150, 330); the other experts' groups fall in the smaller classes
-    layer = Layer(S.TINY, 2, max_tokens=m, shared_fmt=shared)
+    # chunks (m=150, 330); the other experts' groups fall in the smaller classes, or
+    # (mixed dispatch) on the GEMV kernels when they have at most 8 rows
+    mode = moe.MOE_DISPATCH_MIXED if dispatch == "mixed" else moe.MOE_DISPATCH_MMQ
+    layer = Layer(S.TINY, 2, max_tokens=m, shared_fmt=shared, dispatch=mode)
     try:
         layer.bias[3] = 100.0
         layer.d_bias.copy_(layer.bias.to(layer.dev))
-        check_layer(layer, S.make_tokens(m, 256, 2), f"hot expert m={m} {shared}")
+        check_layer(layer, S.make_tokens(m, 256, 2), f"hot expert m={m} {shared} {dispatch}")
     finally:
         layer.close()
 
@@ -246,10 +249,14 @@ def test_real_small_batch_m8_kquant_shared(real_experts):
         layer.close()
 
 
-def test_real_prefill_m512(real_experts):
-    layer = Layer(S.REAL, 1, bias=None, router_std=0.02, max_tokens=512, experts=real_experts)
+@pytest.mark.parametrize("dispatch", ["mixed", "mmq"])
+def test_real_prefill_m512(real_experts, dispatch):
+    # uniform routing: about 8 rows per expert, so the mixed dispatch runs both the
+    # GEMV kernels (groups of <= 8 rows) and the MMQ classes
+    mode = moe.MOE_DISPATCH_MIXED if dispatch == "mixed" else moe.MOE_DISPATCH_MMQ
+    layer = Layer(S.REAL, 1, bias=None, router_std=0.02, max_tokens=512, experts=real_experts, dispatch=mode)
     try:
         x = S.make_tokens(512, S.REAL.dim, 1, index=2)
-        check_layer(layer, x, "prefill m=512", sample_rows=[0, 511])
+        check_layer(layer, x, f"prefill m=512 {dispatch}", sample_rows=[0, 511])
     finally:
         layer.close()
