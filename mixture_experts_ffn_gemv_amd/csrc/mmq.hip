@@ -38,10 +38,17 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 
 }  // namespace
 
-// Workgroups are spread over the 8 XCDs round-robin by id; the tiles of one
-// chunk are given consecutive logical ids on one XCD so that their shared
-// activation rows are fetched into one L2 (nb_pad is a multiple of 8).
-MOE_DEV int xcd_logical_block(int b, int nb_pad) { return (b & 7) * (nb_pad >> 3) + (b >> 3); }
+// Workgroups are dispatched to the 8 XCDs round-robin by id (block b on XCD
+// b % 8). The grid is sized for the most chunks a call can have; the nb_act
+// blocks that have work this call are split into 8 contiguous ranges, one per
+// XCD, so that every XCD gets an equal share and the tiles of one chunk sit on
+// one XCD, whose L2 then holds the chunk's activation rows. Blocks past their
+// XCD's range get nb_act (no work).
+MOE_DEV int xcd_logical_block(int b, int nb_act) {
+    const int per = (nb_act + 7) >> 3;
+    const int i = b >> 3;
+    return i < per ? min((b & 7) * per + i, nb_act) : nb_act;
+}
 
 // ------------------------------------------------------------------ Q2_K gate/up
 // Weights are the A operand (16 rows of W1 and the same 16 rows of W3 per
@@ -92,10 +99,10 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     const int D = a.D, I = a.I;
     const int nsb = D / QK;
     const int tiles = I / TILE_ROWS;
-    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    if (lb >= nb) return;
+    const int nb_act = min(nb, *a.n_chunks * tiles);   // blocks with work this call (nb: the grid's)
+    const int lb = xcd_logical_block(blockIdx.x, nb_act);
+    if (lb >= nb_act) return;
     const int c = lb / tiles, rt = lb % tiles;
-    if (c >= *a.n_chunks) return;
     const Chunk ch = a.chunks[c];
     const bool shared = ch.expert < 0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -316,10 +323,10 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     const int nsb = I / QK;
     const int rowbytes = nsb * Q3K_BYTES;
     const int tiles = D / TILE_ROWS;
-    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    if (lb >= nb) return;
+    const int nb_act = min(nb, *a.n_chunks * tiles);   // blocks with work this call (nb: the grid's)
+    const int lb = xcd_logical_block(blockIdx.x, nb_act);
+    if (lb >= nb_act) return;
     const int c = lb / tiles, rt = lb % tiles;
-    if (c >= *a.n_chunks) return;
     const Chunk ch = a.chunks[c];
     const bool shared = ch.expert < 0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
