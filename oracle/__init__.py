@@ -14,7 +14,9 @@ Sources (the pages this is written from):
     expert equations ("All 22 steps"), the ``Gate``/``Expert``/``MoE`` code
     excerpts and ``config.json``.
 The Q2_K / Q3_K / q8_1 byte layouts are not printed on the pages (they only
-name the formats); they follow the public GGUF K-quant block format.
+name the formats); they follow the public GGUF K-quant block format. The
+MXFP4 scale layout is not printed either (the pages give the e2m1 element type
+of the upstream experts); it follows the OCP microscaling format.
 
 Parity status per function is stated in each module's header.
 """
@@ -28,6 +30,10 @@ from .formats import (  # noqa: F401
     fp16_rne,
     dequant_q2k,
     dequant_q3k,
+    FP4_BLOCK,
+    e2m1_value,
+    e8m0_value,
+    dequant_mxfp4,
     quantize_q8_1,
     q8_1_values,
 )

@@ -12,9 +12,19 @@ Formats:
     layouts below are the public GGUF ones, restated here in our own words.
   * q8_1: 32-value blocks of int8 with an fp16 scale d and fp16 d*sum (named on
     the pages: "the activation quantised to q8_1").
+  * MXFP4: the routed experts' own format upstream (Open Model Atlas, "DeepSeek
+    V4.1 · Mixture of experts": the experts are stored as float4_e2m1fn_x2, two
+    FP4 values per byte, in the model.py excerpt and config.json expert_dtype
+    "fp4"). The pages give the element type only; the scale layout read here is
+    the OCP microscaling one: per 32 consecutive weights of a row one E8M0
+    scale 2^(E-127); each weight an e2m1 code (sign bit 3, two exponent bits with
+    bias 1, one mantissa bit), the even weight of a pair in the low nibble. A
+    matrix is its codes [rows, cols/2] followed by its scales [rows, cols/32].
 
 Pins (tests/test_oracle_formats.py): single-field probes and closed forms for
-both block decoders, constructed rounding ties, q8_1 closed forms.
+both block decoders, constructed rounding ties, q8_1 closed forms; for MXFP4
+the eight e2m1 magnitudes against the format's definition, E8M0 powers of two,
+one-nibble and one-scale probes, and exactly representable matrices.
 """
 
 import numpy as np
@@ -160,3 +170,39 @@ def q8_1_values(q, d16):
     k = q.shape[-1]
     qb = q.reshape(q.shape[:-1] + (k // Q8_BLOCK, Q8_BLOCK)).astype(np.float64)
     return (qb * np.asarray(d16)[..., None]).reshape(q.shape)
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+FP4_BLOCK = 32      # weights per E8M0 scale
+
+
+def e2m1_value(code):
+    """e2m1 code(s) (0..15) -> float64: bit 3 the sign, bits 2-1 the exponent
+    (bias 1; 0 is subnormal), bit 0 the mantissa."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    mant = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * mant, np.exp2(e - 1.0) * (1.0 + 0.5 * mant))
+    return sign * mag
+
+
+def e8m0_value(byte):
+    """E8M0 scale byte(s) -> 2^(E - 127) as float64 (NaN for 255)."""
+    b = np.asarray(byte, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b - 127.0))
+
+
+def dequant_mxfp4(raw, n_rows, n_cols):
+    """uint8 bytes of one MXFP4 matrix [codes n_rows x n_cols/2 | scales n_rows x
+    n_cols/32] -> float64 [n_rows, n_cols]."""
+    raw = np.asarray(raw, dtype=np.uint8).reshape(-1)
+    nc = n_rows * n_cols // 2
+    assert raw.size == nc + n_rows * n_cols // FP4_BLOCK, raw.size
+    codes = raw[:nc].reshape(n_rows, n_cols // 2)
+    lo = e2m1_value(codes & 15)
+    hi = e2m1_value(codes >> 4)
+    vals = np.stack([lo, hi], axis=-1).reshape(n_rows, n_cols)
+    scale = e8m0_value(raw[nc:].reshape(n_rows, n_cols // FP4_BLOCK))
+    return vals * np.repeat(scale, FP4_BLOCK, axis=1)

@@ -19,6 +19,11 @@ What it computes, per token t (each step cites the passage it follows):
      g <= L and -L <= u <= L when L > 0, h = g sigma(g) u, then E = W2 q8_1(h)
      (atlas "Routed expert" equations; ``Expert.forward`` in the atlas' model.py
      excerpt for the clamp condition; moe_v41 module doc for q8_1 activations).
+  5'. routed experts in MXFP4 (the upstream checkpoint's format; Open Model
+     Atlas model.py excerpt: Expert with dtype float4_e2m1fn_x2): the same FFN
+     on the unquantised bf16 x with the dequantised weights, h rounded to bf16
+     before W2, as the excerpt's Linear layers compute in the activation dtype
+     (the bf16 path of step 6).
   6. shared expert, added after the routed sum (atlas Delta_ffn = y_routed +
      y_shared; metrale ``shared_side``: added into acc after the routed
      experts). bf16 shared: unquantised x, h rounded to bf16 before W2 (the
@@ -42,10 +47,12 @@ from dataclasses import dataclass
 import numpy as np
 
 from .formats import (
+    FP4_BLOCK,
     Q2K_BYTES,
     Q3K_BYTES,
     QK_K,
     bf16_bits_to_f64,
+    dequant_mxfp4,
     dequant_rows,
     f32_to_bf16_bits,
     q8_1_values,
@@ -64,6 +71,7 @@ class MoeCfg:
     norm_topk_prob: bool = True
     route_scale: float = 1.5
     swiglu_limit: float = 10.0
+    expert_fmt: str = "kquant"   # the routed experts: "kquant" (Q2_K/Q3_K) or "fp4" (MXFP4)
 
 
 class NonFiniteKey(ValueError):
@@ -131,10 +139,17 @@ def swiglu_clamped(g, u, limit):
     return g / (1.0 + np.exp(-g)) * u
 
 
-def slot_matrices(cfg, raw):
-    """Decode one expert slice [W1 Q2_K | W3 Q2_K | W2 Q3_K] (raw block bytes,
-    row-major, W1/W3 [inter, dim], W2 [dim, inter]) -> three float64 matrices."""
+def slot_matrices(cfg, raw, fmt="kquant"):
+    """Decode one expert slice [W1 | W3 | W2] (W1/W3 [inter, dim], W2 [dim, inter])
+    -> three float64 matrices. fmt "kquant": Q2_K, Q2_K, Q3_K blocks, rows in order;
+    "fp4": three MXFP4 matrices."""
     raw = np.asarray(raw, dtype=np.uint8).reshape(-1)
+    if fmt == "fp4":
+        n13 = cfg.inter * cfg.dim // 2 + cfg.inter * cfg.dim // FP4_BLOCK
+        n2 = cfg.dim * cfg.inter // 2 + cfg.dim * cfg.inter // FP4_BLOCK
+        assert raw.size == 2 * n13 + n2, (raw.size, 2 * n13 + n2)
+        return (dequant_mxfp4(raw[:n13], cfg.inter, cfg.dim), dequant_mxfp4(raw[n13:2 * n13], cfg.inter, cfg.dim),
+                dequant_mxfp4(raw[2 * n13:], cfg.dim, cfg.inter))
     n13 = cfg.inter * (cfg.dim // QK_K) * Q2K_BYTES
     n2 = cfg.dim * (cfg.inter // QK_K) * Q3K_BYTES
     assert raw.size == 2 * n13 + n2, (raw.size, 2 * n13 + n2)
@@ -162,8 +177,9 @@ def expert_ffn_kquant(x_f32, w1, w3, w2, limit):
 
 
 def shared_ffn_bf16(x, w1, w3, w2, limit):
-    """bf16 shared expert: unquantised x [T, dim] (float64 of bf16 values), f64
-    g/u, clamped SwiGLU, h rounded to bf16 (through f32), then W2."""
+    """bf16-activation expert (the bf16 shared expert; also a routed MXFP4 expert
+    with its dequantised weights): unquantised x [T, dim] (float64 of bf16
+    values), f64 g/u, clamped SwiGLU, h rounded to bf16 (through f32), then W2."""
     g = x @ w1.T
     u = x @ w3.T
     h = swiglu_clamped(g, u, limit)
@@ -192,9 +208,12 @@ def moe_layer(cfg, x_bits, router_bits, bias, expert_slot, shared=None):
     # per-pick expert outputs, each expert decoded once for all tokens that picked it
     picks = np.zeros((m, cfg.topk, cfg.dim), dtype=np.float64)
     for e in np.unique(idx):
-        w1, w3, w2 = slot_matrices(cfg, expert_slot(int(e)))
+        w1, w3, w2 = slot_matrices(cfg, expert_slot(int(e)), cfg.expert_fmt)
         rows, cols = np.nonzero(idx == e)
-        picks[rows, cols] = expert_ffn_kquant(x32[rows], w1, w3, w2, cfg.swiglu_limit)
+        if cfg.expert_fmt == "fp4":
+            picks[rows, cols] = shared_ffn_bf16(x[rows], w1, w3, w2, cfg.swiglu_limit)
+        else:
+            picks[rows, cols] = expert_ffn_kquant(x32[rows], w1, w3, w2, cfg.swiglu_limit)
     # routed sum in pick order, then the shared expert
     y = np.zeros((m, cfg.dim), dtype=np.float64)
     for i in range(cfg.topk):

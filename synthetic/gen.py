@@ -6,7 +6,9 @@ dim 5120, moe_inter_dim 2304, 384 routed experts, 6 active, 1 shared):
   * bias f32 [n_routed] ~ U(lo, hi), or zero, or the skewed ranking below;
   * routed expert e: W1, W3 [inter, dim] and W2 [dim, inter] drawn f32 ~ N(0, 0.02)
     and packed into Q2_K (W1, W3) and Q3_K (W2) blocks; the expert's slice is
-    [W1 | W3 | W2] raw block bytes, rows in order;
+    [W1 | W3 | W2] raw block bytes, rows in order; or (fmt "fp4") the same draws
+    packed as microscaled FP4: per 32 weights of a row one E8M0 power-of-two
+    scale and 32 e2m1 codes, each matrix [codes rows x cols/2 | scales rows x cols/32];
   * shared expert: the same draws kept as bf16, or packed like a routed expert;
   * tokens bf16 [m, dim] ~ N(0, 1) rounded to bf16.
 Every stream has its own seed derived from (seed, tag, index, matrix), so any
@@ -158,38 +160,79 @@ def encode_q3k(w):
     return out.reshape(rows, (cols // QK) * Q3K_BYTES)
 
 
-def expert_layout(shape):
+FP4_BLOCK = 32                                    # weights per E8M0 scale
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)   # between the magnitudes 0 .5 1 1.5 2 3 4 6
+
+
+def encode_mxfp4(w):
+    """f32 [rows, cols] (cols % 32 == 0) -> uint8 [rows * cols/2 + rows * cols/32]:
+    the codes [rows, cols/2] (weight 2i of a row in the low nibble of byte i, 2i + 1
+    in the high nibble), then the scales [rows, cols/32].
+
+    Per 32-weight block: E = 127 + ceil(log2(amax / 6)) (clamped to 1..254; 127 for
+    an all-zero block), so |w| / 2^(E-127) <= 6; each weight is coded as the sign
+    bit (bit 3) and the index (bits 0-2) of the nearest e2m1 magnitude.
+    """
+    rows, cols = w.shape
+    x = w.reshape(rows, cols // FP4_BLOCK, FP4_BLOCK).float()
+    amax = x.abs().amax(-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax.clamp_min(1e-38) / 6.0)), torch.zeros_like(amax))
+    e = (e + 127).clamp(1, 254)
+    scale = torch.exp2(e - 127)[..., None]
+    mag = (x.abs() / scale).clamp(max=6.0)
+    mids = torch.tensor(_E2M1_MIDPOINTS, dtype=torch.float32, device=w.device)
+    idx = torch.bucketize(mag, mids).to(torch.int32)            # 0..7
+    code = idx | torch.where((x < 0) & (idx > 0), 8, 0).to(torch.int32)
+    code = code.reshape(rows, cols // 2, 2)
+    packed = (code[..., 0] | (code[..., 1] << 4)).to(torch.uint8)
+    return torch.cat([packed.reshape(-1), e.to(torch.uint8).reshape(-1)])
+
+
+def mxfp4_bytes(rows, cols):
+    return rows * cols // 2 + rows * cols // FP4_BLOCK
+
+
+def expert_layout(shape, fmt="kquant"):
     """(slot_bytes, off_w1, off_w3, off_w2) of one expert slice [W1 | W3 | W2]."""
-    n13 = shape.inter * (shape.dim // QK) * Q2K_BYTES
-    n2 = shape.dim * (shape.inter // QK) * Q3K_BYTES
+    if fmt == "fp4":
+        n13 = mxfp4_bytes(shape.inter, shape.dim)
+        n2 = mxfp4_bytes(shape.dim, shape.inter)
+    else:
+        n13 = shape.inter * (shape.dim // QK) * Q2K_BYTES
+        n2 = shape.dim * (shape.inter // QK) * Q3K_BYTES
     return 2 * n13 + n2, 0, n13, 2 * n13
 
 
-def _slot_from_f32(shape, w1, w3, w2, out=None):
-    size, o1, o3, o2 = expert_layout(shape)
+def _slot_from_f32(shape, w1, w3, w2, out=None, fmt="kquant"):
+    size, o1, o3, o2 = expert_layout(shape, fmt)
     if out is None:
         out = torch.empty(size, dtype=torch.uint8, device=w1.device)
-    out[o1:o3] = encode_q2k(w1).reshape(-1)
-    out[o3:o2] = encode_q2k(w3).reshape(-1)
-    out[o2:] = encode_q3k(w2).reshape(-1)
+    if fmt == "fp4":
+        out[o1:o3] = encode_mxfp4(w1)
+        out[o3:o2] = encode_mxfp4(w3)
+        out[o2:] = encode_mxfp4(w2)
+    else:
+        out[o1:o3] = encode_q2k(w1).reshape(-1)
+        out[o3:o2] = encode_q2k(w3).reshape(-1)
+        out[o2:] = encode_q3k(w2).reshape(-1)
     return out
 
 
-def make_expert_slot(shape, seed, expert, std=0.02, device="cpu", out=None):
+def make_expert_slot(shape, seed, expert, std=0.02, device="cpu", out=None, fmt="kquant"):
     """Routed expert `expert`'s slice as uint8 [slot_bytes] on `device`."""
     w1 = f32_normal((shape.inter, shape.dim), std, stream_seed(seed, TAG_EXPERT, expert, 0), device)
     w3 = f32_normal((shape.inter, shape.dim), std, stream_seed(seed, TAG_EXPERT, expert, 1), device)
     w2 = f32_normal((shape.dim, shape.inter), std, stream_seed(seed, TAG_EXPERT, expert, 2), device)
-    return _slot_from_f32(shape, w1, w3, w2, out)
+    return _slot_from_f32(shape, w1, w3, w2, out, fmt)
 
 
-def make_experts(shape, seed, std=0.02, device="cpu", experts=None):
+def make_experts(shape, seed, std=0.02, device="cpu", experts=None, fmt="kquant"):
     """All routed experts as one uint8 arena [n_routed, slot_bytes] (row e = expert e)."""
-    size = expert_layout(shape)[0]
+    size = expert_layout(shape, fmt)[0]
     n = shape.n_routed
     arena = torch.empty((n, size), dtype=torch.uint8, device=device)
     for e in range(n) if experts is None else experts:
-        make_expert_slot(shape, seed, e, std, device, out=arena[e])
+        make_expert_slot(shape, seed, e, std, device, out=arena[e], fmt=fmt)
     return arena
 
 
