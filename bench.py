@@ -52,6 +52,9 @@ WORKLOADS = {
                    desc="decode m=1 (GEMV path), bf16 shared expert"),
     "small": dict(m=8, layers=4, bias=(-0.05, 0.05), shared="kquant", pool=256,
                   desc="small batch m=8 (GEMV path), K-quant shared expert"),
+    "decode_fp4": dict(m=1, layers=4, bias=(-0.05, 0.05), shared="bf16", pool=256, experts="fp4",
+                       desc="decode m=1, MXFP4 routed experts (e2m1 codes, E8M0 scale per 32 weights) on bf16 "
+                            "activations, bf16 shared expert"),
     "prefill": dict(m=512, layers=1, bias=None, shared="bf16", pool=512,
                     desc="prefill m=512 (MMQ path), uniform routing, bf16 shared expert"),
     "prefill_mixed": dict(m=512, layers=1, bias=None, shared="bf16", pool=512, dispatch="mixed",
@@ -67,6 +70,7 @@ WORKLOADS = {
 DOMINANT = {
     "decode": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "small": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
+    "decode_fp4": ("gateup", r"^void moe::fp4_gateup_kernel<1>"),
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_mixed": ("gateup", r"^void moe::gateup_q2k_kernel<8>"),    # the groups of <= 8 rows
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
@@ -203,6 +207,16 @@ class Bench:
         torch.cuda.synchronize()
         log(f"experts drawn in {time.time() - t0:.1f}s ({self.experts.numel() / 1e9:.2f} GB)")
         self.slot_bytes = self.experts.shape[1]
+        self._fp4 = None
+
+    def fp4_arena(self):
+        """The 384 experts in MXFP4 (7.2 GB), drawn from the same seeds on first use."""
+        if self._fp4 is None:
+            t0 = time.time()
+            self._fp4 = self.S.make_experts(self.shape, 1, device=self.dev, fmt="fp4")
+            self.torch.cuda.synchronize()
+            log(f"MXFP4 experts drawn in {time.time() - t0:.1f}s ({self._fp4.numel() / 1e9:.2f} GB)")
+        return self._fp4
 
     def layers(self, wl):
         torch, moe, S, shape = self.torch, self.moe, self.S, self.shape
@@ -245,7 +259,9 @@ class Bench:
         else:
             tokens = S.make_tokens(pool_n, shape.dim, 1, index={"decode": 0, "small": 3}.get(wl, 2))
         d_tokens = tokens.to(self.dev)
-        cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8))
+        fp4 = spec.get("experts") == "fp4"
+        cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8),
+                           expert_fmt=moe.MOE_EXPERT_MXFP4 if fp4 else moe.MOE_EXPERT_KQUANT)
         ctx = moe.moe_create(cfg)
         if spec.get("dispatch") == "mixed":
             moe.moe_set_dispatch(ctx, moe.MOE_DISPATCH_MIXED)
@@ -257,7 +273,7 @@ class Bench:
             moe.moe_set_slots(ctx, slot_arena, spec["slots"])
             moe.moe_set_host_arena(ctx, host, self.slot_bytes)
         else:
-            moe.moe_set_slots(ctx, self.packed, shape.n_routed)
+            moe.moe_set_slots(ctx, self.fp4_arena() if fp4 else self.packed, shape.n_routed)
             for e in range(shape.n_routed):
                 moe.moe_slot_bind(ctx, e, e)
         out = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
@@ -365,9 +381,9 @@ class Bench:
             return s / steps if n else 0.0
 
         ms_step = ms_total / steps
-        expert_b = self.slot_bytes
+        expert_b = moe.moe_expert_layout(cfg)[0]
         n_exp = sum(distinct) / len(distinct)
-        q2k_matrix = shape.inter * (shape.dim // 256) * 84
+        q2k_matrix = (S.mxfp4_bytes(shape.inter, shape.dim) if fp4 else shape.inter * (shape.dim // 256) * 84)
         shared_b = 3 * shape.dim * shape.inter * 2 if spec["shared"] == "bf16" else expert_b
         routed_b = n_exp * expert_b
         expert_bytes = routed_b + shared_b
@@ -493,7 +509,7 @@ def main():
     layers, tokens = head.pop("_layers"), head.pop("_tokens")
     extra = {}
     if wl == "decode" and not args.no_extra:
-        for other in ("small", "prefill", "prefill_mixed", "prefill_hot", "skewed"):
+        for other in ("small", "decode_fp4", "prefill", "prefill_mixed", "prefill_hot", "skewed"):
             st = 100 if WORKLOADS[other]["m"] <= 8 else 5 if other == "skewed" else 10
             wu = 3 if other == "skewed" else 5
             log(f"{other}: {wu} warmup + {st} timed steps")

@@ -68,7 +68,23 @@ typedef struct moe_cfg {
     float route_scale;      /* routing weight multiplier */
     float swiglu_limit;     /* clamp L; <= 0 disables both clamps */
     int32_t max_tokens;     /* largest m any call may pass: 1..65536; sizes the scratch */
+    int32_t expert_fmt;     /* MOE_EXPERT_KQUANT (0) or MOE_EXPERT_MXFP4 (1): the routed experts' format */
 } moe_cfg;
+
+/* Routed expert formats (moe_cfg.expert_fmt).
+ * MOE_EXPERT_KQUANT: GGUF Q2_K gate/up and Q3_K down blocks, read against q8_1
+ *   activations (metrale moe_v41 module documentation).
+ * MOE_EXPERT_MXFP4: the upstream checkpoint's FP4 experts (Open Model Atlas,
+ *   "DeepSeek V4.1 · Mixture of experts": float4_e2m1fn_x2 weights): per 32
+ *   consecutive weights of a row one E8M0 scale byte 2^(E-127), and 32 e2m1
+ *   codes, two per byte with the even weight in the low nibble (the OCP
+ *   microscaling layout; the pages give only the element type). A matrix
+ *   [rows, cols] is its codes [rows, cols/2] followed by its scales
+ *   [rows, cols/32]. The experts run on the unquantised bf16 x with f32
+ *   accumulation, h rounded to bf16 before W2. The shared expert must then be
+ *   bf16 or none. */
+#define MOE_EXPERT_KQUANT 0
+#define MOE_EXPERT_MXFP4 1
 
 /* One layer's resident weights (metrale's MoeV41LayerWeights). Routed experts
  * are not here: they are found through the slot table (moe_set_slots). */
@@ -114,8 +130,9 @@ int moe_destroy(moe_ctx* ctx);
  * block 1, ... (block s of row r at ((r/8)*nsb + s)*8*B + (r%8)*B, nsb blocks
  * per row of B bytes), so that every 8-row tile and every block column of a
  * panel is one contiguous run. moe_pack_expert turns a slice in plain GGUF
- * row order into this layout. All four outputs are required. MOE_EINVAL on a
- * bad cfg. */
+ * row order into this layout. With expert_fmt MOE_EXPERT_MXFP4 the slice is
+ * [W1 | W3 | W2] of MXFP4 matrices (codes then scales, rows in order; no
+ * panels). All four outputs are required. MOE_EINVAL on a bad cfg. */
 int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, size_t* off_w3,
                       size_t* off_w2);
 
@@ -126,7 +143,8 @@ int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, si
  * arena slices (pack on the device, then copy) and a K-quant shared expert.
  * MOE_EINVAL for a bad cfg, NULL or overlapping buffers; MOE_EHIP on a launch
  * error. (A layout step of this library: the blocks themselves are the
- * pages' GGUF Q2_K / Q3_K blocks, untouched.) */
+ * pages' GGUF Q2_K / Q3_K blocks, untouched.) For MXFP4 experts the slot layout
+ * is the plain one and this is a copy. */
 int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream);
 
 /* Give the context a caller-owned device arena of n_slots slices of slot_bytes

@@ -26,6 +26,9 @@ MOE_SHARED_NONE = 0
 MOE_SHARED_BF16 = 1
 MOE_SHARED_KQUANT = 2
 
+MOE_EXPERT_KQUANT = 0
+MOE_EXPERT_MXFP4 = 1
+
 MOE_DISPATCH_MMQ = 0
 MOE_DISPATCH_MIXED = 1
 
@@ -52,6 +55,7 @@ class moe_cfg(ctypes.Structure):
         ("route_scale", ctypes.c_float),
         ("swiglu_limit", ctypes.c_float),
         ("max_tokens", ctypes.c_int32),
+        ("expert_fmt", ctypes.c_int32),
     ]
 
 
@@ -154,9 +158,9 @@ def _stream(stream):
 
 
 def make_cfg(dim, inter, n_routed, topk, gate_temp=1.0, norm_topk_prob=True, route_scale=1.5,
-             swiglu_limit=10.0, max_tokens=1):
+             swiglu_limit=10.0, max_tokens=1, expert_fmt=MOE_EXPERT_KQUANT):
     return moe_cfg(dim, inter, n_routed, topk, gate_temp, int(bool(norm_topk_prob)), route_scale,
-                   swiglu_limit, max_tokens)
+                   swiglu_limit, max_tokens, expert_fmt)
 
 
 def make_weights(router_w, router_bias, shared_fmt=MOE_SHARED_NONE, shared_w1=None, shared_w3=None,

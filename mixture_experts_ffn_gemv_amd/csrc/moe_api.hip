@@ -121,12 +121,15 @@ int check_cfg(const moe_cfg* c) {
     if (!(c->gate_temp > 0.f)) return MOE_EINVAL;
     if (c->max_tokens < 1 || c->max_tokens > 65536) return MOE_EINVAL;
     if ((int64_t)c->max_tokens * c->topk > (1 << 22)) return MOE_EINVAL;
+    if (c->expert_fmt != MOE_EXPERT_KQUANT && c->expert_fmt != MOE_EXPERT_MXFP4) return MOE_EINVAL;
     return MOE_OK;
 }
 
 void layout_of(const moe_cfg& c, size_t& slot, size_t& o1, size_t& o3, size_t& o2) {
-    const size_t n13 = (size_t)c.inter * (c.dim / QK) * Q2K_BYTES;
-    const size_t n2 = (size_t)c.dim * (c.inter / QK) * Q3K_BYTES;
+    const size_t DI = (size_t)c.dim * c.inter;
+    const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;   // codes (2 per byte) + one scale byte per 32
+    const size_t n13 = fp4 ? DI / 2 + DI / 32 : (size_t)c.inter * (c.dim / QK) * Q2K_BYTES;
+    const size_t n2 = fp4 ? DI / 2 + DI / 32 : (size_t)c.dim * (c.inter / QK) * Q3K_BYTES;
     o1 = 0;
     o3 = n13;
     o2 = 2 * n13;
@@ -207,6 +210,7 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
     if (!aligned(w->router_w, 16) || !aligned(w->router_bias, 4)) return MOE_EINVAL;
     if (w->shared_fmt == MOE_SHARED_NONE) return MOE_OK;
     if (w->shared_fmt != MOE_SHARED_BF16 && w->shared_fmt != MOE_SHARED_KQUANT) return MOE_EINVAL;
+    if (w->shared_fmt == MOE_SHARED_KQUANT && ctx->cfg.expert_fmt == MOE_EXPERT_MXFP4) return MOE_EINVAL;
     if (w->shared_w1 == nullptr || w->shared_w3 == nullptr || w->shared_w2 == nullptr) return MOE_EINVAL;
     if (!aligned(w->shared_w1, 16) || !aligned(w->shared_w3, 16) || !aligned(w->shared_w2, 16)) return MOE_EINVAL;
     if (w->shared_fmt == MOE_SHARED_BF16 && ctx->cfg.dim > 8192) return MOE_EINVAL;
@@ -273,6 +277,8 @@ int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream
     uint8_t* d8 = (uint8_t*)dst;
     if (s8 < d8 + bytes && d8 < s8 + bytes) return MOE_EINVAL;
     const hipStream_t st = (hipStream_t)stream;
+    if (cfg->expert_fmt == MOE_EXPERT_MXFP4)
+        return hipMemcpyAsync(d8, s8, bytes, hipMemcpyDeviceToDevice, st) == hipSuccess ? MOE_OK : MOE_EHIP;
     const int D = cfg->dim, I = cfg->inter;
     struct M { size_t off; int rows, nsb, B; } mats[3] = {
         {o1, I, D / QK, Q2K_BYTES}, {o3, I, D / QK, Q2K_BYTES}, {o2, D, I / QK, Q3K_BYTES}};
@@ -303,8 +309,15 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
         if (hipGetDeviceProperties(&prop, ctx->device) == hipSuccess && prop.multiProcessorCount > 0)
             ctx->n_cu = prop.multiProcessorCount;
     }
-    ctx->decode_ok = decode_supported(c.dim, c.inter);
-    ctx->mmq_ok = mmq_supported(c.dim, c.inter);
+    // K-quant experts: the decode and MMQ kernels where their tiles fit this shape;
+    // MXFP4 experts: their own chunked kernels at every m
+    const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
+    if (fp4 && !fp4_supported(c.dim, c.inter)) {
+        delete ctx;
+        return MOE_EINVAL;
+    }
+    ctx->decode_ok = !fp4 && decode_supported(c.dim, c.inter);
+    ctx->mmq_ok = !fp4 && mmq_supported(c.dim, c.inter);
     const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
     const size_t P = M * c.topk;
     ctx->max_pairs = (int)P;
@@ -730,6 +743,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.sh_w1 = kq ? (const uint8_t*)w->shared_w1 : nullptr;
     a.sh_w3 = kq ? (const uint8_t*)w->shared_w3 : nullptr;
     a.sh_w2 = kq ? (const uint8_t*)w->shared_w2 : nullptr;
+    a.x16 = x;
     a.xq = ctx->xq;
     a.xd = ctx->xd;
     a.xs16 = ctx->xs16;
@@ -813,12 +827,19 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
             rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_mmq(a, plan, false, st); });
             if (rc != MOE_OK) return rc;
         } else {
-            rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, nch, st); });
-            if (rc != MOE_OK) return rc;
-            rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
-            if (rc != MOE_OK) return rc;
-            rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, nch, st); });
-            if (rc != MOE_OK) return rc;
+            if (c.expert_fmt == MOE_EXPERT_MXFP4) {   // bf16 h, no q8_1 step
+                rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_fp4(a, rows_max, nch, true, st); });
+                if (rc != MOE_OK) return rc;
+                rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_fp4(a, rows_max, nch, false, st); });
+                if (rc != MOE_OK) return rc;
+            } else {
+                rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q2k(a, rows_max, nch, st); });
+                if (rc != MOE_OK) return rc;
+                rc = timed(ctx, st, MOE_K_QUANT, [&] { return launch_quantize_h(a, P, kq ? m : 0, st); });
+                if (rc != MOE_OK) return rc;
+                rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_down_q3k(a, rows_max, nch, st); });
+                if (rc != MOE_OK) return rc;
+            }
         }
         if (waves.size() > 1) {
             hipEvent_t ew = wave_event(ctx->ev_wave, wv, false);

@@ -61,11 +61,12 @@ struct ExpertArgs {
     const uint8_t* sh_w1;       // K-quant shared expert (NULL when bf16 / none)
     const uint8_t* sh_w3;
     const uint8_t* sh_w2;
+    const uint16_t* x16;        // bf16 x [m, D] (MXFP4 experts read it unquantised)
     const int8_t* xq;           // q8_1 of x: int8 [m, D], d f32 [m, D/32], 16-sums i32 [m, D/16]
     const float* xd;
     const int32_t* xs16;
     const float* xs16f;         // fp16(d) * (sum of each 16 quants) of x, f32 [m, D/16] (MMQ min term)
-    float* h_routed;            // f32 [pairs, I] in position order
+    float* h_routed;            // f32 [pairs, I] in position order (bf16 [pairs, I] for MXFP4 experts)
     float* h_shared;            // f32 [m, I]
     int8_t* hq_routed;          // q8_1 of h_routed: int8 [pairs, I], d f32 [pairs, I/32], 16-sums i32 [pairs, I/16]
     float* hd_routed;

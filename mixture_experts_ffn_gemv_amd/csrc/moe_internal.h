@@ -111,6 +111,9 @@ hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int 
 hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,
                                    const uint16_t* w2, uint16_t* h, float* ys, float limit, hipStream_t st);
 hipError_t launch_gateup_q2k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
+// MXFP4 experts: gate/up (h bf16 into h_routed) or down (E rows), chunks of <= rows_max rows
+bool fp4_supported(int D, int I);
+hipError_t launch_fp4(const ExpertArgs& a, int rows_max, int max_chunks, bool gateup, hipStream_t st);
 hipError_t launch_quantize_h(const ExpertArgs& a, int routed_rows, int shared_rows, hipStream_t st);
 hipError_t launch_down_q3k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
 // decode path (single-row chunks from the small-batch routing)

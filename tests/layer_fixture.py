@@ -22,18 +22,22 @@ def bits(t):
 class Layer:
     def __init__(self, shape, seed, *, shared_fmt="bf16", bias=(-0.1, 0.1), router_std=0.05, max_tokens=8,
                  expert_device="cpu", gate_temp=1.0, norm=True, route_scale=1.5, limit=10.0, bind_all=True,
-                 n_slots=None, experts=None, host_arena=False, dispatch=None, verbose=False):
+                 n_slots=None, experts=None, host_arena=False, dispatch=None, expert_fmt="kquant",
+                 verbose=False):
         self.shape = shape
         self.dev = torch.device("cuda")
         t0 = time.time()
         self.wr, self.bias = S.make_router(shape, seed, router_std, bias)
-        self.arena_src = experts if experts is not None else S.make_experts(shape, seed, device=expert_device)
+        self.expert_fmt = expert_fmt
+        self.arena_src = (experts if experts is not None
+                          else S.make_experts(shape, seed, device=expert_device, fmt=expert_fmt))
         self.shared = None if shared_fmt == "none" else S.make_shared(shape, seed, shared_fmt)
         self.cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, gate_temp=gate_temp,
                                 norm_topk_prob=norm, route_scale=route_scale, swiglu_limit=limit,
-                                max_tokens=max_tokens)
+                                max_tokens=max_tokens,
+                                expert_fmt=moe.MOE_EXPERT_MXFP4 if expert_fmt == "fp4" else moe.MOE_EXPERT_KQUANT)
         self.ocfg_kw = dict(gate_temp=gate_temp, norm_topk_prob=norm, route_scale=route_scale,
-                            swiglu_limit=limit)
+                            swiglu_limit=limit, expert_fmt=expert_fmt)
         self.ctx = moe.moe_create(self.cfg)
         if dispatch is not None:
             moe.moe_set_dispatch(self.ctx, dispatch)
@@ -64,7 +68,9 @@ class Layer:
                 fmt = moe.MOE_SHARED_BF16
             else:
                 slot = torch.empty(self.shared["slot"].shape, dtype=torch.uint8, device=self.dev)
-                moe.moe_pack_expert(self.cfg, self.shared["slot"].to(self.dev), slot)
+                # a K-quant slice, packed with the K-quant layout whatever the routed format
+                kcfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max_tokens)
+                moe.moe_pack_expert(kcfg, self.shared["slot"].to(self.dev), slot)
                 _, o1, o3, o2 = S.expert_layout(shape)
                 self.d_shared = {"slot": slot, "w1": slot[o1:o3], "w3": slot[o3:o2], "w2": slot[o2:]}
                 fmt = moe.MOE_SHARED_KQUANT

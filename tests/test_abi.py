@@ -39,6 +39,17 @@ def test_expert_layout_matches_block_sizes(lib):
         assert moe.moe_expert_layout(cfg) == S.expert_layout(shape)
 
 
+def test_mxfp4_layout_matches_encoder(lib):
+    for shape in (S.TINY, S.REAL, S.LayerShape(512, 768, 40, 9)):
+        cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=4,
+                           expert_fmt=moe.MOE_EXPERT_MXFP4)
+        assert moe.moe_expert_layout(cfg) == S.expert_layout(shape, "fp4")
+    bad = moe.make_cfg(256, 256, 16, 2, max_tokens=4, expert_fmt=2)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_expert_layout(bad)
+    assert e.value.code == moe.MOE_EINVAL
+
+
 @pytest.mark.parametrize("bad", [dict(dim=300), dict(dim=0), dict(inter=100), dict(n_routed=0),
                                  dict(topk=0), dict(topk=17), dict(max_tokens=0), dict(gate_temp=0.0),
                                  dict(dim=8448)])

@@ -118,6 +118,41 @@ def test_mid_decode_bf16_shared(m):
         layer.close()
 
 
+FP4_SHAPE = S.LayerShape(512, 256, 16, 3)     # dim != inter, so a transposed operand fails
+
+
+@pytest.mark.parametrize("shared", ["bf16", "none"])
+@pytest.mark.parametrize("m", [1, 3, 8, 13, 70])
+def test_fp4_experts(shared, m):
+    # MXFP4 routed experts: single-row chunks up to 8 tokens, chunks of up to 8 rows above
+    layer = Layer(FP4_SHAPE, 6, max_tokens=80, shared_fmt=shared, expert_fmt="fp4")
+    try:
+        check_layer(layer, S.make_tokens(m, FP4_SHAPE.dim, 6, index=m), f"fp4 {shared} m={m}")
+    finally:
+        layer.close()
+
+
+def test_fp4_hot_expert_and_clamps():
+    # one expert takes every token (a 40-row group in 8-row chunks), clamps at 0.25
+    layer = Layer(FP4_SHAPE, 7, max_tokens=40, expert_fmt="fp4", limit=0.25)
+    try:
+        layer.bias[5] = 100.0
+        layer.d_bias.copy_(layer.bias.to(layer.dev))
+        check_layer(layer, S.make_tokens(40, FP4_SHAPE.dim, 7), "fp4 hot expert")
+    finally:
+        layer.close()
+
+
+def test_fp4_rejects_kquant_shared():
+    with pytest.raises(moe.MoeError) as e:
+        layer = Layer(FP4_SHAPE, 6, max_tokens=4, shared_fmt="kquant", expert_fmt="fp4")
+        try:
+            layer.forward(S.make_tokens(1, FP4_SHAPE.dim, 6).cuda())
+        finally:
+            layer.close()
+    assert e.value.code == moe.MOE_EINVAL
+
+
 def test_tiny_topk1():
     shape = S.LayerShape(256, 256, 16, 1)
     layer = Layer(shape, 3, max_tokens=8)
@@ -227,6 +262,28 @@ def real_experts():
     yield a
     del a
     torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def real_fp4_experts():
+    say("[real] drawing 384 MXFP4 experts on the GPU")
+    a = S.make_experts(S.REAL, 1, device="cuda", fmt="fp4")
+    torch.cuda.synchronize()
+    yield a
+    del a
+    torch.cuda.empty_cache()
+
+
+def test_real_fp4_decode_m1(real_fp4_experts):
+    layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=64, experts=real_fp4_experts,
+                  expert_fmt="fp4")
+    try:
+        pool = S.make_tokens(256, S.REAL.dim, 1)
+        for t in (0, 131):
+            check_layer(layer, pool[t:t + 1], f"fp4 decode m=1 token {t}")
+        check_layer(layer, pool[64:128], "fp4 m=64", sample_rows=[0, 63])
+    finally:
+        layer.close()
 
 
 def test_real_decode_m1(real_experts):
