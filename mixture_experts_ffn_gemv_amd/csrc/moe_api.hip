@@ -651,8 +651,9 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     const bool small = m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS;
     const bool use_mmq = !small && ctx->mmq_ok;
     // decode with every picked expert in its slot: the bf16 shared expert rides in
-    // the same launches (its gate/up rows as extra workgroups of the two routing
-    // kernels, its down inside the routed down kernel), no second stream
+    // the routing launches, its gate/up rows as extra workgroups of the router
+    // launch, its down rows (into ys, added by the routed down kernel) as extra
+    // workgroups of the top-k launch; no second stream
     const bool shared_fused = bf16_shared && small && ctx->decode_ok && ctx->host_arena == nullptr;
     SharedRows sr_a{}, sr_b{};
     if (shared_fused) {
@@ -666,9 +667,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         sr_a.limit = c.swiglu_limit;
         sr_b = sr_a;
         sr_a.row0 = 0;
-        sr_a.rows = c.inter / 2;
-        sr_b.row0 = sr_a.rows;
-        sr_b.rows = c.inter - sr_a.rows;
+        sr_a.rows = c.inter;
+        sr_b.w1 = sr_b.w3 = nullptr;
+        sr_b.w2 = (const uint16_t*)w->shared_w2;
+        sr_b.ys = ctx->ys;
+        sr_b.row0 = 0;
+        sr_b.rows = c.dim;
     }
     if (bf16_shared && !shared_fused) {
         // the shared expert needs only x: run it beside the routing and the routed experts
@@ -787,9 +791,6 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (rc != MOE_OK) return rc;
         if (bf16_shared && !shared_fused && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
         rc = timed(ctx, st, MOE_K_DOWN, [&] {
-            if (shared_fused)
-                return launch_down_combine(a, P, m, nch, nullptr, (const uint16_t*)w->shared_w2,
-                                           (const uint16_t*)ctx->h_shared, (uint16_t*)out_bf16, st);
             return launch_down_combine(a, P, m, nch, ys, nullptr, nullptr, (uint16_t*)out_bf16, st);
         });
         if (rc != MOE_OK) return rc;

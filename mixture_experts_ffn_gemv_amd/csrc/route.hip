@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __res
     const int nrouter = E * ntg;
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
     if ((int)blockIdx.x >= nrouter + nq) {   // the shared expert's rows
-        shared_gateup_block(sr, blockIdx.x - nrouter - nq);
+        shared_rows_block(sr, blockIdx.x - nrouter - nq);
         return;
     }
     if ((int)blockIdx.x >= nrouter) {
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                            int32_t* __restrict__ n_chunks,
                                                            const int32_t* __restrict__ slot_table, SharedRows sr) {
     if (blockIdx.x > 0) {   // the shared expert's rows
-        shared_gateup_block(sr, blockIdx.x - 1);
+        shared_rows_block(sr, blockIdx.x - 1);
         return;
     }
     __shared__ __align__(16) float keys[1024];
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict_
                                                         int32_t* __restrict__ n_chunks,
                                                         const int32_t* __restrict__ slot_table, SharedRows sr) {
     if (blockIdx.x > 0) {   // the shared expert's rows
-        shared_gateup_block(sr, blockIdx.x - 1);
+        shared_rows_block(sr, blockIdx.x - 1);
         return;
     }
     __shared__ float keys[64 * M1_MAX_KEYS], scores[64 * M1_MAX_KEYS];
@@ -578,7 +578,7 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
     SharedRows none{};
     const SharedRows& s = sr ? *sr : none;
-    const int nsh = sr ? shared_rows_blocks(sr->rows, 256) : 0;
+    const int nsh = sr ? shared_rows_blocks(*sr, 256) : 0;
     if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
     if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
     if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
@@ -602,7 +602,7 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
     const SharedRows& s = sr ? *sr : none;
     if (m == 1 && E <= 64 * M1_MAX_KEYS && k <= 64) {
         const int th = std::max(128, (E + 63) / 64 * 64);   // shared-expert rows take two wavefronts each
-        const int grid = 1 + (sr ? shared_rows_blocks(sr->rows, th) : 0);
+        const int grid = 1 + (sr ? shared_rows_blocks(*sr, th) : 0);
 #define ROUTE_M1(KPL) launch_kernel(route_m1_kernel<KPL>, grid, th, 0, st, logits, bias, E, k, gate_temp, norm, \
                                     route_scale, idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, \
                                     chunks, n_chunks, slot_table, s)
@@ -611,7 +611,7 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
 #undef ROUTE_M1
         return e;
     }
-    const int grid = 1 + (sr ? shared_rows_blocks(sr->rows, 1024) : 0);
+    const int grid = 1 + (sr ? shared_rows_blocks(*sr, 1024) : 0);
     return launch_kernel(route_small_kernel, grid, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale,
                          idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks,
                          slot_table, s);

@@ -10,20 +10,23 @@
 namespace moe {
 
 struct SharedRows {
-    const uint16_t* w1;   // bf16 [I, D] row-major; NULL: no shared-expert rows in this launch
+    const uint16_t* w1;   // gate/up rows: bf16 [I, D] row-major (NULL with w2 NULL: no shared rows)
     const uint16_t* w3;   // bf16 [I, D]
     const uint16_t* x;    // bf16 [m, D]
-    uint16_t* h;          // bf16 [m, I]
-    int32_t row0, rows;   // the rows [row0, row0 + rows) this launch computes
+    uint16_t* h;          // bf16 [m, I] (written by gate/up rows, read by down rows)
+    const uint16_t* w2;   // down rows instead: bf16 [D, I] row-major, ys = W2 h (f32 [m, D])
+    float* ys;
+    int32_t row0, rows;   // the rows [row0, row0 + rows) this launch computes (of h, or of ys)
     int32_t D, I, m;      // m <= 8
     float limit;
 };
 
-// Workgroups needed for `rows` rows with `threads` threads each (a row per two wavefronts).
-// (threads >= 128; the routing launches that carry shared rows use at least that)
-inline int shared_rows_blocks(int rows, int threads) {
-    const int rpw = threads / 128;
-    return rows <= 0 || rpw <= 0 ? 0 : (rows + rpw - 1) / rpw;
+// Workgroups needed for the launch's rows with `threads` threads each: a gate/up
+// row per two wavefronts, a down row per wavefront. (threads >= 128; the
+// routing launches that carry shared rows use at least that)
+inline int shared_rows_blocks(const SharedRows& sr, int threads) {
+    const int rpw = sr.w2 != nullptr ? threads / 64 : threads / 128;
+    return sr.rows <= 0 || rpw <= 0 ? 0 : (sr.rows + rpw - 1) / rpw;
 }
 
 MOE_DEV float dot2_bf16x(uint32_t a, uint32_t b, float c) {
@@ -86,6 +89,50 @@ MOE_DEV void shared_gateup_block(const SharedRows& sr, int blk) {
             sr.h[(size_t)t * sr.I + r] = (uint16_t)f32_to_bf16(swiglu(dots[t], up[rl][t], sr.limit));
         }
     }
+}
+
+// Workgroup `blk` of the shared down rows: wavefront i takes output row
+// row0 + blk * (wavefronts) + i of W2, 16-byte pieces lane, lane + 64, ... (every
+// load of the wavefront 1 KB contiguous), dotted with the same pieces of each
+// token's h; the wavefront sums and lane 0 writes ys.
+MOE_DEV void shared_down_block(const SharedRows& sr, int blk) {
+    const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rr = blk * nw + wv;
+    if (rr >= sr.rows) return;
+    const int r = sr.row0 + rr;
+    const int n16 = sr.I / 8;   // 16-byte pieces per row (I <= 8192: at most 16 per lane)
+    const uint4* W = reinterpret_cast<const uint4*>(sr.w2 + (size_t)r * sr.I);
+    uint4 wq[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int k = lane + 64 * j;
+        wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        if (t >= sr.m) break;
+        const uint4* H = reinterpret_cast<const uint4*>(sr.h + (size_t)t * sr.I);
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int k = lane + 64 * j;
+            if (k < n16) {
+                const uint4 hv = H[k];
+                acc = dot2_bf16x(wq[j].x, hv.x, acc);
+                acc = dot2_bf16x(wq[j].y, hv.y, acc);
+                acc = dot2_bf16x(wq[j].z, hv.z, acc);
+                acc = dot2_bf16x(wq[j].w, hv.w, acc);
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) sr.ys[(size_t)t * sr.D + r] = acc;
+    }
+}
+
+// the launch's shared rows, gate/up or down
+MOE_DEV void shared_rows_block(const SharedRows& sr, int blk) {
+    if (sr.w2 != nullptr) shared_down_block(sr, blk);
+    else shared_gateup_block(sr, blk);
 }
 
 }  // namespace moe
