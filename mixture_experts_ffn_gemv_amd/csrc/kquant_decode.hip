@@ -32,11 +32,6 @@ constexpr int DC_ROWS = 8;    // output rows per down workgroup: one panel
 // 16-value sums
 MOE_DEV int rec_bytes(int I) { return I + (I / QB) * 4 + (I / 16) * 4; }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-MOE_DEV float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
-}
 
 }  // namespace
 
@@ -208,11 +203,10 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
 // on 2-byte boundaries) and dots all 256 weights against the chunk's q8_1 h,
 // whose records the pass loads into LDS. The per-(row, chunk) sums over the
 // superblocks and the weighted sum over the chunks of each token run in a
-// fixed order (chunks in list order, then the shared expert's f32 output).
+// fixed order (chunks in list order, then the shared expert's f32 output ys,
+// when given).
 __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int routed_rows, int m, int max_chunks,
                                                             int G, const float* __restrict__ ys,
-                                                            const uint16_t* __restrict__ sh_w2,
-                                                            const uint16_t* __restrict__ h_sh,
                                                             uint16_t* __restrict__ out) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
@@ -232,7 +226,6 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     float* part = c_w + max_chunks;                      // [G][8][nsb]
     float* acc = part + G * DC_ROWS * nsb;               // [m][8]
     float* esum = acc + m * DC_ROWS;                     // [G][8]
-    float* shp = esum + G * DC_ROWS;                     // [8][I / 64][m]: bf16 shared expert partials
     const int nch = min(*a.n_chunks, max_chunks);
     for (int q = tid; q < nch; q += bd) {
         const Chunk ch = a.chunks[q];
@@ -243,32 +236,6 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
         c_w[q] = ch.weight;
     }
     for (int q = tid; q < m * DC_ROWS; q += bd) acc[q] = 0.f;
-    // bf16 shared expert (when given): this panel's W2 rows against h (bf16 [m, I]),
-    // one (row, 64-element slice) per job (one job per thread at the decode shapes),
-    // partials summed in slice order below
-    const int nsj = I / 64;
-    if (sh_w2 != nullptr) {
-        for (int job = tid; job < DC_ROWS * nsj; job += bd) {
-            const int rr = job / nsj, ks = job % nsj;
-            const uint4* wp = reinterpret_cast<const uint4*>(sh_w2 + (size_t)(r0 + rr) * I + 64 * ks);
-            uint4 wv[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) wv[q] = wp[q];
-            for (int t = 0; t < m; ++t) {
-                const uint4* hp = reinterpret_cast<const uint4*>(h_sh + (size_t)t * I + 64 * ks);
-                float v = 0.f;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint4 hv = hp[q];
-                    v = dot2_bf16(wv[q].x, hv.x, v);
-                    v = dot2_bf16(wv[q].y, hv.y, v);
-                    v = dot2_bf16(wv[q].z, hv.z, v);
-                    v = dot2_bf16(wv[q].w, hv.w, v);
-                }
-                shp[(rr * nsj + ks) * m + t] = v;
-            }
-        }
-    }
     __syncthreads();
 
     const int r = tid & 7, sc = tid >> 3, s = sc % nsb, cl = sc / nsb;
@@ -364,23 +331,11 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
         }
         barrier_lds();   // the records and partials are reused by the next pass
     }
-    // output (token t, row rr) = q / 8: 8 threads per output, each summing every eighth
-    // shared-expert partial in order, then across the 8 (all threads run the same trips)
-    for (int q0 = 0; q0 < m * DC_ROWS * 8; q0 += bd) {
-        const int q = q0 + tid, o = q >> 3, j = q & 7;
-        const int t = o / DC_ROWS, rr = o % DC_ROWS;
-        const bool live = o < m * DC_ROWS;
-        float e = 0.f;
-        if (live && sh_w2 != nullptr)
-            for (int k = j; k < nsj; k += 8) e += shp[(rr * nsj + k) * m + t];
-        e += __shfl_xor(e, 1, 8);
-        e += __shfl_xor(e, 2, 8);
-        e += __shfl_xor(e, 4, 8);
-        if (live && j == 0) {
-            float v = acc[o];
-            if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
-            out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v + e);
-        }
+    for (int q = tid; q < m * DC_ROWS; q += bd) {   // output (token t, row rr) = q / 8, q % 8
+        const int t = q / DC_ROWS, rr = q % DC_ROWS;
+        float v = acc[q];
+        if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
+        out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v);
     }
 }
 
@@ -408,7 +363,7 @@ hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks
 }
 
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
-                               const uint16_t* sh_w2_bf16, const uint16_t* h_sh_bf16, uint16_t* out, hipStream_t st) {
+                               uint16_t* out, hipStream_t st) {
     const int nsb = a.I / QK;
     const int lanes = DC_ROWS * nsb;                      // per chunk
     const int G = std::max(1, std::min(max_chunks, 1024 / lanes));
@@ -416,10 +371,9 @@ hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int 
     const int rec16 = (int)(decode_rec_bytes(a.I) / 16);
     const int nu = (G * rec16 + threads - 1) / threads;
     const size_t lds = (size_t)std::max(nu, 3) * threads * 16 + (size_t)max_chunks * 16 + (size_t)G * DC_ROWS * nsb * 4 +
-                       (size_t)m * DC_ROWS * 4 + (size_t)G * DC_ROWS * 4 +
-                       (sh_w2_bf16 ? (size_t)DC_ROWS * (a.I / 64) * m * 4 : 0);
+                       (size_t)m * DC_ROWS * 4 + (size_t)G * DC_ROWS * 4;
     return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, G, ys,
-                         sh_w2_bf16, h_sh_bf16, out);
+                         out);
 }
 
 }  // namespace moe

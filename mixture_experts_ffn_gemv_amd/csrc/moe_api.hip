@@ -791,7 +791,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (rc != MOE_OK) return rc;
         if (bf16_shared && !shared_fused && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
         rc = timed(ctx, st, MOE_K_DOWN, [&] {
-            return launch_down_combine(a, P, m, nch, ys, nullptr, nullptr, (uint16_t*)out_bf16, st);
+            return launch_down_combine(a, P, m, nch, ys, (uint16_t*)out_bf16, st);
         });
         if (rc != MOE_OK) return rc;
         return finish_call(ctx, weights_out, idx_out, P, st);

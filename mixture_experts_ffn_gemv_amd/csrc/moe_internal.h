@@ -121,9 +121,9 @@ bool decode_supported(int D, int I);
 size_t decode_rec_bytes(int I);
 // gate/up writing the q8_1 records of h
 hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st);
-// down + weighted combine; a bf16 shared expert's down (W2 bf16 [D, I], h bf16 [m, I]) rides along when given
+// down + weighted combine (+ the shared expert's f32 output ys when given), bf16 store
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
-                               const uint16_t* sh_w2_bf16, const uint16_t* h_sh_bf16, uint16_t* out, hipStream_t st);
+                               uint16_t* out, hipStream_t st);
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int m, int D, int I, const uint16_t* w1,
                                      const uint16_t* w3, uint16_t* h_bf16, float limit, hipStream_t st);
 hipError_t launch_shared_bf16_down(const uint16_t* h_bf16, int m, int D, int I, const uint16_t* w2, float* ys,

@@ -29,6 +29,10 @@ inline int shared_rows_blocks(const SharedRows& sr, int threads) {
     return sr.rows <= 0 || rpw <= 0 ? 0 : (sr.rows + rpw - 1) / rpw;
 }
 
+// 16-byte pieces of a row a lane holds in registers at once (rows of up to 6144
+// values in one round; longer rows take a second, synchronous round)
+constexpr int SR_PIECES = 12;
+
 MOE_DEV float dot2_bf16x(uint32_t a, uint32_t b, float c) {
     typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
@@ -37,8 +41,9 @@ MOE_DEV float dot2_bf16x(uint32_t a, uint32_t b, float c) {
 // Workgroup `blk` of the shared rows: wavefront 2i takes row (row0 + blk * rpw + i)
 // of W1, wavefront 2i + 1 the same row of W3 (rpw = wavefronts / 2). A lane
 // holds 16-byte pieces lane, lane + 64, ... of its row (every load of the
-// wavefront is 1 KB contiguous), dots them with the same pieces of each token
-// row of x, and the wavefront sums; the gate wavefront applies the SwiGLU.
+// wavefront 1 KB contiguous; up to SR_PIECES per round), dots them with the
+// same pieces of each token row of x, and the wavefront sums; the gate
+// wavefront applies the SwiGLU.
 MOE_DEV void shared_gateup_block(const SharedRows& sr, int blk) {
     __shared__ float up[16][8];
     const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -46,35 +51,42 @@ MOE_DEV void shared_gateup_block(const SharedRows& sr, int blk) {
     const int rr = blk * rpw + rl;
     const bool valid = wv < 2 * rpw && rr < sr.rows;
     const int r = sr.row0 + rr;
-    const int n16 = sr.D / 8;   // 16-byte pieces per row (D <= 8192: at most 16 per lane)
+    const int n16 = sr.D / 8;   // 16-byte pieces per row
     float dots[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) dots[t] = 0.f;
     if (valid) {
         const uint4* W = reinterpret_cast<const uint4*>(((wv & 1) ? sr.w3 : sr.w1) + (size_t)r * sr.D);
-        uint4 wq[16];
+        for (int j0 = 0; j0 * 64 < n16; j0 += SR_PIECES) {
+            uint4 wq[SR_PIECES];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int k = lane + 64 * j;
-            wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
+            for (int j = 0; j < SR_PIECES; ++j) {
+                const int k = lane + 64 * (j0 + j);
+                wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if (t >= sr.m) break;
+                const uint4* X = reinterpret_cast<const uint4*>(sr.x + (size_t)t * sr.D);
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < SR_PIECES; ++j) {
+                    const int k = lane + 64 * (j0 + j);
+                    if (k < n16) {
+                        const uint4 xv = X[k];
+                        acc = dot2_bf16x(wq[j].x, xv.x, acc);
+                        acc = dot2_bf16x(wq[j].y, xv.y, acc);
+                        acc = dot2_bf16x(wq[j].z, xv.z, acc);
+                        acc = dot2_bf16x(wq[j].w, xv.w, acc);
+                    }
+                }
+                dots[t] += acc;
+            }
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             if (t >= sr.m) break;
-            const uint4* X = reinterpret_cast<const uint4*>(sr.x + (size_t)t * sr.D);
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int k = lane + 64 * j;
-                if (k < n16) {
-                    const uint4 xv = X[k];
-                    acc = dot2_bf16x(wq[j].x, xv.x, acc);
-                    acc = dot2_bf16x(wq[j].y, xv.y, acc);
-                    acc = dot2_bf16x(wq[j].z, xv.z, acc);
-                    acc = dot2_bf16x(wq[j].w, xv.w, acc);
-                }
-            }
-            dots[t] = wave_sum(acc);
+            dots[t] = wave_sum(dots[t]);
         }
         if ((wv & 1) && lane == 0) {
 #pragma unroll
@@ -100,32 +112,42 @@ MOE_DEV void shared_down_block(const SharedRows& sr, int blk) {
     const int rr = blk * nw + wv;
     if (rr >= sr.rows) return;
     const int r = sr.row0 + rr;
-    const int n16 = sr.I / 8;   // 16-byte pieces per row (I <= 8192: at most 16 per lane)
+    const int n16 = sr.I / 8;   // 16-byte pieces per row
     const uint4* W = reinterpret_cast<const uint4*>(sr.w2 + (size_t)r * sr.I);
-    uint4 wq[16];
+    float dots[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int k = lane + 64 * j;
-        wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
+    for (int t = 0; t < 8; ++t) dots[t] = 0.f;
+    for (int j0 = 0; j0 * 64 < n16; j0 += SR_PIECES) {
+        uint4 wq[SR_PIECES];
+#pragma unroll
+        for (int j = 0; j < SR_PIECES; ++j) {
+            const int k = lane + 64 * (j0 + j);
+            wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t >= sr.m) break;
+            const uint4* H = reinterpret_cast<const uint4*>(sr.h + (size_t)t * sr.I);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < SR_PIECES; ++j) {
+                const int k = lane + 64 * (j0 + j);
+                if (k < n16) {
+                    const uint4 hv = H[k];
+                    acc = dot2_bf16x(wq[j].x, hv.x, acc);
+                    acc = dot2_bf16x(wq[j].y, hv.y, acc);
+                    acc = dot2_bf16x(wq[j].z, hv.z, acc);
+                    acc = dot2_bf16x(wq[j].w, hv.w, acc);
+                }
+            }
+            dots[t] += acc;
+        }
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         if (t >= sr.m) break;
-        const uint4* H = reinterpret_cast<const uint4*>(sr.h + (size_t)t * sr.I);
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int k = lane + 64 * j;
-            if (k < n16) {
-                const uint4 hv = H[k];
-                acc = dot2_bf16x(wq[j].x, hv.x, acc);
-                acc = dot2_bf16x(wq[j].y, hv.y, acc);
-                acc = dot2_bf16x(wq[j].z, hv.z, acc);
-                acc = dot2_bf16x(wq[j].w, hv.w, acc);
-            }
-        }
-        acc = wave_sum(acc);
-        if (lane == 0) sr.ys[(size_t)t * sr.D + r] = acc;
+        const float v = wave_sum(dots[t]);
+        if (lane == 0) sr.ys[(size_t)t * sr.D + r] = v;
     }
 }
 
