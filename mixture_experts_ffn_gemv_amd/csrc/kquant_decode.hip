@@ -32,6 +32,12 @@ constexpr int DC_ROWS = 8;    // output rows per down workgroup: one panel
 // 16-value sums
 MOE_DEV int rec_bytes(int I) { return I + (I / QB) * 4 + (I / 16) * 4; }
 
+// a lane's value from another lane of its 16-lane row (DPP control CTRL)
+template <int CTRL>
+MOE_DEV int dpp16(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
 
 }  // namespace
 
@@ -85,14 +91,15 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
         w3 = base + a.off_w3;
     }
     // the token's q8_1 activations: quants (D bytes), block scales (L f32),
-    // 16-value sums (2L i32), requested first, through registers into LDS
+    // fp16(d) times the 16-value sums (2L f32), requested first, through registers
+    // into LDS
     const int nx16 = (D + 4 * L + 8 * L) / 16;
     const int nxu = (nx16 + bd - 1) / bd;
     uint4 xv0 = make_uint4(0, 0, 0, 0);
     {
         const uint8_t* xq = reinterpret_cast<const uint8_t*>(a.xq + (size_t)ch.token * D);
         const uint8_t* xd = reinterpret_cast<const uint8_t*>(a.xd + (size_t)ch.token * L);
-        const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.xs16 + (size_t)ch.token * 2 * L);
+        const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.xs16f + (size_t)ch.token * 2 * L);
         for (int u = 0; u < nxu; ++u) {
             const int f = u * bd + tid;
             if (f < nx16) {
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
         const uint32_t dd = wq[k][20];
         const uint32_t* xq32 = reinterpret_cast<const uint32_t*>(xl) + s * (QK / 4);
         const float* dxp = reinterpret_cast<const float*>(xl + D) + s * 8;
-        const int* s16p = reinterpret_cast<const int*>(xl + D + 4 * L) + s * 16;
+        const float* s16p = reinterpret_cast<const float*>(xl + D + 4 * L) + s * 16;
         float fs = 0.f, ms = 0.f;
         // q8_1 block t = 4 hh + j of x meets plane j of qs half hh: qs byte b of half
         // hh holds weight 128 hh + 32 j + b in bits 2j..2j+1 (sub-block 2t + b / 16)
@@ -158,10 +165,10 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
             const uint32_t sw = sc[t >> 1] >> (16 * (t & 1));   // scale bytes 2t, 2t + 1
             const int isum = __mul24((int)(sw & 15u), il) + __mul24((int)((sw >> 8) & 15u), ih);
             const float dx = dxp[t];
-            const int2 s16 = reinterpret_cast<const int2*>(s16p)[t];
+            const float2 s16 = reinterpret_cast<const float2*>(s16p)[t];   // fp16(d) * sum per 16
             fs = fmaf((j & 1) ? 0.25f * dx : dx, (float)isum, fs);
-            ms = fmaf((float)((sw >> 4) & 15u), dx * (float)s16.x, ms);
-            ms = fmaf((float)((sw >> 12) & 15u), dx * (float)s16.y, ms);
+            ms = fmaf((float)((sw >> 4) & 15u), s16.x, ms);
+            ms = fmaf((float)((sw >> 12) & 15u), s16.y, ms);
         }
         const float d = half_bits_to_f32(dd & 0xFFFFu), dmin = half_bits_to_f32(dd >> 16);
         red[((p * 2 + m) * PANEL + r) * nsb + s] = fmaf(d, fs, -dmin * ms);
@@ -179,15 +186,21 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
             us += ru[q];
         }
         const float h = swiglu(gs, us, a.limit);
+        // the block's amax across the 32 lanes: within each 16 by DPP, then across the two
         float amax = fabsf(h);
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+        amax = fmaxf(amax, __int_as_float(dpp16<0xB1>(__float_as_int(amax))));    // quad_perm [1,0,3,2]
+        amax = fmaxf(amax, __int_as_float(dpp16<0x4E>(__float_as_int(amax))));    // quad_perm [2,3,0,1]
+        amax = fmaxf(amax, __int_as_float(dpp16<0x124>(__float_as_int(amax))));   // row_ror:4
+        amax = fmaxf(amax, __int_as_float(dpp16<0x128>(__float_as_int(amax))));   // row_ror:8
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 32));
         const float d = amax / 127.0f;
         const int qi = (d == 0.f) ? 0 : (int)roundf(h / d);
         reinterpret_cast<int8_t*>(out + r0)[tid] = (int8_t)qi;
-        int qs = qi;
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) qs += __shfl_xor(qs, off, 16);
+        int qs = qi;   // the 16-value sums, by DPP within each 16
+        qs += dpp16<0xB1>(qs);
+        qs += dpp16<0x4E>(qs);
+        qs += dpp16<0x124>(qs);
+        qs += dpp16<0x128>(qs);
         if (tid == 0) reinterpret_cast<float*>(out + I)[tile] = round_to_fp16(d);
         if ((tid & 15) == 0) reinterpret_cast<int32_t*>(out + I + (I / QB) * 4)[2 * tile + (tid >> 4)] = qs;
     }

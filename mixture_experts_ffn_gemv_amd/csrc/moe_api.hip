@@ -223,7 +223,7 @@ int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int3
     int rc = timed(ctx, st, MOE_K_ROUTER, [&] {
         if (m <= ROUTE_SMALL_MAX_M)
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, nullptr,
-                                       nullptr, nullptr, st);
+                                       nullptr, nullptr, nullptr, st);
         return launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
     });
     if (rc != MOE_OK) return rc;
@@ -704,7 +704,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
-                                       ctx->xd, ctx->xs16, st, shared_fused ? &sr_a : nullptr);
+                                       ctx->xd, ctx->xs16, ctx->xs16f, st, shared_fused ? &sr_a : nullptr);
         });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_TOPK, [&] {

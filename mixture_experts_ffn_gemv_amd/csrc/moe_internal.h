@@ -80,9 +80,11 @@ inline ChunkPlan mmq_chunk_plan(int m, int k, int E, bool shared, bool mixed) {
     return pl;
 }
 
-// router logits for m tokens, plus q8_1 of x in the same launch when xq != NULL
+// router logits for m tokens, plus q8_1 of x in the same launch when xq != NULL (with
+// the per-16 quant sums as i32 and as fp16(d) * sum in f32 when those are non-NULL)
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st, const SharedRows* sr = nullptr);
+                               int8_t* xq, float* xd, int32_t* xs16, float* xs16f, hipStream_t st,
+                               const SharedRows* sr = nullptr);
 // top-k and bucketing in one workgroup, for m * topk <= 512 and m <= 8
 constexpr int ROUTE_SMALL_MAX_M = 8;
 constexpr int ROUTE_SMALL_MAX_PAIRS = 512;

@@ -59,7 +59,7 @@ template <int TT>
 __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __restrict__ x, int m,
                                                            const uint16_t* __restrict__ wr, int D, int E, int ntg,
                                                            float* __restrict__ logits, int8_t* __restrict__ xq,
-                                                           float* __restrict__ xd, int32_t* __restrict__ xs16,
+                                                           float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f,
                                                            SharedRows sr) {
     const int nrouter = E * ntg;
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __res
     }
     if ((int)blockIdx.x >= nrouter) {
         const int b = (blockIdx.x - nrouter) * 256 + threadIdx.x;
-        if (b < m * (D / QB)) quantize_block_bf16(x, b, xq, xd, xs16);
+        if (b < m * (D / QB)) quantize_block_bf16(x, b, xq, xd, xs16, xs16f);
         return;
     }
     const int e = blockIdx.x % E;
@@ -574,17 +574,18 @@ hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const in
 }
 
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                               int8_t* xq, float* xd, int32_t* xs16, hipStream_t st, const SharedRows* sr) {
+                               int8_t* xq, float* xd, int32_t* xs16, float* xs16f, hipStream_t st,
+                               const SharedRows* sr) {
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
     SharedRows none{};
     const SharedRows& s = sr ? *sr : none;
     const int nsh = sr ? shared_rows_blocks(*sr, 256) : 0;
-    if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
-    if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
-    if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, s);
+    if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
+    if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
+    if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
     const int ntg = (m + 7) / 8;
     return launch_kernel(router_quant_kernel<8>, E * ntg + nq + nsh, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd,
-                         xs16, s);
+                         xs16, xs16f, s);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
