@@ -303,9 +303,11 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
                 int il = 0, ih = 0;
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) {
-                    // q3 + 4 = low two bits | high bit << 2, for 4 weights
-                    const uint32_t v = ((B[8 + 8 * hh + cc] >> (2 * j)) & 0x03030303u) |
-                                       (((B[cc] >> (4 * hh + j)) & 0x01010101u) << 2);
+                    // q3 + 4 = low two bits | high bit << 2, for 4 weights (the hmask bit
+                    // of plane 4 hh + j shifted straight to bit 2 of each byte)
+                    const int hs = 4 * hh + j - 2;
+                    const uint32_t hb = (hs >= 0 ? B[cc] >> hs : B[cc] << -hs) & 0x04040404u;
+                    const uint32_t v = ((B[8 + 8 * hh + cc] >> (2 * j)) & 0x03030303u) | hb;
                     if (cc < 4) il = sdot4(v, xv[cc], il);
                     else ih = sdot4(v, xv[cc], ih);
                 }
