@@ -153,6 +153,51 @@ def test_fp4_rejects_kquant_shared():
     assert e.value.code == moe.MOE_EINVAL
 
 
+@pytest.mark.parametrize("dims", [(8192, 2048), (2048, 8192)])
+@pytest.mark.parametrize("m", [1, 3, 12])
+def test_largest_dims(dims, m):
+    # dim or inter at the 8192 limit: the decode kernels' widest workgroups (1024
+    # threads), the bf16 shared rows' second round of pieces, and above 8 tokens
+    # the MMQ tiles or (where the W2 tile does not fit LDS) the GEMV kernels
+    shape = S.LayerShape(dims[0], dims[1], 4, 2)
+    layer = Layer(shape, 8, max_tokens=12)
+    try:
+        check_layer(layer, S.make_tokens(m, shape.dim, 8, index=m), f"dims {dims} m={m}",
+                    sample_rows=None if m <= 3 else [0, m - 1])
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("m", [1, 12])
+def test_fp4_largest_dim(m):
+    shape = S.LayerShape(8192, 2048, 4, 2)        # an 8192-wide row: four pieces per lane
+    layer = Layer(shape, 9, max_tokens=12, expert_fmt="fp4")
+    try:
+        check_layer(layer, S.make_tokens(m, shape.dim, 9, index=m), f"fp4 dims 8192x2048 m={m}",
+                    sample_rows=None if m == 1 else [0, m - 1])
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("m", [1, 5, 20])
+def test_every_expert_picked(m):
+    # k = E: every token picks all 8 experts (the selection is a full sort)
+    layer = Layer(S.LayerShape(256, 256, 8, 8), 10, max_tokens=20)
+    try:
+        check_layer(layer, S.make_tokens(m, 256, 10, index=m), f"k=E m={m}")
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("m", [1, 13])
+def test_single_expert(m):
+    layer = Layer(S.LayerShape(256, 256, 1, 1), 11, max_tokens=13)
+    try:
+        check_layer(layer, S.make_tokens(m, 256, 11, index=m), f"E=1 m={m}")
+    finally:
+        layer.close()
+
+
 def test_tiny_topk1():
     shape = S.LayerShape(256, 256, 16, 1)
     layer = Layer(shape, 3, max_tokens=8)
