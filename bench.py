@@ -60,6 +60,9 @@ WORKLOADS = {
     "prefill_mixed": dict(m=512, layers=1, bias=None, shared="bf16", pool=512, dispatch="mixed",
                           desc="prefill m=512 with groups of <= 8 rows on the GEMV kernels and larger ones on "
                                "MMQ, uniform routing, bf16 shared expert"),
+    "prefill_fp4": dict(m=512, layers=1, bias=None, shared="bf16", pool=512, experts="fp4",
+                        desc="prefill m=512, MXFP4 routed experts on bf16 activations, uniform routing, bf16 "
+                             "shared expert"),
     "prefill_hot": dict(m=512, layers=1, bias="hot", shared="bf16", pool=512,
                         desc="prefill m=512 (MMQ path), 6 hot experts take every token, bf16 shared expert"),
     "skewed": dict(m=2048, layers=1, bias="skewed", shared="bf16", pool=2048, slots=96,
@@ -71,6 +74,7 @@ DOMINANT = {
     "decode": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "small": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "decode_fp4": ("gateup", r"^void moe::fp4_gateup_kernel<1>"),
+    "prefill_fp4": ("gateup", r"^void moe::fp4_gateup_kernel<8>"),
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_mixed": ("gateup", r"^void moe::gateup_q2k_kernel<8>"),    # the groups of <= 8 rows
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class

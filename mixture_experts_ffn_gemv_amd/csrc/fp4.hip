@@ -181,6 +181,232 @@ __global__ __launch_bounds__(FP4_WAVES * 64) void fp4_down_kernel(ExpertArgs a) 
     }
 }
 
+// ------------------------------------------------------------------ batched (matrix cores)
+// Above 8 tokens the chunks of the MMQ size classes run on v_mfma_f32_16x16x32_bf16:
+// the weights are the A operand (16 rows per wavefront, 64 per workgroup), the
+// chunk's token rows the B operand (NS sub-tiles of 16). Per 128-wide K stage the
+// workgroup's code bytes and scale bytes and the chunk's bf16 rows go from global
+// memory straight into LDS (global-to-LDS loads, double-buffered); a lane turns
+// its 8 weights of a 32-block (4 code bytes) into the bf16 A operand with the
+// scaled conversion, so the block scale costs nothing beyond the conversion.
+
+namespace {
+constexpr int FM_ROWS = 64;    // weight rows per workgroup
+constexpr int FM_K = 128;      // K per stage: 4 blocks of 32
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+template <int NS, int NM>
+struct FmLds {   // per buffer: NM matrices' codes [m][row][64 B], scales [m][row][4 B], rows [R][256 B]
+    static constexpr int R = NS * 16;
+    static constexpr int codes = NM * FM_ROWS * (FM_K / 2);
+    static constexpr int sc_off = codes;
+    static constexpr int x_off = sc_off + NM * FM_ROWS * 4;
+    static constexpr int buf = x_off + R * FM_K * 2;
+    static constexpr int bytes = 2 * buf;
+};
+
+// the A operand: 8 weights (4 code bytes, one 32-block's scale) as bf16
+MOE_DEV bf16x8_t fp4_operand(uint32_t codes, float sc) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    u4 w;
+    w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+    w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+    w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+    w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+    return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// One stage's loads into buffer `buf`: NM matrices' 64 rows x 64 code bytes and 4 scale
+// bytes from rows r0.. of each matrix (codes then scales, row length K), and the R
+// bf16 rows' 128 values from `xrow` (one pointer per 16-byte unit of this thread).
+template <int NS, int NM>
+MOE_DEV void fm_stage(uint8_t* buf, const uint8_t* const (&mat)[NM], int r0, int K, int Rows, int kt,
+                      const uint16_t* const (&xsrc)[NS]) {
+    using LL = FmLds<NS, NM>;
+    const int tid = threadIdx.x, wv = tid >> 6;
+    const size_t cb = (size_t)Rows * (K / 2);
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {   // unit p = 256 u + tid: matrix u, row (tid / 4), 16-byte chunk tid % 4
+        const int row = tid >> 2, c = tid & 3;
+        load_lds16(mat[u] + (size_t)(r0 + row) * (K / 2) + kt * (FM_K / 2) + c * 16,
+                   buf + (u * 256 + wv * 64) * 16);
+    }
+    if (tid < NM * FM_ROWS) {        // a lane per (matrix, row): its 4 scale bytes
+        const int m = tid / FM_ROWS, row = tid % FM_ROWS;
+        load_lds4(mat[m] + cb + (size_t)(r0 + row) * (K / 32) + kt * 4, buf + LL::sc_off + (wv * 64) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u)     // unit p = 256 u + tid: token row p / 16, 16-byte chunk p % 16
+        load_lds16(xsrc[u] + kt * FM_K, buf + LL::x_off + (u * 256 + wv * 64) * 16);
+}
+}  // namespace
+
+template <int NS>
+__global__ __launch_bounds__(256) void fp4_mmq_gateup_kernel(ExpertArgs a, int nb) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    using LL = FmLds<NS, 2>;
+    const int D = a.D, I = a.I;
+    const int tiles = I / FM_ROWS;
+    const int nb_act = min(nb, *a.n_chunks * tiles);
+    const int lb = xcd_logical_block(blockIdx.x, nb_act);
+    if (lb >= nb_act) return;
+    const int c = lb / tiles, rt = lb % tiles;
+    const Chunk ch = a.chunks[c];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    const int r0 = rt * FM_ROWS;
+    uint16_t* h = reinterpret_cast<uint16_t*>(a.h_routed);   // bf16 [pairs, I]
+    bool skip;
+    const uint8_t* base = chunk_slice(a, ch, skip);
+    if (skip) return;
+    if (base == nullptr) {
+        if (tid == 0 && rt == 0) atomicOr(a.err, ERR_NOTRESIDENT);
+        for (int q = tid; q < FM_ROWS * ch.nrows; q += 256)
+            h[(size_t)(ch.row0 + q / FM_ROWS) * I + r0 + q % FM_ROWS] = 0;
+        return;
+    }
+    const uint8_t* const mat[2] = {base + a.off_w1, base + a.off_w3};
+    // this thread's token-row units: row (256 u + tid) / 16 (rows past the chunk repeat its last)
+    const uint16_t* xsrc[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int p = u * 256 + tid, t = min(p / 16, ch.nrows - 1);
+        xsrc[u] = a.x16 + (size_t)(a.perm[ch.row0 + t] / a.topk) * D + (p % 16) * 8;
+    }
+    const int ns = min(NS, (ch.nrows + 15) / 16);
+    f4_t accg[NS], accu[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) accg[s] = accu[s] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    const int nk = D / FM_K;
+    const int row = 16 * wv + l16;
+    fm_stage<NS, 2>(smem, mat, r0, D, I, 0, xsrc);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm_loads<0>();   // stage kt is in LDS ...
+        barrier_lds();        // ... for every wave; the other buffer is free
+        const uint8_t* buf = smem + (kt & 1) * LL::buf;
+        if (kt + 1 < nk) fm_stage<NS, 2>(smem + ((kt + 1) & 1) * LL::buf, mat, r0, D, I, kt + 1, xsrc);
+        const uint32_t sw1 = reinterpret_cast<const uint32_t*>(buf + LL::sc_off)[row];
+        const uint32_t sw3 = reinterpret_cast<const uint32_t*>(buf + LL::sc_off)[FM_ROWS + row];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {   // 32-block b of the stage: this lane's K values 8g..8g+7
+            const uint32_t c1 = reinterpret_cast<const uint32_t*>(buf)[row * 16 + 4 * b + g];
+            const uint32_t c3 = reinterpret_cast<const uint32_t*>(buf)[(FM_ROWS + row) * 16 + 4 * b + g];
+            const bf16x8_t A1 = fp4_operand(c1, e8m0_scale((sw1 >> (8 * b)) & 255u));
+            const bf16x8_t A3 = fp4_operand(c3, e8m0_scale((sw3 >> (8 * b)) & 255u));
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (s >= ns) break;
+                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
+                    buf + LL::x_off + (size_t)(16 * s + l16) * (FM_K * 2) + (32 * b + 8 * g) * 2);
+                accg[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, accg[s], 0, 0, 0);
+                accu[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, B, accu[s], 0, 0, 0);
+            }
+        }
+    }
+    wait_vm_loads<0>();   // no load into LDS outlives the workgroup
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int t = 16 * s + l16;
+        if (t < ch.nrows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                h[(size_t)(ch.row0 + t) * I + r0 + 16 * wv + 4 * g + i] =
+                    (uint16_t)f32_to_bf16(swiglu(accg[s][i], accu[s][i], a.limit));
+        }
+    }
+}
+
+template <int NS>
+__global__ __launch_bounds__(256) void fp4_mmq_down_kernel(ExpertArgs a, int nb) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    using LL = FmLds<NS, 1>;
+    const int D = a.D, I = a.I;
+    const int tiles = D / FM_ROWS;
+    const int nb_act = min(nb, *a.n_chunks * tiles);
+    const int lb = xcd_logical_block(blockIdx.x, nb_act);
+    if (lb >= nb_act) return;
+    const int c = lb / tiles, rt = lb % tiles;
+    const Chunk ch = a.chunks[c];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    const int r0 = rt * FM_ROWS;
+    bool skip;
+    const uint8_t* base = chunk_slice(a, ch, skip);
+    if (skip) return;
+    if (base == nullptr) {
+        for (int q = tid; q < FM_ROWS * ch.nrows; q += 256)
+            a.e_rows[(size_t)(ch.row0 + q / FM_ROWS) * D + r0 + q % FM_ROWS] = 0.f;
+        return;
+    }
+    const uint8_t* const mat[1] = {base + a.off_w2};
+    const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.h_routed);
+    const uint16_t* xsrc[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int p = u * 256 + tid, t = min(p / 16, ch.nrows - 1);
+        xsrc[u] = hb + (size_t)(ch.row0 + t) * I + (p % 16) * 8;
+    }
+    const int ns = min(NS, (ch.nrows + 15) / 16);
+    f4_t acc[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[s] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    const int nk = I / FM_K;
+    const int row = 16 * wv + l16;
+    fm_stage<NS, 1>(smem, mat, r0, I, D, 0, xsrc);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm_loads<0>();
+        barrier_lds();
+        const uint8_t* buf = smem + (kt & 1) * LL::buf;
+        if (kt + 1 < nk) fm_stage<NS, 1>(smem + ((kt + 1) & 1) * LL::buf, mat, r0, I, D, kt + 1, xsrc);
+        const uint32_t sw = reinterpret_cast<const uint32_t*>(buf + LL::sc_off)[row];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t c2 = reinterpret_cast<const uint32_t*>(buf)[row * 16 + 4 * b + g];
+            const bf16x8_t A = fp4_operand(c2, e8m0_scale((sw >> (8 * b)) & 255u));
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (s >= ns) break;
+                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
+                    buf + LL::x_off + (size_t)(16 * s + l16) * (FM_K * 2) + (32 * b + 8 * g) * 2);
+                acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[s], 0, 0, 0);
+            }
+        }
+    }
+    wait_vm_loads<0>();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int t = 16 * s + l16;
+        if (t < ch.nrows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.e_rows[(size_t)(ch.row0 + t) * D + r0 + 16 * wv + 4 * g + i] = acc[s][i];
+        }
+    }
+}
+
+bool fp4_mmq_supported(int D, int I) { return D % FM_K == 0 && I % FM_K == 0 && D % FM_ROWS == 0 && I % FM_ROWS == 0; }
+
+template <int NS>
+static hipError_t launch_fp4_mmq_ns(const ExpertArgs& a, int max_chunks, bool gateup, hipStream_t st) {
+    const int nb = max_chunks * (gateup ? a.I / FM_ROWS : a.D / FM_ROWS);
+    const int nb_pad = (nb + 7) / 8 * 8;
+    if (gateup) return launch_kernel(fp4_mmq_gateup_kernel<NS>, nb_pad, 256, (size_t)FmLds<NS, 2>::bytes, st, a, nb);
+    return launch_kernel(fp4_mmq_down_kernel<NS>, nb_pad, 256, (size_t)FmLds<NS, 1>::bytes, st, a, nb);
+}
+
+hipError_t launch_fp4_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st) {
+    for (int c = 0; c < MMQ_CLASSES; ++c) {
+        if (plan.cap[c] <= 0) continue;
+        ExpertArgs ac = a;
+        ac.chunks = a.chunks + plan.base[c];
+        ac.n_chunks = a.n_chunks + c;
+        const hipError_t e = c == 0   ? launch_fp4_mmq_ns<1>(ac, plan.cap[c], gateup, st)
+                             : c == 1 ? launch_fp4_mmq_ns<2>(ac, plan.cap[c], gateup, st)
+                                      : launch_fp4_mmq_ns<4>(ac, plan.cap[c], gateup, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 bool fp4_supported(int D, int I) {
     // a row fits MAXP pieces per lane; the row tiles divide both dims
     return D % 256 == 0 && I % 256 == 0 && D <= MAXP * 64 * FP4_BLOCK && I <= MAXP * 64 * FP4_BLOCK;

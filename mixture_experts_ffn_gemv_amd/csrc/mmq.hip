@@ -38,17 +38,6 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 
 }  // namespace
 
-// Workgroups are dispatched to the 8 XCDs round-robin by id (block b on XCD
-// b % 8). The grid is sized for the most chunks a call can have; the nb_act
-// blocks that have work this call are split into 8 contiguous ranges, one per
-// XCD, so that every XCD gets an equal share and the tiles of one chunk sit on
-// one XCD, whose L2 then holds the chunk's activation rows. Blocks past their
-// XCD's range get nb_act (no work).
-MOE_DEV int xcd_logical_block(int b, int nb_act) {
-    const int per = (nb_act + 7) >> 3;
-    const int i = b >> 3;
-    return i < per ? min((b & 7) * per + i, nb_act) : nb_act;
-}
 
 // ------------------------------------------------------------------ Q2_K gate/up
 // Weights are the A operand (16 rows of W1 and the same 16 rows of W3 per

@@ -310,14 +310,15 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
             ctx->n_cu = prop.multiProcessorCount;
     }
     // K-quant experts: the decode and MMQ kernels where their tiles fit this shape;
-    // MXFP4 experts: their own chunked kernels at every m
+    // MXFP4 experts: their own chunked GEMV kernels up to 8 tokens, their
+    // matrix-core kernels above
     const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
     if (fp4 && !fp4_supported(c.dim, c.inter)) {
         delete ctx;
         return MOE_EINVAL;
     }
     ctx->decode_ok = !fp4 && decode_supported(c.dim, c.inter);
-    ctx->mmq_ok = !fp4 && mmq_supported(c.dim, c.inter);
+    ctx->mmq_ok = fp4 ? fp4_mmq_supported(c.dim, c.inter) : mmq_supported(c.dim, c.inter);
     const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
     const size_t P = M * c.topk;
     ctx->max_pairs = (int)P;
@@ -700,7 +701,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (hipEventRecord(ctx->ev_join, ctx->side) != hipSuccess) return MOE_EHIP;
     }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
-    const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq, ctx->mixed);
+    const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
+    const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq, ctx->mixed && !fp4);
     if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
@@ -806,7 +808,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
             rc = run_wave(ctx, waves, wv, st);
             if (rc != MOE_OK) return rc;
         }
-        if (use_mmq) {
+        if (use_mmq && fp4) {   // bf16 h, no q8_1 step
+            rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_fp4_mmq(a, plan, true, st); });
+            if (rc != MOE_OK) return rc;
+            rc = timed(ctx, st, MOE_K_DOWN, [&] { return launch_fp4_mmq(a, plan, false, st); });
+            if (rc != MOE_OK) return rc;
+        } else if (use_mmq) {
             // a mixed plan's small groups on the GEMV kernels, the rest on MMQ
             ExpertArgs ag = a;
             ag.chunks = a.chunks + plan.base[GEMV_LIST];

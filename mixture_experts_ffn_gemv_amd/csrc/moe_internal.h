@@ -107,6 +107,7 @@ hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chu
 hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, hipStream_t st);
 bool mmq_supported(int D, int I);
 // one launch per class with reserved slots; a.chunks / a.n_chunks point at class 0
+hipError_t launch_fp4_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st);
 hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st);
 hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                               hipStream_t st);
@@ -116,6 +117,8 @@ hipError_t launch_gateup_q2k(const ExpertArgs& a, int rows_max, int max_chunks, 
 // MXFP4 experts: gate/up (h bf16 into h_routed) or down (E rows), chunks of <= rows_max rows
 bool fp4_supported(int D, int I);
 hipError_t launch_fp4(const ExpertArgs& a, int rows_max, int max_chunks, bool gateup, hipStream_t st);
+// MXFP4 experts above 8 tokens: the MMQ chunk classes on bf16 matrix-core tiles
+bool fp4_mmq_supported(int D, int I);
 hipError_t launch_quantize_h(const ExpertArgs& a, int routed_rows, int shared_rows, hipStream_t st);
 hipError_t launch_down_q3k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);
 // decode path (single-row chunks from the small-batch routing)
