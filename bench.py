@@ -73,8 +73,8 @@ WORKLOADS = {
 DOMINANT = {
     "decode": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "small": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
-    "decode_fp4": ("gateup", r"^void moe::fp4_gateup_kernel<1>"),
-    "prefill_fp4": ("gateup", r"^void moe::fp4_gateup_kernel<8>"),
+    "decode_fp4": ("gateup", r"^void moe::fp4_gemv_kernel<2, 1>"),
+    "prefill_fp4": ("gateup", r"^void moe::fp4_mmq_gateup_kernel<1>"),  # the <= 16-row class
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_mixed": ("gateup", r"^void moe::gateup_q2k_kernel<8>"),    # the groups of <= 8 rows
     "prefill_hot": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<4>"),  # the 64-row class
@@ -214,11 +214,16 @@ class Bench:
         self._fp4 = None
 
     def fp4_arena(self):
-        """The 384 experts in MXFP4 (7.2 GB), drawn from the same seeds on first use."""
+        """The 384 experts in MXFP4 (7.2 GB) in the library's tiled slot layout, drawn
+        from the same seeds on first use."""
         if self._fp4 is None:
             t0 = time.time()
-            self._fp4 = self.S.make_experts(self.shape, 1, device=self.dev, fmt="fp4")
+            plain = self.S.make_experts(self.shape, 1, device=self.dev, fmt="fp4")
+            shape, moe = self.shape, self.moe
+            cfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, expert_fmt=moe.MOE_EXPERT_MXFP4)
+            self._fp4 = moe.pack_experts(cfg, plain)
             self.torch.cuda.synchronize()
+            del plain
             log(f"MXFP4 experts drawn in {time.time() - t0:.1f}s ({self._fp4.numel() / 1e9:.2f} GB)")
         return self._fp4
 

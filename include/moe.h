@@ -78,9 +78,10 @@ typedef struct moe_cfg {
  *   "DeepSeek V4.1 · Mixture of experts": float4_e2m1fn_x2 weights): per 32
  *   consecutive weights of a row one E8M0 scale byte 2^(E-127), and 32 e2m1
  *   codes, two per byte with the even weight in the low nibble (the OCP
- *   microscaling layout; the pages give only the element type). A matrix
- *   [rows, cols] is its codes [rows, cols/2] followed by its scales
- *   [rows, cols/32]. The experts run on the unquantised bf16 x with f32
+ *   microscaling layout; the pages give only the element type). In plain
+ *   order a matrix [rows, cols] is its codes [rows, cols/2] followed by its
+ *   scales [rows, cols/32]; slots hold the tiled order of moe_expert_layout
+ *   (moe_pack_expert). The experts run on the unquantised bf16 x with f32
  *   accumulation, h rounded to bf16 before W2. The shared expert must then be
  *   bf16 or none. */
 #define MOE_EXPERT_KQUANT 0
@@ -131,8 +132,11 @@ int moe_destroy(moe_ctx* ctx);
  * per row of B bytes), so that every 8-row tile and every block column of a
  * panel is one contiguous run. moe_pack_expert turns a slice in plain GGUF
  * row order into this layout. With expert_fmt MOE_EXPERT_MXFP4 the slice is
- * [W1 | W3 | W2] of MXFP4 matrices (codes then scales, rows in order; no
- * panels). All four outputs are required. MOE_EINVAL on a bad cfg. */
+ * [W1 | W3 | W2] of MXFP4 matrices, each [rows, cols] in tiles of 64 rows x 128
+ * columns: tile (rows 64i.., columns 128s..) has index t = i * (cols/128) + s,
+ * its codes (64 rows x 64 bytes, row after row) at byte 4096 t of the matrix,
+ * and its scales (64 rows x 4 bytes) at byte rows*cols/2 + 256 t, after all
+ * the codes. All four outputs are required. MOE_EINVAL on a bad cfg. */
 int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, size_t* off_w3,
                       size_t* off_w2);
 
@@ -143,8 +147,10 @@ int moe_expert_layout(const moe_cfg* cfg, size_t* slot_bytes, size_t* off_w1, si
  * arena slices (pack on the device, then copy) and a K-quant shared expert.
  * MOE_EINVAL for a bad cfg, NULL or overlapping buffers; MOE_EHIP on a launch
  * error. (A layout step of this library: the blocks themselves are the
- * pages' GGUF Q2_K / Q3_K blocks, untouched.) For MXFP4 experts the slot layout
- * is the plain one and this is a copy. */
+ * pages' GGUF Q2_K / Q3_K blocks, untouched.) For MXFP4 experts the source is
+ * the plain layout (each matrix's codes [rows, cols/2] then its scales
+ * [rows, cols/32]) and the destination the tiles above; codes and scales are
+ * moved, not changed. */
 int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream);
 
 /* Give the context a caller-owned device arena of n_slots slices of slot_bytes

@@ -3,24 +3,30 @@
 // float4_e2m1fn_x2 weights; config.json expert_dtype "fp4"). The pages give the
 // element type only; the scales follow the OCP microscaling layout: per 32
 // consecutive weights of a row one E8M0 scale 2^(E-127), each weight an e2m1
-// code, two per byte (the even weight in the low nibble). A matrix [rows, cols]
-// is its codes [rows, cols/2] followed by its scales [rows, cols/32]; an expert
-// slice is [W1 | W3 | W2].
+// code, two per byte (the even weight in the low nibble). In plain order a matrix
+// [rows, cols] is its codes [rows, cols/2] followed by its scales [rows, cols/32];
+// an expert slice is [W1 | W3 | W2]. A slot holds each matrix in tiles of 64 rows
+// x 128 columns (fp4_code_off / fp4_scale_off; moe_pack_expert writes them): a
+// tile's 4096 code bytes are one contiguous run, so the batched kernel reads
+// each K stage of its 64 rows as one block of HBM rather than 64 pieces 64
+// bytes long, one per row (which left it near half the streaming rate).
 //
-// The activations stay bf16, as in the excerpt's Linear layers: each lane turns
-// a 16-byte piece of codes (one 32-weight block) into bf16 pairs with the
-// gfx950 scaled conversion (exact: the codes have two significant bits and the
-// scale is a power of two) and dots them with bf16 pairs of x (f32
-// accumulation). h is rounded to bf16 before W2.
+// The activations stay bf16, as in the excerpt's Linear layers: a lane turns 4
+// code bytes (8 weights of one 32-weight block) into a bf16 matrix-core operand
+// with the gfx950 scaled conversion (exact: the codes have two significant bits
+// and the scale is a power of two), and v_mfma_f32_16x16x32_bf16 takes 16 weight
+// rows against 16 token rows (f32 accumulation). h is rounded to bf16 before W2.
 //
-// A chunk holds up to T token rows of one expert (positions row0.. in
-// expert-sorted pick order). The chunk's bf16 rows go into LDS once per
-// workgroup; each wavefront then reads whole rows of the weights (coalesced
-// 16-byte pieces).
-//  fp4_gateup_kernel: a wavefront per row r of h, holding pieces of W1 row r
-//      and W3 row r, so the clamped SwiGLU needs no exchange; h bf16 [pairs, I].
-//  fp4_down_kernel:   a wavefront per output row of W2 against the chunk's h
-//      rows; E f32 [pairs, D], summed per token by the combine kernel.
+// A chunk holds token rows of one expert (positions row0.. in expert-sorted pick
+// order). Two kernels per matrix pair:
+//  fp4_gemv_kernel<NM, T>: chunks of at most T <= 8 rows (decode, small batches); a
+//      workgroup per 16 weight rows, its wavefronts splitting K, each with all
+//      of its loads in flight at once; partial tiles summed in LDS.
+//  fp4_mmq_{gateup,down}_kernel<NS>: the MMQ size classes above 8 tokens; a
+//      workgroup per 64 weight rows streaming K through double-buffered LDS.
+// Gate/up (NM = 2) holds W1 and W3 rows side by side, so the clamped SwiGLU
+// needs no exchange, and writes h bf16 [pairs, I]; down (NM = 1) writes E f32
+// [pairs, D], summed per token by the combine kernel.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -29,72 +35,8 @@ namespace moe {
 namespace {
 
 constexpr int FP4_BLOCK = 32;    // weights per E8M0 scale, and per lane piece (16 code bytes)
-constexpr int FP4_WAVES = 8;     // rows per workgroup (one per wavefront)
-constexpr int MAXP = 4;          // pieces of a row per lane: rows of at most 4 x 64 x 32 = 8192 weights
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 MOE_DEV float e8m0_scale(uint32_t e) { return e == 255u ? __builtin_nanf("") : ldexpf(1.f, (int)e - 127); }
-
-// the 32 weights of a piece as 16 bf16 pairs (pair k: weights 2k, 2k + 1)
-MOE_DEV void piece_to_bf16(const uint4& q, float sc, uint32_t (&w)[16]) {
-    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 0));
-        w[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 1));
-        w[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 2));
-        w[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], sc, 3));
-    }
-}
-
-MOE_DEV float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
-}
-
-// the chunk's token rows of a bf16 matrix [*, K] into LDS (rows past nrows are zero)
-template <int T>
-MOE_DEV void stage_rows(uint4* dst, const uint16_t* src, const int (&row)[T], int nrows, int K) {
-    const int k8 = K / 8;
-    for (int u = threadIdx.x; u < T * k8; u += blockDim.x) {
-        const int i = u / k8, k = u % k8;
-        dst[u] = i < nrows ? reinterpret_cast<const uint4*>(src + (size_t)row[i] * K)[k] : make_uint4(0, 0, 0, 0);
-    }
-}
-
-// one row of an MXFP4 matrix (K weights) against T bf16 rows in LDS: acc[t] += row . x[t]
-template <int T>
-MOE_DEV void row_dot(const uint8_t* codes, const uint8_t* scales, const uint4* xl, int K, float (&acc)[T]) {
-    const int lane = threadIdx.x & 63, np = K / FP4_BLOCK, k8 = K / 8;
-    uint4 q[MAXP];
-    uint32_t e[MAXP];
-#pragma unroll
-    for (int j = 0; j < MAXP; ++j) {
-        const int p = min(lane + 64 * j, np - 1);
-        q[j] = reinterpret_cast<const uint4*>(codes)[p];
-        e[j] = scales[p];
-    }
-#pragma unroll
-    for (int j = 0; j < MAXP; ++j) {
-        const int p = lane + 64 * j;
-        if (p >= np) break;
-        uint32_t w[16];
-        piece_to_bf16(q[j], e8m0_scale(e[j]), w);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint4* xp = xl + (size_t)t * k8 + 4 * p;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 xv = xp[i];
-                acc[t] = dot2(w[4 * i + 0], xv.x, acc[t]);
-                acc[t] = dot2(w[4 * i + 1], xv.y, acc[t]);
-                acc[t] = dot2(w[4 * i + 2], xv.z, acc[t]);
-                acc[t] = dot2(w[4 * i + 3], xv.w, acc[t]);
-            }
-        }
-    }
-}
 
 // the expert's slice, or nullptr (with the chunk's outputs to be zeroed or skipped)
 MOE_DEV const uint8_t* chunk_slice(const ExpertArgs& a, const Chunk& ch, bool& skip) {
@@ -106,89 +48,22 @@ MOE_DEV const uint8_t* chunk_slice(const ExpertArgs& a, const Chunk& ch, bool& s
 
 }  // namespace
 
-template <int T>
-__global__ __launch_bounds__(FP4_WAVES * 64) void fp4_gateup_kernel(ExpertArgs a) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int D = a.D, I = a.I;
-    const int tiles = I / FP4_WAVES;
-    const int c = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-    if (c >= *a.n_chunks) return;
-    const Chunk ch = a.chunks[c];
-    const int lane = threadIdx.x & 63, r = tile * FP4_WAVES + (threadIdx.x >> 6);
-    uint16_t* h = reinterpret_cast<uint16_t*>(a.h_routed);   // bf16 [pairs, I]
-    bool skip;
-    const uint8_t* base = chunk_slice(a, ch, skip);
-    if (skip) return;
-    if (base == nullptr) {   // not resident: flag it, and its rows of h are zero
-        if (threadIdx.x == 0 && tile == 0) atomicOr(a.err, ERR_NOTRESIDENT);
-        if (lane < ch.nrows) h[(size_t)(ch.row0 + lane) * I + r] = 0;
-        return;
-    }
-    int tok[T];
-#pragma unroll
-    for (int i = 0; i < T; ++i) tok[i] = i < ch.nrows ? a.perm[ch.row0 + i] / a.topk : 0;
-    uint4* xl = reinterpret_cast<uint4*>(smem);
-    stage_rows<T>(xl, a.x16, tok, ch.nrows, D);
-    __syncthreads();
-    const size_t cb = (size_t)I * (D / 2);   // code bytes of W1 (scales follow)
-    float g[T], u[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) g[t] = u[t] = 0.f;
-    const uint8_t* w1 = base + a.off_w1;
-    const uint8_t* w3 = base + a.off_w3;
-    row_dot<T>(w1 + (size_t)r * (D / 2), w1 + cb + (size_t)r * (D / FP4_BLOCK), xl, D, g);
-    row_dot<T>(w3 + (size_t)r * (D / 2), w3 + cb + (size_t)r * (D / FP4_BLOCK), xl, D, u);
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float gs = wave_sum(g[t]), us = wave_sum(u[t]);
-        if (lane == t && t < ch.nrows)
-            h[(size_t)(ch.row0 + t) * I + r] = (uint16_t)f32_to_bf16(swiglu(gs, us, a.limit));
-    }
-}
-
-template <int T>
-__global__ __launch_bounds__(FP4_WAVES * 64) void fp4_down_kernel(ExpertArgs a) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int D = a.D, I = a.I;
-    const int tiles = D / FP4_WAVES;
-    const int c = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-    if (c >= *a.n_chunks) return;
-    const Chunk ch = a.chunks[c];
-    const int lane = threadIdx.x & 63, d = tile * FP4_WAVES + (threadIdx.x >> 6);
-    bool skip;
-    const uint8_t* base = chunk_slice(a, ch, skip);
-    if (skip) return;
-    if (base == nullptr) {
-        if (lane < ch.nrows) a.e_rows[(size_t)(ch.row0 + lane) * D + d] = 0.f;
-        return;
-    }
-    int rows[T];
-#pragma unroll
-    for (int i = 0; i < T; ++i) rows[i] = ch.row0 + min(i, ch.nrows - 1);
-    uint4* hl = reinterpret_cast<uint4*>(smem);
-    stage_rows<T>(hl, reinterpret_cast<const uint16_t*>(a.h_routed), rows, ch.nrows, I);
-    __syncthreads();
-    const uint8_t* w2 = base + a.off_w2;
-    const size_t cb = (size_t)D * (I / 2);
-    float e[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) e[t] = 0.f;
-    row_dot<T>(w2 + (size_t)d * (I / 2), w2 + cb + (size_t)d * (I / FP4_BLOCK), hl, I, e);
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float es = wave_sum(e[t]);
-        if (lane == t && t < ch.nrows) a.e_rows[(size_t)(ch.row0 + t) * D + d] = es;
-    }
-}
-
 // ------------------------------------------------------------------ batched (matrix cores)
 // Above 8 tokens the chunks of the MMQ size classes run on v_mfma_f32_16x16x32_bf16:
 // the weights are the A operand (16 rows per wavefront, 64 per workgroup), the
 // chunk's token rows the B operand (NS sub-tiles of 16). Per 128-wide K stage the
 // workgroup's code bytes and scale bytes and the chunk's bf16 rows go from global
-// memory straight into LDS (global-to-LDS loads, double-buffered); a lane turns
-// its 8 weights of a 32-block (4 code bytes) into the bf16 A operand with the
-// scaled conversion, so the block scale costs nothing beyond the conversion.
+// memory straight into LDS (global-to-LDS loads, double-buffered). Lane group g
+// (lanes 16g..16g+15) owns 32-block g of the stage: one 16-byte LDS read gives a
+// lane its row's whole block, and MFMA step j takes the block's weights 8j..8j+7
+// (the sum over K does not depend on which step adds which term), so the B
+// operand of lane (t, g) at step j is token t's values 32g+8j..32g+8j+7. The
+// scaled conversion turns 4 code bytes into the bf16 A operand with the block
+// scale applied, so the scale costs nothing beyond the conversion.
+// LDS banks: the 16 lanes of a group read one block from each of 16 rows, so code
+// block c of row r is stored at slot c ^ ((r >> 2) & 3) of the row's 64 bytes; token
+// rows are 256 bytes, so 16-byte chunk c of row t is stored at chunk c ^ (t & 15).
+// Either way the 16 reads of a lane group fall on distinct banks.
 
 namespace {
 constexpr int FM_ROWS = 64;    // weight rows per workgroup
@@ -196,6 +71,7 @@ constexpr int FM_K = 128;      // K per stage: 4 blocks of 32
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int NS, int NM>
 struct FmLds {   // per buffer: NM matrices' codes [m][row][64 B], scales [m][row][4 B], rows [R][256 B]
@@ -207,7 +83,7 @@ struct FmLds {   // per buffer: NM matrices' codes [m][row][64 B], scales [m][ro
     static constexpr int bytes = 2 * buf;
 };
 
-// the A operand: 8 weights (4 code bytes, one 32-block's scale) as bf16
+// the A operand: 8 weights (4 code bytes of one 32-block, its scale) as bf16
 MOE_DEV bf16x8_t fp4_operand(uint32_t codes, float sc) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     u4 w;
@@ -220,7 +96,8 @@ MOE_DEV bf16x8_t fp4_operand(uint32_t codes, float sc) {
 
 // One stage's loads into buffer `buf`: NM matrices' 64 rows x 64 code bytes and 4 scale
 // bytes from rows r0.. of each matrix (codes then scales, row length K), and the R
-// bf16 rows' 128 values from `xrow` (one pointer per 16-byte unit of this thread).
+// bf16 rows' 128 values from `xsrc` (one pointer per 16-byte unit of this thread,
+// already pointing at the swizzled chunk its LDS slot holds).
 template <int NS, int NM>
 MOE_DEV void fm_stage(uint8_t* buf, const uint8_t* const (&mat)[NM], int r0, int K, int Rows, int kt,
                       const uint16_t* const (&xsrc)[NS]) {
@@ -228,14 +105,13 @@ MOE_DEV void fm_stage(uint8_t* buf, const uint8_t* const (&mat)[NM], int r0, int
     const int tid = threadIdx.x, wv = tid >> 6;
     const size_t cb = (size_t)Rows * (K / 2);
 #pragma unroll
-    for (int u = 0; u < NM; ++u) {   // unit p = 256 u + tid: matrix u, row (tid / 4), 16-byte chunk tid % 4
-        const int row = tid >> 2, c = tid & 3;
-        load_lds16(mat[u] + (size_t)(r0 + row) * (K / 2) + kt * (FM_K / 2) + c * 16,
-                   buf + (u * 256 + wv * 64) * 16);
+    for (int u = 0; u < NM; ++u) {   // unit p = 256 u + tid: matrix u, row tid / 4, slot tid % 4 (swizzled block)
+        const int row = tid >> 2, c = (tid & 3) ^ ((row >> 2) & 3);
+        load_lds16(mat[u] + fp4_code_off(r0 + row, 4 * kt + c, K), buf + (u * 256 + wv * 64) * 16);
     }
     if (tid < NM * FM_ROWS) {        // a lane per (matrix, row): its 4 scale bytes
         const int m = tid / FM_ROWS, row = tid % FM_ROWS;
-        load_lds4(mat[m] + cb + (size_t)(r0 + row) * (K / 32) + kt * 4, buf + LL::sc_off + (wv * 64) * 4);
+        load_lds4(mat[m] + cb + fp4_scale_off(r0 + row, 4 * kt, K), buf + LL::sc_off + (wv * 64) * 4);
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u)     // unit p = 256 u + tid: token row p / 16, 16-byte chunk p % 16
@@ -267,12 +143,14 @@ __global__ __launch_bounds__(256) void fp4_mmq_gateup_kernel(ExpertArgs a, int n
         return;
     }
     const uint8_t* const mat[2] = {base + a.off_w1, base + a.off_w3};
-    // this thread's token-row units: row (256 u + tid) / 16 (rows past the chunk repeat its last)
+    // this thread's token-row units: LDS slot p = 256 u + tid is chunk p % 16 of row
+    // t = p / 16 and holds that row's chunk (p % 16) ^ (t & 15) (rows past the chunk
+    // repeat its last)
     const uint16_t* xsrc[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        const int p = u * 256 + tid, t = min(p / 16, ch.nrows - 1);
-        xsrc[u] = a.x16 + (size_t)(a.perm[ch.row0 + t] / a.topk) * D + (p % 16) * 8;
+        const int p = u * 256 + tid, t = p / 16, tr = min(t, ch.nrows - 1);
+        xsrc[u] = a.x16 + (size_t)(a.perm[ch.row0 + tr] / a.topk) * D + ((p % 16) ^ (t & 15)) * 8;
     }
     const int ns = min(NS, (ch.nrows + 15) / 16);
     f4_t accg[NS], accu[NS];
@@ -286,19 +164,21 @@ __global__ __launch_bounds__(256) void fp4_mmq_gateup_kernel(ExpertArgs a, int n
         barrier_lds();        // ... for every wave; the other buffer is free
         const uint8_t* buf = smem + (kt & 1) * LL::buf;
         if (kt + 1 < nk) fm_stage<NS, 2>(smem + ((kt + 1) & 1) * LL::buf, mat, r0, D, I, kt + 1, xsrc);
-        const uint32_t sw1 = reinterpret_cast<const uint32_t*>(buf + LL::sc_off)[row];
-        const uint32_t sw3 = reinterpret_cast<const uint32_t*>(buf + LL::sc_off)[FM_ROWS + row];
+        // block g of this lane's row in both matrices: 16 code bytes and a scale byte
+        const int slot = g ^ ((row >> 2) & 3);   // row and FM_ROWS + row share (r >> 2) & 3
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(buf + (row * 4 + slot) * 16);
+        const u32x4_t c3 = *reinterpret_cast<const u32x4_t*>(buf + ((FM_ROWS + row) * 4 + slot) * 16);
+        const float s1 = e8m0_scale(buf[LL::sc_off + row * 4 + g]);
+        const float s3 = e8m0_scale(buf[LL::sc_off + (FM_ROWS + row) * 4 + g]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {   // 32-block b of the stage: this lane's K values 8g..8g+7
-            const uint32_t c1 = reinterpret_cast<const uint32_t*>(buf)[row * 16 + 4 * b + g];
-            const uint32_t c3 = reinterpret_cast<const uint32_t*>(buf)[(FM_ROWS + row) * 16 + 4 * b + g];
-            const bf16x8_t A1 = fp4_operand(c1, e8m0_scale((sw1 >> (8 * b)) & 255u));
-            const bf16x8_t A3 = fp4_operand(c3, e8m0_scale((sw3 >> (8 * b)) & 255u));
+        for (int j = 0; j < 4; ++j) {   // step j: the block's weights 8j..8j+7
+            const bf16x8_t A1 = fp4_operand(c1[j], s1);
+            const bf16x8_t A3 = fp4_operand(c3[j], s3);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
                 const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
-                    buf + LL::x_off + (size_t)(16 * s + l16) * (FM_K * 2) + (32 * b + 8 * g) * 2);
+                    buf + LL::x_off + (16 * s + l16) * (FM_K * 2) + (((4 * g + j) ^ l16) * 16));
                 accg[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, accg[s], 0, 0, 0);
                 accu[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, B, accu[s], 0, 0, 0);
             }
@@ -340,11 +220,11 @@ __global__ __launch_bounds__(256) void fp4_mmq_down_kernel(ExpertArgs a, int nb)
     }
     const uint8_t* const mat[1] = {base + a.off_w2};
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.h_routed);
-    const uint16_t* xsrc[NS];
+    const uint16_t* xsrc[NS];   // swizzled like the gate/up kernel's token rows
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        const int p = u * 256 + tid, t = min(p / 16, ch.nrows - 1);
-        xsrc[u] = hb + (size_t)(ch.row0 + t) * I + (p % 16) * 8;
+        const int p = u * 256 + tid, t = p / 16, tr = min(t, ch.nrows - 1);
+        xsrc[u] = hb + (size_t)(ch.row0 + tr) * I + ((p % 16) ^ (t & 15)) * 8;
     }
     const int ns = min(NS, (ch.nrows + 15) / 16);
     f4_t acc[NS];
@@ -358,16 +238,16 @@ __global__ __launch_bounds__(256) void fp4_mmq_down_kernel(ExpertArgs a, int nb)
         barrier_lds();
         const uint8_t* buf = smem + (kt & 1) * LL::buf;
         if (kt + 1 < nk) fm_stage<NS, 1>(smem + ((kt + 1) & 1) * LL::buf, mat, r0, I, D, kt + 1, xsrc);
-        const uint32_t sw = reinterpret_cast<const uint32_t*>(buf + LL::sc_off)[row];
+        const u32x4_t c2 = *reinterpret_cast<const u32x4_t*>(buf + (row * 4 + (g ^ ((row >> 2) & 3))) * 16);
+        const float s2 = e8m0_scale(buf[LL::sc_off + row * 4 + g]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t c2 = reinterpret_cast<const uint32_t*>(buf)[row * 16 + 4 * b + g];
-            const bf16x8_t A = fp4_operand(c2, e8m0_scale((sw >> (8 * b)) & 255u));
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8_t A = fp4_operand(c2[j], s2);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
                 const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
-                    buf + LL::x_off + (size_t)(16 * s + l16) * (FM_K * 2) + (32 * b + 8 * g) * 2);
+                    buf + LL::x_off + (16 * s + l16) * (FM_K * 2) + (((4 * g + j) ^ l16) * 16));
                 acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[s], 0, 0, 0);
             }
         }
@@ -380,6 +260,120 @@ __global__ __launch_bounds__(256) void fp4_mmq_down_kernel(ExpertArgs a, int nb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) a.e_rows[(size_t)(ch.row0 + t) * D + r0 + 16 * wv + 4 * g + i] = acc[s][i];
         }
+    }
+}
+
+// ------------------------------------------------------------------ small chunks (split K)
+// A workgroup per (chunk, 16 weight rows); wavefront w takes K stages
+// FG_SPW w .. FG_SPW w + FG_SPW - 1 (of 128 columns), lane (l16, g) row l16 and
+// block g of each stage, as in the batched kernels. All of a lane's code and
+// scale loads are issued before anything waits (one contiguous 1 KB run per
+// wavefront load: 16 rows x 64 bytes of a tile), then the chunk's token rows go
+// into LDS (row stride K + 8 bf16), and each stage is 4 MFMA steps per matrix
+// with token t's values in B column t (zero for t >= rows). The wavefronts'
+// 16 x 16 partial tiles are summed in LDS.
+constexpr int FG_ROWS = 16;   // weight rows per workgroup
+constexpr int FG_SPW = 4;     // K stages per wavefront: at most 16 wavefronts for K <= 8192
+
+template <int NM, int T>
+__global__ __launch_bounds__(1024) void fp4_gemv_kernel(ExpertArgs a, int nb) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int D = a.D, I = a.I;
+    const int Rows = NM == 2 ? I : D, K = NM == 2 ? D : I;
+    const int tiles = Rows / FG_ROWS;
+    const int nb_act = min(nb, *a.n_chunks * tiles);
+    const int lb = xcd_logical_block(blockIdx.x, nb_act);
+    if (lb >= nb_act) return;
+    const int c = lb / tiles, r0 = (lb % tiles) * FG_ROWS;
+    const Chunk ch = a.chunks[c];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    uint16_t* h = reinterpret_cast<uint16_t*>(a.h_routed);   // bf16 [pairs, I]
+    bool skip;
+    const uint8_t* base = chunk_slice(a, ch, skip);
+    if (skip) return;
+    if (base == nullptr) {   // not resident: flag it, and its outputs are zero
+        if (NM == 2 && tid == 0 && r0 == 0) atomicOr(a.err, ERR_NOTRESIDENT);
+        for (int q = tid; q < FG_ROWS * ch.nrows; q += blockDim.x) {
+            const size_t o = (size_t)(ch.row0 + q / FG_ROWS) * Rows + r0 + q % FG_ROWS;
+            if (NM == 2) h[o] = 0;
+            else a.e_rows[o] = 0.f;
+        }
+        return;
+    }
+    const int nk = K / FM_K, row = r0 + l16;
+    const size_t cb = (size_t)Rows * (K / 2);
+    const uint8_t* mat[NM];
+    mat[0] = base + (NM == 2 ? a.off_w1 : a.off_w2);
+    if (NM == 2) mat[NM - 1] = base + a.off_w3;
+    u32x4_t q[NM][FG_SPW];
+    uint32_t e[NM][FG_SPW];
+#pragma unroll
+    for (int s = 0; s < FG_SPW; ++s) {   // stages past K repeat the last one (in bounds, not used)
+        const int st = min(wv * FG_SPW + s, nk - 1);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            q[m][s] = *reinterpret_cast<const u32x4_t*>(mat[m] + fp4_code_off(row, 4 * st + g, K));
+            e[m][s] = mat[m][cb + fp4_scale_off(row, 4 * st + g, K)];
+        }
+    }
+    // the chunk's token rows (T >= rows): thread k < K / 8 moves 8 values of each
+    // (the workgroup has at least K / 8 threads; loads past the rows or past K repeat
+    // the last, in bounds and unused)
+    const int ld = K + 8, k8 = K / 8, kx = min(tid, k8 - 1);
+    uint16_t* xl = reinterpret_cast<uint16_t*>(smem);
+    uint4 xr[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int tr = ch.row0 + min(t, ch.nrows - 1);
+        const uint16_t* src = NM == 2 ? a.x16 + (size_t)(a.perm[tr] / a.topk) * D : h + (size_t)tr * I;
+        xr[t] = reinterpret_cast<const uint4*>(src)[kx];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        if (t < ch.nrows && tid < k8) *reinterpret_cast<uint4*>(xl + t * ld + 8 * tid) = xr[t];
+    __syncthreads();
+    f4_t acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = (f4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < FG_SPW; ++s) {
+        const int st = wv * FG_SPW + s;
+        if (st >= nk) break;   // uniform per wavefront
+        float sc[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) sc[m] = e8m0_scale(e[m][s]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8_t B = {};
+            if (l16 < T && l16 < ch.nrows)
+                B = *reinterpret_cast<const bf16x8_t*>(xl + l16 * ld + FM_K * st + 32 * g + 8 * j);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4_operand(q[m][s][j], sc[m]), B, acc[m], 0, 0, 0);
+        }
+    }
+    // lane (l16, g) holds rows 4g..4g+3 of column l16; the token rows are done with
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);   // [wavefront][matrix][row 16][column 16]
+    if (l16 < T && l16 < ch.nrows) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[((wv * NM + m) * 16 + 4 * g + i) * 16 + l16] = acc[m][i];
+    }
+    __syncthreads();
+    for (int qq = tid; qq < FG_ROWS * ch.nrows; qq += blockDim.x) {
+        const int rr = qq % FG_ROWS, t = qq / FG_ROWS;
+        float v[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            v[m] = 0.f;
+            for (int w = 0; w < nw; ++w) v[m] += red[((w * NM + m) * 16 + rr) * 16 + t];
+        }
+        const size_t o = (size_t)(ch.row0 + t) * Rows + r0 + rr;
+        if (NM == 2) h[o] = (uint16_t)f32_to_bf16(swiglu(v[0], v[NM - 1], a.limit));
+        else a.e_rows[o] = v[0];
     }
 }
 
@@ -408,17 +402,19 @@ hipError_t launch_fp4_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateu
 }
 
 bool fp4_supported(int D, int I) {
-    // a row fits MAXP pieces per lane; the row tiles divide both dims
-    return D % 256 == 0 && I % 256 == 0 && D <= MAXP * 64 * FP4_BLOCK && I <= MAXP * 64 * FP4_BLOCK;
+    // the 64 x 128 slot tiles divide both dims; K <= 8192 keeps a workgroup within 16 wavefronts
+    return D % 256 == 0 && I % 256 == 0 && D <= FG_SPW * 16 * FM_K && I <= FG_SPW * 16 * FM_K;
 }
 
 template <int T>
 static hipError_t launch_fp4_t(const ExpertArgs& a, int max_chunks, bool gateup, hipStream_t st) {
-    if (gateup)
-        return launch_kernel(fp4_gateup_kernel<T>, max_chunks * (a.I / FP4_WAVES), FP4_WAVES * 64,
-                             (size_t)T * a.D * 2, st, a);
-    return launch_kernel(fp4_down_kernel<T>, max_chunks * (a.D / FP4_WAVES), FP4_WAVES * 64, (size_t)T * a.I * 2,
-                         st, a);
+    const int K = gateup ? a.D : a.I, Rows = gateup ? a.I : a.D;
+    const int nw = (K / FM_K + FG_SPW - 1) / FG_SPW;   // 64 nw >= K / 8 threads
+    const int nb = max_chunks * (Rows / FG_ROWS);
+    const int nb_pad = (nb + 7) / 8 * 8;   // whole rounds over the 8 XCDs
+    const size_t lds = std::max((size_t)T * (K + 8) * 2, (size_t)nw * (gateup ? 2 : 1) * 256 * 4);
+    if (gateup) return launch_kernel(fp4_gemv_kernel<2, T>, nb_pad, nw * 64, lds, st, a, nb);
+    return launch_kernel(fp4_gemv_kernel<1, T>, nb_pad, nw * 64, lds, st, a, nb);
 }
 
 hipError_t launch_fp4(const ExpertArgs& a, int rows_max, int max_chunks, bool gateup, hipStream_t st) {

@@ -268,6 +268,21 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(const uint8_t* __restr
     for (int i = 0; i < B / 2; ++i) out[i] = in[i];
 }
 
+// One thread per 32-weight piece of a rows x K MXFP4 matrix: its 16 code bytes
+// and its scale byte move from plain row order to the tiles of the slot layout.
+__global__ __launch_bounds__(256) void pack_fp4_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                       int rows, int K) {
+    const int np = K / 32;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)rows * np) return;
+    const int r = (int)(q / np), p = (int)(q % np);
+    const size_t cb = (size_t)rows * (K / 2);
+    const uint16_t* in = reinterpret_cast<const uint16_t*>(src + q * 16);
+    uint16_t* out = reinterpret_cast<uint16_t*>(dst + fp4_code_off(r, p, K));
+    for (int i = 0; i < 8; ++i) out[i] = in[i];
+    dst[cb + fp4_scale_off(r, p, K)] = src[cb + q];
+}
+
 int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream) {
     if (check_cfg(cfg) != MOE_OK || src == nullptr || dst == nullptr) return MOE_EINVAL;
     if (((uintptr_t)src | (uintptr_t)dst) & 1) return MOE_EINVAL;
@@ -277,9 +292,17 @@ int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream
     uint8_t* d8 = (uint8_t*)dst;
     if (s8 < d8 + bytes && d8 < s8 + bytes) return MOE_EINVAL;
     const hipStream_t st = (hipStream_t)stream;
-    if (cfg->expert_fmt == MOE_EXPERT_MXFP4)
-        return hipMemcpyAsync(d8, s8, bytes, hipMemcpyDeviceToDevice, st) == hipSuccess ? MOE_OK : MOE_EHIP;
     const int D = cfg->dim, I = cfg->inter;
+    if (cfg->expert_fmt == MOE_EXPERT_MXFP4) {
+        struct F { size_t off; int rows, K; } mats[3] = {{o1, I, D}, {o3, I, D}, {o2, D, I}};
+        for (const F& m : mats) {
+            const int64_t n = (int64_t)m.rows * (m.K / 32);
+            if (hip_status(launch_kernel(pack_fp4_kernel, (int)((n + 255) / 256), 256, 0, st, s8 + m.off, d8 + m.off,
+                                         m.rows, m.K)) != MOE_OK)
+                return MOE_EHIP;
+        }
+        return MOE_OK;
+    }
     struct M { size_t off; int rows, nsb, B; } mats[3] = {
         {o1, I, D / QK, Q2K_BYTES}, {o3, I, D / QK, Q2K_BYTES}, {o2, D, I / QK, Q3K_BYTES}};
     for (const M& m : mats) {

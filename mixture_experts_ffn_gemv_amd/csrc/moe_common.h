@@ -28,6 +28,18 @@ MOE_DEV __host__ int panel_off(int r, int s, int nsb, int B) {
     return ((r / PANEL) * nsb + s) * PANEL * B + (r % PANEL) * B;
 }
 
+// MXFP4 slot layout: a matrix [rows, K] is stored in tiles of 64 rows x 128
+// columns, tile (rows 64i.., columns 128s..) at index i * (K / 128) + s. A tile's
+// code bytes are its 64 rows x 64 bytes, row after row (4096 bytes per tile);
+// after all codes come the scale bytes, 64 rows x 4 per tile in the same order.
+// Piece p of row r is the 16 code bytes and the scale of weights 32p..32p+31.
+MOE_DEV __host__ inline size_t fp4_code_off(int r, int p, int K) {
+    return ((size_t)((r >> 6) * (K >> 7) + (p >> 2)) * 64 + (r & 63)) * 64 + (p & 3) * 16;
+}
+MOE_DEV __host__ inline size_t fp4_scale_off(int r, int p, int K) {   // from the end of the codes
+    return ((size_t)((r >> 6) * (K >> 7) + (p >> 2)) * 64 + (r & 63)) * 4 + (p & 3);
+}
+
 // device error word bits
 constexpr int ERR_NONFINITE = 1;
 constexpr int ERR_NOTRESIDENT = 2;
