@@ -676,9 +676,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     const bool use_mmq = !small && ctx->mmq_ok;
     // decode with every picked expert in its slot: the bf16 shared expert rides in
     // the routing launches, its gate/up rows as extra workgroups of the router
-    // launch, its down rows (into ys, added by the routed down kernel) as extra
-    // workgroups of the top-k launch; no second stream
-    const bool shared_fused = bf16_shared && small && ctx->decode_ok && ctx->host_arena == nullptr;
+    // launch, its down rows (into ys, added by the routed down kernel or, for
+    // MXFP4 experts, by the combine kernel) as extra workgroups of the top-k
+    // launch; no second stream
+    const bool fp4_experts = c.expert_fmt == MOE_EXPERT_MXFP4;
+    const bool shared_fused =
+        bf16_shared && small && (ctx->decode_ok || fp4_experts) && ctx->host_arena == nullptr;
     SharedRows sr_a{}, sr_b{};
     if (shared_fused) {
         sr_a.w1 = (const uint16_t*)w->shared_w1;
