@@ -7,7 +7,11 @@
 //
 // C[M, N] = A[M, K] B[N, K]^T, both operands K-contiguous bf16. Workgroup tile
 // 64 (A rows) x 128 (B rows) x 64 (K), four wavefronts, each owning 32 B rows;
-// v_mfma_f32_16x16x32_bf16 tiles; LDS double buffer with padded rows.
+// v_mfma_f32_16x16x32_bf16 tiles; LDS double buffer with padded rows. The f32
+// output may be split over K (grid z): split s sums K steps [s nk / S,
+// (s + 1) nk / S) into its own partial array; the router's top-k adds them.
+#include <algorithm>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -54,6 +58,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ wa,
                                                         const uint16_t* __restrict__ wb, int N, int K,
                                                         void* __restrict__ out, float limit) {
+    const int nk_all = K / BK, splits = gridDim.z, sidx = blockIdx.z;
+    const int kt0 = sidx * nk_all / splits, nk = (sidx + 1) * nk_all / splits - kt0;
+    if (EPI == EPI_F32) out = reinterpret_cast<float*>(out) + (size_t)sidx * M * N;
     __shared__ __align__(16) uint16_t sA[2][BM * PITCH];
     __shared__ __align__(16) uint16_t sB[2][BN * PITCH];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -62,7 +69,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     const int n0 = blockIdx.x * rows_per_b;
     const int a_valid = M - m0;
     // B rows: EPI_F32 -> wa rows n0..n0+127; EPI_SWIGLU -> wa rows n0..n0+63 then wb rows n0..n0+63
-    const uint16_t* Ab = A + (size_t)m0 * K;
+    const uint16_t* Ab = A + (size_t)m0 * K + kt0 * BK;
+    if (EPI == EPI_F32) wa += kt0 * BK;
 
     uint4 ra[2], rb[4];
     auto load_b = [&](int k0) {
@@ -90,7 +98,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < nk) {
@@ -148,10 +155,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     }
 }
 
-// logits f32 [m, E] = x W_R^T
+// logits f32 [m, E] = x W_R^T, split over K into up to 8 partial arrays while the
+// tiles alone would not give every CU a workgroup and the scratch has room
 hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                              hipStream_t st) {
-    dim3 grid((E + BN - 1) / BN, (m + BM - 1) / BM);
+                              int max_rows, int* splits, hipStream_t st) {
+    const int tiles = ((E + BN - 1) / BN) * ((m + BM - 1) / BM);
+    int s = (256 + tiles - 1) / tiles;
+    s = std::max(1, std::min({s, 8, D / BK, max_rows / m}));
+    *splits = s;
+    dim3 grid((E + BN - 1) / BN, (m + BM - 1) / BM, s);
     return launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, 0, st, x, m, wr, wr, E, D, logits, 0.f);
 }
 

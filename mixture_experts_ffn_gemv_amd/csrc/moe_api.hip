@@ -46,6 +46,7 @@ struct moe_ctx {
     uint8_t* dev = nullptr;
     // scratch views
     float* logits = nullptr;
+    int logit_rows = 0;      // rows of the logits scratch: room for the router's split-K partials
     int32_t* idx = nullptr;
     float* gw = nullptr;
     int8_t* xq = nullptr;
@@ -220,16 +221,18 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
 // router logits and the top-k into (idx, gw) (moe_route)
 int run_route(moe_ctx* ctx, const moe_weights* w, const uint16_t* x, int m, int32_t* idx, float* gw, hipStream_t st) {
     const moe_cfg& c = ctx->cfg;
+    int splits = 1;
     int rc = timed(ctx, st, MOE_K_ROUTER, [&] {
         if (m <= ROUTE_SMALL_MAX_M)
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, nullptr,
                                        nullptr, nullptr, nullptr, st);
-        return launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
+        return launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits,
+                                  ctx->logit_rows, &splits, st);
     });
     if (rc != MOE_OK) return rc;
     return timed(ctx, st, MOE_K_TOPK, [&] {
-        return launch_topk(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp, c.norm_topk_prob,
-                           c.route_scale, idx, gw, ctx->err, st);
+        return launch_topk(ctx->logits, splits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp,
+                           c.norm_topk_prob, c.route_scale, idx, gw, ctx->err, st);
     });
 }
 
@@ -355,7 +358,9 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     layout_of(c, ctx->slot_bytes, ctx->off_w1, ctx->off_w3, ctx->off_w2);
 
     Carver cv;
-    const size_t o_logits = cv.take<float>(M * E);
+    // the router's partial logits: up to 8 splits of m rows, within 4096 rows
+    ctx->logit_rows = (int)std::max<size_t>(M, std::min<size_t>(8 * M, 4096));
+    const size_t o_logits = cv.take<float>((size_t)ctx->logit_rows * E);
     const size_t o_idx = cv.take<int32_t>(P);
     const size_t o_gw = cv.take<float>(P);
     const size_t o_xq = cv.take<int8_t>(M * D);
@@ -679,9 +684,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     // launch, its down rows (into ys, added by the routed down kernel or, for
     // MXFP4 experts, by the combine kernel) as extra workgroups of the top-k
     // launch; no second stream
-    const bool fp4_experts = c.expert_fmt == MOE_EXPERT_MXFP4;
-    const bool shared_fused =
-        bf16_shared && small && (ctx->decode_ok || fp4_experts) && ctx->host_arena == nullptr;
+    const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
+    const bool shared_fused = bf16_shared && small && (ctx->decode_ok || fp4) && ctx->host_arena == nullptr;
     SharedRows sr_a{}, sr_b{};
     if (shared_fused) {
         sr_a.w1 = (const uint16_t*)w->shared_w1;
@@ -727,7 +731,6 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         if (hipEventRecord(ctx->ev_join, ctx->side) != hipSuccess) return MOE_EHIP;
     }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
-    const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
     const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq, ctx->mixed && !fp4);
     if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
@@ -743,15 +746,17 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         });
         if (rc != MOE_OK) return rc;
     } else {
+        int splits = 1;
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
-            hipError_t e = launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, st);
-            if (e != hipSuccess) return e;
+            hipError_t e = launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits,
+                                              ctx->logit_rows, &splits, st);
+            if (e != hipSuccess || fp4) return e;   // MXFP4 experts read x itself
             return launch_quantize_rows(x, m, c.dim, ctx->xq, ctx->xd, ctx->xs16, ctx->xs16f, st);
         });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_TOPK, [&] {
-            return launch_topk(ctx->logits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp, c.norm_topk_prob,
-                               c.route_scale, ctx->idx, ctx->gw, ctx->err, st);
+            return launch_topk(ctx->logits, splits, w->router_bias, m, c.n_routed, c.topk, c.gate_temp,
+                               c.norm_topk_prob, c.route_scale, ctx->idx, ctx->gw, ctx->err, st);
         });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_BUCKET, [&] {

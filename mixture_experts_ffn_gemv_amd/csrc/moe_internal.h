@@ -95,8 +95,9 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
                               const SharedRows* sr = nullptr);
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
                                 float* xs16f, hipStream_t st);
-hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp, int norm,
-                       float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st);
+// logits: `splits` partial arrays [m, E] (from launch_router_gemm), summed in order
+hipError_t launch_topk(const float* logits, int splits, const float* bias, int m, int E, int k, float gate_temp,
+                       int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st);
 // plan == nullptr: one chunk list of at most GEMV_ROWS rows per chunk (n_chunks[0]);
 // otherwise the plan's lists (three MMQ classes, and the GEMV list of a mixed plan)
 // at plan->base[c], counts in n_chunks[c]
@@ -109,8 +110,10 @@ bool mmq_supported(int D, int I);
 // one launch per class with reserved slots; a.chunks / a.n_chunks point at class 0
 hipError_t launch_fp4_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st);
 hipError_t launch_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st);
+// logits [m, E] as `*splits` partial arrays one after another (split K, so that a
+// small m still fills the chip); logits must hold max_rows x E floats
 hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
-                              hipStream_t st);
+                              int max_rows, int* splits, hipStream_t st);
 hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,
                                    const uint16_t* w2, uint16_t* h, float* ys, float limit, hipStream_t st);
 hipError_t launch_gateup_q2k(const ExpertArgs& a, int rows_max, int max_chunks, hipStream_t st);

@@ -204,7 +204,8 @@ MOE_DEV float pick_weight(const float* pick_s, int r, int k, int norm, float rou
 }
 
 // One workgroup per token, thread e owns expert e (blockDim = E rounded up to 64).
-__global__ __launch_bounds__(1024) void topk_rank_kernel(const float* __restrict__ logits,
+// `splits` partial logit arrays [m, E] one after another (their sum is the logits).
+__global__ __launch_bounds__(1024) void topk_rank_kernel(const float* __restrict__ logits, int splits,
                                                          const float* __restrict__ bias, int E, int k,
                                                          float gate_temp, int norm, float route_scale,
                                                          int32_t* __restrict__ idx, float* __restrict__ gw,
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(1024) void topk_rank_kernel(const float* __restrict
     const int e = threadIdx.x;
     float key, s;
     bool bad;
-    score_key(logits + (size_t)t * E, bias, e, E, gate_temp, s, key, bad);
+    score_key(logits + (size_t)t * E, bias, e, E, gate_temp, s, key, bad, splits, (size_t)gridDim.x * E);
     keys[e] = key;                       // threads >= E pad with -inf (never beat a real key)
     if (__any(bad) && (e & 63) == 0) atomicOr(err, ERR_NONFINITE);
     __syncthreads();
@@ -618,10 +619,11 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
                          slot_table, s);
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
+hipError_t launch_topk(const float* logits, int splits, const float* bias, int m, int E, int k, float gate_temp,
                        int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st) {
     const int threads = (E + 63) / 64 * 64;
-    return launch_kernel(topk_rank_kernel, m, threads, 0, st, logits, bias, E, k, gate_temp, norm, route_scale, idx, gw, err);
+    return launch_kernel(topk_rank_kernel, m, threads, 0, st, logits, splits, bias, E, k, gate_temp, norm,
+                         route_scale, idx, gw, err);
 }
 
 hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,

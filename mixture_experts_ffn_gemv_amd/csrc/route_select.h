@@ -16,13 +16,17 @@
 namespace moe {
 
 // A NaN key raises `bad` and is ordered as -inf, so k picks always exist.
+// The logit is the sum of `splits` partial rows `split_stride` floats apart
+// (a split-K router product), added in split order.
 MOE_DEV void score_key(const float* __restrict__ logits_row, const float* __restrict__ bias, int e, int E,
-                       float gate_temp, float& s, float& key, bool& bad) {
+                       float gate_temp, float& s, float& key, bool& bad, int splits = 1, size_t split_stride = 0) {
     key = -INFINITY;
     s = 0.f;
     bad = false;
     if (e < E) {
-        const float z = logits_row[e], b = bias[e];   // both requested before the arithmetic
+        const float b = bias[e];   // requested before the arithmetic
+        float z = logits_row[e];
+        for (int i = 1; i < splits; ++i) z += logits_row[i * split_stride + e];
         const float v = z / gate_temp;
         const float sp = v > 20.f ? v : log1pf(expf(v));
         s = sqrtf(sp);
