@@ -7,9 +7,13 @@
 //
 // C[M, N] = A[M, K] B[N, K]^T, both operands K-contiguous bf16. Workgroup tile
 // 64 (A rows) x 128 (B rows) x 64 (K), four wavefronts, each owning 32 B rows;
-// v_mfma_f32_16x16x32_bf16 tiles; LDS double buffer with padded rows. The f32
-// output may be split over K (grid z): split s sums K steps [s nk / S,
-// (s + 1) nk / S) into its own partial array; the router's top-k adds them.
+// v_mfma_f32_16x16x32_bf16 tiles. Each K step's tiles go from global memory
+// straight into LDS (global-to-LDS loads, 16 bytes per lane), double-buffered:
+// step k + 1 is in flight while step k is multiplied. A tile row is 128 bytes
+// (8 chunks of 16); chunk c of row r is stored at slot c ^ ((r >> 1) & 7), so
+// the 16 rows one operand read touches fall on distinct banks. The f32 output
+// may be split over K (grid z): split s sums K steps [s nk / S, (s + 1) nk / S)
+// into its own partial array; the router's top-k adds them.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -23,30 +27,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int BM = 64, BN = 128, BK = 64;
-constexpr int PITCH = BK + 8;   // bf16 elements per LDS row (16 bytes of padding)
+constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
 
 enum Epilogue { EPI_F32 = 0, EPI_SWIGLU = 1 };
 
-// one 16-byte chunk per (row, k-chunk); 64 x 8 chunks for A, 128 x 8 for B
-MOE_DEV void load_tile(const uint16_t* __restrict__ src, int rows_valid, int ld, int k0, int nrows,
-                       uint16_t* __restrict__ lds, int tid, uint4* regs, int nreg) {
-    for (int q = 0; q < nreg; ++q) {
-        const int c = tid + q * 256;
-        const int row = c >> 3, kc = c & 7;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < nrows && row < rows_valid)
-            v = *reinterpret_cast<const uint4*>(src + (size_t)row * ld + k0 + kc * 8);
-        regs[q] = v;
-    }
-}
-
-MOE_DEV void store_tile(uint16_t* __restrict__ lds, int tid, const uint4* regs, int nreg) {
-    for (int q = 0; q < nreg; ++q) {
-        const int c = tid + q * 256;
-        const int row = c >> 3, kc = c & 7;
-        *reinterpret_cast<uint4*>(lds + row * PITCH + kc * 8) = regs[q];
-    }
-}
+MOE_DEV int swz(int row, int c) { return row * (BK * 2) + ((c ^ ((row >> 1) & 7)) << 4); }
 
 }  // namespace
 
@@ -58,39 +43,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ wa,
                                                         const uint16_t* __restrict__ wb, int N, int K,
                                                         void* __restrict__ out, float limit) {
+    extern __shared__ __align__(16) uint8_t smem[];
     const int nk_all = K / BK, splits = gridDim.z, sidx = blockIdx.z;
     const int kt0 = sidx * nk_all / splits, nk = (sidx + 1) * nk_all / splits - kt0;
     if (EPI == EPI_F32) out = reinterpret_cast<float*>(out) + (size_t)sidx * M * N;
-    __shared__ __align__(16) uint16_t sA[2][BM * PITCH];
-    __shared__ __align__(16) uint16_t sB[2][BN * PITCH];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m0 = blockIdx.y * BM;
     const int rows_per_b = EPI == EPI_SWIGLU ? BN / 2 : BN;
     const int n0 = blockIdx.x * rows_per_b;
-    const int a_valid = M - m0;
-    // B rows: EPI_F32 -> wa rows n0..n0+127; EPI_SWIGLU -> wa rows n0..n0+63 then wb rows n0..n0+63
-    const uint16_t* Ab = A + (size_t)m0 * K + kt0 * BK;
-    if (EPI == EPI_F32) wa += kt0 * BK;
 
-    uint4 ra[2], rb[4];
-    auto load_b = [&](int k0) {
-        if (EPI == EPI_SWIGLU) {
-            // chunks 0..511 -> wa rows, 512..1023 -> wb rows
-            for (int q = 0; q < 4; ++q) {
-                const int c = tid + q * 256;
-                const int row = c >> 3, kc = c & 7;
-                const uint16_t* base = row < 64 ? wa + (size_t)(n0 + row) * K : wb + (size_t)(n0 + row - 64) * K;
-                rb[q] = *reinterpret_cast<const uint4*>(base + k0 + kc * 8);
-            }
-        } else {
-            load_tile(wa + (size_t)n0 * K, N - n0, K, k0, BN, nullptr, tid, rb, 4);
-        }
+    // this thread's 16-byte units: LDS slot p = 256 u + tid holds row p / 8, chunk
+    // (p % 8) ^ ((row >> 1) & 7) of its tile (rows past the matrix repeat its last row;
+    // their products are never stored)
+    const uint16_t* srcA[2];
+    const uint16_t* srcB[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int p = u * 256 + tid, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        srcA[u] = A + (size_t)(m0 + min(row, M - m0 - 1)) * K + kt0 * BK + c * 8;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int p = u * 256 + tid, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+        const uint16_t* base;
+        if (EPI == EPI_SWIGLU) base = row < 64 ? wa + (size_t)(n0 + row) * K : wb + (size_t)(n0 + row - 64) * K;
+        else base = wa + (size_t)(n0 + min(row, N - n0 - 1)) * K;
+        srcB[u] = base + kt0 * BK + c * 8;
+    }
+    auto stage = [&](int kt, uint8_t* buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) load_lds16(srcA[u] + kt * BK, buf + (u * 256 + wv * 64) * 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_lds16(srcB[u] + kt * BK, buf + A_BYTES + (u * 256 + wv * 64) * 16);
     };
-    load_tile(Ab, a_valid, K, 0, BM, nullptr, tid, ra, 2);
-    load_b(0);
-    store_tile(sA[0], tid, ra, 2);
-    store_tile(sB[0], tid, rb, 4);
-    __syncthreads();
 
     f32x4_t acc[4][2];
 #pragma unroll
@@ -98,26 +83,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
+    const int l16 = lane & 15, g = lane >> 4;
+    stage(0, smem);
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            load_tile(Ab, a_valid, K, (kt + 1) * BK, BM, nullptr, tid, ra, 2);
-            load_b((kt + 1) * BK);
-        }
-        const uint16_t* a_s = sA[cur];
-        const uint16_t* b_s = sB[cur];
+        wait_vm_loads<0>();   // step kt is in LDS ...
+        barrier_lds();        // ... for every wave; the other buffer is free
+        const uint8_t* buf = smem + (kt & 1) * STAGE;
+        if (kt + 1 < nk) stage(kt + 1, smem + ((kt + 1) & 1) * STAGE);
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            const int c = 4 * kk + g;   // this lane's K values 32 kk + 8 g .. + 7
             bf16x8_t af[4], bfr[2];
-            const int koff = kk + 8 * (lane >> 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + (16 * i + (lane & 15)) * PITCH + koff);
+            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(buf + swz(16 * i + l16, c));
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 // wave wv owns B rows {16 j' + ...}: for SwiGLU, rows 16 wv.. of wa and the same of wb
                 const int brow = EPI == EPI_SWIGLU ? (j == 0 ? 16 * wv : 64 + 16 * wv) : 32 * wv + 16 * j;
-                bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + (brow + (lane & 15)) * PITCH + koff);
+                bfr[j] = *reinterpret_cast<const bf16x8_t*>(buf + A_BYTES + swz(brow + l16, c));
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -125,12 +108,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) {
-            store_tile(sA[cur ^ 1], tid, ra, 2);
-            store_tile(sB[cur ^ 1], tid, rb, 4);
-        }
-        __syncthreads();
     }
+    wait_vm_loads<0>();   // no load into LDS outlives the workgroup
 
     // C layout: lane holds column (B row) lane % 16 of the 16x16 tile, rows 4 (lane / 16) + r
     const int col = lane & 15;
@@ -164,17 +143,17 @@ hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int 
     s = std::max(1, std::min({s, 8, D / BK, max_rows / m}));
     *splits = s;
     dim3 grid((E + BN - 1) / BN, (m + BM - 1) / BM, s);
-    return launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, 0, st, x, m, wr, wr, E, D, logits, 0.f);
+    return launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, 2 * STAGE, st, x, m, wr, wr, E, D, logits, 0.f);
 }
 
 // h bf16 [m, I] = SwiGLU(x W1^T, x W3^T);  ys f32 [m, D] = h W2^T
 hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,
                                    const uint16_t* w2, uint16_t* h, float* ys, float limit, hipStream_t st) {
     dim3 g1(I / (BN / 2), (m + BM - 1) / BM);
-    hipError_t e = launch_kernel(gemm_bf16_kernel<EPI_SWIGLU>, g1, 256, 0, st, x, m, w1, w3, I, D, h, limit);
+    hipError_t e = launch_kernel(gemm_bf16_kernel<EPI_SWIGLU>, g1, 256, 2 * STAGE, st, x, m, w1, w3, I, D, h, limit);
     if (e != hipSuccess) return e;
     dim3 g2(D / BN, (m + BM - 1) / BM);
-    return launch_kernel(gemm_bf16_kernel<EPI_F32>, g2, 256, 0, st, h, m, w2, w2, D, I, ys, 0.f);
+    return launch_kernel(gemm_bf16_kernel<EPI_F32>, g2, 256, 2 * STAGE, st, h, m, w2, w2, D, I, ys, 0.f);
 }
 
 }  // namespace moe
