@@ -518,7 +518,7 @@ def main():
     layers, tokens = head.pop("_layers"), head.pop("_tokens")
     extra = {}
     if wl == "decode" and not args.no_extra:
-        for other in ("small", "decode_fp4", "prefill", "prefill_mixed", "prefill_hot", "skewed"):
+        for other in ("small", "decode_fp4", "prefill", "prefill_fp4", "prefill_mixed", "prefill_hot", "skewed"):
             st = 100 if WORKLOADS[other]["m"] <= 8 else 5 if other == "skewed" else 10
             wu = 3 if other == "skewed" else 5
             log(f"{other}: {wu} warmup + {st} timed steps")
