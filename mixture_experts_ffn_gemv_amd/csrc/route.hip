@@ -364,11 +364,13 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------- small batches: top-k + bucketing
-// One workgroup of 1024 threads for m <= 8 tokens: the rank selection for
-// floor(1024 / E') tokens at a time (E' = E rounded up to 64), then the
-// bucketing of the m * k picks (counts, offsets, active experts, stable
+// One workgroup of 1024 threads for m <= 8 tokens: every (token, expert) logit
+// is requested at once (thread e loads expert e of each token), then wavefront t
+// takes token t's top-k (the one-wavefront selection, no block barriers), then
+// the bucketing of the m * k picks (counts, offsets, active experts, stable
 // placement, and one single-row chunk per pick, then one per token for a
 // K-quant shared expert) without leaving the workgroup.
+template <int KPL>
 __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ bias, int m, int E, int k,
                                                            float gate_temp, int norm, float route_scale,
@@ -385,35 +387,47 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
         shared_rows_block(sr, blockIdx.x - 1);
         return;
     }
-    __shared__ __align__(16) float keys[1024];
-    __shared__ float cand_key[1024], cand_s[1024];
-    __shared__ int cand_id[1024];
-    __shared__ float pick_s[512];
-    __shared__ int pick_e[512];
+    constexpr int MT = ROUTE_SMALL_MAX_M;
+    __shared__ float keys[MT][64 * KPL], scores[MT][64 * KPL];
+    __shared__ float pick_w[ROUTE_SMALL_MAX_PAIRS];
+    __shared__ int pick_e[ROUTE_SMALL_MAX_PAIRS];
     __shared__ int cnt[1024];
     __shared__ int offs[1025];
     __shared__ int scan_lds[16];
-    __shared__ int ncand;
-    const int tid = threadIdx.x;
-    const int Ep = (E + 63) / 64 * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     bool bad_any = false;
-    for (int t = 0; t < m; ++t) {
-        float s = 0.f, key = -INFINITY;
-        bool bad = false;
-        if (tid < Ep) score_key(logits + (size_t)t * E, bias, tid, E, gate_temp, s, key, bad);
-        if (tid < Ep) keys[tid] = key;
-        bad_any |= bad;
-        __syncthreads();
-        topk_two_step(keys, Ep, key, s, tid, tid < E, k, cand_key, cand_id, cand_s, &ncand, pick_e + t * k,
-                      pick_s + t * k);
+    if (tid < 64 * KPL) {
+        // tokens past m and experts past E repeat the last ones (in bounds, not kept)
+        const int ec = min(tid, E - 1);
+        const float b = bias[ec];
+        float z[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) z[t] = logits[(size_t)min(t, m - 1) * E + ec];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            float sv, kv;
+            bool bad;
+            score_of(z[t], b, gate_temp, sv, kv, bad);
+            keys[t][tid] = kv;
+            scores[t][tid] = sv;
+            bad_any |= bad && t < m && tid < E;
+        }
+    }
+    __syncthreads();
+    if (wv < m) {   // wavefront t: token t's picks, in order, and their weights
+        int my_e;
+        float my_s;
+        wave_topk<KPL>(keys[wv], scores[wv], E, k, my_e, my_s);
+        const float w = wave_pick_weight(my_s, k, norm, route_scale);
+        if (lane < k) {
+            pick_e[wv * k + lane] = my_e;
+            pick_w[wv * k + lane] = w;
+            idx[wv * k + lane] = my_e;
+            gw[wv * k + lane] = w;
+        }
     }
     if (__any(bad_any) && (tid & 63) == 0) atomicOr(err, ERR_NONFINITE);
     const int P = m * k;
-    for (int p = tid; p < P; p += 1024) {
-        const int t = p / k, r = p % k;
-        idx[p] = pick_e[p];
-        gw[p] = pick_weight(pick_s + t * k, r, k, norm, route_scale);
-    }
     cnt[tid] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[pick_e[p]], 1);
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
         c.nrows = 1;
         c.slot = slot_table[pe];
         c.token = p / k;
-        c.weight = pick_weight(pick_s + (p / k) * k, p % k, k, norm, route_scale);
+        c.weight = pick_w[p];
         c.pad0 = c.pad1 = 0;
         chunks[pos] = c;
     }
@@ -614,9 +628,13 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
         return e;
     }
     const int grid = 1 + (sr ? shared_rows_blocks(*sr, 1024) : 0);
-    return launch_kernel(route_small_kernel, grid, 1024, 0, st, logits, bias, m, E, k, gate_temp, norm, route_scale,
-                         idx, gw, err, shared_chunks, offsets, active, n_active, perm, inv, chunks, n_chunks,
-                         slot_table, s);
+#define ROUTE_SMALL(KPL) launch_kernel(route_small_kernel<KPL>, grid, 1024, 0, st, logits, bias, m, E, k, gate_temp, \
+                                       norm, route_scale, idx, gw, err, shared_chunks, offsets, active, n_active, \
+                                       perm, inv, chunks, n_chunks, slot_table, s)
+    const int kpl = topk_kpl(E);
+    const hipError_t e = kpl == 2 ? ROUTE_SMALL(2) : kpl == 6 ? ROUTE_SMALL(6) : ROUTE_SMALL(16);
+#undef ROUTE_SMALL
+    return e;
 }
 
 hipError_t launch_topk(const float* logits, int splits, const float* bias, int m, int E, int k, float gate_temp,

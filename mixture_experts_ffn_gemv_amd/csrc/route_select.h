@@ -15,9 +15,20 @@
 
 namespace moe {
 
-// A NaN key raises `bad` and is ordered as -inf, so k picks always exist.
-// The logit is the sum of `splits` partial rows `split_stride` floats apart
-// (a split-K router product), added in split order.
+// Score and key of logit z with bias b. A NaN key raises `bad` and is ordered
+// as -inf, so k picks always exist.
+MOE_DEV void score_of(float z, float b, float gate_temp, float& s, float& key, bool& bad) {
+    const float v = z / gate_temp;
+    const float sp = v > 20.f ? v : log1pf(expf(v));
+    s = sqrtf(sp);
+    key = s + b;
+    bad = key != key;
+    if (bad) key = -INFINITY;
+}
+
+// Expert e's score and key from a logits row (e >= E: key -inf). The logit is the
+// sum of `splits` partial rows `split_stride` floats apart (a split-K router
+// product), added in split order.
 MOE_DEV void score_key(const float* __restrict__ logits_row, const float* __restrict__ bias, int e, int E,
                        float gate_temp, float& s, float& key, bool& bad, int splits = 1, size_t split_stride = 0) {
     key = -INFINITY;
@@ -27,14 +38,7 @@ MOE_DEV void score_key(const float* __restrict__ logits_row, const float* __rest
         const float b = bias[e];   // requested before the arithmetic
         float z = logits_row[e];
         for (int i = 1; i < splits; ++i) z += logits_row[i * split_stride + e];
-        const float v = z / gate_temp;
-        const float sp = v > 20.f ? v : log1pf(expf(v));
-        s = sqrtf(sp);
-        key = s + b;
-        if (key != key) {
-            bad = true;
-            key = -INFINITY;
-        }
+        score_of(z, b, gate_temp, s, key, bad);
     }
 }
 
