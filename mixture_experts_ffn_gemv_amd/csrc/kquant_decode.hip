@@ -13,9 +13,10 @@
 //      into registers at the start; the epilogue applies the clamped SwiGLU and
 //      writes the q8_1 block the 32 values of h form (no f32 h in memory).
 //  down_combine_kernel: one workgroup = 8 rows of the output dimension for
-//      every chunk. It loads the chunks' q8_1(h) records into LDS and each
-//      lane's Q3_K block into registers, accumulates G * E per token in a
-//      fixed order (the chunks' order, then the shared expert), and stores bf16.
+//      one token's chunks (its picks, then its row of a K-quant shared expert).
+//      It loads their q8_1(h) records into LDS and each lane's Q3_K block into
+//      registers, accumulates G * E in a fixed order (the chunks' order, then
+//      the bf16 shared expert's ys), and stores bf16.
 #include <algorithm>
 
 #include "moe_common.h"
@@ -208,8 +209,10 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
 }
 
 // ------------------------------------------------------------------ Q3_K down + combine
-// One workgroup = one panel of 8 output rows for every chunk; a pass takes G
-// chunks at once. Lanes: tid = r + 8 (s + nsb cl): row r of the panel,
+// One workgroup = one panel of 8 output rows for one token (workgroup b: token
+// b / (D / 8), panel b % (D / 8)); its chunks are the token's k picks (at m = 1
+// every chunk in list order, else the positions inv[] gives, in pick order) and
+// then its K-quant shared-expert row; a pass takes G of them at once. Lanes: tid = r + 8 (s + nsb cl): row r of the panel,
 // superblock s, chunk cl of the pass. A lane loads its 110-byte block straight
 // from global memory into registers (the 8 rows of a superblock column are one
 // contiguous run, so a wavefront reads whole runs), realigns it (blocks start
@@ -218,6 +221,7 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
 // superblocks and the weighted sum over the chunks of each token run in a
 // fixed order (chunks in list order, then the shared expert's f32 output ys,
 // when given).
+template <bool TOK>   // TOK: m > 1, a workgroup per (token, panel); else the one token's chunks in list order
 __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int routed_rows, int m, int max_chunks,
                                                             int G, const float* __restrict__ ys,
                                                             uint16_t* __restrict__ out) {
@@ -225,7 +229,9 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     const int D = a.D, I = a.I;
     const int nsb = I / QK;
     const int rowbytes = nsb * Q3K_BYTES;
-    const int r0 = blockIdx.x * DC_ROWS;
+    const int panels = D / DC_ROWS;
+    const int tsel = TOK ? blockIdx.x / panels : 0;
+    const int r0 = (TOK ? blockIdx.x % panels : blockIdx.x) * DC_ROWS;
     const int tid = threadIdx.x, bd = blockDim.x;
     const int rec = rec_bytes(I);
     const int rec16 = rec / 16;                          // a multiple of 16 bytes (I a multiple of 256)
@@ -237,18 +243,20 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     int* c_tok = c_row + max_chunks;
     float* c_w = reinterpret_cast<float*>(c_tok + max_chunks);
     float* part = c_w + max_chunks;                      // [G][8][nsb]
-    float* acc = part + G * DC_ROWS * nsb;               // [m][8]
-    float* esum = acc + m * DC_ROWS;                     // [G][8]
-    const int nch = min(*a.n_chunks, max_chunks);
+    float* acc = part + G * DC_ROWS * nsb;               // [8]
+    float* esum = acc + DC_ROWS;                         // [G][8]
+    const int k = a.topk;
+    const int nch = TOK ? min(k + (a.sh_w2 != nullptr ? 1 : 0), max_chunks) : min(*a.n_chunks, max_chunks);
     for (int q = tid; q < nch; q += bd) {
-        const Chunk ch = a.chunks[q];
+        const int ci = !TOK ? q : q < k ? a.inv[tsel * k + q] : routed_rows + tsel;
+        const Chunk ch = a.chunks[ci];
         const bool sh = ch.expert < 0;
         c_slot[q] = sh ? -2 : ch.slot;
         c_row[q] = sh ? routed_rows + ch.row0 : ch.row0;
         c_tok[q] = ch.token;
         c_w[q] = ch.weight;
     }
-    for (int q = tid; q < m * DC_ROWS; q += bd) acc[q] = 0.f;
+    for (int q = tid; q < DC_ROWS; q += bd) acc[q] = 0.f;
     __syncthreads();
 
     const int r = tid & 7, sc = tid >> 3, s = sc % nsb, cl = sc / nsb;
@@ -335,22 +343,20 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
             esum[q] = e;
         }
         barrier_lds();
-        if (tid < m * DC_ROWS) {   // token tid / 8, row tid % 8: this pass's chunks in order
-            const int t = tid >> 3, rr = tid & 7;
+        if (tid < DC_ROWS) {   // row tid: this pass's chunks of the token in order
             float v = acc[tid];
             for (int q = 0; q < ng; ++q) {
                 const int c = g0 + q;
-                if (c_tok[c] == t && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + rr], v);
+                if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + tid], v);
             }
             acc[tid] = v;
         }
         barrier_lds();   // the records and partials are reused by the next pass
     }
-    for (int q = tid; q < m * DC_ROWS; q += bd) {   // output (token t, row rr) = q / 8, q % 8
-        const int t = q / DC_ROWS, rr = q % DC_ROWS;
-        float v = acc[q];
-        if (ys != nullptr) v += ys[(size_t)t * D + r0 + rr];
-        out[(size_t)t * D + r0 + rr] = (uint16_t)f32_to_bf16(v);
+    if (tid < DC_ROWS) {
+        float v = acc[tid];
+        if (ys != nullptr) v += ys[(size_t)tsel * D + r0 + tid];
+        out[(size_t)tsel * D + r0 + tid] = (uint16_t)f32_to_bf16(v);
     }
 }
 
@@ -381,14 +387,18 @@ hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int 
                                uint16_t* out, hipStream_t st) {
     const int nsb = a.I / QK;
     const int lanes = DC_ROWS * nsb;                      // per chunk
-    const int G = std::max(1, std::min(max_chunks, 1024 / lanes));
+    const int per_tok = std::min(max_chunks, a.topk + (a.sh_w2 != nullptr ? 1 : 0));
+    const int G = std::max(1, std::min(per_tok, 1024 / lanes));
     const int threads = round64(lanes * G);
     const int rec16 = (int)(decode_rec_bytes(a.I) / 16);
     const int nu = (G * rec16 + threads - 1) / threads;
-    const size_t lds = (size_t)std::max(nu, 3) * threads * 16 + (size_t)max_chunks * 16 + (size_t)G * DC_ROWS * nsb * 4 +
-                       (size_t)m * DC_ROWS * 4 + (size_t)G * DC_ROWS * 4;
-    return launch_kernel(down_combine_kernel, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, max_chunks, G, ys,
-                         out);
+    const size_t lds = (size_t)std::max(nu, 3) * threads * 16 + (size_t)per_tok * 16 + (size_t)G * DC_ROWS * nsb * 4 +
+                       (size_t)DC_ROWS * 4 + (size_t)G * DC_ROWS * 4;
+    if (m == 1)
+        return launch_kernel(down_combine_kernel<false>, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, per_tok,
+                             G, ys, out);
+    return launch_kernel(down_combine_kernel<true>, (a.D / DC_ROWS) * m, threads, lds, st, a, routed_rows, m, per_tok,
+                         G, ys, out);
 }
 
 }  // namespace moe

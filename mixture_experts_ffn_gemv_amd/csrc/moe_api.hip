@@ -770,6 +770,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.chunks = ctx->chunks;
     a.n_chunks = ctx->n_chunks;
     a.perm = ctx->perm;
+    a.inv = ctx->inv;
     a.topk = c.topk;
     a.slot_table = ctx->slot_table_dev;
     a.arena = ctx->arena;

@@ -66,6 +66,7 @@ struct ExpertArgs {
     const Chunk* chunks;
     const int32_t* n_chunks;
     const int32_t* perm;        // position -> pair (token * topk + pick)
+    const int32_t* inv;         // pair -> position (its chunk, on the small-batch routing)
     int32_t topk;
     const int32_t* slot_table;  // expert -> slot or -1
     const uint8_t* arena;
