@@ -118,116 +118,60 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------- top-k
-// rank_e = #{f : key_f > key_e or (key_f == key_e and f < e)} over n (multiple of
-// 16) keys in LDS; the picks are the experts of rank < k, in rank order.
-MOE_DEV int key_rank(const float* keys, int n, float key, int e) {
-    const float4* k4 = reinterpret_cast<const float4*>(keys);
-    int rank = 0;
-    for (int q = 0; q < n / 4; q += 4) {
-        float4 kk[4];
+// The logit of expert e (< E) from `splits` (<= 8) partial arrays `stride` floats
+// apart: all eight loads in flight at once (past `splits` they repeat the last
+// one), then added in split order.
+MOE_DEV float split_logit(const float* __restrict__ row, size_t stride, int splits, int e) {
+    float p[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kk[u] = k4[q + u];
+    for (int i = 0; i < 8; ++i) p[i] = row[(size_t)min(i, splits - 1) * stride + e];
+    float z = p[0];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int f = 4 * (q + u);
-            rank += (kk[u].x > key || (kk[u].x == key && f + 0 < e)) ? 1 : 0;
-            rank += (kk[u].y > key || (kk[u].y == key && f + 1 < e)) ? 1 : 0;
-            rank += (kk[u].z > key || (kk[u].z == key && f + 2 < e)) ? 1 : 0;
-            rank += (kk[u].w > key || (kk[u].w == key && f + 3 < e)) ? 1 : 0;
-        }
-    }
-    return rank;
+    for (int i = 1; i < 8; ++i)
+        if (i < splits) z += p[i];
+    return z;
 }
 
-// Top-k of the n keys in LDS `keys` (n = a multiple of 64, thread e of the group
-// owns key e) in two steps: every wavefront ranks its own 64 keys, the k best
-// of each wavefront become candidates (the overall k best are among them), then
-// each candidate is ranked among all candidates. Writes pick_e / pick_s[0, k).
-// `cand_key` / `cand_id` hold at least n/64 * min(k, 64) entries; `ncand` is an
-// LDS counter. Must be called by every thread of the block (it has barriers);
-// `own` is false for threads outside the group.
-MOE_DEV void topk_two_step(const float* keys, int n, float key, float s, int e, bool own, int k, float* cand_key,
-                           int* cand_id, float* cand_s, int* ncand, int* pick_e, float* pick_s) {
-    const int kw = min(k, 64);
-    if (threadIdx.x == 0) *ncand = 0;
-    __syncthreads();
-    if (own) {
-        const int base = e & ~63;
-        const int wrank = key_rank(keys + base, 64, key, e - base);
-        if (wrank < kw) {
-            const int slot = atomicAdd(ncand, 1);
-            cand_key[slot] = key;
-            cand_id[slot] = e;
-            cand_s[slot] = s;
-        }
-    }
-    __syncthreads();
-    const int nc = *ncand;
-    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-        const float ck = cand_key[c];
-        const int ci = cand_id[c];
-        int rank = 0;
-        int q = 0;
-        for (; q + 8 <= nc; q += 8) {   // eight independent LDS reads per step
-            float qk[8];
-            int qi[8];
+// One wavefront per token (four per workgroup): its keys into LDS, then the
+// one-wavefront top-k (no block barriers). `splits` partial logit arrays [m, E]
+// one after another (the split-K router product); their sum is the logits.
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ logits, int splits,
+                                                        const float* __restrict__ bias, int m, int E, int k,
+                                                        float gate_temp, int norm, float route_scale,
+                                                        int32_t* __restrict__ idx, float* __restrict__ gw,
+                                                        int32_t* __restrict__ err) {
+    __shared__ float keys[4][64 * KPL], scores[4][64 * KPL];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= m) return;   // a whole wavefront; nothing below waits for the others
+    bool bad_any = false;
+    float z[KPL], b[KPL];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                qk[u] = cand_key[q + u];
-                qi[u] = cand_id[q + u];
-            }
+    for (int i = 0; i < KPL; ++i) {   // experts past E repeat the last one (their keys are -inf)
+        const int ec = min(lane + 64 * i, E - 1);
+        b[i] = bias[ec];
+        z[i] = split_logit(logits + (size_t)t * E, (size_t)m * E, splits, ec);
+    }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) rank += (qk[u] > ck || (qk[u] == ck && qi[u] < ci)) ? 1 : 0;
-        }
-        for (; q < nc; ++q) {
-            const float qk = cand_key[q];
-            rank += (qk > ck || (qk == ck && cand_id[q] < ci)) ? 1 : 0;
-        }
-        if (rank < k) {
-            pick_e[rank] = ci;
-            pick_s[rank] = cand_s[c];
-        }
+    for (int i = 0; i < KPL; ++i) {
+        float s, key;
+        bool bad;
+        score_of(z[i], b[i], gate_temp, s, key, bad);
+        const bool in = lane + 64 * i < E;
+        keys[wv][lane + 64 * i] = in ? key : -INFINITY;
+        scores[wv][lane + 64 * i] = s;
+        bad_any |= bad && in;
     }
-    __syncthreads();
-}
-
-// weights: the unbiased scores of the picks, divided by (their sum in pick order
-// + 1e-20) when norm and k > 1, times route_scale
-MOE_DEV float pick_weight(const float* pick_s, int r, int k, int norm, float route_scale) {
-    float wgt = pick_s[r];
-    if (norm && k > 1) {
-        float sum = 0.f;
-        for (int q = 0; q < k; ++q) sum += pick_s[q];
-        wgt = wgt / (sum + 1e-20f);
-    }
-    return wgt * route_scale;
-}
-
-// One workgroup per token, thread e owns expert e (blockDim = E rounded up to 64).
-// `splits` partial logit arrays [m, E] one after another (their sum is the logits).
-__global__ __launch_bounds__(1024) void topk_rank_kernel(const float* __restrict__ logits, int splits,
-                                                         const float* __restrict__ bias, int E, int k,
-                                                         float gate_temp, int norm, float route_scale,
-                                                         int32_t* __restrict__ idx, float* __restrict__ gw,
-                                                         int32_t* __restrict__ err) {
-    __shared__ __align__(16) float keys[1024];
-    __shared__ float cand_key[1024], cand_s[1024];
-    __shared__ int cand_id[1024];
-    __shared__ float pick_s[64];
-    __shared__ int pick_e[64];
-    __shared__ int ncand;
-    const int t = blockIdx.x;
-    const int e = threadIdx.x;
-    float key, s;
-    bool bad;
-    score_key(logits + (size_t)t * E, bias, e, E, gate_temp, s, key, bad, splits, (size_t)gridDim.x * E);
-    keys[e] = key;                       // threads >= E pad with -inf (never beat a real key)
-    if (__any(bad) && (e & 63) == 0) atomicOr(err, ERR_NONFINITE);
-    __syncthreads();
-    topk_two_step(keys, (int)blockDim.x, key, s, e, e < E, k, cand_key, cand_id, cand_s, &ncand, pick_e, pick_s);
-    if (e < k) {
-        idx[(size_t)t * k + e] = pick_e[e];
-        gw[(size_t)t * k + e] = pick_weight(pick_s, e, k, norm, route_scale);
+    if (__any(bad_any) && lane == 0) atomicOr(err, ERR_NONFINITE);
+    __builtin_amdgcn_wave_barrier();   // the wavefront's LDS stores come before its reads of them
+    int my_e;
+    float my_s;
+    wave_topk<KPL>(keys[wv], scores[wv], E, k, my_e, my_s);
+    const float w = wave_pick_weight(my_s, k, norm, route_scale);
+    if (lane < k) {
+        idx[(size_t)t * k + lane] = my_e;
+        gw[(size_t)t * k + lane] = w;
     }
 }
 
@@ -639,9 +583,13 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
 
 hipError_t launch_topk(const float* logits, int splits, const float* bias, int m, int E, int k, float gate_temp,
                        int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st) {
-    const int threads = (E + 63) / 64 * 64;
-    return launch_kernel(topk_rank_kernel, m, threads, 0, st, logits, splits, bias, E, k, gate_temp, norm,
-                         route_scale, idx, gw, err);
+    // a wavefront per token (k <= 64 and E <= 1024, as the configuration checks ensure)
+    const int grid = (m + 3) / 4, kpl = topk_kpl(E);
+#define TOPK_WAVE(KPL) launch_kernel(topk_wave_kernel<KPL>, grid, 256, 0, st, logits, splits, bias, m, E, k, \
+                                     gate_temp, norm, route_scale, idx, gw, err)
+    const hipError_t e = kpl == 2 ? TOPK_WAVE(2) : kpl == 6 ? TOPK_WAVE(6) : TOPK_WAVE(16);
+#undef TOPK_WAVE
+    return e;
 }
 
 hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
