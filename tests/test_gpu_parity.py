@@ -216,6 +216,44 @@ def test_tiny_wide_topk_ragged():
         layer.close()
 
 
+@pytest.mark.parametrize("m", [1, 5, 12])
+def test_widest_routing_layer(m):
+    # E = 1024 experts (16 keys per lane in the one-wavefront selection) and k = 64
+    # picks, the configuration's limits: the m = 1 and m <= 8 routing kernels and,
+    # at m = 12, the split-K router product with the per-token wavefront top-k
+    shape = S.LayerShape(256, 256, 1024, 64)
+    layer = Layer(shape, 12, max_tokens=12, expert_device="cuda")
+    try:
+        check_layer(layer, S.make_tokens(m, 256, 12, index=m), f"E=1024 k=64 m={m}",
+                    sample_rows=None if m <= 5 else [0, m - 1])
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("dim,E,k,m", [(1280, 1024, 64, 200), (1280, 384, 6, 9), (768, 100, 7, 77),
+                                       (256, 1024, 1, 3000)])
+def test_route_only_against_oracle(dim, E, k, m):
+    # routing alone at shapes the layer tests do not reach: the router product split
+    # over K unevenly (dim / 64 = 20 or 12 steps over up to 8 splits), every key
+    # count per lane (2, 6, 16), and m = 3000, where the logits scratch leaves no room
+    # for a second split. The experts are irrelevant here (zero slices).
+    shape = S.LayerShape(dim, 256, E, k)
+    zeros = torch.zeros((E, S.expert_layout(shape)[0]), dtype=torch.uint8, device="cuda")
+    layer = Layer(shape, 13, max_tokens=m, experts=zeros, router_std=0.02)
+    try:
+        x = S.make_tokens(m, dim, 13).cuda()
+        gw = torch.empty(m, k, dtype=torch.float32, device="cuda")
+        idx = torch.empty(m, k, dtype=torch.int32, device="cuda")
+        say(f"[route dim={dim} E={E} k={k} m={m}]")
+        moe.moe_route(layer.ctx, layer.w, x, m, gw, idx)
+        assert layer.check() == moe.MOE_OK
+        ridx, rg, rkeys, _ = layer.oracle_route(x)
+        exempt = compare_routing(idx.cpu().numpy(), gw.cpu().numpy(), ridx, rg, rkeys)
+        say(f"[route dim={dim} E={E} k={k} m={m}] ok ({exempt} near-tie exemptions)")
+    finally:
+        layer.close()
+
+
 def test_tiny_deterministic():
     layer = Layer(S.TINY, 0, max_tokens=16)
     try:
