@@ -22,8 +22,9 @@
 //  fp4_gemv_kernel<NM, T>: chunks of at most T <= 8 rows (decode, small batches); a
 //      workgroup per 16 weight rows, its wavefronts splitting K, each with all
 //      of its loads in flight at once; partial tiles summed in LDS.
-//  fp4_mmq_{gateup,down}_kernel<NS>: the MMQ size classes above 8 tokens; a
-//      workgroup per 64 weight rows streaming K through double-buffered LDS.
+//  fp4_mmq_kernel<NS, DOWN>: the MMQ size classes above 8 tokens; a workgroup
+//      per 64 rows of W1 and of W3 (gate/up) or per 128 rows of W2 (down),
+//      streaming K through double-buffered LDS.
 // Gate/up (NM = 2) holds W1 and W3 rows side by side, so the clamped SwiGLU
 // needs no exchange, and writes h bf16 [pairs, I]; down (NM = 1) writes E f32
 // [pairs, D], summed per token by the combine kernel.
@@ -94,24 +95,24 @@ MOE_DEV bf16x8_t fp4_operand(uint32_t codes, float sc) {
     return __builtin_bit_cast(bf16x8_t, w);
 }
 
-// One stage's loads into buffer `buf`: NM matrices' 64 rows x 64 code bytes and 4 scale
-// bytes from rows r0.. of each matrix (codes then scales, row length K), and the R
-// bf16 rows' 128 values from `xsrc` (one pointer per 16-byte unit of this thread,
-// already pointing at the swizzled chunk its LDS slot holds).
+// One stage's loads into buffer `buf`: NM 64-row tiles' 64 x 64 code bytes and 4 scale
+// bytes per row (tile u: codes from cm[u], scales from sm[u], at rows r0.. of a
+// matrix with rows of K weights), and the R bf16 rows' 128 values from `xsrc` (one
+// pointer per 16-byte unit of this thread, already pointing at the swizzled chunk
+// its LDS slot holds).
 template <int NS, int NM>
-MOE_DEV void fm_stage(uint8_t* buf, const uint8_t* const (&mat)[NM], int r0, int K, int Rows, int kt,
-                      const uint16_t* const (&xsrc)[NS]) {
+MOE_DEV void fm_stage(uint8_t* buf, const uint8_t* const (&cm)[NM], const uint8_t* const (&sm)[NM], int r0, int K,
+                      int kt, const uint16_t* const (&xsrc)[NS]) {
     using LL = FmLds<NS, NM>;
     const int tid = threadIdx.x, wv = tid >> 6;
-    const size_t cb = (size_t)Rows * (K / 2);
 #pragma unroll
-    for (int u = 0; u < NM; ++u) {   // unit p = 256 u + tid: matrix u, row tid / 4, slot tid % 4 (swizzled block)
+    for (int u = 0; u < NM; ++u) {   // unit p = 256 u + tid: tile u, row tid / 4, slot tid % 4 (swizzled block)
         const int row = tid >> 2, c = (tid & 3) ^ ((row >> 2) & 3);
-        load_lds16(mat[u] + fp4_code_off(r0 + row, 4 * kt + c, K), buf + (u * 256 + wv * 64) * 16);
+        load_lds16(cm[u] + fp4_code_off(r0 + row, 4 * kt + c, K), buf + (u * 256 + wv * 64) * 16);
     }
-    if (tid < NM * FM_ROWS) {        // a lane per (matrix, row): its 4 scale bytes
+    if (tid < NM * FM_ROWS) {        // a lane per (tile, row): its 4 scale bytes
         const int m = tid / FM_ROWS, row = tid % FM_ROWS;
-        load_lds4(mat[m] + cb + fp4_scale_off(r0 + row, 4 * kt, K), buf + LL::sc_off + (wv * 64) * 4);
+        load_lds4(sm[m] + fp4_scale_off(r0 + row, 4 * kt, K), buf + LL::sc_off + (wv * 64) * 4);
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u)     // unit p = 256 u + tid: token row p / 16, 16-byte chunk p % 16
@@ -119,30 +120,52 @@ MOE_DEV void fm_stage(uint8_t* buf, const uint8_t* const (&mat)[NM], int r0, int
 }
 }  // namespace
 
-template <int NS>
-__global__ __launch_bounds__(256) void fp4_mmq_gateup_kernel(ExpertArgs a, int nb) {
+// Gate/up (DOWN false): tile 0 is 64 rows of W1, tile 1 the same rows of W3, the
+// B operand the tokens' x rows, and h = bf16(SwiGLU) of the two. Down (DOWN true):
+// tiles 0 and 1 are 128 consecutive rows of W2 (r0.. and r0 + 64..), the B operand
+// the chunk's bf16 h rows, and both tiles' products go to E f32 [pairs, D].
+template <int NS, bool DOWN>
+__global__ __launch_bounds__(256) void fp4_mmq_kernel(ExpertArgs a, int nb) {
     extern __shared__ __align__(16) uint8_t smem[];
     using LL = FmLds<NS, 2>;
     const int D = a.D, I = a.I;
-    const int tiles = I / FM_ROWS;
+    const int Rows = DOWN ? D : I, K = DOWN ? I : D;
+    const int rows_wg = DOWN ? 2 * FM_ROWS : FM_ROWS;
+    const int tiles = Rows / rows_wg;
     const int nb_act = min(nb, *a.n_chunks * tiles);
     const int lb = xcd_logical_block(blockIdx.x, nb_act);
     if (lb >= nb_act) return;
     const int c = lb / tiles, rt = lb % tiles;
     const Chunk ch = a.chunks[c];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
-    const int r0 = rt * FM_ROWS;
+    const int r0 = rt * rows_wg;
     uint16_t* h = reinterpret_cast<uint16_t*>(a.h_routed);   // bf16 [pairs, I]
     bool skip;
     const uint8_t* base = chunk_slice(a, ch, skip);
     if (skip) return;
-    if (base == nullptr) {
-        if (tid == 0 && rt == 0) atomicOr(a.err, ERR_NOTRESIDENT);
-        for (int q = tid; q < FM_ROWS * ch.nrows; q += 256)
-            h[(size_t)(ch.row0 + q / FM_ROWS) * I + r0 + q % FM_ROWS] = 0;
+    if (base == nullptr) {   // not resident: flag it (gate/up), and the outputs are zero
+        if (!DOWN && tid == 0 && rt == 0) atomicOr(a.err, ERR_NOTRESIDENT);
+        for (int q = tid; q < rows_wg * ch.nrows; q += 256) {
+            const size_t o = (size_t)(ch.row0 + q / rows_wg) * Rows + r0 + q % rows_wg;
+            if (DOWN) a.e_rows[o] = 0.f;
+            else h[o] = 0;
+        }
         return;
     }
-    const uint8_t* const mat[2] = {base + a.off_w1, base + a.off_w3};
+    const size_t cb = (size_t)Rows * (K / 2);   // code bytes of a matrix (its scales follow)
+    const uint8_t* cm[2];
+    const uint8_t* sm[2];
+    if (DOWN) {   // the second tile: one tile row further on, in the codes and in the scales
+        cm[0] = base + a.off_w2;
+        cm[1] = cm[0] + (size_t)(K / FM_K) * 4096;
+        sm[0] = cm[0] + cb;
+        sm[1] = sm[0] + (size_t)(K / FM_K) * 256;
+    } else {
+        cm[0] = base + a.off_w1;
+        cm[1] = base + a.off_w3;
+        sm[0] = cm[0] + cb;
+        sm[1] = cm[1] + cb;
+    }
     // this thread's token-row units: LDS slot p = 256 u + tid is chunk p % 16 of row
     // t = p / 16 and holds that row's chunk (p % 16) ^ (t & 15) (rows past the chunk
     // repeat its last)
@@ -150,37 +173,39 @@ __global__ __launch_bounds__(256) void fp4_mmq_gateup_kernel(ExpertArgs a, int n
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
         const int p = u * 256 + tid, t = p / 16, tr = min(t, ch.nrows - 1);
-        xsrc[u] = a.x16 + (size_t)(a.perm[ch.row0 + tr] / a.topk) * D + ((p % 16) ^ (t & 15)) * 8;
+        const int sw = ((p % 16) ^ (t & 15)) * 8;
+        xsrc[u] = DOWN ? h + (size_t)(ch.row0 + tr) * I + sw
+                       : a.x16 + (size_t)(a.perm[ch.row0 + tr] / a.topk) * D + sw;
     }
     const int ns = min(NS, (ch.nrows + 15) / 16);
-    f4_t accg[NS], accu[NS];
+    f4_t acc0[NS], acc1[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) accg[s] = accu[s] = (f4_t){0.f, 0.f, 0.f, 0.f};
-    const int nk = D / FM_K;
+    for (int s = 0; s < NS; ++s) acc0[s] = acc1[s] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    const int nk = K / FM_K;
     const int row = 16 * wv + l16;
-    fm_stage<NS, 2>(smem, mat, r0, D, I, 0, xsrc);
+    fm_stage<NS, 2>(smem, cm, sm, r0, K, 0, xsrc);
     for (int kt = 0; kt < nk; ++kt) {
         wait_vm_loads<0>();   // stage kt is in LDS ...
         barrier_lds();        // ... for every wave; the other buffer is free
         const uint8_t* buf = smem + (kt & 1) * LL::buf;
-        if (kt + 1 < nk) fm_stage<NS, 2>(smem + ((kt + 1) & 1) * LL::buf, mat, r0, D, I, kt + 1, xsrc);
-        // block g of this lane's row in both matrices: 16 code bytes and a scale byte
+        if (kt + 1 < nk) fm_stage<NS, 2>(smem + ((kt + 1) & 1) * LL::buf, cm, sm, r0, K, kt + 1, xsrc);
+        // block g of this lane's row in both tiles: 16 code bytes and a scale byte
         const int slot = g ^ ((row >> 2) & 3);   // row and FM_ROWS + row share (r >> 2) & 3
-        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(buf + (row * 4 + slot) * 16);
-        const u32x4_t c3 = *reinterpret_cast<const u32x4_t*>(buf + ((FM_ROWS + row) * 4 + slot) * 16);
-        const float s1 = e8m0_scale(buf[LL::sc_off + row * 4 + g]);
-        const float s3 = e8m0_scale(buf[LL::sc_off + (FM_ROWS + row) * 4 + g]);
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(buf + (row * 4 + slot) * 16);
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(buf + ((FM_ROWS + row) * 4 + slot) * 16);
+        const float s0 = e8m0_scale(buf[LL::sc_off + row * 4 + g]);
+        const float s1 = e8m0_scale(buf[LL::sc_off + (FM_ROWS + row) * 4 + g]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {   // step j: the block's weights 8j..8j+7
+            const bf16x8_t A0 = fp4_operand(c0[j], s0);
             const bf16x8_t A1 = fp4_operand(c1[j], s1);
-            const bf16x8_t A3 = fp4_operand(c3[j], s3);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s >= ns) break;
                 const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
                     buf + LL::x_off + (16 * s + l16) * (FM_K * 2) + (((4 * g + j) ^ l16) * 16));
-                accg[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, accg[s], 0, 0, 0);
-                accu[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, B, accu[s], 0, 0, 0);
+                acc0[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc0[s], 0, 0, 0);
+                acc1[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc1[s], 0, 0, 0);
             }
         }
     }
@@ -190,75 +215,15 @@ __global__ __launch_bounds__(256) void fp4_mmq_gateup_kernel(ExpertArgs a, int n
         const int t = 16 * s + l16;
         if (t < ch.nrows) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                h[(size_t)(ch.row0 + t) * I + r0 + 16 * wv + 4 * g + i] =
-                    (uint16_t)f32_to_bf16(swiglu(accg[s][i], accu[s][i], a.limit));
-        }
-    }
-}
-
-template <int NS>
-__global__ __launch_bounds__(256) void fp4_mmq_down_kernel(ExpertArgs a, int nb) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    using LL = FmLds<NS, 1>;
-    const int D = a.D, I = a.I;
-    const int tiles = D / FM_ROWS;
-    const int nb_act = min(nb, *a.n_chunks * tiles);
-    const int lb = xcd_logical_block(blockIdx.x, nb_act);
-    if (lb >= nb_act) return;
-    const int c = lb / tiles, rt = lb % tiles;
-    const Chunk ch = a.chunks[c];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, g = lane >> 4;
-    const int r0 = rt * FM_ROWS;
-    bool skip;
-    const uint8_t* base = chunk_slice(a, ch, skip);
-    if (skip) return;
-    if (base == nullptr) {
-        for (int q = tid; q < FM_ROWS * ch.nrows; q += 256)
-            a.e_rows[(size_t)(ch.row0 + q / FM_ROWS) * D + r0 + q % FM_ROWS] = 0.f;
-        return;
-    }
-    const uint8_t* const mat[1] = {base + a.off_w2};
-    const uint16_t* hb = reinterpret_cast<const uint16_t*>(a.h_routed);
-    const uint16_t* xsrc[NS];   // swizzled like the gate/up kernel's token rows
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const int p = u * 256 + tid, t = p / 16, tr = min(t, ch.nrows - 1);
-        xsrc[u] = hb + (size_t)(ch.row0 + tr) * I + ((p % 16) ^ (t & 15)) * 8;
-    }
-    const int ns = min(NS, (ch.nrows + 15) / 16);
-    f4_t acc[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) acc[s] = (f4_t){0.f, 0.f, 0.f, 0.f};
-    const int nk = I / FM_K;
-    const int row = 16 * wv + l16;
-    fm_stage<NS, 1>(smem, mat, r0, I, D, 0, xsrc);
-    for (int kt = 0; kt < nk; ++kt) {
-        wait_vm_loads<0>();
-        barrier_lds();
-        const uint8_t* buf = smem + (kt & 1) * LL::buf;
-        if (kt + 1 < nk) fm_stage<NS, 1>(smem + ((kt + 1) & 1) * LL::buf, mat, r0, I, D, kt + 1, xsrc);
-        const u32x4_t c2 = *reinterpret_cast<const u32x4_t*>(buf + (row * 4 + (g ^ ((row >> 2) & 3))) * 16);
-        const float s2 = e8m0_scale(buf[LL::sc_off + row * 4 + g]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8_t A = fp4_operand(c2[j], s2);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (s >= ns) break;
-                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(
-                    buf + LL::x_off + (16 * s + l16) * (FM_K * 2) + (((4 * g + j) ^ l16) * 16));
-                acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[s], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const size_t o = (size_t)(ch.row0 + t) * Rows + r0 + 16 * wv + 4 * g + i;
+                if (DOWN) {
+                    a.e_rows[o] = acc0[s][i];
+                    a.e_rows[o + FM_ROWS] = acc1[s][i];
+                } else {
+                    h[o] = (uint16_t)f32_to_bf16(swiglu(acc0[s][i], acc1[s][i], a.limit));
+                }
             }
-        }
-    }
-    wait_vm_loads<0>();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int t = 16 * s + l16;
-        if (t < ch.nrows) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.e_rows[(size_t)(ch.row0 + t) * D + r0 + 16 * wv + 4 * g + i] = acc[s][i];
         }
     }
 }
@@ -377,14 +342,14 @@ __global__ __launch_bounds__(1024) void fp4_gemv_kernel(ExpertArgs a, int nb) {
     }
 }
 
-bool fp4_mmq_supported(int D, int I) { return D % FM_K == 0 && I % FM_K == 0 && D % FM_ROWS == 0 && I % FM_ROWS == 0; }
+bool fp4_mmq_supported(int D, int I) { return D % FM_K == 0 && I % FM_K == 0 && D % (2 * FM_ROWS) == 0 && I % FM_ROWS == 0; }
 
 template <int NS>
 static hipError_t launch_fp4_mmq_ns(const ExpertArgs& a, int max_chunks, bool gateup, hipStream_t st) {
-    const int nb = max_chunks * (gateup ? a.I / FM_ROWS : a.D / FM_ROWS);
+    const int nb = max_chunks * (gateup ? a.I / FM_ROWS : a.D / (2 * FM_ROWS));
     const int nb_pad = (nb + 7) / 8 * 8;
-    if (gateup) return launch_kernel(fp4_mmq_gateup_kernel<NS>, nb_pad, 256, (size_t)FmLds<NS, 2>::bytes, st, a, nb);
-    return launch_kernel(fp4_mmq_down_kernel<NS>, nb_pad, 256, (size_t)FmLds<NS, 1>::bytes, st, a, nb);
+    if (gateup) return launch_kernel(fp4_mmq_kernel<NS, false>, nb_pad, 256, (size_t)FmLds<NS, 2>::bytes, st, a, nb);
+    return launch_kernel(fp4_mmq_kernel<NS, true>, nb_pad, 256, (size_t)FmLds<NS, 2>::bytes, st, a, nb);
 }
 
 hipError_t launch_fp4_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateup, hipStream_t st) {
