@@ -332,37 +332,41 @@ class Bench:
             raise RuntimeError(f"{wl} timed region: {moe.strerror(rc)}")
         stats = moe.moe_get_stats(ctx)
 
-        # decode: the same steps replayed from HIP graphs (one per layer, captured
-        # with a fixed input buffer that each step's token is copied into first)
+        # decode: the same steps replayed from one HIP graph holding a forward of every
+        # layer in the rotation (each layer reads its own fixed input buffer); before
+        # each replay one copy fills the buffers with the next tokens of the pool
         graph_ms = None
         if m <= 8 and not streamed:
-            x_static = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
-            out_static = torch.empty((m, shape.dim), dtype=torch.bfloat16, device=self.dev)
-            x_static.copy_(xs(0))
-            graphs = []
-            for lay in layers:
-                moe.moe_forward(ctx, lay["w"], x_static, m, out_static)
-                torch.cuda.synchronize()
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    moe.moe_forward(ctx, lay["w"], x_static, m, out_static)
-                graphs.append(g)
-            for i in range(warmup):
-                x_static.copy_(xs(i))
-                graphs[i % n_layers].replay()
+            x_static = torch.empty((n_layers, m, shape.dim), dtype=torch.bfloat16, device=self.dev)
+            out_static = torch.empty((n_layers, m, shape.dim), dtype=torch.bfloat16, device=self.dev)
+            rounds = (steps + n_layers - 1) // n_layers
+            w_rounds = max(1, (warmup + n_layers - 1) // n_layers)
+            inputs = [torch.stack([xs(r * n_layers + li) for li in range(n_layers)])
+                      for r in range(w_rounds + rounds)]
+            x_static.copy_(inputs[0])
+            for li, lay in enumerate(layers):
+                moe.moe_forward(ctx, lay["w"], x_static[li], m, out_static[li])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for li, lay in enumerate(layers):
+                    moe.moe_forward(ctx, lay["w"], x_static[li], m, out_static[li])
+            for r in range(w_rounds):
+                x_static.copy_(inputs[r])
+                g.replay()
             torch.cuda.synchronize()
             gs = torch.cuda.current_stream()
             ev0.record(gs)
-            for i in range(steps):
-                x_static.copy_(xs(warmup + i))
-                graphs[(warmup + i) % n_layers].replay()
+            for r in range(rounds):
+                x_static.copy_(inputs[w_rounds + r])
+                g.replay()
             ev1.record(gs)
             torch.cuda.synchronize()
-            graph_ms = ev0.elapsed_time(ev1) / steps
+            graph_ms = ev0.elapsed_time(ev1) / (rounds * n_layers)
             rc = moe.moe_check(ctx)
             if rc != moe.MOE_OK:
                 raise RuntimeError(f"{wl} graph replay: {moe.strerror(rc)}")
-            del graphs
+            del g
 
         # the same K steps again with every kernel launch bracketed by HIP events on
         # its own stream (the library records them): per-kernel durations
@@ -429,8 +433,8 @@ class Bench:
                 "ms_per_step": round(graph_ms, 5),
                 "tokens_per_s": round(m / (graph_ms / 1e3), 2),
                 "layer_expert_GB_per_s": round(expert_bytes / (graph_ms / 1e3) / 1e9, 1),
-                "note": "one HIP graph per layer, each step copies its tokens into the graph's input buffer "
-                        "(copy included in the time)",
+                "note": "one HIP graph holding a forward of each layer in the rotation; one copy per replay "
+                        "fills the layers' input buffers with the next tokens (copy included in the time)",
             }
         if m > 8:
             # useful int8 products of the routed experts: 2 ops per multiply-add,
