@@ -73,7 +73,7 @@ WORKLOADS = {
 DOMINANT = {
     "decode": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
     "small": ("gateup", r"^(void )?moe::gateup_q8_kernel\b"),
-    "decode_fp4": ("gateup", r"^void moe::fp4_gemv_kernel<2, 1>"),
+    "decode_fp4": ("gateup", r"^void moe::fp4_gemv_kernel<2, 1, 5>"),
     "prefill_fp4": ("gateup", r"^void moe::fp4_mmq_kernel<1, false>"),  # the <= 16-row class
     "prefill": ("gateup", r"^void moe::mmq_gateup_q2k_kernel<1>"),      # the <= 16-row class
     "prefill_mixed": ("gateup", r"^void moe::gateup_q2k_kernel<8>"),    # the groups of <= 8 rows

@@ -19,7 +19,7 @@
 //
 // A chunk holds token rows of one expert (positions row0.. in expert-sorted pick
 // order). Two kernels per matrix pair:
-//  fp4_gemv_kernel<NM, T>: chunks of at most T <= 8 rows (decode, small batches); a
+//  fp4_gemv_kernel<NM, T, SPW>: chunks of at most T <= 8 rows (decode, small batches); a
 //      workgroup per 16 weight rows, its wavefronts splitting K, each with all
 //      of its loads in flight at once; partial tiles summed in LDS.
 //  fp4_mmq_kernel<NS, DOWN>: the MMQ size classes above 8 tokens; a workgroup
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void fp4_mmq_kernel(ExpertArgs a, int nb) {
 
 // ------------------------------------------------------------------ small chunks (split K)
 // A workgroup per (chunk, 16 weight rows); wavefront w takes K stages
-// FG_SPW w .. FG_SPW w + FG_SPW - 1 (of 128 columns), lane (l16, g) row l16 and
+// SPW w .. SPW w + SPW - 1 (of 128 columns), lane (l16, g) row l16 and
 // block g of each stage, as in the batched kernels. All of a lane's code and
 // scale loads are issued before anything waits (one contiguous 1 KB run per
 // wavefront load: 16 rows x 64 bytes of a tile), then the chunk's token rows go
@@ -238,9 +238,11 @@ __global__ __launch_bounds__(256) void fp4_mmq_kernel(ExpertArgs a, int nb) {
 // with token t's values in B column t (zero for t >= rows). The wavefronts'
 // 16 x 16 partial tiles are summed in LDS.
 constexpr int FG_ROWS = 16;   // weight rows per workgroup
-constexpr int FG_SPW = 4;     // K stages per wavefront: at most 16 wavefronts for K <= 8192
+// K stages per wavefront (at most 16 wavefronts for K <= 8192): gate/up 5 (8
+// wavefronts at D = 5120), down 4, the faster of 3..6 for each at the real shape
+constexpr int FG_SPW_GU = 5, FG_SPW_DN = 4;
 
-template <int NM, int T>
+template <int NM, int T, int SPW>
 __global__ __launch_bounds__(1024) void fp4_gemv_kernel(ExpertArgs a, int nb) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
@@ -271,39 +273,45 @@ __global__ __launch_bounds__(1024) void fp4_gemv_kernel(ExpertArgs a, int nb) {
     const uint8_t* mat[NM];
     mat[0] = base + (NM == 2 ? a.off_w1 : a.off_w2);
     if (NM == 2) mat[NM - 1] = base + a.off_w3;
-    u32x4_t q[NM][FG_SPW];
-    uint32_t e[NM][FG_SPW];
+    u32x4_t q[NM][SPW];
+    uint32_t e[NM][SPW];
 #pragma unroll
-    for (int s = 0; s < FG_SPW; ++s) {   // stages past K repeat the last one (in bounds, not used)
-        const int st = min(wv * FG_SPW + s, nk - 1);
+    for (int s = 0; s < SPW; ++s) {   // stages past K repeat the last one (in bounds, not used)
+        const int st = min(wv * SPW + s, nk - 1);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             q[m][s] = *reinterpret_cast<const u32x4_t*>(mat[m] + fp4_code_off(row, 4 * st + g, K));
             e[m][s] = mat[m][cb + fp4_scale_off(row, 4 * st + g, K)];
         }
     }
-    // the chunk's token rows (T >= rows): thread k < K / 8 moves 8 values of each
-    // (the workgroup has at least K / 8 threads; loads past the rows or past K repeat
-    // the last, in bounds and unused)
-    const int ld = K + 8, k8 = K / 8, kx = min(tid, k8 - 1);
+    // the chunk's token rows (T >= rows): thread i moves 8 values at units i and
+    // i + blockDim of each (the workgroup has 64 ceil(nk / SPW) >= K / (8 XU)
+    // threads; loads past the rows or past K repeat the last, in bounds and unused)
+    constexpr int XU = (SPW + 3) / 4;
+    const int ld = K + 8, k8 = K / 8, bd = blockDim.x;
     uint16_t* xl = reinterpret_cast<uint16_t*>(smem);
-    uint4 xr[T];
+    uint4 xr[T][XU];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int tr = ch.row0 + min(t, ch.nrows - 1);
         const uint16_t* src = NM == 2 ? a.x16 + (size_t)(a.perm[tr] / a.topk) * D : h + (size_t)tr * I;
-        xr[t] = reinterpret_cast<const uint4*>(src)[kx];
+#pragma unroll
+        for (int j = 0; j < XU; ++j) xr[t][j] = reinterpret_cast<const uint4*>(src)[min(tid + j * bd, k8 - 1)];
     }
 #pragma unroll
     for (int t = 0; t < T; ++t)
-        if (t < ch.nrows && tid < k8) *reinterpret_cast<uint4*>(xl + t * ld + 8 * tid) = xr[t];
+#pragma unroll
+        for (int j = 0; j < XU; ++j) {
+            const int u = tid + j * bd;
+            if (t < ch.nrows && u < k8) *reinterpret_cast<uint4*>(xl + t * ld + 8 * u) = xr[t][j];
+        }
     __syncthreads();
     f4_t acc[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[m] = (f4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < FG_SPW; ++s) {
-        const int st = wv * FG_SPW + s;
+    for (int s = 0; s < SPW; ++s) {
+        const int st = wv * SPW + s;
         if (st >= nk) break;   // uniform per wavefront
         float sc[NM];
 #pragma unroll
@@ -367,19 +375,20 @@ hipError_t launch_fp4_mmq(const ExpertArgs& a, const ChunkPlan& plan, bool gateu
 }
 
 bool fp4_supported(int D, int I) {
-    // the 64 x 128 slot tiles divide both dims; K <= 8192 keeps a workgroup within 16 wavefronts
-    return D % 256 == 0 && I % 256 == 0 && D <= FG_SPW * 16 * FM_K && I <= FG_SPW * 16 * FM_K;
+    // the 64 x 128 slot tiles divide both dims; a workgroup stays within 16 wavefronts
+    return D % 256 == 0 && I % 256 == 0 && D <= FG_SPW_GU * 16 * FM_K && I <= FG_SPW_DN * 16 * FM_K;
 }
 
 template <int T>
 static hipError_t launch_fp4_t(const ExpertArgs& a, int max_chunks, bool gateup, hipStream_t st) {
     const int K = gateup ? a.D : a.I, Rows = gateup ? a.I : a.D;
-    const int nw = (K / FM_K + FG_SPW - 1) / FG_SPW;   // 64 nw >= K / 8 threads
+    const int spw = gateup ? FG_SPW_GU : FG_SPW_DN;
+    const int nw = (K / FM_K + spw - 1) / spw;   // 64 nw XU >= K / 8 (XU units per thread)
     const int nb = max_chunks * (Rows / FG_ROWS);
     const int nb_pad = (nb + 7) / 8 * 8;   // whole rounds over the 8 XCDs
     const size_t lds = std::max((size_t)T * (K + 8) * 2, (size_t)nw * (gateup ? 2 : 1) * 256 * 4);
-    if (gateup) return launch_kernel(fp4_gemv_kernel<2, T>, nb_pad, nw * 64, lds, st, a, nb);
-    return launch_kernel(fp4_gemv_kernel<1, T>, nb_pad, nw * 64, lds, st, a, nb);
+    if (gateup) return launch_kernel(fp4_gemv_kernel<2, T, FG_SPW_GU>, nb_pad, nw * 64, lds, st, a, nb);
+    return launch_kernel(fp4_gemv_kernel<1, T, FG_SPW_DN>, nb_pad, nw * 64, lds, st, a, nb);
 }
 
 hipError_t launch_fp4(const ExpertArgs& a, int rows_max, int max_chunks, bool gateup, hipStream_t st) {
