@@ -56,20 +56,69 @@ MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* 
 }
 
 template <int TT>
-__global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __restrict__ x, int m,
+__global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __restrict__ x, int m,
                                                            const uint16_t* __restrict__ wr, int D, int E, int ntg,
                                                            float* __restrict__ logits, int8_t* __restrict__ xq,
                                                            float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f,
                                                            SharedRows sr) {
-    const int nrouter = E * ntg;
-    const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
+    const int nrouter = E * ntg, bd = blockDim.x;
+    const int nq = xq == nullptr ? 0 : (m * (D / QB) + bd - 1) / bd;
     if ((int)blockIdx.x >= nrouter + nq) {   // the shared expert's rows
         shared_rows_block(sr, blockIdx.x - nrouter - nq);
         return;
     }
     if ((int)blockIdx.x >= nrouter) {
-        const int b = (blockIdx.x - nrouter) * 256 + threadIdx.x;
+        const int b = (blockIdx.x - nrouter) * bd + threadIdx.x;
         if (b < m * (D / QB)) quantize_block_bf16(x, b, xq, xd, xs16, xs16f);
+        return;
+    }
+    if constexpr (TT > 1) {
+        // 512 threads: thread i takes 16-byte units i and i + 512 of the expert's row
+        // and of each token row (D / 8 <= 1024 units), every load requested at once
+        // (units past the row and tokens past m repeat the last ones; not kept)
+        constexpr int UM = 2;
+        const int e = blockIdx.x % E, tid = threadIdx.x, nu = D / 8;
+        const uint4* w4 = reinterpret_cast<const uint4*>(wr + (size_t)e * D);
+        uint4 wv[UM], xv[UM][TT];
+#pragma unroll
+        for (int i = 0; i < UM; ++i) {
+            const int c = min(tid + 512 * i, nu - 1);
+            wv[i] = w4[c];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) xv[i][t] = reinterpret_cast<const uint4*>(x + (size_t)min(t, m - 1) * D)[c];
+        }
+        float acc[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < UM; ++i) {
+            if (tid + 512 * i >= nu) break;
+            const uint32_t w8[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const uint32_t x8[4] = {xv[i][t].x, xv[i][t].y, xv[i][t].z, xv[i][t].w};
+                float a = acc[t];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    a = fmaf(bf16_lo(x8[q]), bf16_lo(w8[q]), a);
+                    a = fmaf(bf16_hi(x8[q]), bf16_hi(w8[q]), a);
+                }
+                acc[t] = a;
+            }
+        }
+        __shared__ float part8[8][TT];
+        const int lane = tid & 63, wv8 = tid >> 6;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const float sm = wave_sum(acc[t]);
+            if (lane == 0) part8[wv8][t] = sm;
+        }
+        __syncthreads();
+        if (tid < TT && tid < m) {
+            float z = part8[0][tid];
+            for (int w = 1; w < 8; ++w) z += part8[w][tid];
+            logits[(size_t)tid * E + e] = z;
+        }
         return;
     }
     const int e = blockIdx.x % E;
@@ -535,16 +584,19 @@ hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const in
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                                int8_t* xq, float* xd, int32_t* xs16, float* xs16f, hipStream_t st,
                                const SharedRows* sr) {
-    const int nq = xq == nullptr ? 0 : (m * (D / QB) + 255) / 256;
     SharedRows none{};
     const SharedRows& s = sr ? *sr : none;
-    const int nsh = sr ? shared_rows_blocks(*sr, 256) : 0;
-    if (m == 1) return launch_kernel(router_quant_kernel<1>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
-    if (m == 2) return launch_kernel(router_quant_kernel<2>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
-    if (m <= 4) return launch_kernel(router_quant_kernel<4>, E + nq + nsh, 256, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
-    const int ntg = (m + 7) / 8;
-    return launch_kernel(router_quant_kernel<8>, E * ntg + nq + nsh, 256, 0, st, x, m, wr, D, E, ntg, logits, xq, xd,
-                         xs16, xs16f, s);
+    // m = 1: 256 threads per workgroup, the router row strided over them; m = 2..8:
+    // 512 threads, every load of a row hoisted (the workgroups of one launch share
+    // their size: the q8_1 and shared-row workgroups follow it)
+    const int th = m == 1 ? 256 : 512;
+    const int nq = xq == nullptr ? 0 : (m * (D / QB) + th - 1) / th;
+    const int nsh = sr ? shared_rows_blocks(*sr, th) : 0;
+    const int grid = E + nq + nsh;
+    if (m == 1) return launch_kernel(router_quant_kernel<1>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
+    if (m == 2) return launch_kernel(router_quant_kernel<2>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
+    if (m <= 4) return launch_kernel(router_quant_kernel<4>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
+    return launch_kernel(router_quant_kernel<8>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
