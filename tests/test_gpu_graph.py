@@ -51,6 +51,15 @@ def test_tiny_decode_graph(shared):
         layer.close()
 
 
+@pytest.mark.parametrize("shared", ["bf16", "none"])
+def test_tiny_fp4_decode_graph(shared):
+    layer = Layer(S.LayerShape(512, 256, 16, 3), 2, max_tokens=8, shared_fmt=shared, expert_fmt="fp4")
+    try:
+        capture_and_compare(layer, S.make_tokens(5, 512, 2, index=60), f"tiny fp4 graph {shared}")
+    finally:
+        layer.close()
+
+
 def test_real_decode_graph(real_experts):
     layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=8, experts=real_experts)
     try:

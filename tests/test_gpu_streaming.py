@@ -51,6 +51,31 @@ def test_streamed_layer(m, n_slots, shared):
         layer.close()
 
 
+FP4_SHAPE = S.LayerShape(512, 256, 16, 3)
+
+
+@pytest.mark.parametrize("m,n_slots", [
+    (4, 8),      # small-batch path, one wave
+    (8, 4),      # small-batch path, several waves
+    (40, 4),     # MMQ path, waves
+])
+def test_streamed_fp4_layer(m, n_slots):
+    # MXFP4 experts streamed in their tiled slot layout from the host arena
+    layer = Layer(FP4_SHAPE, 5, max_tokens=max(m, 8), n_slots=n_slots, bind_all=False, host_arena=True,
+                  expert_fmt="fp4")
+    try:
+        x = S.make_tokens(m, FP4_SHAPE.dim, 5, index=200 + m)
+        moe.moe_reset_stats(layer.ctx)
+        check_layer(layer, x, f"streamed fp4 m={m} slots={n_slots}")
+        st = moe.moe_get_stats(layer.ctx)
+        distinct = len(set(layer.oracle_route(x)[0].reshape(-1).tolist()))
+        assert st["misses"] >= distinct - min(distinct, n_slots)
+        assert st["bytes_copied"] == st["misses"] * layer.arena_src.shape[1]
+        assert st["waves"] == (1 if distinct <= n_slots else -(-distinct // max(1, n_slots // 2)))
+    finally:
+        layer.close()
+
+
 def test_streamed_lru_keeps_recent():
     # two batches that each fit the slots: the second one evicts only experts the
     # first one no longer needs, and a third call with the first batch's tokens
