@@ -254,6 +254,18 @@ def test_route_only_against_oracle(dim, E, k, m):
         layer.close()
 
 
+def test_max_tokens():
+    # m = max_tokens = 65536 (the configuration's limit): scratch sized for it, the
+    # chunk lists at their bounds, routing checked for every token and the outputs on
+    # sampled rows
+    m = 65536
+    layer = Layer(S.TINY, 14, max_tokens=m, shared_fmt="kquant")
+    try:
+        check_layer(layer, S.make_tokens(m, S.TINY.dim, 14), "tiny m=65536", sample_rows=[0, 12345, 40000, m - 1])
+    finally:
+        layer.close()
+
+
 def test_tiny_deterministic():
     layer = Layer(S.TINY, 0, max_tokens=16)
     try:
