@@ -93,7 +93,10 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
     }
     // the token's q8_1 activations: quants (D bytes), block scales (L f32),
     // fp16(d) times the 16-value sums (2L f32), requested first, through registers
-    // into LDS
+    // into LDS. Each superblock's 256 quants are followed by 16 bytes of padding
+    // (unit f at f + min(f / 16, nsb)): the lanes of a wavefront read 8 different
+    // superblocks at once, 272 bytes apart, which falls on distinct banks where a
+    // 256-byte stride would not.
     const int nx16 = (D + 4 * L + 8 * L) / 16;
     const int nxu = (nx16 + bd - 1) / bd;
     uint4 xv0 = make_uint4(0, 0, 0, 0);
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
                                                         : xs + (size_t)(f - D / 16 - L / 4) * 16;
                 const uint4 v = *reinterpret_cast<const uint4*>(src);
                 if (u == 0) xv0 = v;   // stored after the weight loads are issued
-                else reinterpret_cast<uint4*>(smem)[f] = v;
+                else reinterpret_cast<uint4*>(smem)[f + min(f >> 4, nsb)] = v;
             }
         }
     }
@@ -130,11 +133,12 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
             for (int i = 0; i < 21; ++i) wq[k][i] = q[i];
         }
     }
-    if (tid < nx16) reinterpret_cast<uint4*>(smem)[tid] = xv0;
+    if (tid < nx16) reinterpret_cast<uint4*>(smem)[tid + min(tid >> 4, nsb)] = xv0;
     barrier_lds();
 
     const uint8_t* xl = smem;
-    float* red = reinterpret_cast<float*>(smem + (size_t)((nx16 + bd - 1) / bd) * bd * 16);   // [8 vectors x 4 panels... ][nsb]
+    const uint8_t* xsc = xl + D + 16 * nsb;   // the block scales, then the 16-value terms
+    float* red = reinterpret_cast<float*>(smem + (size_t)((nx16 + nsb + bd - 1) / bd) * bd * 16);   // [8 vectors x 4 panels... ][nsb]
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int s = sl + NSL * k;
@@ -142,9 +146,9 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
         const uint32_t* sc = wq[k];
         const uint32_t* qw = wq[k] + 4;
         const uint32_t dd = wq[k][20];
-        const uint32_t* xq32 = reinterpret_cast<const uint32_t*>(xl) + s * (QK / 4);
-        const float* dxp = reinterpret_cast<const float*>(xl + D) + s * 8;
-        const float* s16p = reinterpret_cast<const float*>(xl + D + 4 * L) + s * 16;
+        const uint32_t* xq32 = reinterpret_cast<const uint32_t*>(xl) + s * (QK / 4 + 4);
+        const float* dxp = reinterpret_cast<const float*>(xsc) + s * 8;
+        const float* s16p = reinterpret_cast<const float*>(xsc + 4 * L) + s * 16;
         float fs = 0.f, ms = 0.f;
         // q8_1 block t = 4 hh + j of x meets plane j of qs half hh: qs byte b of half
         // hh holds weight 128 hh + 32 j + b in bits 2j..2j+1 (sub-block 2t + b / 16)
@@ -376,7 +380,7 @@ hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks
     const int nsb = a.D / QK;
     const int spl = 64 * nsb <= 1024 ? 1 : 2;                 // superblocks per lane
     const int threads = round64(64 * ((nsb + spl - 1) / spl));  // 8 rows x slots x 2 matrices x 4 panels
-    const int nx16 = (a.D + 12 * (a.D / QB)) / 16;
+    const int nx16 = (a.D + 12 * (a.D / QB)) / 16 + nsb;   // with one padding unit per superblock
     const size_t lds = (size_t)((nx16 + threads - 1) / threads) * threads * 16 + (size_t)64 * nsb * 4;
     const int grid = max_chunks * (a.I / GU_TILE);
     if (spl == 1) return launch_kernel(gateup_q8_kernel<1>, grid, threads, lds, st, a, routed_rows);
