@@ -401,15 +401,21 @@ class Bench:
         routed_b = n_exp * expert_b
         expert_bytes = routed_b + shared_b
         router_b = shape.n_routed * shape.dim * 2
+        # at m <= 8 with K-quant experts the library runs the second half of a bf16
+        # shared expert's down rows (W2s rows D/2..D-1) as extra workgroups of the
+        # routed gate/up launch
+        sh_in_gateup = ((shape.dim - shape.dim // 2) * shape.inter * 2
+                        if m <= 8 and spec["shared"] == "bf16" and not fp4 else 0)
         # Every figure below sets bytes against the time of the kernels that read them.
         # The routed gate/up and down kernels read the picked experts (and a K-quant
         # shared expert's rows, which ride in them); a bf16 shared expert rides in the
         # routing launches at m <= 8 and has kernels of its own above 8 tokens, so the
         # whole-layer figure takes every weight byte over every kernel of the step.
-        routed_k_bytes = routed_b + (shared_b if spec["shared"] == "kquant" else 0)
+        routed_k_bytes = routed_b + (shared_b if spec["shared"] == "kquant" else 0) + sh_in_gateup
         routed_k_ms = avg_ms("gateup") + avg_ms("down")
         all_k_ms = sum(avg_ms(k) for k in ktimes if ktimes[k][1])
-        gateup_bytes = n_exp * 2 * q2k_matrix + (2 * q2k_matrix if spec["shared"] == "kquant" else 0)
+        gateup_bytes = (n_exp * 2 * q2k_matrix + (2 * q2k_matrix if spec["shared"] == "kquant" else 0)
+                        + sh_in_gateup)
         ga = avg_ms("gateup")
         res = {
             "workload": wl,
@@ -424,7 +430,7 @@ class Bench:
             "experts_per_step": n_exp,
             "expert_weight_bytes_per_step": int(expert_bytes),
             "routed_kernels": {
-                "kernels": "gateup + down",
+                "kernels": "gateup + down (and the shared rows riding in them)",
                 "bytes_per_step": int(routed_k_bytes),
                 "summed_ms": round(routed_k_ms, 5),
                 "GB_per_s": round(routed_k_bytes / (routed_k_ms / 1e3) / 1e9, 1),
@@ -574,7 +580,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("gateup_q8 (routed gate/up + SwiGLU + q8_1 of h)" if head["m"] <= 8
+            "kernel": ("gateup_q8 (routed gate/up + SwiGLU + q8_1 of h; with a bf16 shared expert also "
+                       "half of its down rows)" if head["m"] <= 8
                        else "mmq_gateup_q2k (routed gate/up + SwiGLU)"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

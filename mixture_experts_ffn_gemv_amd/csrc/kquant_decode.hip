@@ -54,9 +54,16 @@ MOE_DEV int dpp16(int v) {
 // are masked in place (planes 1 and 3 land at 4x, folded into the activation
 // block scale) and the sub-block scales and mins applied per 16 weights; the
 // per-row sums over the superblocks run in order, then the clamped SwiGLU and
-// the q8_1 block of the 32 values of h across 32 lanes.
+// the q8_1 block of the 32 values of h across 32 lanes. Workgroups past the
+// routed tiles (routed_blocks) compute rows of a bf16 shared expert's down
+// product instead.
 template <int SPL>
-__global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int routed_rows) {
+__global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int routed_rows, int routed_blocks,
+                                                         SharedRows sr) {
+    if ((int)blockIdx.x >= routed_blocks) {   // bf16 shared-expert down rows riding in this launch (5 pieces: <= 80 VGPRs)
+        shared_down_block<5>(sr, blockIdx.x - routed_blocks);
+        return;
+    }
     extern __shared__ __align__(16) uint8_t smem[];
     const int D = a.D, I = a.I;
     const int L = D / QB;
@@ -375,7 +382,8 @@ static int round64(int v) { return (v + 63) / 64 * 64; }
 
 size_t decode_rec_bytes(int I) { return (size_t)I + (size_t)(I / QB) * 4 + (size_t)(I / 16) * 4; }
 
-hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st) {
+hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st,
+                            const SharedRows* sr) {
     if (max_chunks <= 0) return hipSuccess;
     const int nsb = a.D / QK;
     const int spl = 64 * nsb <= 1024 ? 1 : 2;                 // superblocks per lane
@@ -383,8 +391,11 @@ hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks
     const int nx16 = (a.D + 12 * (a.D / QB)) / 16 + nsb;   // with one padding unit per superblock
     const size_t lds = (size_t)((nx16 + threads - 1) / threads) * threads * 16 + (size_t)64 * nsb * 4;
     const int grid = max_chunks * (a.I / GU_TILE);
-    if (spl == 1) return launch_kernel(gateup_q8_kernel<1>, grid, threads, lds, st, a, routed_rows);
-    return launch_kernel(gateup_q8_kernel<2>, grid, threads, lds, st, a, routed_rows);
+    SharedRows none{};
+    const SharedRows& s = sr ? *sr : none;
+    const int nsh = sr ? shared_rows_blocks(*sr, threads) : 0;
+    if (spl == 1) return launch_kernel(gateup_q8_kernel<1>, grid + nsh, threads, lds, st, a, routed_rows, grid, s);
+    return launch_kernel(gateup_q8_kernel<2>, grid + nsh, threads, lds, st, a, routed_rows, grid, s);
 }
 
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,

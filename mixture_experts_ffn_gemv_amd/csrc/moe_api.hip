@@ -680,13 +680,15 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     const bool small = m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS;
     const bool use_mmq = !small && ctx->mmq_ok;
     // decode with every picked expert in its slot: the bf16 shared expert rides in
-    // the routing launches, its gate/up rows as extra workgroups of the router
+    // the routed launches, its gate/up rows as extra workgroups of the router
     // launch, its down rows (into ys, added by the routed down kernel or, for
     // MXFP4 experts, by the combine kernel) as extra workgroups of the top-k
-    // launch; no second stream
+    // launch; with K-quant experts half of the down rows go to the routed gate/up
+    // launch instead, whose workgroups leave CU slots free (the top-k launch is
+    // then shorter and gate/up hardly longer); no second stream
     const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
     const bool shared_fused = bf16_shared && small && (ctx->decode_ok || fp4) && ctx->host_arena == nullptr;
-    SharedRows sr_a{}, sr_b{};
+    SharedRows sr_a{}, sr_b{}, sr_c{};
     if (shared_fused) {
         sr_a.w1 = (const uint16_t*)w->shared_w1;
         sr_a.w3 = (const uint16_t*)w->shared_w3;
@@ -704,6 +706,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         sr_b.ys = ctx->ys;
         sr_b.row0 = 0;
         sr_b.rows = c.dim;
+        if (ctx->decode_ok) {   // K-quant experts: the second half of the down rows rides in the gate/up launch
+            sr_c = sr_b;
+            sr_c.row0 = c.dim / 2;
+            sr_c.rows = c.dim - c.dim / 2;
+            sr_b.rows = c.dim / 2;
+        }
     }
     if (bf16_shared && !shared_fused) {
         // the shared expert needs only x: run it beside the routing and the routed experts
@@ -821,7 +829,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         // one single-row chunk per pick (and per token of a K-quant shared expert):
         // gate/up writes q8_1(h) records, down accumulates G E per token and stores bf16
         const int nch = P + (kq ? m : 0);
-        rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_gateup_q8(a, P, nch, st); });
+        rc = timed(ctx, st, MOE_K_GATEUP,
+                   [&] { return launch_gateup_q8(a, P, nch, st, sr_c.rows > 0 ? &sr_c : nullptr); });
         if (rc != MOE_OK) return rc;
         if (bf16_shared && !shared_fused && hipStreamWaitEvent(st, ctx->ev_join, 0) != hipSuccess) return MOE_EHIP;
         rc = timed(ctx, st, MOE_K_DOWN, [&] {

@@ -128,7 +128,8 @@ hipError_t launch_down_q3k(const ExpertArgs& a, int rows_max, int max_chunks, hi
 bool decode_supported(int D, int I);
 size_t decode_rec_bytes(int I);
 // gate/up writing the q8_1 records of h
-hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st);
+hipError_t launch_gateup_q8(const ExpertArgs& a, int routed_rows, int max_chunks, hipStream_t st,
+                            const SharedRows* sr = nullptr);
 // down + weighted combine (+ the shared expert's f32 output ys when given), bf16 store
 hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int max_chunks, const float* ys,
                                uint16_t* out, hipStream_t st);

@@ -1,6 +1,7 @@
-// The bf16 shared expert's gate/up, as extra workgroups of the routing
-// launches (the routing kernels leave most of the chip idle; the shared
-// expert needs only x). h = bf16(SwiGLU_clamped(W1s x, W3s x)), as in the
+// The bf16 shared expert's rows as extra workgroups of other launches: its
+// gate/up rows in the router launch (the routing kernels leave most of the
+// chip idle; the shared expert needs only x), its down rows in the top-k launch
+// and, with K-quant experts, half of them in the routed gate/up launch. h = bf16(SwiGLU_clamped(W1s x, W3s x)), as in the
 // shared-expert GEMV of the pages (metrale `gemv`, the bf16 shared expert at
 // one token).
 #pragma once
@@ -106,7 +107,9 @@ MOE_DEV void shared_gateup_block(const SharedRows& sr, int blk) {
 // Workgroup `blk` of the shared down rows: wavefront i takes output row
 // row0 + blk * (wavefronts) + i of W2, 16-byte pieces lane, lane + 64, ... (every
 // load of the wavefront 1 KB contiguous), dotted with the same pieces of each
-// token's h; the wavefront sums and lane 0 writes ys.
+// token's h; the wavefront sums and lane 0 writes ys. NP pieces per lane and
+// round (fewer registers for launches that must stay lean).
+template <int NP = SR_PIECES>
 MOE_DEV void shared_down_block(const SharedRows& sr, int blk) {
     const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rr = blk * nw + wv;
@@ -117,10 +120,10 @@ MOE_DEV void shared_down_block(const SharedRows& sr, int blk) {
     float dots[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) dots[t] = 0.f;
-    for (int j0 = 0; j0 * 64 < n16; j0 += SR_PIECES) {
-        uint4 wq[SR_PIECES];
+    for (int j0 = 0; j0 * 64 < n16; j0 += NP) {
+        uint4 wq[NP];
 #pragma unroll
-        for (int j = 0; j < SR_PIECES; ++j) {
+        for (int j = 0; j < NP; ++j) {
             const int k = lane + 64 * (j0 + j);
             wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
         }
@@ -130,7 +133,7 @@ MOE_DEV void shared_down_block(const SharedRows& sr, int blk) {
             const uint4* H = reinterpret_cast<const uint4*>(sr.h + (size_t)t * sr.I);
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < SR_PIECES; ++j) {
+            for (int j = 0; j < NP; ++j) {
                 const int k = lane + 64 * (j0 + j);
                 if (k < n16) {
                     const uint4 hv = H[k];
