@@ -25,6 +25,10 @@ Pins (tests/test_oracle_formats.py): single-field probes and closed forms for
 both block decoders, constructed rounding ties, q8_1 closed forms; for MXFP4
 the eight e2m1 magnitudes against the format's definition, E8M0 powers of two,
 one-nibble and one-scale probes, and exactly representable matrices.
+Whole K-quant matrices (tests/test_oracle_matrices.py): position-coded matrices
+whose every block has its own d, dmin, scales and quants, packed weight by
+weight from the layout and compared value for value (row order, superblock
+order, orientation); the encoder round trip within one quantisation step.
 """
 
 import numpy as np

@@ -36,10 +36,14 @@ Where the pages are silent: gate_temp = 1 and norm_topk_prob = true unless
 given; the routing weight multiplies the expert output after W2; the q8_1
 rounding is round-half-away-from-zero of x/d with the unrounded f32 d.
 
-Pins (tests/test_oracle_layer.py, tests/test_oracle_route.py): brute-force top-k
-rank formulation on tiny inputs, constructed ties, the sum-to-route_scale
-invariant, softplus closed forms, closed-form experts (constant blocks), zero
-input, one-hot routing, identical experts, shared-only.
+Pins (tests/test_oracle_layer.py, tests/test_oracle_route.py,
+tests/test_oracle_matrices.py): brute-force top-k rank formulation on tiny
+inputs, constructed ties, the sum-to-route_scale invariant, softplus closed
+forms, closed-form experts (constant blocks), zero input, one-hot routing,
+identical experts, shared-only; a slice of position-coded matrices decoded
+into W1, W3, W2 in that order; the K-quant expert against a dense float64
+expert on the decoded weights with unquantised activations (a hard error bound
+and the RMS that the two q8_1 roundings predict).
 """
 
 from dataclasses import dataclass
