@@ -161,38 +161,128 @@ def traffic_from(fetch_csv, write_csv, workload):
     print(json.dumps(rec[workload]))
 
 
-def cpu_baseline(lay, tokens, experts, shape, sample):
-    """The oracle, as it stands, on `sample` decode steps of the same workload."""
-    import numpy as np
-    import torch
+CPU_WORKERS_MAX = 16   # the host share of one GPU
+
+
+def _oracle_token(args):
+    """One decode token through the oracle's whole layer (a worker process)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
+    cfg_args, x, wr, bias, experts, shared = args
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.moe_layer(oracle.MoeCfg(*cfg_args), x, wr, bias, lambda e: experts[e], shared)
+        return time.perf_counter() - t0
+
+
+def _oracle_group(args):
+    """One expert's group of a prefill batch: decode its blocks, run its rows (a worker process)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cfg_args, raw, x_rows = args
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        cfg = oracle.MoeCfg(*cfg_args)
+        w1, w3, w2 = oracle.slot_matrices(cfg, raw)
+        oracle.expert_ffn_kquant(x_rows, w1, w3, w2, cfg.swiglu_limit)
+        return time.perf_counter() - t0
+
+
+def _warm(_):
+    """Start a worker: import what the tasks need (not timed)."""
+    from threadpoolctl import threadpool_limits  # noqa: F401
+
+    import oracle  # noqa: F401
+    time.sleep(0.5)
+    return os.getpid()
+
+
+def _pool(workers):
+    import concurrent.futures
+    import multiprocessing
+    return concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=multiprocessing.get_context("spawn"))
+
+
+def cpu_baseline(lay, tokens, experts, shape, decode_tokens=None, prefill_groups=32):
+    """The oracle, as it stands, on the host's cores (worker processes, one BLAS
+    thread each), on bounded samples of the decode and prefill workloads."""
+    import platform
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import synthetic as S
 
     def bits(t):
         return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
+    workers = max(1, min(CPU_WORKERS_MAX, os.cpu_count() or 1))
+    n_dec = decode_tokens or workers
     cfg = oracle.MoeCfg(shape.dim, shape.inter, shape.n_routed, shape.topk)
-    cache = {}
+    cfg_args = (shape.dim, shape.inter, shape.n_routed, shape.topk)
+    cpu_model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+
+    # decode: n_dec tokens of the same pool, one whole-layer oracle call each
     shared = {"fmt": "bf16", **{k: bits(lay["shared"][k]) for k in ("w1", "w3", "w2")}}
-    wr = bits(lay["wr"])
-    bias = lay["bias"].cpu().numpy()
-    xs = [bits(tokens[i:i + 1]) for i in range(sample)]
-    # copy the picked experts out before the clock starts (they come from the GPU pool)
-    for x in xs:
-        idx = oracle.route(cfg, oracle.bf16_bits_to_f64(x), oracle.bf16_bits_to_f64(wr), bias)[0]
-        for e in np.unique(idx):
-            if int(e) not in cache:
-                cache[int(e)] = experts[int(e)].cpu().numpy()
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for x in xs:
-            oracle.moe_layer(cfg, x, wr, bias, lambda e: cache[e], shared)
-        dt = time.perf_counter() - t0
-    return {"value": sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample} decode tokens (m=1) of the first layer: the float64 numpy oracle including "
-                      f"decoding the 6 picked experts' blocks per token; {dt:.1f} s on one host core "
-                      f"(BLAS limited to one thread); host has {os.cpu_count()} logical CPUs"}
+    wr, bias = bits(lay["wr"]), lay["bias"].cpu().numpy()
+    wr64 = oracle.bf16_bits_to_f64(wr)
+    tasks = []
+    for i in range(n_dec):
+        x = bits(tokens[i:i + 1])
+        picks = oracle.route(cfg, oracle.bf16_bits_to_f64(x), wr64, bias)[0]
+        tasks.append((cfg_args, x, wr, bias, {int(e): experts[int(e)].cpu().numpy() for e in np.unique(picks)},
+                      shared))
+    pool = _pool(workers)
+    list(pool.map(_warm, range(workers)))   # start the workers (imports) before the clock
+    t0 = time.perf_counter()
+    list(pool.map(_oracle_token, tasks))
+    dt_dec = time.perf_counter() - t0
+    del tasks
+
+    # prefill m = 512 (uniform routing): the routing and the bf16 shared expert for all
+    # 512 tokens in this process (BLAS on every core), and a sample of the expert
+    # groups (every 12th expert id) in the workers; the whole is the sample scaled by
+    # the groups left out
+    wr_p, bias_p = S.make_router(shape, 1, 0.02, None)
+    sh_p = S.make_shared(shape, 1, "bf16")
+    xp = bits(S.make_tokens(512, shape.dim, 1, index=2))
+    x64 = oracle.bf16_bits_to_f64(xp)
+    t0 = time.perf_counter()
+    idx = oracle.route(cfg, x64, oracle.bf16_bits_to_f64(bits(wr_p)), bias_p.numpy())[0]
+    oracle.shared_ffn_bf16(x64, *(oracle.bf16_bits_to_f64(bits(sh_p[k])) for k in ("w1", "w3", "w2")),
+                           cfg.swiglu_limit)
+    dt_main = time.perf_counter() - t0
+    groups = [e for e in range(0, shape.n_routed, max(1, shape.n_routed // prefill_groups)) if (idx == e).any()]
+    all_groups = len(np.unique(idx))
+    x32 = x64.astype(np.float32)
+    gtasks = [(cfg_args, experts[e].cpu().numpy(), x32[np.nonzero((idx == e).any(axis=1))[0]]) for e in groups]
+    t0 = time.perf_counter()
+    list(pool.map(_oracle_group, gtasks))
+    dt_groups = time.perf_counter() - t0
+    pool.shutdown()
+    est_prefill = dt_main + dt_groups * all_groups / len(groups)
+    return {
+        "value": round(n_dec / dt_dec, 4), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"{n_dec} decode tokens (m=1) of the headline layer, each one call of the float64 numpy "
+                  f"oracle's whole layer (decoding its 6 picked experts' blocks) in {workers} worker processes "
+                  f"(one BLAS thread each): {dt_dec:.1f} s wall; host: {os.cpu_count()} logical CPUs, {cpu_model}",
+        "prefill_m512": {
+            "value": round(512 / est_prefill, 3), "unit": "tokens/s",
+            "sample": f"prefill m=512 (uniform routing): routing and bf16 shared expert for all 512 tokens in one "
+                      f"process with BLAS on every core ({dt_main:.1f} s), plus {len(groups)} of the "
+                      f"{all_groups} expert groups (every 12th expert id, all its rows) decoded and run in "
+                      f"{workers} workers ({dt_groups:.1f} s); the groups' time scaled by {all_groups}/"
+                      f"{len(groups)}: {est_prefill:.1f} s per 512-token step",
+        },
+    }
 
 
 class Bench:
@@ -381,6 +471,8 @@ class Bench:
         ktimes = moe.moe_kernel_times(ctx)
         moe.moe_set_profiling(ctx, False)
 
+        # where a bf16 shared expert's rows run in a call of m tokens (the library's plan)
+        plan = moe.moe_plan_call(ctx, m, moe.MOE_SHARED_BF16 if spec["shared"] == "bf16" else moe.MOE_SHARED_KQUANT)
         # distinct experts per step (the algorithmic bytes follow the routing), untimed
         distinct = []
         for i in range(min(steps, 64)):
@@ -401,11 +493,9 @@ class Bench:
         routed_b = n_exp * expert_b
         expert_bytes = routed_b + shared_b
         router_b = shape.n_routed * shape.dim * 2
-        # at m <= 8 with K-quant experts the library runs the second half of a bf16
-        # shared expert's down rows (W2s rows D/2..D-1) as extra workgroups of the
-        # routed gate/up launch
-        sh_in_gateup = ((shape.dim - shape.dim // 2) * shape.inter * 2
-                        if m <= 8 and spec["shared"] == "bf16" and not fp4 else 0)
+        # the bf16 shared expert's down rows that ride in the routed gate/up launch
+        # (moe_plan_call: at m <= 8 with K-quant experts, part of them)
+        sh_in_gateup = plan["shared_rows_gateup"] * shape.inter * 2 if spec["shared"] == "bf16" else 0
         # Every figure below sets bytes against the time of the kernels that read them.
         # The routed gate/up and down kernels read the picked experts (and a K-quant
         # shared expert's rows, which ride in them); a bf16 shared expert rides in the
@@ -451,6 +541,12 @@ class Bench:
             "gateup_bytes_per_launch": int(gateup_bytes),
             "gateup_avg_launch_ms": round(ga, 5),
             "gateup_GB_per_s": round(gateup_bytes / (ga / 1e3) / 1e9, 1),
+            # the routed experts' W1 / W3 blocks alone over the same launch time (the
+            # shared rows riding in the launch not counted)
+            "gateup_routed_only_GB_per_s": round(n_exp * 2 * q2k_matrix / (ga / 1e3) / 1e9, 1),
+            "plan": plan,
+            "near_ties": {"tokens": int(stats["near_ties"]), "of_tokens": m * steps,
+                          "rule": "k-th largest key minus the largest key left out < 1e-5 (device f32 keys)"},
         }
         if graph_ms is not None:
             res["graph_replay"] = {
@@ -521,7 +617,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", choices=tuple(WORKLOADS), default="decode")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' summaries")
-    ap.add_argument("--cpu-sample", type=int, default=4, help="oracle decode steps for cpu_baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=-1,
+                    help="oracle decode tokens for cpu_baseline (-1: one per worker process; 0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB elementwise copy first (for scaling --pmc byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -601,14 +698,17 @@ def main():
                          "the timed region",
         "kernel_avg_ms": head["kernel_avg_ms"],
     }
+    result["gateup_routed_only_GB_per_s"] = head["gateup_routed_only_GB_per_s"]
+    result["near_ties"] = head["near_ties"]
     for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak", "graph_replay"):
         if k in head:
             result[k] = head[k]
     if extra:
         result["workloads"] = extra
-    if args.cpu_sample > 0 and wl == "decode":
+    if args.cpu_sample != 0 and wl == "decode":
         log("cpu baseline: running the oracle")
-        result["cpu_baseline"] = cpu_baseline(layers[0], tokens, b.experts, b.shape, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(layers[0], tokens, b.experts, b.shape,
+                                              args.cpu_sample if args.cpu_sample > 0 else None)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

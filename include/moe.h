@@ -98,10 +98,13 @@ typedef struct moe_weights {
     const void* shared_w2;     /* device */
 } moe_weights;
 
-/* Counters of the calls since creation or moe_reset_stats (metrale's MoeV41Timing:
- * hits, misses and bytes_read; the time of the routing read-back and of the
- * miss copies). Only calls made with a host arena read the routing back and
- * stream; moe_get_stats / moe_reset_stats wait for the copies still queued. */
+/* Counters of the calls since creation or moe_reset_stats: the fields of
+ * metrale's MoeV41Timing (moe_v41.rs source view, struct MoeV41Timing: route,
+ * fetch and compute milliseconds, hits, misses, bytes read), plus the near-tie
+ * count that the stated pass criterion for the expert indices asks to be
+ * reported. Only calls made with a host arena read the routing back and
+ * stream. moe_get_stats and moe_reset_stats synchronise the device first
+ * (all queued work of the context, and the copies). */
 typedef struct moe_stats {
     uint64_t calls;         /* moe_forward / moe_forward_ex calls */
     uint64_t hits;          /* distinct picked experts already resident at a streamed call's start */
@@ -110,17 +113,30 @@ typedef struct moe_stats {
     uint64_t waves;         /* slot waves run by streamed calls */
     double route_ms;        /* host time waiting for the routing read-back (includes the queued work before it) */
     double fetch_ms;        /* device time of the miss copies (events on the copy stream) */
+    double compute_ms;      /* device time from the first expert kernel to the layer's last kernel (the
+                               combine), summed over the calls made with a host arena or with profiling
+                               on (moe_set_profiling); other calls carry no events and add nothing */
+    uint64_t near_ties;     /* tokens (of moe_forward, moe_forward_ex and moe_route calls) whose k-th
+                               largest key exceeded the largest key not picked by less than 1e-5, in the
+                               device's own f32 keys: where rounding alone may change the selection */
 } moe_stats;
 
 typedef struct moe_ctx moe_ctx;
 
 /* Create a context on the current HIP device: validates cfg, allocates the
  * scratch for cfg->max_tokens tokens. *out is set only on success.
- * MOE_EINVAL (bad cfg / NULL), MOE_ENOMEM, MOE_EHIP. */
+ * The context is the counterpart of metrale's struct MoeV41 (moe_v41.rs source
+ * view): built from a MoeV41Cfg, it owns the per-call device buffers that
+ * struct lists (logits, the q8_1 activations, gate/up/h/down outputs, the
+ * token rows and weights grouped by expert, the slot table) sized for
+ * max_tokens, whose limit route_launch enforces (MoeV41 struct documentation:
+ * m outside 1..=max_tokens is an error), plus the side stream and events of
+ * shared_side. MOE_EINVAL (bad cfg / NULL), MOE_ENOMEM, MOE_EHIP. */
 int moe_create(const moe_cfg* cfg, moe_ctx** out);
 
-/* Free what the context owns (scratch, table, streams, events). Synchronises
- * the device first. NULL is accepted. */
+/* Free what the context owns (scratch, table, streams, events): the buffers
+ * of struct MoeV41 above. Caller-owned memory (slot arena, host arena,
+ * weights) is not touched. Synchronises the device first. NULL is accepted. */
 int moe_destroy(moe_ctx* ctx);
 
 /* Byte layout of one routed expert's slice (the analogue of metrale's
@@ -155,7 +171,11 @@ int moe_pack_expert(const moe_cfg* cfg, const void* src, void* dst, void* stream
 
 /* Give the context a caller-owned device arena of n_slots slices of slot_bytes
  * (256-byte aligned base) and reset the slot table to "nothing resident".
- * MOE_EINVAL for NULL / n_slots < 1 / a misaligned base. */
+ * The arena is the ExpertArena whose slots the ExpertLru fills with the picked
+ * experts' raw slices (metrale moe_v41 module documentation; the analogue of
+ * arena_of on the MoeV41 struct documentation), and the table the
+ * [n_routed] i32 slot_table of struct MoeV41 (moe_v41.rs source view: -1 = not
+ * resident). MOE_EINVAL for NULL / n_slots < 1 / a misaligned base. */
 int moe_set_slots(moe_ctx* ctx, void* arena_dev, int32_t n_slots);
 
 /* Slot table (metrale's slot_table_set): expert -> slot, -1 = not resident.
@@ -168,7 +188,10 @@ int moe_slot_evict(moe_ctx* ctx, int32_t expert);
 int moe_slot_of(const moe_ctx* ctx, int32_t expert, int32_t* slot);
 
 /* Optional page-locked host arena holding every routed expert's slice,
- * expert e at host + e * expert_stride (expert_stride >= slot_bytes). With it,
+ * expert e at host + e * expert_stride (expert_stride >= slot_bytes): the
+ * ExpertSource that misses are read from (metrale moe_v41 module
+ * documentation; the MoeV41 struct documentation's forward takes the
+ * ExpertLru and the source). With it,
  * every moe_forward reads its picks back (one host wait), copies the picked
  * experts that are not resident into device slots (least recently used slots
  * reused, hipMemcpyAsync on the context's copy stream, fenced by events) and
@@ -201,6 +224,27 @@ int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t 
 int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16,
                    float* weights_out, int32_t* idx_out, void* stream);
 
+/* How a call of m tokens with this shared-expert format (MOE_SHARED_*) runs, for
+ * callers that account the bytes each kernel class reads (the per-kernel times
+ * of moe_kernel_times): which routing and expert kernels run, and where the
+ * rows of a bf16 shared expert are computed. The expert path holds for calls
+ * whose picks are all resident or fit one slot wave (several waves run the
+ * GEMV kernels). The selection rule follows the metrale moe_v41 module
+ * documentation (GEMVs for small groups, MMQ above eight rows) as this library
+ * applies it per call. MOE_EINVAL for NULL, m outside 1..max_tokens or a bad
+ * shared_fmt. */
+#define MOE_PATH_DECODE 0   /* m <= 8, K-quant experts: gate/up writing q8_1(h), then down + combine */
+#define MOE_PATH_GEMV 1     /* chunked GEMV kernels (MXFP4 experts up to 8 tokens, slot waves, MIXED groups) */
+#define MOE_PATH_MMQ 2      /* the expert-grouped matrix-core kernels (above 8 tokens) */
+typedef struct moe_plan {
+    int32_t small_routing;      /* 1: one workgroup runs the top-k and bucketing (m <= 8, m * topk <= 512) */
+    int32_t expert_path;        /* MOE_PATH_* */
+    int32_t shared_rows_router; /* bf16 shared gate/up rows computed by extra workgroups of the router launch */
+    int32_t shared_rows_topk;   /* bf16 shared down rows (0..n-1) in the top-k launch */
+    int32_t shared_rows_gateup; /* the rest of them in the routed gate/up launch */
+} moe_plan;
+int moe_plan_call(const moe_ctx* ctx, int32_t m, int32_t shared_fmt, moe_plan* out);
+
 /* How a call of more than 8 tokens runs the routed experts, by group size (the
  * rows that picked one expert). MOE_DISPATCH_MMQ (the default): every group on
  * the int8 matrix-core (MMQ) kernels, the smallest in 16-row tiles.
@@ -223,7 +267,11 @@ int moe_set_dispatch(moe_ctx* ctx, int32_t mode);
 int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_out, float* d_out, void* stream);
 
 /* Synchronise `stream` and return (then clear) the device error word of the
- * calls queued so far: MOE_OK, MOE_ENONFINITE or MOE_ENOTRESIDENT. */
+ * calls queued so far: MOE_OK, MOE_ENONFINITE or MOE_ENOTRESIDENT. The first
+ * is metrale's route_from_logits panic on a NaN key (moe_v41.rs source view),
+ * raised here as a flag by the device top-k; the second a pick whose slot
+ * table entry is -1 (struct MoeV41's slot_table) with no source to read it
+ * from. Other counters (near ties) are left alone. */
 int moe_check(moe_ctx* ctx, void* stream);
 
 /* Per-kernel timing for benchmarks. With profiling on, every kernel launch of

@@ -32,12 +32,16 @@ MOE_EXPERT_MXFP4 = 1
 MOE_DISPATCH_MMQ = 0
 MOE_DISPATCH_MIXED = 1
 
+MOE_PATH_DECODE = 0
+MOE_PATH_GEMV = 1
+MOE_PATH_MMQ = 2
+
 EXPORTED = (
     "moe_create", "moe_destroy", "moe_expert_layout", "moe_pack_expert", "moe_set_slots", "moe_slot_bind",
     "moe_slot_evict",
     "moe_slot_of", "moe_set_host_arena", "moe_route", "moe_forward", "moe_forward_ex", "moe_check",
     "moe_get_stats", "moe_reset_stats", "moe_strerror", "moe_quantize_q8_1", "moe_set_profiling",
-    "moe_kernel_times", "moe_set_dispatch",
+    "moe_kernel_times", "moe_set_dispatch", "moe_plan_call",
 )
 
 KERNEL_CLASSES = ("router", "quant_h", "topk", "bucket", "gateup", "shared_gateup", "down", "shared_down",
@@ -79,6 +83,18 @@ class moe_stats(ctypes.Structure):
         ("waves", ctypes.c_uint64),
         ("route_ms", ctypes.c_double),
         ("fetch_ms", ctypes.c_double),
+        ("compute_ms", ctypes.c_double),
+        ("near_ties", ctypes.c_uint64),
+    ]
+
+
+class moe_plan(ctypes.Structure):
+    _fields_ = [
+        ("small_routing", ctypes.c_int32),
+        ("expert_path", ctypes.c_int32),
+        ("shared_rows_router", ctypes.c_int32),
+        ("shared_rows_topk", ctypes.c_int32),
+        ("shared_rows_gateup", ctypes.c_int32),
     ]
 
 
@@ -120,6 +136,7 @@ def lib():
             "moe_set_profiling": [vp, i32],
             "moe_set_dispatch": [vp, i32],
             "moe_kernel_times": [vp, P(ctypes.c_double), P(ctypes.c_int64), i32],
+            "moe_plan_call": [vp, i32, i32, P(moe_plan)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -235,6 +252,13 @@ def moe_forward(ctx, w, x, m, out, stream=None):
 def moe_forward_ex(ctx, w, x, m, out, weights_out=None, idx_out=None, stream=None):
     return _check(lib().moe_forward_ex(ctx, ctypes.byref(w), _ptr(x), m, _ptr(out), _ptr(weights_out),
                                        _ptr(idx_out), _stream(stream)), "moe_forward_ex")
+
+
+def moe_plan_call(ctx, m, shared_fmt):
+    """-> dict of the moe_plan fields for a call of m tokens."""
+    p = moe_plan()
+    _check(lib().moe_plan_call(ctx, m, shared_fmt, ctypes.byref(p)), "moe_plan_call")
+    return {f: getattr(p, f) for f, _ in moe_plan._fields_}
 
 
 def moe_quantize_q8_1(x, rows, cols, q_out, d_out, stream=None):

@@ -6,7 +6,9 @@
 #include <algorithm>
 #include <chrono>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "moe.h"
@@ -62,7 +64,6 @@ struct moe_ctx {
     Chunk* chunks = nullptr;
     float* h_routed = nullptr;
     uint8_t* hrec = nullptr;
-    float* h_dec = nullptr;
     float* h_shared = nullptr;
     int8_t* hq_routed = nullptr;
     float* hd_routed = nullptr;
@@ -97,6 +98,11 @@ struct moe_ctx {
     uint64_t tick = 0;
     std::vector<hipEvent_t> ev_copy, ev_wave, ev_c0, ev_c1;   // per wave
     mutable std::vector<std::pair<hipEvent_t, hipEvent_t>> fetch_pending;
+    // expert-compute time of calls with a host arena or with profiling on: an event
+    // pair per call, read when the counters are read
+    std::vector<hipEvent_t> ev_comp;
+    size_t comp_next = 0;
+    mutable std::vector<std::pair<hipEvent_t, hipEvent_t>> comp_pending;
     mutable moe_stats stats;
     // per-kernel timing
     bool prof = false;
@@ -112,6 +118,55 @@ struct moe_ctx {
 };
 
 namespace {
+
+// The per-call device buffers of a context sized for M tokens, carved from one
+// allocation at `base` (views set on ctx when base is not NULL); returns the
+// bytes needed. decode_only: just what a call of M <= 8 tokens on the decode
+// kernels (K-quant experts, every pick resident) touches, for the static
+// scratch of moe_forward_static; the other views stay NULL.
+size_t carve_scratch(moe_ctx* ctx, size_t M, bool decode_only, uint8_t* base) {
+    const moe_cfg& c = ctx->cfg;
+    const size_t E = c.n_routed, D = c.dim, I = c.inter;
+    const size_t P = M * c.topk;
+    const size_t m_small = std::min<size_t>(M, ROUTE_SMALL_MAX_M);
+    Carver cv;
+    auto view = [&](auto*& field, size_t off) {
+        if (base != nullptr) field = reinterpret_cast<std::remove_reference_t<decltype(field)>>(base + off);
+    };
+    // the router's partial logits: up to 8 splits of m rows, within 4096 rows (one split at m <= 8)
+    const int logit_rows = decode_only ? (int)M : (int)std::max<size_t>(M, std::min<size_t>(8 * M, 4096));
+    if (base != nullptr) ctx->logit_rows = logit_rows;
+    view(ctx->logits, cv.take<float>((size_t)logit_rows * E));
+    view(ctx->idx, cv.take<int32_t>(P));
+    view(ctx->gw, cv.take<float>(P));
+    view(ctx->xq, cv.take<int8_t>(M * D));
+    view(ctx->xd, cv.take<float>(M * D / QB));
+    view(ctx->xs16, cv.take<int32_t>(M * D / 16));
+    view(ctx->xs16f, cv.take<float>(M * D / 16));
+    view(ctx->offsets, cv.take<int32_t>(E + 1));
+    view(ctx->active, cv.take<int32_t>(E));
+    view(ctx->n_active, cv.take<int32_t>(1));
+    view(ctx->n_chunks, cv.take<int32_t>(PLAN_LISTS));
+    view(ctx->perm, cv.take<int32_t>(P));
+    view(ctx->inv, cv.take<int32_t>(P));
+    view(ctx->chunks, cv.take<Chunk>(decode_only ? m_small * (c.topk + 1) + 1 : (size_t)ctx->max_chunks));
+    view(ctx->h_shared, cv.take<float>(M * I));
+    view(ctx->ys, cv.take<float>(M * D));
+    view(ctx->hrec, cv.take<uint8_t>(m_small * (c.topk + 1) * decode_rec_bytes((int)I)));
+    view(ctx->err, cv.take<int32_t>(STATUS_WORDS));
+    if (!decode_only) {
+        view(ctx->h_routed, cv.take<float>(P * I));
+        view(ctx->hq_routed, cv.take<int8_t>(P * I));
+        view(ctx->hd_routed, cv.take<float>(P * I / QB));
+        view(ctx->hs_routed, cv.take<int32_t>(P * I / 16));
+        view(ctx->hq_shared, cv.take<int8_t>(M * I));
+        view(ctx->hd_shared, cv.take<float>(M * I / QB));
+        view(ctx->hs_shared, cv.take<int32_t>(M * I / 16));
+        view(ctx->e_rows, cv.take<float>(P * D));
+        view(ctx->slot_table_dev, cv.take<int32_t>(E));
+    }
+    return align_up(cv.off, 256);
+}
 
 int check_cfg(const moe_cfg* c) {
     if (c == nullptr) return MOE_EINVAL;
@@ -216,6 +271,39 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
     if (!aligned(w->shared_w1, 16) || !aligned(w->shared_w3, 16) || !aligned(w->shared_w2, 16)) return MOE_EINVAL;
     if (w->shared_fmt == MOE_SHARED_BF16 && ctx->cfg.dim > 8192) return MOE_EINVAL;
     return MOE_OK;
+}
+
+// How a call of m tokens runs: the routing kernels (small: one workgroup for the
+// top-k and bucketing, m <= 8), the expert kernels (MMQ above 8 tokens where the
+// tiles fit; the decode kernels for K-quant experts up to 8 tokens), and where a
+// bf16 shared expert's rows go. Up to 8 tokens with every pick resident (no host
+// arena) the bf16 shared expert rides in the routed launches: its gate/up rows as
+// extra workgroups of the router launch, its down rows (into ys, added by the
+// routed down kernel or, for MXFP4 experts, by the combine kernel) as extra
+// workgroups of the top-k launch; with K-quant experts the second half of the
+// down rows goes to the routed gate/up launch instead, whose workgroups leave CU
+// slots free (the top-k launch is then shorter and gate/up hardly longer). No
+// second stream then.
+struct CallPlan {
+    bool small, use_mmq, fp4, decode, shared_fused;
+    int sh_router_rows, sh_topk_rows, sh_gateup_rows;
+};
+
+CallPlan plan_call(const moe_ctx* ctx, int m, int shared_fmt) {
+    const moe_cfg& c = ctx->cfg;
+    CallPlan pl{};
+    pl.small = m <= ROUTE_SMALL_MAX_M && m * c.topk <= ROUTE_SMALL_MAX_PAIRS;
+    pl.use_mmq = !pl.small && ctx->mmq_ok;
+    pl.fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
+    pl.decode = pl.small && ctx->decode_ok;
+    pl.shared_fused = shared_fmt == MOE_SHARED_BF16 && pl.small && (ctx->decode_ok || pl.fp4) &&
+                      ctx->host_arena == nullptr;
+    if (pl.shared_fused) {
+        pl.sh_router_rows = c.inter;
+        pl.sh_gateup_rows = ctx->decode_ok ? c.dim - c.dim / 2 : 0;
+        pl.sh_topk_rows = c.dim - pl.sh_gateup_rows;
+    }
+    return pl;
 }
 
 // router logits and the top-k into (idx, gw) (moe_route)
@@ -345,9 +433,8 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     }
     ctx->decode_ok = !fp4 && decode_supported(c.dim, c.inter);
     ctx->mmq_ok = fp4 ? fp4_mmq_supported(c.dim, c.inter) : mmq_supported(c.dim, c.inter);
-    const size_t M = c.max_tokens, E = c.n_routed, D = c.dim, I = c.inter;
-    const size_t P = M * c.topk;
-    ctx->max_pairs = (int)P;
+    const size_t M = c.max_tokens;
+    ctx->max_pairs = (int)(M * c.topk);
     // room for the GEMV list, the MMQ plan of any m <= max_tokens (both grow with
     // m) and the single-row chunks of the small-batch routing
     const int m_small = (int)std::min<size_t>(M, ROUTE_SMALL_MAX_M);
@@ -357,75 +444,17 @@ int moe_create(const moe_cfg* cfg, moe_ctx** out) {
     ctx->max_chunks = std::max(ctx->max_chunks, m_small * (c.topk + 1) + 1);
     layout_of(c, ctx->slot_bytes, ctx->off_w1, ctx->off_w3, ctx->off_w2);
 
-    Carver cv;
-    // the router's partial logits: up to 8 splits of m rows, within 4096 rows
-    ctx->logit_rows = (int)std::max<size_t>(M, std::min<size_t>(8 * M, 4096));
-    const size_t o_logits = cv.take<float>((size_t)ctx->logit_rows * E);
-    const size_t o_idx = cv.take<int32_t>(P);
-    const size_t o_gw = cv.take<float>(P);
-    const size_t o_xq = cv.take<int8_t>(M * D);
-    const size_t o_xd = cv.take<float>(M * D / QB);
-    const size_t o_xs = cv.take<int32_t>(M * D / 16);
-    const size_t o_xsf = cv.take<float>(M * D / 16);
-    const size_t o_off = cv.take<int32_t>(E + 1);
-    const size_t o_act = cv.take<int32_t>(E);
-    const size_t o_nact = cv.take<int32_t>(1);
-    const size_t o_nch = cv.take<int32_t>(PLAN_LISTS);
-    const size_t o_perm = cv.take<int32_t>(P);
-    const size_t o_inv = cv.take<int32_t>(P);
-    const size_t o_ch = cv.take<Chunk>(ctx->max_chunks);
-    const size_t o_hr = cv.take<float>(P * I);
-    const size_t o_hs = cv.take<float>(M * I);
-    const size_t o_hqr = cv.take<int8_t>(P * I);
-    const size_t o_hdr = cv.take<float>(P * I / QB);
-    const size_t o_hsr = cv.take<int32_t>(P * I / 16);
-    const size_t o_hqs = cv.take<int8_t>(M * I);
-    const size_t o_hds = cv.take<float>(M * I / QB);
-    const size_t o_hss = cv.take<int32_t>(M * I / 16);
-    const size_t o_er = cv.take<float>(P * D);
-    const size_t o_ys = cv.take<float>(M * D);
-    const size_t o_rec = cv.take<uint8_t>((size_t)m_small * (c.topk + 1) * decode_rec_bytes((int)I));
-    const size_t o_hdec = cv.take<float>((size_t)m_small * (c.topk + 1) * I);
-    const size_t o_err = cv.take<int32_t>(1);
-    const size_t o_tab = cv.take<int32_t>(E);
-    const size_t total = align_up(cv.off, 256);
+    const size_t total = carve_scratch(ctx, M, false, nullptr);
     if (hipMalloc((void**)&ctx->dev, total) != hipSuccess) {
         delete ctx;
         return MOE_ENOMEM;
     }
-    uint8_t* b = ctx->dev;
-    ctx->logits = (float*)(b + o_logits);
-    ctx->idx = (int32_t*)(b + o_idx);
-    ctx->gw = (float*)(b + o_gw);
-    ctx->xq = (int8_t*)(b + o_xq);
-    ctx->xd = (float*)(b + o_xd);
-    ctx->xs16 = (int32_t*)(b + o_xs);
-    ctx->xs16f = (float*)(b + o_xsf);
-    ctx->offsets = (int32_t*)(b + o_off);
-    ctx->active = (int32_t*)(b + o_act);
-    ctx->n_active = (int32_t*)(b + o_nact);
-    ctx->n_chunks = (int32_t*)(b + o_nch);
-    ctx->perm = (int32_t*)(b + o_perm);
-    ctx->inv = (int32_t*)(b + o_inv);
-    ctx->chunks = (Chunk*)(b + o_ch);
-    ctx->h_routed = (float*)(b + o_hr);
-    ctx->h_shared = (float*)(b + o_hs);
-    ctx->hq_routed = (int8_t*)(b + o_hqr);
-    ctx->hd_routed = (float*)(b + o_hdr);
-    ctx->hs_routed = (int32_t*)(b + o_hsr);
-    ctx->hq_shared = (int8_t*)(b + o_hqs);
-    ctx->hd_shared = (float*)(b + o_hds);
-    ctx->hs_shared = (int32_t*)(b + o_hss);
-    ctx->e_rows = (float*)(b + o_er);
-    ctx->hrec = b + o_rec;
-    ctx->h_dec = (float*)(b + o_hdec);
-    ctx->ys = (float*)(b + o_ys);
-    ctx->err = (int32_t*)(b + o_err);
-    ctx->slot_table_dev = (int32_t*)(b + o_tab);
+    carve_scratch(ctx, M, false, ctx->dev);
     if (hipMemset(ctx->dev, 0, total) != hipSuccess) {
         moe_destroy(ctx);
         return MOE_EHIP;
     }
+    const size_t E = c.n_routed;
     if (hipHostMalloc((void**)&ctx->slot_host, sizeof(int32_t) * E, hipHostMallocDefault) != hipSuccess) {
         moe_destroy(ctx);
         return MOE_ENOMEM;
@@ -456,6 +485,7 @@ int moe_destroy(moe_ctx* ctx) {
     if (ctx->idx_host) (void)hipHostFree(ctx->idx_host);
     if (ctx->view_host) (void)hipHostFree(ctx->view_host);
     for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ctx->ev_comp) (void)hipEventDestroy(e);
     if (ctx->slot_host) (void)hipHostFree(ctx->slot_host);
     if (ctx->dev) (void)hipFree(ctx->dev);
     delete ctx;
@@ -567,6 +597,26 @@ static void collect_fetch_times(const moe_ctx* ctx) {
             ctx->stats.fetch_ms += ms;
     }
     ctx->fetch_pending.clear();
+    for (const auto& pr : ctx->comp_pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(pr.second) == hipSuccess && hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess)
+            ctx->stats.compute_ms += ms;
+    }
+    ctx->comp_pending.clear();
+}
+
+// the next start/stop pair for a call's expert-compute time (nullptr pair: none)
+static std::pair<hipEvent_t, hipEvent_t> compute_events(moe_ctx* ctx) {
+    if (ctx->comp_pending.size() >= 1024) collect_fetch_times(ctx);   // bounded: read the oldest back
+    if (ctx->comp_pending.empty()) ctx->comp_next = 0;   // every pair was read back
+    while (ctx->ev_comp.size() < ctx->comp_next + 2) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return {nullptr, nullptr};
+        ctx->ev_comp.push_back(e);
+    }
+    const size_t i = ctx->comp_next;
+    ctx->comp_next += 2;
+    return {ctx->ev_comp[i], ctx->ev_comp[i + 1]};
 }
 
 // Read the picks back (the one host wait of a streamed call) and split the
@@ -677,17 +727,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     rc = upload_table(ctx, st);
     if (rc != MOE_OK) return rc;
     const bool bf16_shared = w->shared_fmt == MOE_SHARED_BF16;
-    const bool small = m <= ROUTE_SMALL_MAX_M && P <= ROUTE_SMALL_MAX_PAIRS;
-    const bool use_mmq = !small && ctx->mmq_ok;
-    // decode with every picked expert in its slot: the bf16 shared expert rides in
-    // the routed launches, its gate/up rows as extra workgroups of the router
-    // launch, its down rows (into ys, added by the routed down kernel or, for
-    // MXFP4 experts, by the combine kernel) as extra workgroups of the top-k
-    // launch; with K-quant experts half of the down rows go to the routed gate/up
-    // launch instead, whose workgroups leave CU slots free (the top-k launch is
-    // then shorter and gate/up hardly longer); no second stream
-    const bool fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
-    const bool shared_fused = bf16_shared && small && (ctx->decode_ok || fp4) && ctx->host_arena == nullptr;
+    const CallPlan pl = plan_call(ctx, m, w->shared_fmt);
+    const bool small = pl.small, use_mmq = pl.use_mmq, fp4 = pl.fp4, shared_fused = pl.shared_fused;
     SharedRows sr_a{}, sr_b{}, sr_c{};
     if (shared_fused) {
         sr_a.w1 = (const uint16_t*)w->shared_w1;
@@ -700,18 +741,15 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         sr_a.limit = c.swiglu_limit;
         sr_b = sr_a;
         sr_a.row0 = 0;
-        sr_a.rows = c.inter;
+        sr_a.rows = pl.sh_router_rows;
         sr_b.w1 = sr_b.w3 = nullptr;
         sr_b.w2 = (const uint16_t*)w->shared_w2;
         sr_b.ys = ctx->ys;
         sr_b.row0 = 0;
-        sr_b.rows = c.dim;
-        if (ctx->decode_ok) {   // K-quant experts: the second half of the down rows rides in the gate/up launch
-            sr_c = sr_b;
-            sr_c.row0 = c.dim / 2;
-            sr_c.rows = c.dim - c.dim / 2;
-            sr_b.rows = c.dim / 2;
-        }
+        sr_b.rows = pl.sh_topk_rows;
+        sr_c = sr_b;
+        sr_c.row0 = pl.sh_topk_rows;
+        sr_c.rows = pl.sh_gateup_rows;
     }
     if (bf16_shared && !shared_fused) {
         // the shared expert needs only x: run it beside the routing and the routed experts
@@ -796,7 +834,6 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.xs16f = ctx->xs16f;
     a.h_routed = ctx->h_routed;
     a.hrec = ctx->hrec;
-    a.h_dec = ctx->h_dec;
     a.h_shared = ctx->h_shared;
     a.hq_routed = ctx->hq_routed;
     a.hd_routed = ctx->hd_routed;
@@ -825,6 +862,18 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
                 return MOE_EHIP;
         }
     }
+    // the expert-compute time of this call (calls with a host arena or with profiling on)
+    std::pair<hipEvent_t, hipEvent_t> comp{nullptr, nullptr};
+    if (ctx->host_arena != nullptr || ctx->prof) {
+        comp = compute_events(ctx);
+        if (comp.first == nullptr || hipEventRecord(comp.first, st) != hipSuccess) return MOE_EHIP;
+    }
+    auto end_compute = [&]() -> int {
+        if (comp.first == nullptr) return MOE_OK;
+        if (hipEventRecord(comp.second, st) != hipSuccess) return MOE_EHIP;
+        ctx->comp_pending.push_back(comp);
+        return MOE_OK;
+    };
     if (small && ctx->decode_ok && waves.size() <= 1) {
         // one single-row chunk per pick (and per token of a K-quant shared expert):
         // gate/up writes q8_1(h) records, down accumulates G E per token and stores bf16
@@ -836,6 +885,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         rc = timed(ctx, st, MOE_K_DOWN, [&] {
             return launch_down_combine(a, P, m, nch, ys, (uint16_t*)out_bf16, st);
         });
+        if (rc != MOE_OK) return rc;
+        rc = end_compute();
         if (rc != MOE_OK) return rc;
         return finish_call(ctx, weights_out, idx_out, P, st);
     }
@@ -901,11 +952,26 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         return launch_combine(ctx->e_rows, ys_all, ctx->gw, ctx->inv, m, c.topk, c.dim, (uint16_t*)out_bf16, st);
     });
     if (rc != MOE_OK) return rc;
+    rc = end_compute();
+    if (rc != MOE_OK) return rc;
     return finish_call(ctx, weights_out, idx_out, P, st);
 }
 
 int moe_forward(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32_t m, void* out_bf16, void* stream) {
     return moe_forward_ex(ctx, w, x_bf16, m, out_bf16, nullptr, nullptr, stream);
+}
+
+int moe_plan_call(const moe_ctx* ctx, int32_t m, int32_t shared_fmt, moe_plan* out) {
+    if (ctx == nullptr || out == nullptr || m < 1 || m > ctx->cfg.max_tokens) return MOE_EINVAL;
+    if (shared_fmt != MOE_SHARED_NONE && shared_fmt != MOE_SHARED_BF16 && shared_fmt != MOE_SHARED_KQUANT)
+        return MOE_EINVAL;
+    const CallPlan pl = plan_call(ctx, m, shared_fmt);
+    out->small_routing = pl.small ? 1 : 0;
+    out->expert_path = pl.use_mmq ? MOE_PATH_MMQ : pl.decode ? MOE_PATH_DECODE : MOE_PATH_GEMV;
+    out->shared_rows_router = pl.sh_router_rows;
+    out->shared_rows_topk = pl.sh_topk_rows;
+    out->shared_rows_gateup = pl.sh_gateup_rows;
+    return MOE_OK;
 }
 
 int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_out, float* d_out, void* stream) {
@@ -971,15 +1037,24 @@ int moe_kernel_times(moe_ctx* ctx, double* ms_sum, int64_t* launches, int32_t n)
 
 int moe_get_stats(const moe_ctx* ctx, moe_stats* out) {
     if (ctx == nullptr || out == nullptr) return MOE_EINVAL;
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
     collect_fetch_times(ctx);
+    uint32_t near = 0;
+    if (hipMemcpy(&near, ctx->err + ERR_NEAR_TIES, sizeof(near), hipMemcpyDeviceToHost) != hipSuccess)
+        return MOE_EHIP;
     *out = ctx->stats;
+    out->near_ties = near;
     return MOE_OK;
 }
 
 int moe_reset_stats(moe_ctx* ctx) {
     if (ctx == nullptr) return MOE_EINVAL;
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
     collect_fetch_times(ctx);
     std::memset(&ctx->stats, 0, sizeof(ctx->stats));
+    const uint32_t zero = 0;
+    if (hipMemcpy(ctx->err + ERR_NEAR_TIES, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+        return MOE_EHIP;
     return MOE_OK;
 }
 

@@ -33,16 +33,20 @@ MOE_DEV __host__ int panel_off(int r, int s, int nsb, int B) {
 // code bytes are its 64 rows x 64 bytes, row after row (4096 bytes per tile);
 // after all codes come the scale bytes, 64 rows x 4 per tile in the same order.
 // Piece p of row r is the 16 code bytes and the scale of weights 32p..32p+31.
-MOE_DEV __host__ inline size_t fp4_code_off(int r, int p, int K) {
+MOE_DEV __host__ size_t fp4_code_off(int r, int p, int K) {
     return ((size_t)((r >> 6) * (K >> 7) + (p >> 2)) * 64 + (r & 63)) * 64 + (p & 3) * 16;
 }
-MOE_DEV __host__ inline size_t fp4_scale_off(int r, int p, int K) {   // from the end of the codes
+MOE_DEV __host__ size_t fp4_scale_off(int r, int p, int K) {   // from the end of the codes
     return ((size_t)((r >> 6) * (K >> 7) + (p >> 2)) * 64 + (r & 63)) * 4 + (p & 3);
 }
 
-// device error word bits
+// device error word bits (word 0 of the context's status words)
 constexpr int ERR_NONFINITE = 1;
 constexpr int ERR_NOTRESIDENT = 2;
+// word 1 of the status words: tokens whose k-th and (k+1)-th keys were a near
+// tie (an unsigned count, added to by the top-k kernels)
+constexpr int ERR_NEAR_TIES = 1;
+constexpr int STATUS_WORDS = 2;
 // slot-table entries: >= 0 a slot; -1 not resident (an error when picked);
 // SLOT_SKIP: picked, but computed in another slot wave of this call (the kernels skip it)
 constexpr int SLOT_NONE = -1;
@@ -89,7 +93,6 @@ struct ExpertArgs {
     int32_t* hs_shared;
     float* e_rows;              // f32 [pairs, D] in position order
     float* ys;                  // f32 [m, D]
-    float* h_dec;               // decode path: f32 h rows (routed positions, then shared-expert tokens)
     uint8_t* hrec;              // decode path: q8_1 record of each h row, [quants I | d f32 I/32 | 16-sums i32 I/16]
     int32_t D, I;
     float limit;

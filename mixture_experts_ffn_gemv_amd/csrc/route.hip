@@ -216,12 +216,14 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
     __builtin_amdgcn_wave_barrier();   // the wavefront's LDS stores come before its reads of them
     int my_e;
     float my_s;
-    wave_topk<KPL>(keys[wv], scores[wv], E, k, my_e, my_s);
+    bool near;
+    wave_topk<KPL>(keys[wv], scores[wv], E, k, my_e, my_s, near);
     const float w = wave_pick_weight(my_s, k, norm, route_scale);
     if (lane < k) {
         idx[(size_t)t * k + lane] = my_e;
         gw[(size_t)t * k + lane] = w;
     }
+    if (near && lane == 0) atomicAdd(reinterpret_cast<unsigned*>(err + ERR_NEAR_TIES), 1u);
 }
 
 // ---------------------------------------------------------------- bucketing
@@ -410,7 +412,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     if (wv < m) {   // wavefront t: token t's picks, in order, and their weights
         int my_e;
         float my_s;
-        wave_topk<KPL>(keys[wv], scores[wv], E, k, my_e, my_s);
+        bool near;
+        wave_topk<KPL>(keys[wv], scores[wv], E, k, my_e, my_s, near);
         const float w = wave_pick_weight(my_s, k, norm, route_scale);
         if (lane < k) {
             pick_e[wv * k + lane] = my_e;
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
             idx[wv * k + lane] = my_e;
             gw[wv * k + lane] = w;
         }
+        if (near && lane == 0) atomicAdd(reinterpret_cast<unsigned*>(err + ERR_NEAR_TIES), 1u);
     }
     if (__any(bad_any) && (tid & 63) == 0) atomicOr(err, ERR_NONFINITE);
     const int P = m * k;
@@ -486,11 +490,14 @@ MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int
                        int32_t* __restrict__ idx, float* __restrict__ gw, int shared_chunks,
                        int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                        int32_t* __restrict__ perm, int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
-                       int32_t* __restrict__ n_chunks, const int32_t* __restrict__ slot_table) {
+                       int32_t* __restrict__ n_chunks, const int32_t* __restrict__ slot_table,
+                       int32_t* __restrict__ err) {
     const int lane = threadIdx.x;
     int my_e;
     float my_s;
-    wave_topk<KPL>(keys, scores, E, k, my_e, my_s);
+    bool near;
+    wave_topk<KPL>(keys, scores, E, k, my_e, my_s, near);
+    if (near && lane == 0) atomicAdd(reinterpret_cast<unsigned*>(err + ERR_NEAR_TIES), 1u);
     const float wgt = wave_pick_weight(my_s, k, norm, route_scale);
     // the picks sorted by expert id (all distinct): position = rank of the id
     int pos = 0;
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict_
     __syncthreads();
     if (tid >= 64) return;
     select_m1<KPL>(keys, scores, E, k, norm, route_scale, idx, gw, shared_chunks, offsets, active, n_active, perm, inv,
-              chunks, n_chunks, slot_table);
+              chunks, n_chunks, slot_table, err);
 }
 
 // After experts were streamed into slots: the single-row chunks of the small-batch

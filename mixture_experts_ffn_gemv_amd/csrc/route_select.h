@@ -1,7 +1,5 @@
-// Device pieces of the routing shared by the routing kernels and the decode
-// gate/up kernel (which repeats the one-token selection per workgroup): the
-// score and key of an expert, and the top-k of up to 64 * KPL keys by a single
-// wavefront.
+// Device pieces of the routing kernels: the score and key of an expert, and
+// the top-k of up to 64 * KPL keys by a single wavefront.
 //
 // Semantics (metrale moe_v41.rs route_from_logits; Open Model Atlas router
 // equations for DeepSeek V4.1): v = z / gate_temp; softplus(v) = v above 20,
@@ -88,20 +86,29 @@ MOE_DEV int ordered_key(float f) {
 // Keys per lane for the one-wavefront top-k of E keys.
 constexpr int topk_kpl(int E) { return E <= 128 ? 2 : E <= 384 ? 6 : 16; }
 
+// The float key behind an ordered int (the inverse of ordered_key).
+MOE_DEV float key_of_ordered(int o) { return __int_as_float(o >= 0 ? o : o ^ 0x7FFFFFFF); }
+
+// Gap below which the k-th and (k+1)-th keys of a token count as a near tie
+// (the selection there may differ from an exact one by rounding alone).
+constexpr float NEAR_TIE_GAP = 1e-5f;
+
 // The k (<= min(64, E)) largest of E <= 64 * KPL keys in LDS, by one whole
 // wavefront, without branches. Lane l holds keys l, l + 64, ... as ordered
 // ints; each of the k rounds takes the largest remaining key across the
 // wavefront and the lowest id holding it (inside a lane the ids grow with the
 // index, so a strict comparison keeps the lowest), then sets it to INT_MIN.
 // The winner is wavefront-uniform, so lane r < k ends with pick r's expert and
-// its score (from `scores`).
+// its score (from `scores`). `near` (wavefront-uniform) is set when k < E and
+// the k-th key exceeds the largest key left out by less than NEAR_TIE_GAP.
 template <int KPL>
-MOE_DEV void wave_topk(const float* keys, const float* scores, int E, int k, int& my_e, float& my_s) {
+MOE_DEV void wave_topk(const float* keys, const float* scores, int E, int k, int& my_e, float& my_s, bool& near) {
     const int lane = threadIdx.x & 63;
     int kk[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) kk[i] = lane + 64 * i < E ? ordered_key(keys[lane + 64 * i]) : INT_MIN;
     my_e = 0;
+    int kth = INT_MIN;
     for (int r = 0; r < k; ++r) {
         int bk = kk[0], bi = lane;
 #pragma unroll
@@ -115,8 +122,17 @@ MOE_DEV void wave_topk(const float* keys, const float* scores, int E, int k, int
 #pragma unroll
         for (int i = 0; i < KPL; ++i) kk[i] = lane + 64 * i == win ? INT_MIN : kk[i];
         my_e = lane == r ? win : my_e;
+        kth = kmax;
     }
     my_s = lane < k ? scores[my_e] : 0.f;
+    near = false;
+    if (k < E) {   // the largest key left out (a real key: E > k of them exist)
+        int bk = kk[0];
+#pragma unroll
+        for (int i = 1; i < KPL; ++i) bk = max(bk, kk[i]);
+        const int next = wave_max_i32(bk);
+        near = key_of_ordered(kth) - key_of_ordered(next) < NEAR_TIE_GAP;
+    }
 }
 
 // The routing weight of lane r's pick: the unbiased score, divided by (the sum

@@ -24,6 +24,7 @@ from .gen import (  # noqa: F401
     expert_layout,
     make_expert_slot,
     make_experts,
+    random_kquant_slot,
     make_router,
     make_shared,
     make_tokens,

@@ -236,6 +236,32 @@ def make_experts(shape, seed, std=0.02, device="cpu", experts=None, fmt="kquant"
     return arena
 
 
+def random_kquant_slot(shape, seed, d_log2=(-10.0, -8.0), d3_log2=(-12.0, -10.0)):
+    """An expert slice [W1 | W3 | W2] of random block bytes: every scale nibble,
+    six-bit scale, quant and hmask bit drawn uniformly, and the fp16 d (and
+    dmin) fields replaced by finite values of random sign with |d| = 2^u, u
+    uniform in d_log2 (Q2_K d and dmin) or d3_log2 (Q3_K d), so the weights stay
+    finite and of moderate size. Blocks no min/max encoder would write."""
+    size, o1, o3, o2 = expert_layout(shape)
+    g = _gen(stream_seed(seed, TAG_EXPERT, 1 << 20), "cpu")
+    raw = torch.randint(0, 256, (size,), generator=g, dtype=torch.int32).to(torch.uint8)
+
+    def fp16_fields(n, lo_hi):
+        mag = torch.exp2(torch.rand(n, generator=g) * (lo_hi[1] - lo_hi[0]) + lo_hi[0])
+        sign = torch.where(torch.rand(n, generator=g) < 0.5, -1.0, 1.0)
+        return _fp16_bytes(mag * sign)
+
+    n13 = shape.inter * (shape.dim // QK)
+    for off in (o1, o3):
+        blocks = raw[off:off + n13 * Q2K_BYTES].view(n13, Q2K_BYTES)
+        blocks[:, 80:82] = fp16_fields(n13, d_log2)
+        blocks[:, 82:84] = fp16_fields(n13, d_log2)
+    n2 = shape.dim * (shape.inter // QK)
+    blocks = raw[o2:o2 + n2 * Q3K_BYTES].view(n2, Q3K_BYTES)
+    blocks[:, 108:110] = fp16_fields(n2, d3_log2)
+    return raw
+
+
 def make_router(shape, seed, std, bias=(-0.1, 0.1)):
     """(router bf16 [n_routed, dim], bias f32 [n_routed]) on the CPU.
     bias: (lo, hi) for U(lo, hi), None for zero, or a tensor."""

@@ -117,6 +117,17 @@ class Layer:
         return oracle.moe_layer(self.oracle_cfg(), bits(x_rows), bits(self.wr), self.bias.numpy(),
                                 self.expert_bytes, self.oracle_shared())
 
+    def oracle_parallel(self, x_rows):
+        """As oracle(), with the rows dealt out to worker processes (real-shape
+        layers, many sampled rows)."""
+        import oracle
+        from oracle_pool import oracle_rows
+        picks = self.oracle_route(x_rows)[0]
+        cfg = self.oracle_cfg()
+        cfg_args = (cfg.dim, cfg.inter, cfg.n_routed, cfg.topk)
+        return oracle_rows(cfg_args, self.ocfg_kw, bits(x_rows), bits(self.wr), self.bias.numpy(),
+                           self.expert_bytes, self.oracle_shared(), picks)
+
     def oracle_route(self, x_rows):
         import oracle
         x = oracle.bf16_bits_to_f64(bits(x_rows))

@@ -77,3 +77,29 @@ def test_strerror_and_null_handling(lib):
     bad = moe.make_cfg(300, 256, 16, 2)
     assert lib.moe_create(ctypes.byref(bad), ctypes.byref(out)) == moe.MOE_EINVAL
     assert out.value is None
+
+
+C_TYPES = {"int32_t": ctypes.c_int32, "float": ctypes.c_float, "uint64_t": ctypes.c_uint64,
+           "double": ctypes.c_double, "const void*": ctypes.c_void_p, "const float*": ctypes.c_void_p}
+
+
+def header_struct(name):
+    """(type, field) pairs of `typedef struct name { ... } name;` in include/moe.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, flags=re.S).group(1)
+    return [(" ".join(t.split()), f) for t, f in re.findall(r"([A-Za-z_][\w ]*\*?)\s+(\w+);", body)]
+
+
+@pytest.mark.parametrize("name", ["moe_cfg", "moe_weights", "moe_stats", "moe_plan"])
+def test_binding_structs_match_header(name):
+    fields = header_struct(name)
+    binding = getattr(moe, name)._fields_
+    assert [f for _, f in fields] == [f for f, _ in binding]
+    for (ctype, f), (_, pytype) in zip(fields, binding):
+        assert ctypes.sizeof(C_TYPES[ctype]) == ctypes.sizeof(pytype), (name, f, ctype)
+
+
+def test_stats_carry_the_timing_fields_and_near_ties():
+    names = [f for _, f in header_struct("moe_stats")]
+    for f in ("hits", "misses", "bytes_copied", "route_ms", "fetch_ms", "compute_ms", "near_ties"):
+        assert f in names

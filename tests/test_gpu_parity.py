@@ -29,9 +29,10 @@ def check_layer(layer, x, label, sample_rows=None):
     idx_h, gw_h = idx.cpu().numpy(), gw.cpu().numpy()
     ridx, rg, rkeys, _ = layer.oracle_route(x)
     exempt = compare_routing(idx_h, gw_h, ridx, rg, rkeys)
-    rows = list(range(m)) if sample_rows is None else sample_rows
+    rows = list(range(m)) if sample_rows is None else sample_rows(idx_h) if callable(sample_rows) else sample_rows
     say(f"[{label}] routing ok ({exempt} near-tie exemptions); oracle on rows {rows}")
-    ref = layer.oracle(x[rows])
+    # several rows of a real-shape layer: the oracle in worker processes
+    ref = layer.oracle_parallel(x[rows]) if len(rows) > 2 and layer.shape.dim >= 2048 else layer.oracle(x[rows])
     got = out.float().cpu().numpy().astype(np.float64)[rows]
     worst = 0.0
     for j, t in enumerate(rows):
@@ -401,6 +402,9 @@ def test_real_small_batch_m8_kquant_shared(real_experts):
         layer.close()
 
 
+PREFILL_ROWS = [0, 31, 63, 64, 97, 128, 170, 213, 255, 256, 300, 341, 383, 384, 447, 480, 511]
+
+
 @pytest.mark.parametrize("dispatch", ["mixed", "mmq"])
 def test_real_prefill_m512(real_experts, dispatch):
     # uniform routing: about 8 rows per expert, so the mixed dispatch runs both the
@@ -409,6 +413,112 @@ def test_real_prefill_m512(real_experts, dispatch):
     layer = Layer(S.REAL, 1, bias=None, router_std=0.02, max_tokens=512, experts=real_experts, dispatch=mode)
     try:
         x = S.make_tokens(512, S.REAL.dim, 1, index=2)
-        check_layer(layer, x, f"prefill m=512 {dispatch}", sample_rows=[0, 511])
+        check_layer(layer, x, f"prefill m=512 {dispatch}", sample_rows=PREFILL_ROWS)
+    finally:
+        layer.close()
+
+
+HOT_EXPERTS = (5, 77, 140, 203, 266, 329)
+# every token picks the six hot experts, so group g holds all 512 tokens in token
+# order and its 64-row chunks end at tokens 63, 127, ...: rows on both sides of
+# every boundary, and the first and last rows
+HOT_ROWS = [0, 1, 63, 64, 127, 128, 191, 192, 255, 256, 319, 320, 383, 384, 447, 448, 510, 511]
+
+
+def test_real_prefill_hot_experts(real_experts):
+    # six 512-row groups, each eight 64-row chunks over 20 superblocks of K (gate/up)
+    # and 9 (down): the shape where the int8 matrix cores bind
+    bias = torch.zeros(S.REAL.n_routed)
+    bias[list(HOT_EXPERTS)] = 100.0
+    layer = Layer(S.REAL, 1, bias=bias, router_std=0.02, max_tokens=512, experts=real_experts)
+    try:
+        x = S.make_tokens(512, S.REAL.dim, 1, index=2)
+        _, _, idx = check_layer(layer, x, "prefill hot experts m=512", sample_rows=HOT_ROWS)
+        assert sorted(set(idx.cpu().numpy().reshape(-1).tolist())) == sorted(HOT_EXPERTS)
+    finally:
+        layer.close()
+
+
+# ----------------------------------------------------------------------------- random block bytes
+
+def random_byte_experts(shape, seed):
+    return torch.stack([S.random_kquant_slot(shape, seed + e) for e in range(shape.n_routed)])
+
+
+@pytest.mark.parametrize("m", [1, 5, 8, 24, 70])
+@pytest.mark.parametrize("shared", ["bf16", "kquant"])
+def test_random_block_bytes(m, shared):
+    # blocks no encoder writes: random scales, quants and high bits, fp16 d and dmin
+    # of either sign; m <= 8 runs the decode kernels, above that the MMQ classes
+    shape = S.LayerShape(512, 256, 16, 3)
+    experts = random_byte_experts(shape, 40)
+    layer = Layer(shape, 4, max_tokens=max(m, 8), experts=experts, shared_fmt=shared)
+    try:
+        if shared == "kquant":
+            # the K-quant shared expert's blocks random as well
+            layer.shared = {"fmt": "kquant", "slot": S.random_kquant_slot(shape, 99)}
+            kcfg = moe.make_cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, max_tokens=max(m, 8))
+            moe.moe_pack_expert(kcfg, layer.shared["slot"].cuda(), layer.d_shared["slot"])
+        check_layer(layer, S.make_tokens(m, shape.dim, 4, index=m), f"random bytes m={m} {shared}")
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("m", [40, 150])
+def test_random_block_bytes_hot_expert(m):
+    # one expert takes every token: multi-chunk MMQ groups over random blocks
+    shape = S.LayerShape(512, 256, 16, 2)
+    bias = torch.zeros(16)
+    bias[9] = 100.0
+    layer = Layer(shape, 6, max_tokens=m, experts=random_byte_experts(shape, 60), bias=bias)
+    try:
+        check_layer(layer, S.make_tokens(m, shape.dim, 6, index=m), f"random bytes hot m={m}")
+    finally:
+        layer.close()
+
+
+# ----------------------------------------------------------------------------- counters
+
+@pytest.mark.parametrize("m", [1, 3, 12])
+def test_near_ties_counted(m):
+    # a zero router: every score is sqrt(ln 2), so the keys follow the bias; expert 1
+    # (the 2nd pick) lies 4e-6 above expert 2, a near tie at the k / k+1 boundary
+    bias = torch.zeros(16)
+    bias[0], bias[1], bias[2] = 0.5, 0.3 + 4e-6, 0.3
+    layer = Layer(S.TINY, 0, max_tokens=16, router_std=0.0, bias=bias)
+    try:
+        x = S.make_tokens(m, 256, 6).cuda()
+        moe.moe_reset_stats(layer.ctx)
+        _, _, idx = layer.forward(x)
+        assert layer.check() == moe.MOE_OK
+        assert idx.cpu().tolist() == [[0, 1]] * m
+        st = moe.moe_get_stats(layer.ctx)
+        assert st["near_ties"] == m and st["calls"] == 1
+        gw = torch.empty(m, 2, device="cuda")
+        moe.moe_route(layer.ctx, layer.w, x, m, gw, idx)
+        assert moe.moe_get_stats(layer.ctx)["near_ties"] == 2 * m
+        moe.moe_reset_stats(layer.ctx)
+        assert moe.moe_get_stats(layer.ctx)["near_ties"] == 0
+        # a clear gap: none
+        layer.d_bias[1] = 0.4
+        layer.forward(x)
+        assert moe.moe_get_stats(layer.ctx)["near_ties"] == 0
+    finally:
+        layer.close()
+
+
+def test_compute_time_with_profiling():
+    layer = Layer(S.TINY, 0, max_tokens=16)
+    try:
+        x = S.make_tokens(12, 256, 1).cuda()
+        moe.moe_reset_stats(layer.ctx)
+        layer.forward(x)
+        assert moe.moe_get_stats(layer.ctx)["compute_ms"] == 0.0    # no events without profiling
+        moe.moe_set_profiling(layer.ctx, True)
+        for m in (1, 12):
+            layer.forward(x[:m])
+        st = moe.moe_get_stats(layer.ctx)
+        moe.moe_set_profiling(layer.ctx, False)
+        assert st["compute_ms"] > 0 and st["calls"] == 3
     finally:
         layer.close()

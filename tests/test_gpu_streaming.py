@@ -5,6 +5,7 @@ back, copies the missing experts' slices into least-recently-used slots, and
 (when the picked experts outnumber the slots) runs the expert kernels in
 waves. Outputs are held to the same bar as the resident tests.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -91,6 +92,47 @@ def test_streamed_lru_keeps_recent():
         resident = [moe.moe_slot_of(layer.ctx, e) for e in range(S.TINY.n_routed)]
         slots = [s for s in resident if s >= 0]
         assert len(slots) == len(set(slots)) and len(slots) <= 8
+    finally:
+        layer.close()
+
+
+def chunk_boundary_rows(idx):
+    """Rows that meet every group of more than 64 rows (the groups cut into
+    several 64-row chunks) on both sides of a chunk boundary: for each such
+    group, largest first, not yet met by a chosen row, the tokens at positions
+    63 and 64 of the group (its rows are in token order); and positions 127/128
+    of the three largest groups."""
+    m = idx.shape[0]
+    cnt = np.bincount(idx.reshape(-1), minlength=S.REAL.n_routed)
+    multi = [int(e) for e in np.argsort(-cnt, kind="stable") if cnt[e] > 64]
+    members = {e: [t for t in range(m) if e in idx[t]] for e in multi}
+    rows, met = set(), set()
+    for e in multi:
+        if e not in met:
+            for p in (63, 64):
+                rows.add(members[e][p])
+                met.update(int(v) for v in idx[members[e][p]])
+    for e in multi[:3]:
+        if cnt[e] > 128:
+            rows.update((members[e][127], members[e][128]))
+    assert multi and all(e in met for e in multi)
+    return sorted(rows)
+
+
+def test_real_streamed_skewed_m2048(real_experts):
+    # the skewed prefill as benchmarked: 2048 tokens, the calibrated Zipf-shaped
+    # bias (the 38 most loaded experts take half of the picks, 39 groups of more
+    # than 64 rows), 96 device slots, every expert in the host arena
+    bias = S.skewed_bias(S.REAL, 4, S.C4_BIAS_SCALE)
+    layer = Layer(S.REAL, 1, bias=bias, router_std=0.02, max_tokens=2048, experts=real_experts, n_slots=96,
+                  bind_all=False, host_arena=True)
+    try:
+        x = S.make_tokens(2048, S.REAL.dim, 4, index=0)
+        moe.moe_reset_stats(layer.ctx)
+        check_layer(layer, x, "streamed skewed m=2048", sample_rows=chunk_boundary_rows)
+        st = moe.moe_get_stats(layer.ctx)
+        print(f"stats {st}", flush=True)
+        assert st["waves"] > 1 and st["misses"] > 0 and st["compute_ms"] > 0
     finally:
         layer.close()
 
