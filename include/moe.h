@@ -50,6 +50,7 @@ extern "C" {
 #define MOE_ENONFINITE (-4)    /* a routing key (score + bias) was NaN */
 #define MOE_ENOTRESIDENT (-5)  /* a picked expert had no slot and no host arena */
 #define MOE_ESTATE (-6)        /* a call needs state that is not set (e.g. no slots) */
+#define MOE_ESCRATCH (-7)      /* moe_forward_static: the call needs more than MOE_STATIC_SCRATCH_BYTES */
 
 /* shared expert formats */
 #define MOE_SHARED_NONE 0
@@ -297,6 +298,38 @@ int moe_kernel_times(moe_ctx* ctx, double* ms_sum, int64_t* launches, int32_t n)
 /* Copy out / clear the counters. */
 int moe_get_stats(const moe_ctx* ctx, moe_stats* out);
 int moe_reset_stats(moe_ctx* ctx);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * path of moe_forward_ex (m <= 8 tokens, m * topk <= 512, K-quant experts),
+ * with no context. Its scratch (logits, q8_1 of x, the routing, chunk list and
+ * q8_1 records of h, the bf16 shared expert's h and output) is a file-scope
+ * device array of MOE_STATIC_SCRATCH_BYTES, one per GPU, held until the process
+ * ends; nothing is allocated, by this call or by any call it makes. The same
+ * kernels run in the same order as moe_forward_ex, so the outputs are
+ * identical to a context's.
+ *   cfg         the layer (cfg->max_tokens is ignored; expert_fmt must be
+ *               MOE_EXPERT_KQUANT)
+ *   w           as for moe_forward (a bf16 shared expert's rows ride in the
+ *               routed launches, as moe_plan_call describes)
+ *   arena       device, the routed experts' slots (moe_expert_layout), 256-byte aligned
+ *   slot_table  device, i32 [n_routed]: expert -> slot, -1 = not resident
+ *   x_bf16, out_bf16, weights_out, idx_out   as for moe_forward_ex
+ *   status      device, i32 [2] or NULL: the kernels OR MOE error flags into
+ *               word 0 (1: a NaN key, 2: a picked expert not resident) and add
+ *               the near-tie count to word 1; the caller clears it. With NULL
+ *               these are dropped.
+ * Every call on a GPU uses that GPU's one array, so two calls that overlap on a
+ * GPU (different streams, threads) race; calls queued on one stream do not.
+ * The array keeps the last call's contents; every buffer a call reads is
+ * written earlier in the same call. MOE_EINVAL for a bad cfg, MXFP4 experts,
+ * NULL or misaligned pointers, m < 1, m > 8 or m * topk > 512; MOE_ESCRATCH if
+ * the call needs more than MOE_STATIC_SCRATCH_BYTES (no valid cfg does at
+ * m <= 8); MOE_EHIP on a runtime error. */
+#define MOE_STATIC_SCRATCH_BYTES (8u << 20)
+int moe_forward_static(const moe_cfg* cfg, const moe_weights* w, const void* arena, const int32_t* slot_table,
+                       const void* x_bf16, int32_t m, void* out_bf16, float* weights_out, int32_t* idx_out,
+                       int32_t* status, void* stream);
 
 /* Static text for a status code. */
 const char* moe_strerror(int code);

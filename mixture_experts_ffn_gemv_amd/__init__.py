@@ -21,6 +21,7 @@ MOE_EHIP = -3
 MOE_ENONFINITE = -4
 MOE_ENOTRESIDENT = -5
 MOE_ESTATE = -6
+MOE_ESCRATCH = -7
 
 MOE_SHARED_NONE = 0
 MOE_SHARED_BF16 = 1
@@ -36,12 +37,14 @@ MOE_PATH_DECODE = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_MMQ = 2
 
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
+
 EXPORTED = (
     "moe_create", "moe_destroy", "moe_expert_layout", "moe_pack_expert", "moe_set_slots", "moe_slot_bind",
     "moe_slot_evict",
     "moe_slot_of", "moe_set_host_arena", "moe_route", "moe_forward", "moe_forward_ex", "moe_check",
     "moe_get_stats", "moe_reset_stats", "moe_strerror", "moe_quantize_q8_1", "moe_set_profiling",
-    "moe_kernel_times", "moe_set_dispatch", "moe_plan_call",
+    "moe_kernel_times", "moe_set_dispatch", "moe_plan_call", "moe_forward_static",
 )
 
 KERNEL_CLASSES = ("router", "quant_h", "topk", "bucket", "gateup", "shared_gateup", "down", "shared_down",
@@ -137,6 +140,7 @@ def lib():
             "moe_set_dispatch": [vp, i32],
             "moe_kernel_times": [vp, P(ctypes.c_double), P(ctypes.c_int64), i32],
             "moe_plan_call": [vp, i32, i32, P(moe_plan)],
+            "moe_forward_static": [P(moe_cfg), P(moe_weights), vp, vp, vp, i32, vp, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -259,6 +263,13 @@ def moe_plan_call(ctx, m, shared_fmt):
     p = moe_plan()
     _check(lib().moe_plan_call(ctx, m, shared_fmt, ctypes.byref(p)), "moe_plan_call")
     return {f: getattr(p, f) for f, _ in moe_plan._fields_}
+
+
+def moe_forward_static(cfg, w, arena, slot_table, x, m, out, weights_out=None, idx_out=None, status=None,
+                       stream=None):
+    return _check(lib().moe_forward_static(ctypes.byref(cfg), ctypes.byref(w), _ptr(arena), _ptr(slot_table),
+                                           _ptr(x), m, _ptr(out), _ptr(weights_out), _ptr(idx_out), _ptr(status),
+                                           _stream(stream)), "moe_forward_static")
 
 
 def moe_quantize_q8_1(x, rows, cols, q_out, d_out, stream=None):

@@ -337,6 +337,7 @@ const char* moe_strerror(int code) {
         case MOE_ENONFINITE: return "NaN routing key";
         case MOE_ENOTRESIDENT: return "picked expert not resident";
         case MOE_ESTATE: return "required state not set";
+        case MOE_ESCRATCH: return "call needs more than the static scratch holds";
         default: return "unknown status";
     }
 }
@@ -972,6 +973,72 @@ int moe_plan_call(const moe_ctx* ctx, int32_t m, int32_t shared_fmt, moe_plan* o
     out->shared_rows_topk = pl.sh_topk_rows;
     out->shared_rows_gateup = pl.sh_gateup_rows;
     return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- the no-allocation variant
+// Scratch of moe_forward_static: one copy per device (each GPU the library runs
+// on holds it until the process ends). Host code never uses this name as an
+// address: it takes the device's own address of the array from
+// hipGetSymbolAddress, once per device, and passes that to the kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_dev[MAX_DEVICES] = {};
+
+// the current device's address of `scratch`, looked up on its first use there
+int static_scratch(uint8_t** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+    if (dev < 0 || dev >= MAX_DEVICES) return MOE_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_EHIP;
+        g_scratch_dev[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_static(const moe_cfg* cfg, const moe_weights* w, const void* arena, const int32_t* slot_table,
+                       const void* x_bf16, int32_t m, void* out_bf16, float* weights_out, int32_t* idx_out,
+                       int32_t* status, void* stream) {
+    if (check_cfg(cfg) != MOE_OK || cfg->expert_fmt != MOE_EXPERT_KQUANT || !decode_supported(cfg->dim, cfg->inter))
+        return MOE_EINVAL;
+    if (arena == nullptr || slot_table == nullptr || x_bf16 == nullptr || out_bf16 == nullptr) return MOE_EINVAL;
+    if (m < 1 || m > ROUTE_SMALL_MAX_M || m * cfg->topk > ROUTE_SMALL_MAX_PAIRS) return MOE_EINVAL;
+    if (!aligned(arena, 256) || !aligned(slot_table, 4) || !aligned(x_bf16, 16) || !aligned(out_bf16, 16) ||
+        !aligned(status, 4))
+        return MOE_EINVAL;
+    // a context on the stack that owns nothing: the caller's arena and slot table,
+    // and views into the static scratch sized for this call's m tokens
+    moe_ctx tmp{};
+    tmp.cfg = *cfg;
+    tmp.cfg.max_tokens = m;
+    tmp.decode_ok = true;
+    tmp.mmq_ok = false;
+    tmp.max_pairs = m * cfg->topk;
+    tmp.max_chunks = m * (cfg->topk + 1) + 1;
+    layout_of(tmp.cfg, tmp.slot_bytes, tmp.off_w1, tmp.off_w3, tmp.off_w2);
+    tmp.arena = (uint8_t*)arena;
+    tmp.slot_table_dev = const_cast<int32_t*>(slot_table);
+    tmp.table_dirty = false;
+    if (carve_scratch(&tmp, m, true, nullptr) > MOE_STATIC_SCRATCH_BYTES) return MOE_ESCRATCH;
+    uint8_t* base = nullptr;
+    const int rc = static_scratch(&base);
+    if (rc != MOE_OK) return rc;
+    carve_scratch(&tmp, m, true, base);
+    if (status != nullptr) tmp.err = status;
+    return moe_forward_ex(&tmp, w, x_bf16, m, out_bf16, weights_out, idx_out, stream);
 }
 
 int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_out, float* d_out, void* stream) {

@@ -64,7 +64,7 @@ def test_expert_layout_rejects_bad_cfg(lib, bad):
 
 
 def test_strerror_and_null_handling(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert moe.strerror(code)
     assert moe.strerror(-99) == "unknown status"
     assert lib.moe_destroy(None) == moe.MOE_OK
@@ -103,3 +103,18 @@ def test_stats_carry_the_timing_fields_and_near_ties():
     names = [f for _, f in header_struct("moe_stats")]
     for f in ("hits", "misses", "bytes_copied", "route_ms", "fetch_ms", "compute_ms", "near_ties"):
         assert f in names
+
+
+def test_static_forward_rejects_bad_arguments_before_any_device_call(lib):
+    # every check below fails before the library touches a device
+    cfg = moe.make_cfg(256, 256, 16, 2)
+    w = moe.make_weights(None, None)
+    args = lambda c, m, arena=1 << 20: (ctypes.byref(c) if c is not None else None, ctypes.byref(w), arena,
+                                         1 << 20, 1 << 20, m, 1 << 20, None, None, None, None)
+    assert lib.moe_forward_static(*args(None, 1)) == moe.MOE_EINVAL
+    assert lib.moe_forward_static(*args(cfg, 1, arena=None)) == moe.MOE_EINVAL
+    for m in (0, 9):
+        assert lib.moe_forward_static(*args(cfg, m)) == moe.MOE_EINVAL
+    fp4 = moe.make_cfg(256, 256, 16, 2, expert_fmt=moe.MOE_EXPERT_MXFP4)
+    assert lib.moe_forward_static(*args(fp4, 1)) == moe.MOE_EINVAL
+    assert lib.moe_forward_static(*args(cfg, 1, arena=(1 << 20) + 16)) == moe.MOE_EINVAL   # arena not 256-aligned
