@@ -50,9 +50,14 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 //    its token rows (quants, block scales, per-16 sums times the block scale)
 //    go from global memory straight into LDS with wavefront-wide loads; the
 //    weights land as [matrix][row][84 bytes] (a 21-dword row stride: the 16
-//    rows a wavefront reads lie in distinct banks), the activations transposed
-//    to [16-byte chunk][token] / [block][token]. Two superblocks are in LDS:
-//    one is computed while the next is in flight.
+//    rows a wavefront reads lie in distinct banks), the quants transposed to
+//    [16-byte chunk][token], the block scales as [token][8 blocks]. Two
+//    superblocks are in LDS: one is computed while the next is in flight.
+//  * Every sub-tile is computed whether or not the chunk fills it (rows past
+//    the chunk repeat its last row and are never stored): no branches inside
+//    the unrolled block loop. Each block's B reads (and scales) are issued one
+//    block ahead, and each block is its own scheduling region, so the compiler
+//    does not hold several blocks' products in registers at once.
 //  * A lane (row = lane % 16, g = lane / 16) takes from its row's superblock
 //    the sixteen scale bytes, d / dmin and the qs bytes 8g..8g+7 of both
 //    halves, which hold its eight K values of all four planes. The A bytes
@@ -72,7 +77,7 @@ struct GateupLds {
     static constexpr int w_off = 0;                          // [2 matrices][64 rows][84 B] (+ overrun)
     static constexpr int q_off = w_off + GW_LOADS * 256 * 16;   // [16 chunks][R] x 16 B
     static constexpr int ndx = (8 * R + 255) / 256;          // dword loads per thread for the block scales
-    static constexpr int dx_off = q_off + 16 * R * 16;       // [8 blocks][R] f32 (+ padding to ndx * 256)
+    static constexpr int dx_off = q_off + 16 * R * 16;       // [R][8 blocks] f32 (+ padding to ndx * 256)
     static constexpr int x16_off = dx_off + ndx * 256 * 4;   // [16 sub-blocks][R] f32
     static constexpr int buf_bytes = (x16_off + 16 * R * 4 + 15) / 16 * 16;
     static constexpr int xch_off = nbuf * buf_bytes;         // [4 waves][2 matrices][16 rows] f32: d of each row
@@ -121,8 +126,17 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));   // rows past the chunk repeat its last row
     const int stok = shared ? ch.row0 + srow : a.perm[ch.row0 + srow] / a.topk;
     const int8_t* xq_row = a.xq + (size_t)stok * D;
-    const float* xd_row = a.xd + (size_t)stok * (D / QB);
     const float* xf_row = a.xs16f + (size_t)stok * (D / 16);
+    // block-scale unit i = 256 u + tid: block i % 8 of token row i / 8 (rows past R or
+    // past the chunk repeat the last one)
+    const float* xd_src[LL::ndx];
+#pragma unroll
+    for (int u = 0; u < LL::ndx; ++u) {
+        const int i = u * 256 + tid;
+        const int tr = max(0, min(min(i >> 3, R - 1), ch.nrows - 1));
+        const int tk = shared ? ch.row0 + tr : a.perm[ch.row0 + tr] / a.topk;
+        xd_src[u] = a.xd + (size_t)tk * (D / QB) + (i & 7);
+    }
     // weight unit f = 256 u + tid of a superblock column: matrix f / 336, panel (f % 336) / 42,
     // 16-byte piece f % 42 (units past the end repeat the last one into the overrun)
     const uint8_t* wsrc[GW_LOADS];
@@ -144,10 +158,8 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             load_lds16(xq_row + (size_t)sb * QK + kc * 16, buf + LL::q_off + (u * 256 + wv * 64) * 16);
         }
 #pragma unroll
-        for (int u = 0; u < LL::ndx; ++u) {
-            const int kb = min((u * 256 + tid) / R, 7);
-            load_lds4(xd_row + (size_t)sb * 8 + kb, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
-        }
+        for (int u = 0; u < LL::ndx; ++u)
+            load_lds4(xd_src[u] + (size_t)sb * 8, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int n = (u * 256 + tid) / R;
@@ -164,7 +176,6 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     f4 accg[NS], accu[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) accg[s] = accu[s] = (f4){0.f, 0.f, 0.f, 0.f};
-    const int ns = min(NS, (ch.nrows + 15) / 16);   // sub-tiles holding tokens
     float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 32;
 
     stage(0, 0);
@@ -189,12 +200,36 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             cw[m][7] = p[13 + 2 * g];
             cw[m][8] = p[20];
         }
-        f4 sg[NS], su[NS];
+        // B of block kb8: the 8 quants of this lane's token (column) and K slice, and
+        // the token's scale of that block
+        auto load_b = [&](int kb8, int64_t* B, float* dx) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) sg[s] = su[s] = (f4){0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < NS; ++s) {
+                B[s] = *reinterpret_cast<const int64_t*>(
+                    buf + LL::q_off + ((2 * kb8 + (g >> 1)) * R + 16 * s + l16) * 16 + 8 * (g & 1));
+                dx[s] = dxl[(16 * s + l16) * 8 + kb8];
+            }
+        };
+        f4 sg[NS], su[NS];
+        int64_t Bn[NS];
+        float dxn[NS];
+        load_b(0, Bn, dxn);
 #pragma unroll
         for (int kb8 = 0; kb8 < 8; ++kb8) {
+            // one block per scheduling region (the next block's B reads issued first);
+            // the empty asm statements below pin each block's rescaled sums in place, so
+            // the compiler cannot sink the rescale past later blocks' products (which
+            // would hold every block's results in registers at once)
+            __builtin_amdgcn_sched_barrier(0);
             const int hh = kb8 >> 2, j = kb8 & 3;
+            int64_t B[NS];
+            float dxc[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                B[s] = Bn[s];
+                dxc[s] = dxn[s];
+            }
+            if (kb8 < 7) load_b(kb8 + 1, Bn, dxn);
             // this lane's 8 weights: positions 8g..8g+7 of plane j, half hh (sub-block 8hh + 2j + g / 2)
             const int nsh = 8 * ((2 * j + (g >> 1)) & 3);
             int64_t Aw[2];
@@ -209,21 +244,24 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
                 const uint32_t b1 = __builtin_amdgcn_perm(lut, lut, s1);
                 Aw[m] = (int64_t)(((uint64_t)b1 << 32) | b0);
             }
+            i32x4_t cg[NS], cu[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                if (s >= ns) break;
-                const int64_t B = *reinterpret_cast<const int64_t*>(
-                    buf + LL::q_off + ((2 * kb8 + (g >> 1)) * R + 16 * s + l16) * 16 + 8 * (g & 1));
-                const float dx = dxl[kb8 * R + 16 * s + l16];
-                const i32x4_t cg = mfma_i8(Aw[0], B);
-                const i32x4_t cu = mfma_i8(Aw[1], B);
+                cg[s] = mfma_i8(Aw[0], B[s]);
+                cu[s] = mfma_i8(Aw[1], B[s]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const float dx = dxc[s];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sg[s][r] = fmaf(dx, (float)cg[r], sg[s][r]);
-                    su[s][r] = fmaf(dx, (float)cu[r], su[s][r]);
+                    sg[s][r] = kb8 == 0 ? dx * (float)cg[s][r] : fmaf(dx, (float)cg[s][r], sg[s][r]);
+                    su[s][r] = kb8 == 0 ? dx * (float)cu[s][r] : fmaf(dx, (float)cu[s][r], su[s][r]);
+                    asm volatile("" : "+v"(sg[s][r]), "+v"(su[s][r]));
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // d of the four C rows 4g..4g+3 (held by the lanes of those rows)
         const float dg = half_bits_to_f32(cw[0][8] & 0xFFFFu), du = half_bits_to_f32(cw[1][8] & 0xFFFFu);
         if (g == 0) {
@@ -243,7 +281,6 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            if (s >= ns) break;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 accg[s][r] = fmaf(dG[r], sg[s][r], accg[s][r]);
@@ -277,9 +314,11 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
 // token's block scale, times -d of the row per superblock.
 //  * Per superblock the 64 rows' blocks (eight panels: one contiguous
 //    880-byte run each) and the h quants and block scales go into LDS with
-//    wavefront-wide loads, the weights as [row][110 bytes], the activations
-//    transposed to [16-byte chunk][token] / [block][token]; two superblocks are
-//    in LDS, one computed while the next is in flight.
+//    wavefront-wide loads, the weights as [row][110 bytes], the quants
+//    transposed to [16-byte chunk][token], the block scales as [token][8
+//    blocks]; two superblocks are in LDS, one computed while the next is in
+//    flight. As for gate/up, every sub-tile is computed (no branches in the
+//    block loop).
 //  * A lane (row = lane % 16, g = lane / 16) realigns once per superblock the
 //    hmask bytes 8g..8g+7, the qs bytes 8g.. of both halves and the scales
 //    (superblocks are 110 bytes, so half of them start at 2 bytes past a dword).
@@ -341,7 +380,15 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     // h rows of the chunk (rows past it repeat its last row; their products are never stored)
     const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));
     const int8_t* hq_row = hq + (size_t)(ch.row0 + srow) * I;
-    const float* hd_row = hd + (size_t)(ch.row0 + srow) * (I / QB);
+    // block-scale unit i = 256 u + tid: block i % 8 of h row i / 8 (rows past R or past
+    // the chunk repeat the last one)
+    const float* hd_src[LL::ndx];
+#pragma unroll
+    for (int u = 0; u < LL::ndx; ++u) {
+        const int i = u * 256 + tid;
+        const int tr = max(0, min(min(i >> 3, R - 1), ch.nrows - 1));
+        hd_src[u] = hd + (size_t)(ch.row0 + tr) * (I / QB) + (i & 7);
+    }
     // weight unit f = 256 u + tid of a superblock column: panel f / 55, piece f % 55
     const uint8_t* wsrc[DW_LOADS];
 #pragma unroll
@@ -361,10 +408,8 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
             load_lds16(hq_row + (size_t)sb * QK + kc * 16, buf + LL::q_off + (u * 256 + wv * 64) * 16);
         }
 #pragma unroll
-        for (int u = 0; u < LL::ndx; ++u) {
-            const int kb = min((u * 256 + tid) / R, 7);
-            load_lds4(hd_row + (size_t)sb * 8 + kb, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
-        }
+        for (int u = 0; u < LL::ndx; ++u)
+            load_lds4(hd_src[u] + (size_t)sb * 8, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
     };
     stage(0, 0);
     // lookup: entry sc6 holds (32 - sc6) * (v - 4) for v = 0..7 (bytes; lies in [-128, 124])
@@ -381,7 +426,6 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     f4 acc[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[s] = (f4){0.f, 0.f, 0.f, 0.f};
-    const int ns = min(NS, (ch.nrows + 15) / 16);
     const int wrow = 16 * wv + l16;
     float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 16;
 
@@ -413,12 +457,30 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
         const uint32_t S0 = funnel(t25, t24, sh), S1 = funnel(t26, t25, sh), S2 = funnel(t27, t26, sh);
         const float dneg = -half_bits_to_f32((t27 >> sh) & 0xFFFFu);
 
-        f4 ss[NS];
+        auto load_b = [&](int kb8, int64_t* B, float* dx) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ss[s] = (f4){0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < NS; ++s) {
+                B[s] = *reinterpret_cast<const int64_t*>(
+                    buf + LL::q_off + ((2 * kb8 + gh) * R + 16 * s + l16) * 16 + 8 * (g & 1));
+                dx[s] = dxl[(16 * s + l16) * 8 + kb8];
+            }
+        };
+        f4 ss[NS];
+        int64_t Bn[NS];
+        float dxn[NS];
+        load_b(0, Bn, dxn);
 #pragma unroll
         for (int kb8 = 0; kb8 < 8; ++kb8) {
+            __builtin_amdgcn_sched_barrier(0);   // one block per scheduling region, as for gate/up
             const int hh = kb8 >> 2, j = kb8 & 3;
+            int64_t B[NS];
+            float dxc[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                B[s] = Bn[s];
+                dxc[s] = dxn[s];
+            }
+            if (kb8 < 7) load_b(kb8 + 1, Bn, dxn);
             // six-bit scale of sub-block n = 8 hh + 2 j + g / 2: low nibble of byte
             // (2j + g/2) (high nibble for hh = 1), two high bits from byte 8 + n % 4
             const int nb4 = (2 * j + gh) & 3;
@@ -432,17 +494,21 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
             const uint32_t v1 = ((qh[1] >> (2 * j)) & 0x03030303u) | (((hm[1] >> hbit) & 0x01010101u) << 2);
             const int64_t Aw = (int64_t)(((uint64_t)__builtin_amdgcn_perm(L.y, L.x, v1) << 32) |
                                          __builtin_amdgcn_perm(L.y, L.x, v0));
+            i32x4_t cc[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) cc[s] = mfma_i8(Aw, B[s]);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                if (s >= ns) break;
-                const int64_t B = *reinterpret_cast<const int64_t*>(
-                    buf + LL::q_off + ((2 * kb8 + gh) * R + 16 * s + l16) * 16 + 8 * (g & 1));
-                const float dx = dxl[kb8 * R + 16 * s + l16];
-                const i32x4_t cc = mfma_i8(Aw, B);
+                const float dx = dxc[s];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ss[s][r] = fmaf(dx, (float)cc[r], ss[s][r]);
+                for (int r = 0; r < 4; ++r)
+                {
+                    ss[s][r] = kb8 == 0 ? dx * (float)cc[s][r] : fmaf(dx, (float)cc[s][r], ss[s][r]);
+                    asm volatile("" : "+v"(ss[s][r]));
+                }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // -d of the four C rows 4g..4g+3 (held by the lanes of those rows)
         if (g == 0) xch[l16] = dneg;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
