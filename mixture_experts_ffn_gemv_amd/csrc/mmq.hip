@@ -47,12 +47,13 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 // one scalar per lane and block).
 //  * Per superblock the workgroup's 2 x 64 weight rows (eight panels of each
 //    matrix: one contiguous 672-byte run per panel) and the activations of
-//    its token rows (quants, block scales, per-16 sums times the block scale)
-//    go from global memory straight into LDS with wavefront-wide loads; the
-//    weights land as [matrix][row][84 bytes] (a 21-dword row stride: the 16
-//    rows a wavefront reads lie in distinct banks), the quants transposed to
-//    [16-byte chunk][token], the block scales as [token][8 blocks]. Two
-//    superblocks are in LDS: one is computed while the next is in flight.
+//    its token rows (quants, block scales, the min-term sums) go from global
+//    memory straight into LDS with wavefront-wide loads; the weights land as
+//    [matrix][row][84 bytes] (a 21-dword row stride: the 16 rows a wavefront
+//    reads lie in distinct banks), the quants transposed to [16-byte
+//    chunk][token], the block scales as [token][8 blocks], the min-term sums as
+//    [token][96 bytes]. Two superblocks are in LDS: one is computed while the
+//    next is in flight.
 //  * Every sub-tile is computed whether or not the chunk fills it (rows past
 //    the chunk repeat its last row and are never stored): no branches inside
 //    the unrolled block loop. Each block's B reads (and scales) are issued one
@@ -63,12 +64,20 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 //    halves, which hold its eight K values of all four planes. The A bytes
 //    sc_n * q come from a byte lookup (v_perm_b32 on [3 sc, 2 sc, sc, 0]
 //    indexed by 3 - q).
-//  * The min part -dmin * m_n * X16_n (X16 = block scale times the sum of 16
-//    quants) is four f32 16x16x4 products per matrix and superblock (K = the
-//    16 sub-blocks).
+//  * The min part -dmin * sum_n m_n * X16_n (X16 = block scale times the sum
+//    of 16 quants, an f32 with at most 24 significant bits) runs on the bf16
+//    matrix core: the quantiser stores each X16 as three bf16 pieces hi + mid
+//    + lo (exact), and two v_mfma_f32_16x16x32_bf16 per matrix and sub-tile
+//    take K = [16 sub-blocks x (hi, mid)] and [16 x (lo, -)] against A = m_n
+//    (exact in bf16); the product of each sub-tile goes out with -dmin of its
+//    rows. Each sub-tile and matrix has its own block region for these two.
 namespace {
 constexpr int GW_UNITS = 2 * TILE_ROWS * Q2K_BYTES / 16;   // 16-byte units of one superblock column (672)
 constexpr int GW_LOADS = (GW_UNITS + 255) / 256;           // per thread (3)
+constexpr int X16_REC = 96;                                // bytes of one token's min-term sums per superblock
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
 
 template <int NS>
 struct GateupLds {
@@ -78,11 +87,18 @@ struct GateupLds {
     static constexpr int q_off = w_off + GW_LOADS * 256 * 16;   // [16 chunks][R] x 16 B
     static constexpr int ndx = (8 * R + 255) / 256;          // dword loads per thread for the block scales
     static constexpr int dx_off = q_off + 16 * R * 16;       // [R][8 blocks] f32 (+ padding to ndx * 256)
-    static constexpr int x16_off = dx_off + ndx * 256 * 4;   // [16 sub-blocks][R] f32
-    static constexpr int buf_bytes = (x16_off + 16 * R * 4 + 15) / 16 * 16;
-    static constexpr int xch_off = nbuf * buf_bytes;         // [4 waves][2 matrices][16 rows] f32: d of each row
-    static constexpr int bytes = xch_off + 4 * 2 * 16 * 4;
+    static constexpr int x16_units = R * X16_REC / 16;       // 16-byte units of the min-term sums
+    static constexpr int nx16 = (x16_units + 255) / 256;     // loads per thread (a wave past the end skips)
+    static constexpr int x16_off = dx_off + ndx * 256 * 4;   // [R][96 B] (+ the last wave's overrun)
+    static constexpr int buf_bytes = x16_off + (x16_units + 63) / 64 * 64 * 16;
+    static constexpr int xch_off = nbuf * buf_bytes;         // [4 waves][d W1, d W3, -dmin W1, -dmin W3][16 rows] f32
+    static constexpr int bytes = xch_off + 4 * 4 * 16 * 4;
 };
+
+// bf16 of two small non-negative integers (exact), packed low | high
+MOE_DEV uint32_t bf16_pair(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
 }  // namespace
 
 template <int NS>
@@ -121,21 +137,30 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         w3 = base + a.off_w3;
     }
     const size_t rowbytes = (size_t)nsb * Q2K_BYTES;
+    // the token (x row) of chunk row t; rows past the chunk repeat its last row
+    auto token_of = [&](int t) {
+        const int tr = max(0, min(t, ch.nrows - 1));
+        return shared ? ch.row0 + tr : a.perm[ch.row0 + tr] / a.topk;
+    };
 
     // staging of one superblock into buffer bi (every thread issues LL::ndma loads)
-    const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));   // rows past the chunk repeat its last row
-    const int stok = shared ? ch.row0 + srow : a.perm[ch.row0 + srow] / a.topk;
-    const int8_t* xq_row = a.xq + (size_t)stok * D;
-    const float* xf_row = a.xs16f + (size_t)stok * (D / 16);
-    // block-scale unit i = 256 u + tid: block i % 8 of token row i / 8 (rows past R or
-    // past the chunk repeat the last one)
+    const int8_t* xq_row = a.xq + (size_t)token_of(tid & (R - 1)) * D;
+    // block-scale unit i = 256 u + tid: block i % 8 of token row i / 8 (rows past R
+    // repeat the last one)
     const float* xd_src[LL::ndx];
 #pragma unroll
     for (int u = 0; u < LL::ndx; ++u) {
         const int i = u * 256 + tid;
-        const int tr = max(0, min(min(i >> 3, R - 1), ch.nrows - 1));
-        const int tk = shared ? ch.row0 + tr : a.perm[ch.row0 + tr] / a.topk;
-        xd_src[u] = a.xd + (size_t)tk * (D / QB) + (i & 7);
+        xd_src[u] = a.xd + (size_t)token_of(min(i >> 3, R - 1)) * (D / QB) + (i & 7);
+    }
+    // min-term unit i = 256 u + tid: 16-byte piece i % 6 of token row i / 6's record
+    // (units past the end repeat the last one into the overrun)
+    const uint8_t* x16_src[LL::nx16];
+#pragma unroll
+    for (int u = 0; u < LL::nx16; ++u) {
+        const int i = min(u * 256 + tid, LL::x16_units - 1);
+        x16_src[u] = reinterpret_cast<const uint8_t*>(a.xs16b) + (size_t)token_of(i / 6) * nsb * X16_REC +
+                     (i % 6) * 16;
     }
     // weight unit f = 256 u + tid of a superblock column: matrix f / 336, panel (f % 336) / 42,
     // 16-byte piece f % 42 (units past the end repeat the last one into the overrun)
@@ -161,10 +186,9 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         for (int u = 0; u < LL::ndx; ++u)
             load_lds4(xd_src[u] + (size_t)sb * 8, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            const int n = (u * 256 + tid) / R;
-            load_lds4(xf_row + (size_t)sb * 16 + n, buf + LL::x16_off + (u * 256 + wv * 64) * 4);
-        }
+        for (int u = 0; u < LL::nx16; ++u)
+            if (u * 256 + wv * 64 < LL::x16_units)   // wave-uniform
+                load_lds16(x16_src[u] + (size_t)sb * X16_REC, buf + LL::x16_off + (u * 256 + wv * 64) * 16);
     };
 
     // this lane's weight rows in LDS (dword offsets), W1 and W3
@@ -176,7 +200,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     f4 accg[NS], accu[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) accg[s] = accu[s] = (f4){0.f, 0.f, 0.f, 0.f};
-    float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 32;
+    float* xch = reinterpret_cast<float*>(smem + LL::xch_off) + wv * 64;
 
     stage(0, 0);
     for (int sb = 0; sb < nsb; ++sb) {
@@ -187,7 +211,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         const uint8_t* buf = smem + bcur * LL::buf_bytes;
         const uint32_t* wl = reinterpret_cast<const uint32_t*>(buf + LL::w_off);
         const float* dxl = reinterpret_cast<const float*>(buf + LL::dx_off);
-        const float* xl = reinterpret_cast<const float*>(buf + LL::x16_off);
+        const uint8_t* x16l = buf + LL::x16_off;
         uint32_t cw[2][9];   // scales, qs 8g.. (2 dwords), qs 32 + 8g.. (2), d | dmin
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -200,6 +224,33 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             cw[m][7] = p[13 + 2 * g];
             cw[m][8] = p[20];
         }
+        // d and -dmin of the four C rows 4g..4g+3 (held by the lanes of those rows)
+        if (g == 0) {
+            xch[l16] = half_bits_to_f32(cw[0][8] & 0xFFFFu);
+            xch[16 + l16] = half_bits_to_f32(cw[1][8] & 0xFFFFu);
+            xch[32 + l16] = -half_bits_to_f32(cw[0][8] >> 16);
+            xch[48 + l16] = -half_bits_to_f32(cw[1][8] >> 16);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const f4 dG = *reinterpret_cast<const f4*>(xch + 4 * g);
+        const f4 dU = *reinterpret_cast<const f4*>(xch + 16 + 4 * g);
+        const f4 nG = *reinterpret_cast<const f4*>(xch + 32 + 4 * g);
+        const f4 nU = *reinterpret_cast<const f4*>(xch + 48 + 4 * g);
+        // min-part A operands: m_n of this lane's row for n = 8 (g % 2) + 0..7 as bf16
+        // (first product: against the hi plane for g < 2, the mid plane for g >= 2;
+        // second: the lo plane for g < 2, nothing for g >= 2)
+        u32x4_v am[2], am2[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t nib = ((g & 1) ? cw[m][2 + h] : cw[m][h]) >> 4 & 0x0F0F0F0Fu;
+                am[m][2 * h] = bf16_pair((float)(nib & 0xFFu), (float)(nib >> 8 & 0xFFu));
+                am[m][2 * h + 1] = bf16_pair((float)(nib >> 16 & 0xFFu), (float)(nib >> 24));
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) am2[m][q] = g < 2 ? am[m][q] : 0u;
+        }
         // B of block kb8: the 8 quants of this lane's token (column) and K slice, and
         // the token's scale of that block
         auto load_b = [&](int kb8, int64_t* B, float* dx) {
@@ -210,10 +261,19 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
                 dx[s] = dxl[(16 * s + l16) * 8 + kb8];
             }
         };
+        // min-part B of sub-tile s: this lane's token's (hi | mid) and (lo | lo) pieces
+        auto load_x16 = [&](int s, u32x4_v& b1, u32x4_v& b2) {
+            const uint8_t* rec = x16l + (16 * s + l16) * X16_REC;
+            b1 = *reinterpret_cast<const u32x4_v*>(rec + 16 * g);
+            b2 = *reinterpret_cast<const u32x4_v*>(rec + 64 + 16 * (g & 1));
+        };
         f4 sg[NS], su[NS];
         int64_t Bn[NS];
         float dxn[NS];
+        u32x4_v xb1, xb2;
+        f4 rmin = {0.f, 0.f, 0.f, 0.f};
         load_b(0, Bn, dxn);
+        load_x16(0, xb1, xb2);
 #pragma unroll
         for (int kb8 = 0; kb8 < 8; ++kb8) {
             // one block per scheduling region (the next block's B reads issued first);
@@ -250,6 +310,24 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
                 cg[s] = mfma_i8(Aw[0], B[s]);
                 cu[s] = mfma_i8(Aw[1], B[s]);
             }
+            // the min part of the previous region's sub-tile and matrix goes out
+            if (kb8 > 0 && ((kb8 - 1) >> 1) < NS) {
+                const int sp = (kb8 - 1) >> 1;
+                f4& acc = (kb8 - 1) & 1 ? accu[sp] : accg[sp];
+                const f4& nd = (kb8 - 1) & 1 ? nU : nG;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(nd[r], rmin[r], acc[r]);
+            }
+            // this region's: sub-tile kb8 / 2, matrix kb8 % 2
+            if ((kb8 >> 1) < NS) {
+                const int m = kb8 & 1;
+                rmin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, am[m]),
+                                                              __builtin_bit_cast(bf16x8_v, xb1),
+                                                              (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                rmin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, am2[m]),
+                                                              __builtin_bit_cast(bf16x8_v, xb2), rmin, 0, 0, 0);
+                if (m == 1 && (kb8 >> 1) + 1 < NS) load_x16((kb8 >> 1) + 1, xb1, xb2);
+            }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const float dx = dxc[s];
@@ -262,22 +340,9 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // d of the four C rows 4g..4g+3 (held by the lanes of those rows)
-        const float dg = half_bits_to_f32(cw[0][8] & 0xFFFFu), du = half_bits_to_f32(cw[1][8] & 0xFFFFu);
-        if (g == 0) {
-            xch[l16] = dg;
-            xch[16 + l16] = du;
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const f4 dG = *reinterpret_cast<const f4*>(xch + 4 * g);
-        const f4 dU = *reinterpret_cast<const f4*>(xch + 16 + 4 * g);
-        // min part: A = -dmin * m_n of this lane's row for sub-block n = 4q + g
-        const float nmg = -half_bits_to_f32(cw[0][8] >> 16), nmu = -half_bits_to_f32(cw[1][8] >> 16);
-        float bmg[4], bmu[4];
+        if (NS == 4) {   // the last region's min part (sub-tile 3, W3)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bmg[q] = nmg * (float)((cw[0][q] >> (8 * g + 4)) & 15u);
-            bmu[q] = nmu * (float)((cw[1][q] >> (8 * g + 4)) & 15u);
+            for (int r = 0; r < 4; ++r) accu[3][r] = fmaf(nU[r], rmin[r], accu[3][r]);
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -286,14 +351,8 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
                 accg[s][r] = fmaf(dG[r], sg[s][r], accg[s][r]);
                 accu[s][r] = fmaf(dU[r], su[s][r], accu[s][r]);
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float x16 = xl[(4 * q + g) * R + 16 * s + l16];
-                accg[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(bmg[q], x16, accg[s], 0, 0, 0);
-                accu[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(bmu[q], x16, accu[s], 0, 0, 0);
-            }
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the d exchange slots are reused next superblock
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the exchange slots are reused next superblock
     }
     wait_vm_loads<0>();   // no load into LDS outlives the workgroup
 #pragma unroll

@@ -55,6 +55,7 @@ struct moe_ctx {
     float* xd = nullptr;
     int32_t* xs16 = nullptr;
     float* xs16f = nullptr;
+    uint16_t* xs16b = nullptr;   // [M][D/256][48] bf16 planes of xs16f (MMQ)
     int32_t* offsets = nullptr;
     int32_t* active = nullptr;
     int32_t* n_active = nullptr;
@@ -155,6 +156,7 @@ size_t carve_scratch(moe_ctx* ctx, size_t M, bool decode_only, uint8_t* base) {
     view(ctx->hrec, cv.take<uint8_t>(m_small * (c.topk + 1) * decode_rec_bytes((int)I)));
     view(ctx->err, cv.take<int32_t>(STATUS_WORDS));
     if (!decode_only) {
+        view(ctx->xs16b, cv.take<uint16_t>(M * D / QK * 48));
         view(ctx->h_routed, cv.take<float>(P * I));
         view(ctx->hq_routed, cv.take<int8_t>(P * I));
         view(ctx->hd_routed, cv.take<float>(P * I / QB));
@@ -798,7 +800,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
             hipError_t e = launch_router_gemm(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits,
                                               ctx->logit_rows, &splits, st);
             if (e != hipSuccess || fp4) return e;   // MXFP4 experts read x itself
-            return launch_quantize_rows(x, m, c.dim, ctx->xq, ctx->xd, ctx->xs16, ctx->xs16f, st);
+            return launch_quantize_rows(x, m, c.dim, ctx->xq, ctx->xd, ctx->xs16, ctx->xs16f, ctx->xs16b, st);
         });
         if (rc != MOE_OK) return rc;
         rc = timed(ctx, st, MOE_K_TOPK, [&] {
@@ -833,6 +835,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     a.xd = ctx->xd;
     a.xs16 = ctx->xs16;
     a.xs16f = ctx->xs16f;
+    a.xs16b = ctx->xs16b;
     a.h_routed = ctx->h_routed;
     a.hrec = ctx->hrec;
     a.h_shared = ctx->h_shared;
@@ -1045,7 +1048,7 @@ int moe_quantize_q8_1(const void* x_bf16, int32_t rows, int32_t cols, int8_t* q_
     if (x_bf16 == nullptr || q_out == nullptr || d_out == nullptr || rows < 1 || cols < QB || cols % QB) return MOE_EINVAL;
     if (!aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(d_out, 4)) return MOE_EINVAL;
     return hip_status(
-        launch_quantize_rows((const uint16_t*)x_bf16, rows, cols, q_out, d_out, nullptr, nullptr, (hipStream_t)stream));
+        launch_quantize_rows((const uint16_t*)x_bf16, rows, cols, q_out, d_out, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int moe_check(moe_ctx* ctx, void* stream) {

@@ -82,7 +82,9 @@ struct ExpertArgs {
     const int8_t* xq;           // q8_1 of x: int8 [m, D], d f32 [m, D/32], 16-sums i32 [m, D/16]
     const float* xd;
     const int32_t* xs16;
-    const float* xs16f;         // fp16(d) * (sum of each 16 quants) of x, f32 [m, D/16] (MMQ min term)
+    const float* xs16f;         // fp16(d) * (sum of each 16 quants) of x, f32 [m, D/16] (decode min term)
+    const uint16_t* xs16b;      // the same values split into three bf16 planes per superblock (MMQ min term):
+                                // [m][D/256][hi 16 | mid 16 | lo 16], hi + mid + lo exactly the f32 value
     float* h_routed;            // f32 [pairs, I] in position order (bf16 [pairs, I] for MXFP4 experts)
     float* h_shared;            // f32 [m, I]
     int8_t* hq_routed;          // q8_1 of h_routed: int8 [pairs, I], d f32 [pairs, I/32], 16-sums i32 [pairs, I/16]

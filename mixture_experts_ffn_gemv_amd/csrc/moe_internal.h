@@ -93,8 +93,9 @@ hipError_t launch_route_small(const float* logits, const float* bias, int m, int
                               int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                               Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table, hipStream_t st,
                               const SharedRows* sr = nullptr);
+// (xs16b: the per-16 sums times d as three bf16 planes per superblock, for the MMQ min term; may be NULL)
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
-                                float* xs16f, hipStream_t st);
+                                float* xs16f, uint16_t* xs16b, hipStream_t st);
 // logits: `splits` partial arrays [m, E] (from launch_router_gemm), summed in order
 hipError_t launch_topk(const float* logits, int splits, const float* bias, int m, int E, int k, float gate_temp,
                        int norm, float route_scale, int32_t* idx, float* gw, int32_t* err, hipStream_t st);

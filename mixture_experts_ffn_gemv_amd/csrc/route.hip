@@ -25,8 +25,21 @@ namespace moe {
 // Blocks past that: q8_1 of x, one lane per 32-value block (int8 quants,
 // fp16(d) as f32, and the two 16-value sums of the quants used by the Q2_K
 // min term): d = amax / 127, q = round-half-away(x / d).
+// v = hi + mid + lo exactly, three bf16 values (truncation splits: v's 24-bit significand
+// in three 8-bit pieces), packed as the low halves of the three returned words
+MOE_DEV void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t vb = __float_as_uint(v);
+    const float r = v - __uint_as_float(vb & 0xFFFF0000u);
+    const uint32_t rb = __float_as_uint(r);
+    const float l = r - __uint_as_float(rb & 0xFFFF0000u);   // at most 8 significant bits
+    hi = vb >> 16;
+    mid = rb >> 16;
+    lo = __float_as_uint(l) >> 16;
+}
+
 MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* __restrict__ xq,
-                                 float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f = nullptr) {
+                                 float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f = nullptr,
+                                 uint16_t* __restrict__ xs16b = nullptr) {
     const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)b * QB);
     float v[32];
 #pragma unroll
@@ -52,6 +65,15 @@ MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* 
     if (xs16f != nullptr) {   // exact: 11-bit scale times a sum of 16 quants
         xs16f[2 * b] = d * (float)sl;
         xs16f[2 * b + 1] = d * (float)sh;
+    }
+    if (xs16b != nullptr) {   // block b % 8 of its superblock: entries 2 (b % 8), + 1 of each plane
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3_bf16(d * (float)sl, h0, m0, l0);
+        split3_bf16(d * (float)sh, h1, m1, l1);
+        uint32_t* rec = reinterpret_cast<uint32_t*>(xs16b + (size_t)(b >> 3) * 48) + (b & 7);
+        rec[0] = h0 | (h1 << 16);
+        rec[8] = m0 | (m1 << 16);
+        rec[16] = l0 | (l1 << 16);
     }
 }
 
@@ -161,9 +183,10 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
 // ---------------------------------------------------------------- q8_1 of rows
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int nblocks,
                                                             int8_t* __restrict__ xq, float* __restrict__ xd,
-                                                            int32_t* __restrict__ xs16, float* __restrict__ xs16f) {
+                                                            int32_t* __restrict__ xs16, float* __restrict__ xs16f,
+                                                            uint16_t* __restrict__ xs16b) {
     const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b < nblocks) quantize_block_bf16(x, b, xq, xd, xs16, xs16f);
+    if (b < nblocks) quantize_block_bf16(x, b, xq, xd, xs16, xs16f, xs16b);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -607,9 +630,9 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
-                                float* xs16f, hipStream_t st) {
+                                float* xs16f, uint16_t* xs16b, hipStream_t st) {
     const int nb = m * (D / QB);
-    return launch_kernel(quantize_rows_kernel, (nb + 255) / 256, 256, 0, st, x, nb, xq, xd, xs16, xs16f);
+    return launch_kernel(quantize_rows_kernel, (nb + 255) / 256, 256, 0, st, x, nb, xq, xd, xs16, xs16f, xs16b);
 }
 
 hipError_t launch_route_small(const float* logits, const float* bias, int m, int E, int k, float gate_temp,
