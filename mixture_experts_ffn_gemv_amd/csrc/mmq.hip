@@ -65,12 +65,16 @@ MOE_DEV i32x4_t mfma_i8(int64_t a, int64_t b) {
 //    sc_n * q come from a byte lookup (v_perm_b32 on [3 sc, 2 sc, sc, 0]
 //    indexed by 3 - q).
 //  * The min part -dmin * sum_n m_n * X16_n (X16 = block scale times the sum
-//    of 16 quants, an f32 with at most 24 significant bits) runs on the bf16
-//    matrix core: the quantiser stores each X16 as three bf16 pieces hi + mid
-//    + lo (exact), and two v_mfma_f32_16x16x32_bf16 per matrix and sub-tile
-//    take K = [16 sub-blocks x (hi, mid)] and [16 x (lo, -)] against A = m_n
-//    (exact in bf16); the product of each sub-tile goes out with -dmin of its
-//    rows. Each sub-tile and matrix has its own block region for these two.
+//    of 16 quants, an f32 with at most 24 significant bits) is a K = 16
+//    product per superblock. With four sub-tiles it runs on the bf16 matrix
+//    core: the quantiser stores each X16 as three bf16 pieces hi + mid + lo
+//    (exact), and two v_mfma_f32_16x16x32_bf16 per matrix and sub-tile take
+//    K = [16 sub-blocks x (hi, mid)] and [16 x (lo, -)] against A = m_n (exact
+//    in bf16); the product goes out with -dmin of its rows, each sub-tile and
+//    matrix in its own block region. With one or two sub-tiles the A operand
+//    of that path would be built for too few products: there it is four
+//    v_mfma_f32_16x16x4_f32 per matrix and sub-tile on the f32 sums, with
+//    A = -dmin * m_n.
 namespace {
 constexpr int GW_UNITS = 2 * TILE_ROWS * Q2K_BYTES / 16;   // 16-byte units of one superblock column (672)
 constexpr int GW_LOADS = (GW_UNITS + 255) / 256;           // per thread (3)
@@ -87,10 +91,13 @@ struct GateupLds {
     static constexpr int q_off = w_off + GW_LOADS * 256 * 16;   // [16 chunks][R] x 16 B
     static constexpr int ndx = (8 * R + 255) / 256;          // dword loads per thread for the block scales
     static constexpr int dx_off = q_off + 16 * R * 16;       // [R][8 blocks] f32 (+ padding to ndx * 256)
-    static constexpr int x16_units = R * X16_REC / 16;       // 16-byte units of the min-term sums
-    static constexpr int nx16 = (x16_units + 255) / 256;     // loads per thread (a wave past the end skips)
-    static constexpr int x16_off = dx_off + ndx * 256 * 4;   // [R][96 B] (+ the last wave's overrun)
-    static constexpr int buf_bytes = x16_off + (x16_units + 63) / 64 * 64 * 16;
+    // the min-term sums: bf16 pieces [R][96 B] for four sub-tiles (16-byte loads; a wave
+    // past the end skips, the last one's overrun is kept), else f32 [16 sub-blocks][R]
+    static constexpr bool bf16_min = NS == 4;
+    static constexpr int x16_units = R * X16_REC / 16;       // 16-byte units of the bf16 pieces
+    static constexpr int nx16 = (x16_units + 255) / 256;     // loads per thread
+    static constexpr int x16_off = dx_off + ndx * 256 * 4;
+    static constexpr int buf_bytes = x16_off + (bf16_min ? (x16_units + 63) / 64 * 64 * 16 : 16 * R * 4);
     static constexpr int xch_off = nbuf * buf_bytes;         // [4 waves][d W1, d W3, -dmin W1, -dmin W3][16 rows] f32
     static constexpr int bytes = xch_off + 4 * 4 * 16 * 4;
 };
@@ -155,12 +162,16 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
     }
     // min-term unit i = 256 u + tid: 16-byte piece i % 6 of token row i / 6's record
     // (units past the end repeat the last one into the overrun)
-    const uint8_t* x16_src[LL::nx16];
+    const uint8_t* x16_src[LL::bf16_min ? LL::nx16 : 1];
+    if constexpr (LL::bf16_min) {
 #pragma unroll
-    for (int u = 0; u < LL::nx16; ++u) {
-        const int i = min(u * 256 + tid, LL::x16_units - 1);
-        x16_src[u] = reinterpret_cast<const uint8_t*>(a.xs16b) + (size_t)token_of(i / 6) * nsb * X16_REC +
-                     (i % 6) * 16;
+        for (int u = 0; u < LL::nx16; ++u) {
+            const int i = min(u * 256 + tid, LL::x16_units - 1);
+            x16_src[u] = reinterpret_cast<const uint8_t*>(a.xs16b) + (size_t)token_of(i / 6) * nsb * X16_REC +
+                         (i % 6) * 16;
+        }
+    } else {   // f32 unit p = 256 u + tid: sub-block p / R of token row p % R (one row per thread)
+        x16_src[0] = reinterpret_cast<const uint8_t*>(a.xs16f + (size_t)token_of(tid & (R - 1)) * (D / 16));
     }
     // weight unit f = 256 u + tid of a superblock column: matrix f / 336, panel (f % 336) / 42,
     // 16-byte piece f % 42 (units past the end repeat the last one into the overrun)
@@ -185,10 +196,18 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
 #pragma unroll
         for (int u = 0; u < LL::ndx; ++u)
             load_lds4(xd_src[u] + (size_t)sb * 8, buf + LL::dx_off + (u * 256 + wv * 64) * 4);
+        if constexpr (LL::bf16_min) {
 #pragma unroll
-        for (int u = 0; u < LL::nx16; ++u)
-            if (u * 256 + wv * 64 < LL::x16_units)   // wave-uniform
-                load_lds16(x16_src[u] + (size_t)sb * X16_REC, buf + LL::x16_off + (u * 256 + wv * 64) * 16);
+            for (int u = 0; u < LL::nx16; ++u)
+                if (u * 256 + wv * 64 < LL::x16_units)   // wave-uniform
+                    load_lds16(x16_src[u] + (size_t)sb * X16_REC, buf + LL::x16_off + (u * 256 + wv * 64) * 16);
+        } else {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                const int n = (u * 256 + tid) / R;
+                load_lds4(x16_src[0] + ((size_t)sb * 16 + n) * 4, buf + LL::x16_off + (u * 256 + wv * 64) * 4);
+            }
+        }
     };
 
     // this lane's weight rows in LDS (dword offsets), W1 and W3
@@ -242,9 +261,13 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         u32x4_v am[2], am2[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
+            if constexpr (!LL::bf16_min) break;
+            // scale bytes 8 (g % 2)..+7 (read again from LDS: a lane-dependent pick among
+            // the registers would go through scratch memory)
+            const uint2 sw = *reinterpret_cast<const uint2*>(wl + (m ? wo3 : wo1) + 2 * (g & 1));
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint32_t nib = ((g & 1) ? cw[m][2 + h] : cw[m][h]) >> 4 & 0x0F0F0F0Fu;
+                const uint32_t nib = (h ? sw.y : sw.x) >> 4 & 0x0F0F0F0Fu;
                 am[m][2 * h] = bf16_pair((float)(nib & 0xFFu), (float)(nib >> 8 & 0xFFu));
                 am[m][2 * h + 1] = bf16_pair((float)(nib >> 16 & 0xFFu), (float)(nib >> 24));
             }
@@ -273,7 +296,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
         u32x4_v xb1, xb2;
         f4 rmin = {0.f, 0.f, 0.f, 0.f};
         load_b(0, Bn, dxn);
-        load_x16(0, xb1, xb2);
+        if constexpr (LL::bf16_min) load_x16(0, xb1, xb2);
 #pragma unroll
         for (int kb8 = 0; kb8 < 8; ++kb8) {
             // one block per scheduling region (the next block's B reads issued first);
@@ -311,7 +334,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
                 cu[s] = mfma_i8(Aw[1], B[s]);
             }
             // the min part of the previous region's sub-tile and matrix goes out
-            if (kb8 > 0 && ((kb8 - 1) >> 1) < NS) {
+            if (LL::bf16_min && kb8 > 0) {
                 const int sp = (kb8 - 1) >> 1;
                 f4& acc = (kb8 - 1) & 1 ? accu[sp] : accg[sp];
                 const f4& nd = (kb8 - 1) & 1 ? nU : nG;
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
                 for (int r = 0; r < 4; ++r) acc[r] = fmaf(nd[r], rmin[r], acc[r]);
             }
             // this region's: sub-tile kb8 / 2, matrix kb8 % 2
-            if ((kb8 >> 1) < NS) {
+            if constexpr (LL::bf16_min) {
                 const int m = kb8 & 1;
                 rmin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, am[m]),
                                                               __builtin_bit_cast(bf16x8_v, xb1),
@@ -340,7 +363,7 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (NS == 4) {   // the last region's min part (sub-tile 3, W3)
+        if constexpr (LL::bf16_min) {   // the last region's min part (sub-tile 3, W3)
 #pragma unroll
             for (int r = 0; r < 4; ++r) accu[3][r] = fmaf(nU[r], rmin[r], accu[3][r]);
         }
@@ -350,6 +373,25 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
             for (int r = 0; r < 4; ++r) {
                 accg[s][r] = fmaf(dG[r], sg[s][r], accg[s][r]);
                 accu[s][r] = fmaf(dU[r], su[s][r], accu[s][r]);
+            }
+        }
+        if constexpr (!LL::bf16_min) {
+            // min part on the f32 sums: A = -dmin * m_n of this lane's row for sub-block n = 4q + g
+            const float* xl = reinterpret_cast<const float*>(x16l);
+            float bmg[4], bmu[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bmg[q] = -half_bits_to_f32(cw[0][8] >> 16) * (float)((cw[0][q] >> (8 * g + 4)) & 15u);
+                bmu[q] = -half_bits_to_f32(cw[1][8] >> 16) * (float)((cw[1][q] >> (8 * g + 4)) & 15u);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float x16 = xl[(4 * q + g) * R + 16 * s + l16];
+                    accg[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(bmg[q], x16, accg[s], 0, 0, 0);
+                    accu[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(bmu[q], x16, accu[s], 0, 0, 0);
+                }
             }
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the exchange slots are reused next superblock
