@@ -566,13 +566,26 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
                 dx[s] = dxl[(16 * s + l16) * 8 + kb8];
             }
         };
+        // the lookup entry of block kb8: six-bit scale of sub-block n = 8 hh + 2 j + g / 2
+        // (low nibble of byte 2j + g/2, high nibble for hh = 1; two high bits from byte
+        // 8 + n % 4)
+        auto load_lut = [&](int kb8) {
+            const int hh = kb8 >> 2, j = kb8 & 3;
+            const int nb4 = (2 * j + gh) & 3;
+            const uint32_t low4 = ((j < 2 ? S0 : S1) >> (8 * nb4 + 4 * hh)) & 15u;
+            const uint32_t hi2 = (S2 >> (8 * nb4 + 2 * (2 * hh + (j >> 1)))) & 3u;
+            return lut[low4 | (hi2 << 4)];
+        };
         f4 ss[NS];
         int64_t Bn[NS];
         float dxn[NS];
         load_b(0, Bn, dxn);
+        uint2 Ln = load_lut(0);
 #pragma unroll
         for (int kb8 = 0; kb8 < 8; ++kb8) {
-            __builtin_amdgcn_sched_barrier(0);   // one block per scheduling region, as for gate/up
+            // one block per scheduling region, as for gate/up (the next block's B reads and
+            // lookup entry issued first)
+            __builtin_amdgcn_sched_barrier(0);
             const int hh = kb8 >> 2, j = kb8 & 3;
             int64_t B[NS];
             float dxc[NS];
@@ -581,13 +594,11 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
                 B[s] = Bn[s];
                 dxc[s] = dxn[s];
             }
-            if (kb8 < 7) load_b(kb8 + 1, Bn, dxn);
-            // six-bit scale of sub-block n = 8 hh + 2 j + g / 2: low nibble of byte
-            // (2j + g/2) (high nibble for hh = 1), two high bits from byte 8 + n % 4
-            const int nb4 = (2 * j + gh) & 3;
-            const uint32_t low4 = ((j < 2 ? S0 : S1) >> (8 * nb4 + 4 * hh)) & 15u;
-            const uint32_t hi2 = (S2 >> (8 * nb4 + 2 * (2 * hh + (j >> 1)))) & 3u;
-            const uint2 L = lut[low4 | (hi2 << 4)];
+            const uint2 L = Ln;
+            if (kb8 < 7) {
+                load_b(kb8 + 1, Bn, dxn);
+                Ln = load_lut(kb8 + 1);
+            }
             // q3 + 4 for positions 8g..8g+7 of plane j, half hh
             const uint32_t* qh = hh ? q1 : q0;
             const int hbit = 4 * hh + j;
