@@ -268,6 +268,12 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
         c_w[q] = ch.weight;
     }
     for (int q = tid; q < DC_ROWS; q += bd) acc[q] = 0.f;
+    // the shared expert's output for this workgroup's rows, requested now (it is added last)
+    const float ysv = (ys != nullptr && tid < DC_ROWS) ? ys[(size_t)tsel * D + r0 + tid] : 0.f;
+    // with every (chunk, row) of a pass in one wavefront, wavefront 0 finishes each pass
+    // with shuffles (lanes 0..7 carry the rows' sums across passes)
+    const bool wave_sum = G * DC_ROWS <= 64;
+    float accv = 0.f;
     __syncthreads();
 
     const int r = tid & 7, sc = tid >> 3, s = sc % nsb, cl = sc / nsb;
@@ -346,27 +352,47 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
             part[(cl * DC_ROWS + r) * nsb + s] = half_bits_to_f32(B[27] & 0xFFFFu) * fs;
         }
         barrier_lds();
-        // E of each (chunk, row): its superblock partials in order
-        for (int q = tid; q < ng * DC_ROWS; q += bd) {
-            const float* pe = part + q * nsb;
-            float e = 0.f;
-            for (int k = 0; k < nsb; ++k) e += pe[k];
-            esum[q] = e;
-        }
-        barrier_lds();
-        if (tid < DC_ROWS) {   // row tid: this pass's chunks of the token in order
-            float v = acc[tid];
-            for (int q = 0; q < ng; ++q) {
-                const int c = g0 + q;
-                if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + tid], v);
+        if (wave_sum) {
+            if (tid < 64) {
+                // lane q: E of (chunk q / 8, row q % 8), its superblock partials in order; then
+                // row q % 8 takes this pass's chunks of the token in order (every lane joins
+                // the shuffles, lanes 0..7 keep the sums)
+                float e = 0.f;
+                if (tid < ng * DC_ROWS) {
+                    const float* pe = part + tid * nsb;
+                    for (int k = 0; k < nsb; ++k) e += pe[k];
+                }
+                float v = accv;
+                for (int q = 0; q < ng; ++q) {
+                    const int c = g0 + q;
+                    const float ec = __shfl(e, q * DC_ROWS + (tid & (DC_ROWS - 1)));
+                    if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], ec, v);
+                }
+                accv = v;
             }
-            acc[tid] = v;
+        } else {
+            // E of each (chunk, row): its superblock partials in order
+            for (int q = tid; q < ng * DC_ROWS; q += bd) {
+                const float* pe = part + q * nsb;
+                float e = 0.f;
+                for (int k = 0; k < nsb; ++k) e += pe[k];
+                esum[q] = e;
+            }
+            barrier_lds();
+            if (tid < DC_ROWS) {   // row tid: this pass's chunks of the token in order
+                float v = acc[tid];
+                for (int q = 0; q < ng; ++q) {
+                    const int c = g0 + q;
+                    if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + tid], v);
+                }
+                acc[tid] = v;
+            }
         }
-        barrier_lds();   // the records and partials are reused by the next pass
+        if (g0 + G < nch) barrier_lds();   // the records and partials are reused by the next pass
     }
     if (tid < DC_ROWS) {
-        float v = acc[tid];
-        if (ys != nullptr) v += ys[(size_t)tsel * D + r0 + tid];
+        float v = wave_sum ? accv : acc[tid];
+        if (ys != nullptr) v += ysv;
         out[(size_t)tsel * D + r0 + tid] = (uint16_t)f32_to_bf16(v);
     }
 }
