@@ -63,6 +63,8 @@ struct moe_ctx {
     int32_t* perm = nullptr;
     int32_t* inv = nullptr;
     Chunk* chunks = nullptr;
+    Chunk* wave_chunks = nullptr;     // one slot wave's chunks (lists compacted, same bases)
+    int32_t* wave_n_chunks = nullptr;
     float* h_routed = nullptr;
     uint8_t* hrec = nullptr;
     float* h_shared = nullptr;
@@ -157,6 +159,8 @@ size_t carve_scratch(moe_ctx* ctx, size_t M, bool decode_only, uint8_t* base) {
     view(ctx->err, cv.take<int32_t>(STATUS_WORDS));
     if (!decode_only) {
         view(ctx->xs16b, cv.take<uint16_t>(M * D / QK * 48));
+        view(ctx->wave_chunks, cv.take<Chunk>((size_t)ctx->max_chunks));
+        view(ctx->wave_n_chunks, cv.take<int32_t>(PLAN_LISTS));
         view(ctx->h_routed, cv.take<float>(P * I));
         view(ctx->hq_routed, cv.take<int8_t>(P * I));
         view(ctx->hd_routed, cv.take<float>(P * I / QB));
@@ -899,10 +903,19 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     const int rows_max = small ? 1 : std::min(m, GEMV_ROWS);
     const int nch = small ? P + (kq ? m : 0) : chunks;
     const size_t n_runs = std::max<size_t>(1, waves.size());
+    const ExpertArgs a_all = a;   // each wave's launches take a copy (with its own chunk lists)
     for (size_t wv = 0; wv < n_runs; ++wv) {
+        ExpertArgs a = a_all;
         if (waves.size() > 1) {
             rc = run_wave(ctx, waves, wv, st);
             if (rc != MOE_OK) return rc;
+            if (use_mmq) {   // this wave's chunks only, so that its launches spread them over the XCDs
+                if (hip_status(launch_compact_wave(a_all.chunks, a_all.n_chunks, ctx->slot_table_dev, wv == 0, plan,
+                                                   ctx->wave_chunks, ctx->wave_n_chunks, st)) != MOE_OK)
+                    return MOE_EHIP;
+                a.chunks = ctx->wave_chunks;
+                a.n_chunks = ctx->wave_n_chunks;
+            }
         }
         if (use_mmq && fp4) {   // bf16 h, no q8_1 step
             rc = timed(ctx, st, MOE_K_GATEUP, [&] { return launch_fp4_mmq(a, plan, true, st); });

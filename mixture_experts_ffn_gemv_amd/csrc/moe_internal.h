@@ -105,6 +105,10 @@ hipError_t launch_topk(const float* logits, int splits, const float* bias, int m
 hipError_t launch_bucket(const int32_t* idx, int m, int k, int E, int shared_chunks, const ChunkPlan* plan,
                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
                          Chunk* chunks, int32_t* n_chunks, hipStream_t st);
+// the chunks of the plan's lists that one slot wave computes (the others' experts read
+// SLOT_SKIP in its table), compacted list by list at the same bases, with their counts
+hipError_t launch_compact_wave(const Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, bool first_wave,
+                               const ChunkPlan& plan, Chunk* out, int32_t* n_out, hipStream_t st);
 // the small-batch chunks re-read their experts' slots (after miss streaming)
 hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, hipStream_t st);
 bool mmq_supported(int D, int I);

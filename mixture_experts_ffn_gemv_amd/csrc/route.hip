@@ -606,7 +606,51 @@ __global__ __launch_bounds__(256) void refresh_slots_kernel(Chunk* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- one slot wave's chunks
+// The chunks a slot wave computes, so that its launches spread them over the XCDs
+// (the experts of a wave are mostly neighbours in the chunk order, which the tile
+// order would otherwise place on one or two XCDs): for each list c of the plan,
+// the chunks whose expert the wave's slot table does not mark SLOT_SKIP, in their
+// order, at the list's base, and their count; a K-quant shared expert's chunks
+// (expert -1) in the first wave only. One workgroup per list.
+__global__ __launch_bounds__(256) void compact_wave_kernel(const Chunk* __restrict__ in, const int32_t* __restrict__ n_in,
+                                                           const int32_t* __restrict__ slot_table, int first_wave,
+                                                           ChunkPlan plan, Chunk* __restrict__ out,
+                                                           int32_t* __restrict__ n_out) {
+    __shared__ int wsum[4];
+    __shared__ int kept;
+    const int c = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int base = plan.base[c], n = min(n_in[c], plan.cap[c]);
+    if (threadIdx.x == 0) kept = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        const int i = i0 + threadIdx.x;
+        Chunk ch{};
+        bool keep = false;
+        if (i < n) {
+            ch = in[base + i];
+            keep = ch.expert < 0 ? first_wave != 0 : slot_table[ch.expert] != SLOT_SKIP;
+        }
+        const unsigned long long bal = __ballot(keep);
+        if (lane == 0) wsum[wv] = __popcll(bal);
+        __syncthreads();
+        int off = kept + __popcll(bal & ((1ull << lane) - 1));
+        for (int w = 0; w < wv; ++w) off += wsum[w];
+        if (keep) out[base + off] = ch;
+        __syncthreads();
+        if (threadIdx.x == 0) kept += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) n_out[c] = kept;
+}
+
 // ---------------------------------------------------------------- launchers
+hipError_t launch_compact_wave(const Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, bool first_wave,
+                               const ChunkPlan& plan, Chunk* out, int32_t* n_out, hipStream_t st) {
+    return launch_kernel(compact_wave_kernel, PLAN_LISTS, 256, 0, st, chunks, n_chunks, slot_table,
+                         first_wave ? 1 : 0, plan, out, n_out);
+}
+
 hipError_t launch_refresh_slots(Chunk* chunks, const int32_t* n_chunks, const int32_t* slot_table, hipStream_t st) {
     return launch_kernel(refresh_slots_kernel, 1, 256, 0, st, chunks, n_chunks, slot_table);
 }
