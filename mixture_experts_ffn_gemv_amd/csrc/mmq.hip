@@ -416,9 +416,9 @@ __global__ __launch_bounds__(256) void mmq_gateup_q2k_kernel(ExpertArgs a, int n
 //  * Per superblock the 64 rows' blocks (eight panels: one contiguous
 //    880-byte run each) and the h quants and block scales go into LDS with
 //    wavefront-wide loads, the weights as [row][110 bytes], the quants
-//    transposed to [16-byte chunk][token], the block scales as [token][8
-//    blocks]; two superblocks are in LDS, one computed while the next is in
-//    flight. As for gate/up, every sub-tile is computed (no branches in the
+//    transposed to [16-byte chunk][token], the block scales as [8
+//    blocks][token]; two superblocks are in LDS, one computed while the next is
+//    in flight. As for gate/up, every sub-tile is computed (no branches in the
 //    block loop).
 //  * A lane (row = lane % 16, g = lane / 16) realigns once per superblock the
 //    hmask bytes 8g..8g+7, the qs bytes 8g.. of both halves and the scales
@@ -435,7 +435,7 @@ struct DownLds {
     static constexpr int ndx = (8 * R + 255) / 256;
     static constexpr int w_bytes = DW_LOADS * 256 * 16;   // [64 rows][110 B] (+ overrun)
     static constexpr int q_off = w_bytes;
-    static constexpr int dx_off = q_off + 16 * R * 16;
+    static constexpr int dx_off = q_off + 16 * R * 16;    // [8 blocks][R] f32 (+ overrun)
     static constexpr int buf_bytes = dx_off + ndx * 256 * 4;
     static constexpr int lut_off = 2 * buf_bytes;
     static constexpr int xch_off = lut_off + 64 * 8;
@@ -481,14 +481,15 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
     // h rows of the chunk (rows past it repeat its last row; their products are never stored)
     const int srow = max(0, min(tid & (R - 1), ch.nrows - 1));
     const int8_t* hq_row = hq + (size_t)(ch.row0 + srow) * I;
-    // block-scale unit i = 256 u + tid: block i % 8 of h row i / 8 (rows past R or past
-    // the chunk repeat the last one)
+    // block-scale unit i = 256 u + tid: block i / R of h row i % R (rows past the chunk
+    // repeat its last row; units past the eight blocks repeat block 7 into the overrun),
+    // laid out [block][row] as for gate/up
     const float* hd_src[LL::ndx];
 #pragma unroll
     for (int u = 0; u < LL::ndx; ++u) {
         const int i = u * 256 + tid;
-        const int tr = max(0, min(min(i >> 3, R - 1), ch.nrows - 1));
-        hd_src[u] = hd + (size_t)(ch.row0 + tr) * (I / QB) + (i & 7);
+        const int tr = max(0, min(i % R, ch.nrows - 1));
+        hd_src[u] = hd + (size_t)(ch.row0 + tr) * (I / QB) + min(i / R, 7);
     }
     // weight unit f = 256 u + tid of a superblock column: panel f / 55, piece f % 55
     const uint8_t* wsrc[DW_LOADS];
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(256) void mmq_down_q3k_kernel(ExpertArgs a, int nb)
             for (int s = 0; s < NS; ++s) {
                 B[s] = *reinterpret_cast<const int64_t*>(
                     buf + LL::q_off + ((2 * kb8 + gh) * R + 16 * s + l16) * 16 + 8 * (g & 1));
-                dx[s] = dxl[(16 * s + l16) * 8 + kb8];
+                dx[s] = dxl[kb8 * R + 16 * s + l16];
             }
         };
         // the lookup entry of block kb8: six-bit scale of sub-block n = 8 hh + 2 j + g / 2
