@@ -21,8 +21,12 @@ quantisation; tokens ~N(0, 1) in bf16):
                recently used slots reused, waves when the picks outnumber the
                slots). The LRU is warmed with 3 untimed calls.
 A step is one moe_forward call (every kernel of the layer). Prints one JSON
-line for the chosen workload; with the decode headline the other three are
+line for the chosen workload; with the decode headline the others are
 summarised under "workloads" (unless --no-extra). Progress goes to stderr.
+At m <= 8 the line also gives the median, p10 and p90 of single calls, each
+between its own event pair: cold (the rotation above) and warm (one token
+through one layer again and again, so the last-level cache serves what it
+holds of that layer).
 
 --traffic-from FETCH.csv WRITE.csv turns two rocprofv3 --pmc counter files
 (FETCH_SIZE, then WRITE_SIZE, of a run with --copy-calibration) into HBM bytes
@@ -471,6 +475,34 @@ class Bench:
         ktimes = moe.moe_kernel_times(ctx)
         moe.moe_set_profiling(ctx, False)
 
+        # one event pair per call: the spread of single calls with the rotation above
+        # (cold: each call's experts, router and shared expert mostly come from HBM), and
+        # of the same token through the same layer again and again (warm: what the 256 MB
+        # last-level cache holds of that layer serves the repeats)
+        per_call = None
+        if m <= 8 and not streamed:
+            def call_times(fn, n):
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(n)]
+                torch.cuda.synchronize()
+                for i, (a, b) in enumerate(evs):
+                    a.record(stream)
+                    fn(i)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                t = sorted(a.elapsed_time(b) for a, b in evs)
+                pick = lambda q: round(t[min(n - 1, int(q * (n - 1) + 0.5))], 5)
+                return {"median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9), "calls": n}
+            n_calls = max(10, min(steps, 200))
+            cold = call_times(lambda i: step(warmup + i), n_calls)
+            x0 = xs(0)
+            warm = call_times(lambda i: moe.moe_forward(ctx, layers[0]["w"], x0, m, out, stream), n_calls)
+            if moe.moe_check(ctx) != moe.MOE_OK:
+                raise RuntimeError(f"{wl} per-call timing: {moe.strerror(moe.moe_check(ctx))}")
+            per_call = {"cold": cold, "warm": warm,
+                        "note": "one event pair per call; cold: the rotation of the timed region (tokens from "
+                                "the pool, layers in turn); warm: one token through one layer repeatedly"}
+
         # where a bf16 shared expert's rows run in a call of m tokens (the library's plan)
         plan = moe.moe_plan_call(ctx, m, moe.MOE_SHARED_BF16 if spec["shared"] == "bf16" else moe.MOE_SHARED_KQUANT)
         # distinct experts per step (the algorithmic bytes follow the routing), untimed
@@ -548,6 +580,8 @@ class Bench:
             "near_ties": {"tokens": int(stats["near_ties"]), "of_tokens": m * steps,
                           "rule": "k-th largest key minus the largest key left out < 1e-5 (device f32 keys)"},
         }
+        if per_call is not None:
+            res["per_call"] = per_call
         if graph_ms is not None:
             res["graph_replay"] = {
                 "ms_per_step": round(graph_ms, 5),
@@ -700,7 +734,7 @@ def main():
     }
     result["gateup_routed_only_GB_per_s"] = head["gateup_routed_only_GB_per_s"]
     result["near_ties"] = head["near_ties"]
-    for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak", "graph_replay"):
+    for k in ("mmq_i8_mfma_util", "mmq_i8_TOPS", "mmq_frac_of_hbm_peak", "per_call", "graph_replay"):
         if k in head:
             result[k] = head[k]
     if extra:
