@@ -238,10 +238,12 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
 #define MOE_PATH_GEMV 1     /* chunked GEMV kernels (MXFP4 experts up to 8 tokens, slot waves, MIXED groups) */
 #define MOE_PATH_MMQ 2      /* the expert-grouped matrix-core kernels (above 8 tokens) */
 typedef struct moe_plan {
-    int32_t small_routing;      /* 1: one workgroup runs the top-k and bucketing (m <= 8, m * topk <= 512) */
+    int32_t small_routing;      /* 1: one workgroup runs the top-k and bucketing (m <= 8, m * topk <= 512;
+                                   one token on the K-quant decode kernels: the last router
+                                   workgroup, in the router launch, so no top-k launch follows) */
     int32_t expert_path;        /* MOE_PATH_* */
     int32_t shared_rows_router; /* bf16 shared gate/up rows computed by extra workgroups of the router launch */
-    int32_t shared_rows_topk;   /* bf16 shared down rows (0..n-1) in the top-k launch */
+    int32_t shared_rows_topk;   /* bf16 shared down rows (0..n-1) in the top-k launch (0 when there is none) */
     int32_t shared_rows_gateup; /* the rest of them in the routed gate/up launch */
 } moe_plan;
 int moe_plan_call(const moe_ctx* ctx, int32_t m, int32_t shared_fmt, moe_plan* out);
@@ -322,7 +324,9 @@ int moe_reset_stats(moe_ctx* ctx);
  * Every call on a GPU uses that GPU's one array, so two calls that overlap on a
  * GPU (different streams, threads) race; calls queued on one stream do not.
  * The array keeps the last call's contents; every buffer a call reads is
- * written earlier in the same call. MOE_EINVAL for a bad cfg, MXFP4 experts,
+ * written earlier in the same call, except the one-token router launch's
+ * arrival counters at its start, which every call leaves at zero (the array
+ * starts zeroed). MOE_EINVAL for a bad cfg, MXFP4 experts,
  * NULL or misaligned pointers, m < 1, m > 8 or m * topk > 512; MOE_ESCRATCH if
  * the call needs more than MOE_STATIC_SCRATCH_BYTES (no valid cfg does at
  * m <= 8); MOE_EHIP on a runtime error. */

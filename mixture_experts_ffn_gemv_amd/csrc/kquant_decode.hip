@@ -73,9 +73,11 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
     const int tiles = I / GU_TILE;
     const int c = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int tid = threadIdx.x, bd = blockDim.x, wv = tid >> 6;
-    const int nch = *a.n_chunks;
-    if (c >= nch) return;
+    // the chunk (in bounds: the grid covers the list's capacity) and the count,
+    // requested together (the test reads both, so neither load waits for the other)
     const Chunk ch = a.chunks[c];
+    const int nch = *a.n_chunks;
+    if ((c >= nch) | (ch.nrows <= 0)) return;
     const bool shared = ch.expert < 0;
     const int r0 = tile * GU_TILE;
     const int rec = rec_bytes(I);
@@ -257,8 +259,11 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     float* acc = part + G * DC_ROWS * nsb;               // [8]
     float* esum = acc + DC_ROWS;                         // [G][8]
     const int k = a.topk;
+    // this workgroup's chunks into LDS: one token's are the list's first entries
+    // (max_chunks <= blockDim), staged whatever their count, which is requested
+    // alongside (entries past it are never read)
     const int nch = TOK ? min(k + (a.sh_w2 != nullptr ? 1 : 0), max_chunks) : min(*a.n_chunks, max_chunks);
-    for (int q = tid; q < nch; q += bd) {
+    for (int q = tid; q < (TOK ? nch : max_chunks); q += bd) {
         const int ci = !TOK ? q : q < k ? a.inv[tsel * k + q] : routed_rows + tsel;
         const Chunk ch = a.chunks[ci];
         const bool sh = ch.expert < 0;

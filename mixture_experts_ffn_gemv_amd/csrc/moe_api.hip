@@ -81,6 +81,7 @@ struct moe_ctx {
     float* e_rows = nullptr;
     float* ys = nullptr;
     int32_t* err = nullptr;
+    uint32_t* arrive = nullptr;   // the one-token router launch's arrival counters (0 between calls)
     int32_t* slot_table_dev = nullptr;
     // slots
     uint8_t* arena = nullptr;
@@ -136,6 +137,9 @@ size_t carve_scratch(moe_ctx* ctx, size_t M, bool decode_only, uint8_t* base) {
     auto view = [&](auto*& field, size_t off) {
         if (base != nullptr) field = reinterpret_cast<std::remove_reference_t<decltype(field)>>(base + off);
     };
+    // first, at the same offset for every M: the arrival counters, which every call
+    // leaves at 0 (the static scratch holds them across calls of any size)
+    view(ctx->arrive, cv.take<uint32_t>(ROUTER_ARRIVE_WORDS));
     // the router's partial logits: up to 8 splits of m rows, within 4096 rows (one split at m <= 8)
     const int logit_rows = decode_only ? (int)M : (int)std::max<size_t>(M, std::min<size_t>(8 * M, 4096));
     if (base != nullptr) ctx->logit_rows = logit_rows;
@@ -292,6 +296,7 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
 // second stream then.
 struct CallPlan {
     bool small, use_mmq, fp4, decode, shared_fused;
+    bool fold_topk;   // one token on the decode kernels: the router launch also selects
     int sh_router_rows, sh_topk_rows, sh_gateup_rows;
 };
 
@@ -302,11 +307,12 @@ CallPlan plan_call(const moe_ctx* ctx, int m, int shared_fmt) {
     pl.use_mmq = !pl.small && ctx->mmq_ok;
     pl.fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
     pl.decode = pl.small && ctx->decode_ok;
+    pl.fold_topk = m == 1 && pl.decode && !pl.fp4 && router_select_m1_ok(c.n_routed, c.topk);
     pl.shared_fused = shared_fmt == MOE_SHARED_BF16 && pl.small && (ctx->decode_ok || pl.fp4) &&
                       ctx->host_arena == nullptr;
     if (pl.shared_fused) {
         pl.sh_router_rows = c.inter;
-        pl.sh_gateup_rows = ctx->decode_ok ? c.dim - c.dim / 2 : 0;
+        pl.sh_gateup_rows = !ctx->decode_ok ? 0 : pl.fold_topk ? c.dim : c.dim - c.dim / 2;
         pl.sh_topk_rows = c.dim - pl.sh_gateup_rows;
     }
     return pl;
@@ -785,7 +791,33 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     }
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
     const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq, ctx->mixed && !fp4);
-    if (small) {
+    if (pl.fold_topk) {
+        RouteM1 ro{};
+        ro.bias = w->router_bias;
+        ro.E = c.n_routed;
+        ro.k = c.topk;
+        ro.gate_temp = c.gate_temp;
+        ro.norm = c.norm_topk_prob;
+        ro.route_scale = c.route_scale;
+        ro.idx = ctx->idx;
+        ro.gw = ctx->gw;
+        ro.err = ctx->err;
+        ro.shared_chunks = kq ? 1 : 0;
+        ro.offsets = ctx->offsets;
+        ro.active = ctx->active;
+        ro.n_active = ctx->n_active;
+        ro.perm = ctx->perm;
+        ro.inv = ctx->inv;
+        ro.chunks = ctx->chunks;
+        ro.n_chunks = ctx->n_chunks;
+        ro.slot_table = ctx->slot_table_dev;
+        ro.arrive = ctx->arrive;
+        rc = timed(ctx, st, MOE_K_ROUTER, [&] {
+            return launch_router_select_m1(x, (const uint16_t*)w->router_w, c.dim, ctx->logits, ctx->xq, ctx->xd,
+                                           ctx->xs16, ctx->xs16f, ro, st, shared_fused ? &sr_a : nullptr);
+        });
+        if (rc != MOE_OK) return rc;
+    } else if (small) {
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
             return launch_router_quant(x, m, (const uint16_t*)w->router_w, c.dim, c.n_routed, ctx->logits, ctx->xq,
                                        ctx->xd, ctx->xs16, ctx->xs16f, st, shared_fused ? &sr_a : nullptr);

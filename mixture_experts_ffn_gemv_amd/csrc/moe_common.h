@@ -240,6 +240,29 @@ MOE_DEV int xcd_logical_block(int b, int nb_act) {
     return i < per ? min((b & 7) * per + i, nb_act) : nb_act;
 }
 
+// A raw buffer resource over [p, p + bytes) (bytes < 2^32): a load through it whose
+// lane offset lies past the end returns zeros instead of reading memory. p and
+// bytes must be the same in every lane of the wavefront: they are taken from the
+// first active lane, so that the resource sits in scalar registers.
+MOE_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0, n, 0x00020000);
+}
+// 16 bytes at byte offset `off` (a multiple of 16) of a buffer resource
+MOE_DEV uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 16 bytes per lane at byte offset `off` of a buffer resource straight into LDS (lane
+// l writes lds + 16 l; lds is the same in every lane); past the end, zeros land
+MOE_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+}
+
 MOE_DEV float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);

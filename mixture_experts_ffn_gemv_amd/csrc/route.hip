@@ -17,6 +17,10 @@
 
 namespace moe {
 
+// one-token selection inside the router launch: bias and slot entries each router
+// thread prefetches (256 threads: E <= 1024)
+constexpr int M1_PREFETCH = 4;
+
 // ---------------------------------------------------------------- router logits + q8_1(x)
 // One launch, two kinds of workgroups. Blocks [0, E * ntg): router logits
 // z[t, e] = sum_d x[t, d] * W_R[e, d] with f32 accumulation, one workgroup per
@@ -77,16 +81,30 @@ MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* 
     }
 }
 
-template <int TT>
+// the one-token selection by the last router workgroup (defined with the top-k
+// kernels); b[i], sl[i]: bias and slot of expert threadIdx.x + 256 i
+template <int KPL>
+MOE_DEV void select_tail_m1(const float* logits, const RouteM1& ro, const float (&b)[M1_PREFETCH],
+                            const int (&sl)[M1_PREFETCH]);
+
+// KPL > 0 (one token, TT = 1): each router workgroup counts its arrival after its
+// logit is stored, and the last of the E to arrive runs the top-k of route_m1 on
+// all E logits (no workgroup waits for another: the last one finds every logit
+// already written). The count runs in two levels: workgroup e counts in group
+// e % ARRIVE_GROUPS, the last of each group in the top counter (each counter on
+// a cache line of its own), since increments of one address are performed one
+// after another. Every router workgroup requests the bias and slot-table
+// entries the selection needs at its start, so that the last one has them at hand.
+template <int TT, int KPL = 0>
 __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __restrict__ x, int m,
                                                            const uint16_t* __restrict__ wr, int D, int E, int ntg,
                                                            float* __restrict__ logits, int8_t* __restrict__ xq,
                                                            float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f,
-                                                           SharedRows sr) {
+                                                           SharedRows sr, RouteM1 ro) {
     const int nrouter = E * ntg, bd = blockDim.x;
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + bd - 1) / bd;
-    if ((int)blockIdx.x >= nrouter + nq) {   // the shared expert's rows
-        shared_rows_block(sr, blockIdx.x - nrouter - nq);
+    if ((int)blockIdx.x >= nrouter + nq) {   // the shared expert's gate/up rows
+        shared_gateup_block(sr, blockIdx.x - nrouter - nq);
         return;
     }
     if ((int)blockIdx.x >= nrouter) {
@@ -143,29 +161,47 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
         }
         return;
     }
+    // one token, 256 threads: thread i takes 16-byte units i, i + 256, i + 512 of the
+    // expert's row and of x per round (768 units: rows of up to 6144 values in one
+    // round), every load of a round requested at once in straight-line code (units
+    // past the row read the last one and are not added)
     const int e = blockIdx.x % E;
-    const int t0 = (blockIdx.x / E) * TT;
-    const uint2* w = reinterpret_cast<const uint2*>(wr + (size_t)e * D);
-    float acc[TT];
+    float pb[M1_PREFETCH];
+    int psl[M1_PREFETCH];
+    if constexpr (KPL > 0) {
 #pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-    const int nc = D / 4;
-    for (int c = threadIdx.x; c < nc; c += 256) {
-        const uint2 wv = w[c];
-        const float w0 = bf16_lo(wv.x), w1 = bf16_hi(wv.x), w2 = bf16_lo(wv.y), w3 = bf16_hi(wv.y);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            if (t0 + t < m) {
-                const uint2 xv = reinterpret_cast<const uint2*>(x + (size_t)(t0 + t) * D)[c];
-                float a = acc[t];
-                a = fmaf(bf16_lo(xv.x), w0, a);
-                a = fmaf(bf16_hi(xv.x), w1, a);
-                a = fmaf(bf16_lo(xv.y), w2, a);
-                a = fmaf(bf16_hi(xv.y), w3, a);
-                acc[t] = a;
-            }
+        for (int i = 0; i < M1_PREFETCH; ++i) {
+            const int ee = min((int)threadIdx.x + 256 * i, E - 1);
+            pb[i] = ro.bias[ee];
+            psl[i] = ro.slot_table[ee];
         }
     }
+    const uint4* w4 = reinterpret_cast<const uint4*>(wr + (size_t)e * D);
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    constexpr int U1 = 3;
+    const int nu = D / 8;
+    float acc[TT] = {0.f};
+    for (int base = 0; base < nu; base += 256 * U1) {
+        uint4 xv[U1], wv[U1];
+#pragma unroll
+        for (int i = 0; i < U1; ++i) xv[i] = x4[min(base + (int)threadIdx.x + 256 * i, nu - 1)];
+#pragma unroll
+        for (int i = 0; i < U1; ++i) wv[i] = w4[min(base + (int)threadIdx.x + 256 * i, nu - 1)];
+#pragma unroll
+        for (int i = 0; i < U1; ++i) {
+            if (base + (int)threadIdx.x + 256 * i >= nu) break;
+            const uint32_t w8[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+            const uint32_t x8[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            float a = acc[0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a = fmaf(bf16_lo(x8[q]), bf16_lo(w8[q]), a);
+                a = fmaf(bf16_hi(x8[q]), bf16_hi(w8[q]), a);
+            }
+            acc[0] = a;
+        }
+    }
+    const int t0 = 0;
     __shared__ float part[4][TT];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
@@ -174,6 +210,28 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
         if (lane == 0) part[wv][t] = s;
     }
     __syncthreads();
+    if constexpr (KPL > 0) {
+        // The logit goes out as a device-coherent store (it passes every cache that
+        // another XCD does not share) and the thread waits for it to complete before
+        // counting its workgroup's arrival; the last workgroup reads the logits the
+        // same way. (A release fence would write the whole L2 back in each of the E
+        // workgroups, which costs more than the selection saves.)
+        __shared__ int last;
+        if (threadIdx.x == 0) {
+            const float z = ((part[0][0] + part[1][0]) + part[2][0]) + part[3][0];
+            __hip_atomic_store(logits + e, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            // counters wrap to 0 after their last arrival
+            const int g = e % ARRIVE_GROUPS, ng = min(E, ARRIVE_GROUPS);
+            const unsigned n_in_g = (unsigned)((E - g + ARRIVE_GROUPS - 1) / ARRIVE_GROUPS);
+            bool l = atomicInc(ro.arrive + ARRIVE_STRIDE * (1 + g), n_in_g - 1) == n_in_g - 1;
+            if (l) l = atomicInc(ro.arrive, (unsigned)(ng - 1)) == (unsigned)(ng - 1);
+            last = l;
+        }
+        __syncthreads();
+        if (last) select_tail_m1<KPL>(logits, ro, pb, psl);
+        return;
+    }
     if (threadIdx.x < TT && t0 + (int)threadIdx.x < m) {
         const int t = threadIdx.x;
         logits[(size_t)(t0 + t) * E + e] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
@@ -402,7 +460,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
                                                            int32_t* __restrict__ n_chunks,
                                                            const int32_t* __restrict__ slot_table, SharedRows sr) {
     if (blockIdx.x > 0) {   // the shared expert's rows
-        shared_rows_block(sr, blockIdx.x - 1);
+        shared_down_block<SR_DOWN_PIECES>(sr, blockIdx.x - 1);
         return;
     }
     constexpr int MT = ROUTE_SMALL_MAX_M;
@@ -564,6 +622,41 @@ MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int
     }
 }
 
+// The last router workgroup (any size that is a multiple of 64): every thread
+// scores experts tid, tid + blockDim, ... into LDS (the logits read device-coherently),
+// then the first wavefront selects.
+template <int KPL>
+MOE_DEV void select_tail_m1(const float* logits, const RouteM1& ro, const float (&b)[M1_PREFETCH],
+                            const int (&sl)[M1_PREFETCH]) {
+    static_assert(64 * KPL <= 256 * M1_PREFETCH, "one key per prefetched entry");
+    __shared__ float keys[64 * KPL], scores[64 * KPL];
+    __shared__ int slots[64 * KPL];
+    float z[M1_PREFETCH];
+#pragma unroll
+    for (int i = 0; i < M1_PREFETCH; ++i) {   // every logit requested at once
+        const int e = threadIdx.x + 256 * i;
+        z[i] = e < ro.E ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+    }
+    bool bad_any = false;
+#pragma unroll
+    for (int i = 0; i < M1_PREFETCH; ++i) {
+        const int e = threadIdx.x + 256 * i;
+        if (e >= 64 * KPL) break;
+        float sv = 0.f, kv = -INFINITY;
+        bool bad = false;
+        if (e < ro.E) score_of(z[i], b[i], ro.gate_temp, sv, kv, bad);
+        keys[e] = kv;
+        scores[e] = sv;
+        slots[e] = sl[i];
+        bad_any |= bad;
+    }
+    if (__any(bad_any) && (threadIdx.x & 63) == 0) atomicOr(ro.err, ERR_NONFINITE);
+    __syncthreads();
+    if (threadIdx.x >= 64) return;
+    select_m1<KPL>(keys, scores, ro.E, ro.k, ro.norm, ro.route_scale, ro.idx, ro.gw, ro.shared_chunks, ro.offsets,
+                   ro.active, ro.n_active, ro.perm, ro.inv, ro.chunks, ro.n_chunks, slots, ro.err);
+}
+
 template <int KPL>
 __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
                                                         int E, int k, float gate_temp, int norm, float route_scale,
@@ -575,7 +668,7 @@ __global__ __launch_bounds__(1024) void route_m1_kernel(const float* __restrict_
                                                         int32_t* __restrict__ n_chunks,
                                                         const int32_t* __restrict__ slot_table, SharedRows sr) {
     if (blockIdx.x > 0) {   // the shared expert's rows
-        shared_rows_block(sr, blockIdx.x - 1);
+        shared_down_block<SR_DOWN_PIECES>(sr, blockIdx.x - 1);
         return;
     }
     __shared__ float keys[64 * M1_MAX_KEYS], scores[64 * M1_MAX_KEYS];
@@ -667,10 +760,28 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + th - 1) / th;
     const int nsh = sr ? shared_rows_blocks(*sr, th) : 0;
     const int grid = E + nq + nsh;
-    if (m == 1) return launch_kernel(router_quant_kernel<1>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
-    if (m == 2) return launch_kernel(router_quant_kernel<2>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
-    if (m <= 4) return launch_kernel(router_quant_kernel<4>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
-    return launch_kernel(router_quant_kernel<8>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s);
+    const RouteM1 no{};
+    if (m == 1) return launch_kernel(router_quant_kernel<1>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
+    if (m == 2) return launch_kernel(router_quant_kernel<2>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
+    if (m <= 4) return launch_kernel(router_quant_kernel<4>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
+    return launch_kernel(router_quant_kernel<8>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
+}
+
+bool router_select_m1_ok(int E, int k) { return E >= 1 && E <= 64 * M1_MAX_KEYS && k >= 1 && k <= 64 && k <= E; }
+
+hipError_t launch_router_select_m1(const uint16_t* x, const uint16_t* wr, int D, float* logits, int8_t* xq,
+                                   float* xd, int32_t* xs16, float* xs16f, const RouteM1& ro, hipStream_t st,
+                                   const SharedRows* sr) {
+    if (!router_select_m1_ok(ro.E, ro.k) || ro.arrive == nullptr) return hipErrorInvalidValue;
+    SharedRows none{};
+    const SharedRows& s = sr ? *sr : none;
+    const int th = 256;
+    const int nq = xq == nullptr ? 0 : (D / QB + th - 1) / th;
+    const int grid = ro.E + nq + (sr ? shared_rows_blocks(*sr, th) : 0);
+    const int kpl = topk_kpl(ro.E);
+    if (kpl == 2) return launch_kernel(router_quant_kernel<1, 2>, grid, th, 0, st, x, 1, wr, D, ro.E, 1, logits, xq, xd, xs16, xs16f, s, ro);
+    if (kpl == 6) return launch_kernel(router_quant_kernel<1, 6>, grid, th, 0, st, x, 1, wr, D, ro.E, 1, logits, xq, xd, xs16, xs16f, s, ro);
+    return launch_kernel(router_quant_kernel<1, 16>, grid, th, 0, st, x, 1, wr, D, ro.E, 1, logits, xq, xd, xs16, xs16f, s, ro);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,

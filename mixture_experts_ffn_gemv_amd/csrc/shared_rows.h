@@ -33,6 +33,8 @@ inline int shared_rows_blocks(const SharedRows& sr, int threads) {
 // 16-byte pieces of a row a lane holds in registers at once (rows of up to 6144
 // values in one round; longer rows take a second, synchronous round)
 constexpr int SR_PIECES = 12;
+// the same for the down rows of the routing launches (rows of up to 3072 values in one round)
+constexpr int SR_DOWN_PIECES = 6;
 
 MOE_DEV float dot2_bf16x(uint32_t a, uint32_t b, float c) {
     typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -42,122 +44,110 @@ MOE_DEV float dot2_bf16x(uint32_t a, uint32_t b, float c) {
 // Workgroup `blk` of the shared rows: wavefront 2i takes row (row0 + blk * rpw + i)
 // of W1, wavefront 2i + 1 the same row of W3 (rpw = wavefronts / 2). A lane
 // holds 16-byte pieces lane, lane + 64, ... of its row (every load of the
-// wavefront 1 KB contiguous; up to SR_PIECES per round), dots them with the
-// same pieces of each token row of x, and the wavefront sums; the gate
-// wavefront applies the SwiGLU.
+// wavefront 1 KB contiguous; up to SR_PIECES per round) and dots them with the
+// same pieces of each token row of x; the wavefront sums (lane t keeps token
+// t's sum) and the gate wavefront applies the SwiGLU. The weights go straight
+// into registers through a buffer resource over the row (pieces past its end
+// read as zeros); each token's pieces of x come once per workgroup into LDS
+// (buffer loads into LDS, requested before the weights for the first token;
+// pieces past the row land as zeros), where the wavefronts read them.
 MOE_DEV void shared_gateup_block(const SharedRows& sr, int blk) {
     __shared__ float up[16][8];
+    __shared__ __align__(16) uint4 xs[SR_PIECES * 64];
     const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rpw = nw >> 1, rl = wv >> 1;
     const int rr = blk * rpw + rl;
     const bool valid = wv < 2 * rpw && rr < sr.rows;
     const int r = sr.row0 + rr;
     const int n16 = sr.D / 8;   // 16-byte pieces per row
-    float dots[8];
+    const uint32_t row_bytes = (uint32_t)sr.D * 2;
+    float mine = 0.f;   // lane t < m: token t's dot
+    const auto W = buffer_rsrc(((wv & 1) ? sr.w3 : sr.w1) + (size_t)(valid ? r : sr.row0) * sr.D, row_bytes);
+    // token t's pieces [p0, p0 + SR_PIECES * 64) of x into xs: 16 bytes per thread and
+    // load (pieces past the row land as zeros)
+    auto stage_x = [&](int t, int p0) {
+        const auto X = buffer_rsrc(sr.x + (size_t)t * sr.D, row_bytes);
+        for (int i = threadIdx.x; i < SR_PIECES * 64; i += blockDim.x) buffer_load_lds16(X, xs + (i - lane), 16 * (p0 + i));
+    };
+    for (int p0 = 0; p0 < n16; p0 += SR_PIECES * 64) {
+        const uint32_t off = 16 * (p0 + lane);
+        stage_x(0, p0);
+        uint4 wq[SR_PIECES];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) dots[t] = 0.f;
-    if (valid) {
-        const uint4* W = reinterpret_cast<const uint4*>(((wv & 1) ? sr.w3 : sr.w1) + (size_t)r * sr.D);
-        for (int j0 = 0; j0 * 64 < n16; j0 += SR_PIECES) {
-            uint4 wq[SR_PIECES];
+        for (int j = 0; j < SR_PIECES; ++j) wq[j] = buffer_load16(W, off + 1024 * j);
+        for (int t = 0; t < sr.m; ++t) {
+            if (t > 0) {
+                __syncthreads();   // every wavefront is done with token t - 1's pieces
+                stage_x(t, p0);
+            }
+            // this wavefront's DMA has landed (for the first token it was issued before
+            // the weights, which may stay in flight)
+            if (t == 0) wait_vm_loads<SR_PIECES>();
+            else wait_vm_loads<0>();
+            __syncthreads();
+            float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < SR_PIECES; ++j) {
-                const int k = lane + 64 * (j0 + j);
-                wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 xv = xs[lane + 64 * j];
+                acc = dot2_bf16x(wq[j].x, xv.x, acc);
+                acc = dot2_bf16x(wq[j].y, xv.y, acc);
+                acc = dot2_bf16x(wq[j].z, xv.z, acc);
+                acc = dot2_bf16x(wq[j].w, xv.w, acc);
             }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                if (t >= sr.m) break;
-                const uint4* X = reinterpret_cast<const uint4*>(sr.x + (size_t)t * sr.D);
-                float acc = 0.f;
-#pragma unroll
-                for (int j = 0; j < SR_PIECES; ++j) {
-                    const int k = lane + 64 * (j0 + j);
-                    if (k < n16) {
-                        const uint4 xv = X[k];
-                        acc = dot2_bf16x(wq[j].x, xv.x, acc);
-                        acc = dot2_bf16x(wq[j].y, xv.y, acc);
-                        acc = dot2_bf16x(wq[j].z, xv.z, acc);
-                        acc = dot2_bf16x(wq[j].w, xv.w, acc);
-                    }
-                }
-                dots[t] += acc;
-            }
+            const float sum = wave_sum(acc);
+            if (lane == t) mine += sum;
         }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t >= sr.m) break;
-            dots[t] = wave_sum(dots[t]);
-        }
-        if ((wv & 1) && lane == 0) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) up[rl][t] = dots[t];
-        }
+        __syncthreads();   // xs is restaged by the next round
     }
+    if (valid && (wv & 1) && lane < sr.m) up[rl][lane] = mine;
     __syncthreads();
-    if (valid && !(wv & 1) && lane == 0) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t >= sr.m) break;
-            sr.h[(size_t)t * sr.I + r] = (uint16_t)f32_to_bf16(swiglu(dots[t], up[rl][t], sr.limit));
-        }
-    }
+    if (valid && !(wv & 1) && lane < sr.m)
+        sr.h[(size_t)lane * sr.I + r] = (uint16_t)f32_to_bf16(swiglu(mine, up[rl][lane], sr.limit));
 }
 
 // Workgroup `blk` of the shared down rows: wavefront i takes output row
 // row0 + blk * (wavefronts) + i of W2, 16-byte pieces lane, lane + 64, ... (every
 // load of the wavefront 1 KB contiguous), dotted with the same pieces of each
-// token's h; the wavefront sums and lane 0 writes ys. NP pieces per lane and
-// round (fewer registers for launches that must stay lean).
+// token's h; the wavefront sums and lane t writes token t's ys. NP pieces per
+// lane and round (fewer registers for launches that must stay lean); loads are
+// requested as in the gate/up rows.
 template <int NP = SR_PIECES>
 MOE_DEV void shared_down_block(const SharedRows& sr, int blk) {
     const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rr = blk * nw + wv;
     if (rr >= sr.rows) return;
     const int r = sr.row0 + rr;
-    const int n16 = sr.I / 8;   // 16-byte pieces per row
-    const uint4* W = reinterpret_cast<const uint4*>(sr.w2 + (size_t)r * sr.I);
-    float dots[8];
+    const uint32_t row_bytes = (uint32_t)sr.I * 2;
+    const auto W = buffer_rsrc(sr.w2 + (size_t)r * sr.I, row_bytes);
+    float mine = 0.f;   // lane t < m: token t's dot
+    for (uint32_t o0 = 0; o0 < row_bytes; o0 += NP * 1024) {
+        const uint32_t off = o0 + 16 * lane;
+        uint4 hq[NP], wq[NP];
+        const auto H0 = buffer_rsrc(sr.h, row_bytes);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) dots[t] = 0.f;
-    for (int j0 = 0; j0 * 64 < n16; j0 += NP) {
-        uint4 wq[NP];
+        for (int j = 0; j < NP; ++j) hq[j] = buffer_load16(H0, off + 1024 * j);
 #pragma unroll
-        for (int j = 0; j < NP; ++j) {
-            const int k = lane + 64 * (j0 + j);
-            wq[j] = k < n16 ? W[k] : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int j = 0; j < NP; ++j) wq[j] = buffer_load16(W, off + 1024 * j);
+#pragma unroll 1
+        for (int t = 0; t < sr.m; ++t) {
+            if (t > 0) {
+                const auto H = buffer_rsrc(sr.h + (size_t)t * sr.I, row_bytes);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t >= sr.m) break;
-            const uint4* H = reinterpret_cast<const uint4*>(sr.h + (size_t)t * sr.I);
+                for (int j = 0; j < NP; ++j) hq[j] = buffer_load16(H, off + 1024 * j);
+            }
             float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
-                const int k = lane + 64 * (j0 + j);
-                if (k < n16) {
-                    const uint4 hv = H[k];
-                    acc = dot2_bf16x(wq[j].x, hv.x, acc);
-                    acc = dot2_bf16x(wq[j].y, hv.y, acc);
-                    acc = dot2_bf16x(wq[j].z, hv.z, acc);
-                    acc = dot2_bf16x(wq[j].w, hv.w, acc);
-                }
+                acc = dot2_bf16x(wq[j].x, hq[j].x, acc);
+                acc = dot2_bf16x(wq[j].y, hq[j].y, acc);
+                acc = dot2_bf16x(wq[j].z, hq[j].z, acc);
+                acc = dot2_bf16x(wq[j].w, hq[j].w, acc);
             }
-            dots[t] += acc;
+            const float sum = wave_sum(acc);
+            if (lane == t) mine += sum;
         }
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        if (t >= sr.m) break;
-        const float v = wave_sum(dots[t]);
-        if (lane == 0) sr.ys[(size_t)t * sr.D + r] = v;
-    }
-}
-
-// the launch's shared rows, gate/up or down
-MOE_DEV void shared_rows_block(const SharedRows& sr, int blk) {
-    if (sr.w2 != nullptr) shared_down_block(sr, blk);
-    else shared_gateup_block(sr, blk);
+    if (lane < sr.m) sr.ys[(size_t)lane * sr.D + r] = mine;
 }
 
 }  // namespace moe
