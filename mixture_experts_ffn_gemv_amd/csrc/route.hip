@@ -84,7 +84,7 @@ MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* 
 // the one-token selection by the last router workgroup (defined with the top-k
 // kernels); b[i], sl[i]: bias and slot of expert threadIdx.x + 256 i
 template <int KPL>
-MOE_DEV void select_tail_m1(const float* logits, const RouteM1& ro, const float (&b)[M1_PREFETCH],
+MOE_DEV void select_tail_m1(const float* scores_in, const RouteM1& ro, const float (&b)[M1_PREFETCH],
                             const int (&sl)[M1_PREFETCH]);
 
 // KPL > 0 (one token, TT = 1): each router workgroup counts its arrival after its
@@ -216,10 +216,15 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
         // counting its workgroup's arrival; the last workgroup reads the logits the
         // same way. (A release fence would write the whole L2 back in each of the E
         // workgroups, which costs more than the selection saves.)
+        // What goes out is the expert's score sqrt(softplus(z / gate_temp)) rather than
+        // its logit z: the last workgroup then adds only the bias.
         __shared__ int last;
         if (threadIdx.x == 0) {
             const float z = ((part[0][0] + part[1][0]) + part[2][0]) + part[3][0];
-            __hip_atomic_store(logits + e, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float sv, kv;
+            bool bad;
+            score_of(z, 0.f, ro.gate_temp, sv, kv, bad);
+            __hip_atomic_store(logits + e, sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_s_waitcnt(0);
             // counters wrap to 0 after their last arrival
             const int g = e % ARRIVE_GROUPS, ng = min(E, ARRIVE_GROUPS);
@@ -579,10 +584,28 @@ MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int
     bool near;
     wave_topk<KPL>(keys, scores, E, k, my_e, my_s, near);
     if (near && lane == 0) atomicAdd(reinterpret_cast<unsigned*>(err + ERR_NEAR_TIES), 1u);
-    const float wgt = wave_pick_weight(my_s, k, norm, route_scale);
-    // the picks sorted by expert id (all distinct): position = rank of the id
+    // up to M1_FAST_K picks: every pick's id and score in scalar registers once (entries
+    // past k: id INT_MAX, score 0, which leave the counts and the in-order sum as they are)
+    constexpr int M1_FAST_K = 8;
+    const bool fast = k <= M1_FAST_K;
+    int pe[M1_FAST_K];
+    float wgt;
     int pos = 0;
-    for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(my_e, q) < my_e ? 1 : 0;
+    if (fast) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < M1_FAST_K; ++q) {
+            pe[q] = q < k ? __builtin_amdgcn_readlane(my_e, q) : INT_MAX;
+            sum += q < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), q)) : 0.f;
+        }
+        wgt = (norm && k > 1 ? my_s / (sum + 1e-20f) : my_s) * route_scale;
+#pragma unroll
+        for (int q = 0; q < M1_FAST_K; ++q) pos += pe[q] < my_e ? 1 : 0;
+    } else {
+        wgt = wave_pick_weight(my_s, k, norm, route_scale);
+        for (int q = 0; q < k; ++q) pos += __builtin_amdgcn_readlane(my_e, q) < my_e ? 1 : 0;
+    }
+    // the picks sorted by expert id (all distinct): position = rank of the id
     if (lane < k) {
         idx[lane] = my_e;
         gw[lane] = wgt;
@@ -610,43 +633,52 @@ MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int
         c.pad0 = c.pad1 = 0;
         chunks[k] = c;
     }
-    // offsets[e] = picks with a smaller id
-    for (int e = lane; e <= E; e += 64) {
-        int cnt = 0;
-        for (int q = 0; q < k; ++q) cnt += __builtin_amdgcn_readlane(my_e, q) < e ? 1 : 0;
-        offsets[e] = cnt;
-    }
     if (lane == 0) {
         *n_active = k;
         *n_chunks = k + (shared_chunks ? 1 : 0);
     }
+    // offsets[e] = picks with a smaller id
+    for (int e = lane; e <= E; e += 64) {
+        int cnt = 0;
+        if (fast) {
+#pragma unroll
+            for (int q = 0; q < M1_FAST_K; ++q) cnt += pe[q] < e ? 1 : 0;
+        } else {
+            for (int q = 0; q < k; ++q) cnt += __builtin_amdgcn_readlane(my_e, q) < e ? 1 : 0;
+        }
+        offsets[e] = cnt;
+    }
 }
 
-// The last router workgroup (any size that is a multiple of 64): every thread
-// scores experts tid, tid + blockDim, ... into LDS (the logits read device-coherently),
-// then the first wavefront selects.
+// The last router workgroup (256 threads): every thread forms the keys of experts
+// tid, tid + 256, ... from their scores (read device-coherently) and prefetched
+// biases into LDS, then the first wavefront selects.
 template <int KPL>
-MOE_DEV void select_tail_m1(const float* logits, const RouteM1& ro, const float (&b)[M1_PREFETCH],
+MOE_DEV void select_tail_m1(const float* scores_in, const RouteM1& ro, const float (&b)[M1_PREFETCH],
                             const int (&sl)[M1_PREFETCH]) {
     static_assert(64 * KPL <= 256 * M1_PREFETCH, "one key per prefetched entry");
     __shared__ float keys[64 * KPL], scores[64 * KPL];
     __shared__ int slots[64 * KPL];
-    float z[M1_PREFETCH];
+    float sc[M1_PREFETCH];
 #pragma unroll
-    for (int i = 0; i < M1_PREFETCH; ++i) {   // every logit requested at once
+    for (int i = 0; i < M1_PREFETCH; ++i) {   // every score requested at once
         const int e = threadIdx.x + 256 * i;
-        z[i] = e < ro.E ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+        sc[i] = e < ro.E ? __hip_atomic_load(scores_in + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
     }
     bool bad_any = false;
 #pragma unroll
     for (int i = 0; i < M1_PREFETCH; ++i) {
         const int e = threadIdx.x + 256 * i;
         if (e >= 64 * KPL) break;
-        float sv = 0.f, kv = -INFINITY;
+        float kv = -INFINITY;
         bool bad = false;
-        if (e < ro.E) score_of(z[i], b[i], ro.gate_temp, sv, kv, bad);
+        if (e < ro.E) {   // the key as score_of forms it: score + bias, NaN -> -inf
+            kv = sc[i] + b[i];
+            bad = kv != kv;
+            if (bad) kv = -INFINITY;
+        }
         keys[e] = kv;
-        scores[e] = sv;
+        scores[e] = e < ro.E ? sc[i] : 0.f;
         slots[e] = sl[i];
         bad_any |= bad;
     }
