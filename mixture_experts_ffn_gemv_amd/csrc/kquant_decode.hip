@@ -255,8 +255,9 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     int* c_row = c_slot + max_chunks;
     int* c_tok = c_row + max_chunks;
     float* c_w = reinterpret_cast<float*>(c_tok + max_chunks);
-    float* part = c_w + max_chunks;                      // [G][8][nsb]
-    float* acc = part + G * DC_ROWS * nsb;               // [8]
+    const int pst = (nsb + 3) & ~3;                      // partials per (chunk, row), padded to 16 bytes
+    float* part = c_w + max_chunks;                      // [G][8][pst] (16-byte aligned: 4 arrays of max_chunks words)
+    float* acc = part + G * DC_ROWS * pst;               // [8]
     float* esum = acc + DC_ROWS;                         // [G][8]
     const int k = a.topk;
     // this workgroup's chunks into LDS: one token's are the list's first entries
@@ -354,35 +355,42 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
                 const int isum = __mul24((lo0 | (hi0 << 4)) - 32, il) + __mul24((lo1 | (hi1 << 4)) - 32, ih);
                 fs = fmaf(hd[t], (float)isum, fs);
             }
-            part[(cl * DC_ROWS + r) * nsb + s] = half_bits_to_f32(B[27] & 0xFFFFu) * fs;
+            part[(cl * DC_ROWS + r) * pst + s] = half_bits_to_f32(B[27] & 0xFFFFu) * fs;
         }
         barrier_lds();
+        // E of (chunk q / 8, row q % 8): its superblock partials in order (read 16 bytes at a time)
+        auto e_of = [&](int q) {
+            const float4* pe = reinterpret_cast<const float4*>(part + q * pst);
+            float e = 0.f;
+#pragma unroll 4
+            for (int k4 = 0; k4 < pst / 4; ++k4) {
+                const float4 v = pe[k4];
+                e += v.x;   // 4 k4 < nsb for every k4 < pst / 4
+                if (4 * k4 + 1 < nsb) e += v.y;
+                if (4 * k4 + 2 < nsb) e += v.z;
+                if (4 * k4 + 3 < nsb) e += v.w;
+            }
+            return e;
+        };
         if (wave_sum) {
             if (tid < 64) {
-                // lane q: E of (chunk q / 8, row q % 8), its superblock partials in order; then
-                // row q % 8 takes this pass's chunks of the token in order (every lane joins
-                // the shuffles, lanes 0..7 keep the sums)
-                float e = 0.f;
-                if (tid < ng * DC_ROWS) {
-                    const float* pe = part + tid * nsb;
-                    for (int k = 0; k < nsb; ++k) e += pe[k];
+                // lane q: E of (chunk q / 8, row q % 8) into LDS; then row q % 8 (lanes 0..7) takes
+                // this pass's chunks of the token in order, from LDS (one wavefront: its LDS
+                // writes come before its reads)
+                if (tid < ng * DC_ROWS) esum[tid] = e_of(tid);
+                __builtin_amdgcn_wave_barrier();
+                if (tid < DC_ROWS) {
+                    float v = accv;
+                    for (int q = 0; q < ng; ++q) {
+                        const int c = g0 + q;
+                        if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + tid], v);
+                    }
+                    accv = v;
                 }
-                float v = accv;
-                for (int q = 0; q < ng; ++q) {
-                    const int c = g0 + q;
-                    const float ec = __shfl(e, q * DC_ROWS + (tid & (DC_ROWS - 1)));
-                    if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], ec, v);
-                }
-                accv = v;
             }
         } else {
             // E of each (chunk, row): its superblock partials in order
-            for (int q = tid; q < ng * DC_ROWS; q += bd) {
-                const float* pe = part + q * nsb;
-                float e = 0.f;
-                for (int k = 0; k < nsb; ++k) e += pe[k];
-                esum[q] = e;
-            }
+            for (int q = tid; q < ng * DC_ROWS; q += bd) esum[q] = e_of(q);
             barrier_lds();
             if (tid < DC_ROWS) {   // row tid: this pass's chunks of the token in order
                 float v = acc[tid];
@@ -438,7 +446,8 @@ hipError_t launch_down_combine(const ExpertArgs& a, int routed_rows, int m, int 
     const int threads = round64(lanes * G);
     const int rec16 = (int)(decode_rec_bytes(a.I) / 16);
     const int nu = (G * rec16 + threads - 1) / threads;
-    const size_t lds = (size_t)std::max(nu, 3) * threads * 16 + (size_t)per_tok * 16 + (size_t)G * DC_ROWS * nsb * 4 +
+    const int pst = (nsb + 3) & ~3;
+    const size_t lds = (size_t)std::max(nu, 3) * threads * 16 + (size_t)per_tok * 16 + (size_t)G * DC_ROWS * pst * 4 +
                        (size_t)DC_ROWS * 4 + (size_t)G * DC_ROWS * 4;
     if (m == 1)
         return launch_kernel(down_combine_kernel<false>, a.D / DC_ROWS, threads, lds, st, a, routed_rows, m, per_tok,
