@@ -222,6 +222,33 @@ __global__ __launch_bounds__(1024) void gateup_q8_kernel(ExpertArgs a, int route
 }
 
 // ------------------------------------------------------------------ Q3_K down + combine
+// v + the weighted E of a pass's ng chunks g0.. that belong to token tsel and are
+// resident, in chunk order (e: this row's E of chunk q at e[q * DC_ROWS]). Up to 8
+// chunks every LDS read is requested before the first product.
+MOE_DEV float combine_pass(float v, int g0, int ng, int tsel, const int* c_tok, const int* c_slot, const float* c_w,
+                           const float* e) {
+    if (ng <= 8) {
+        bool use[8];
+        float w[8], ev[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = g0 + min(q, ng - 1);
+            use[q] = (q < ng) & (c_tok[c] == tsel) & (c_slot[c] != -1);   // no short circuit: reads batched
+            w[q] = c_w[c];
+            ev[q] = e[min(q, ng - 1) * DC_ROWS];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (use[q]) v = fmaf(w[q], ev[q], v);
+        return v;
+    }
+    for (int q = 0; q < ng; ++q) {
+        const int c = g0 + q;
+        if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], e[q * DC_ROWS], v);
+    }
+    return v;
+}
+
 // One workgroup = one panel of 8 output rows for one token (workgroup b: token
 // b / (D / 8), panel b % (D / 8)); its chunks are the token's k picks (at m = 1
 // every chunk in list order, else the positions inv[] gives, in pick order) and
@@ -277,10 +304,12 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     // the shared expert's output for this workgroup's rows, requested now (it is added last)
     const float ysv = (ys != nullptr && tid < DC_ROWS) ? ys[(size_t)tsel * D + r0 + tid] : 0.f;
     // with every (chunk, row) of a pass in one wavefront, wavefront 0 finishes each pass
-    // with shuffles (lanes 0..7 carry the rows' sums across passes)
+    // (lanes 0..7 carry the rows' sums across passes)
     const bool wave_sum = G * DC_ROWS <= 64;
     float accv = 0.f;
-    __syncthreads();
+    // the chunk entries in LDS for every wavefront; the ys load stays in flight (a full
+    // workgroup barrier would wait for it, behind the other workgroups' weight loads)
+    barrier_lds();
 
     const int r = tid & 7, sc = tid >> 3, s = sc % nsb, cl = sc / nsb;
     const uint32_t* h32 = reinterpret_cast<const uint32_t*>(hrec) + (size_t)cl * (rec / 4);
@@ -358,17 +387,27 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
             part[(cl * DC_ROWS + r) * pst + s] = half_bits_to_f32(B[27] & 0xFFFFu) * fs;
         }
         barrier_lds();
-        // E of (chunk q / 8, row q % 8): its superblock partials in order (read 16 bytes at a time)
+        // E of (chunk q / 8, row q % 8): its superblock partials in order, read 16 bytes at a
+        // time (up to 16 partials every read requested before the first add)
         auto e_of = [&](int q) {
             const float4* pe = reinterpret_cast<const float4*>(part + q * pst);
+            const int n4 = pst / 4;
             float e = 0.f;
-#pragma unroll 4
-            for (int k4 = 0; k4 < pst / 4; ++k4) {
-                const float4 v = pe[k4];
-                e += v.x;   // 4 k4 < nsb for every k4 < pst / 4
+            auto add4 = [&](const float4& v, int k4) {
+                e += v.x;   // 4 k4 < nsb for every k4 < n4
                 if (4 * k4 + 1 < nsb) e += v.y;
                 if (4 * k4 + 2 < nsb) e += v.z;
                 if (4 * k4 + 3 < nsb) e += v.w;
+            };
+            if (n4 <= 4) {
+                float4 v[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) v[k4] = pe[min(k4, n4 - 1)];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4)
+                    if (k4 < n4) add4(v[k4], k4);
+            } else {
+                for (int k4 = 0; k4 < n4; ++k4) add4(pe[k4], k4);
             }
             return e;
         };
@@ -379,27 +418,14 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
                 // writes come before its reads)
                 if (tid < ng * DC_ROWS) esum[tid] = e_of(tid);
                 __builtin_amdgcn_wave_barrier();
-                if (tid < DC_ROWS) {
-                    float v = accv;
-                    for (int q = 0; q < ng; ++q) {
-                        const int c = g0 + q;
-                        if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + tid], v);
-                    }
-                    accv = v;
-                }
+                if (tid < DC_ROWS) accv = combine_pass(accv, g0, ng, tsel, c_tok, c_slot, c_w, esum + tid);
             }
         } else {
             // E of each (chunk, row): its superblock partials in order
             for (int q = tid; q < ng * DC_ROWS; q += bd) esum[q] = e_of(q);
             barrier_lds();
-            if (tid < DC_ROWS) {   // row tid: this pass's chunks of the token in order
-                float v = acc[tid];
-                for (int q = 0; q < ng; ++q) {
-                    const int c = g0 + q;
-                    if (c_tok[c] == tsel && c_slot[c] != -1) v = fmaf(c_w[c], esum[q * DC_ROWS + tid], v);
-                }
-                acc[tid] = v;
-            }
+            if (tid < DC_ROWS)   // row tid: this pass's chunks of the token in order
+                acc[tid] = combine_pass(acc[tid], g0, ng, tsel, c_tok, c_slot, c_w, esum + tid);
         }
         if (g0 + G < nch) barrier_lds();   // the records and partials are reused by the next pass
     }
