@@ -315,13 +315,14 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
     const uint32_t* h32 = reinterpret_cast<const uint32_t*>(hrec) + (size_t)cl * (rec / 4);
     for (int g0 = 0; g0 < nch; g0 += G) {
         const int ng = min(G, nch - g0);
-        // this pass's q8_1(h) records (units past the end repeat the last one) and this
+        // this pass's q8_1(h) records (units past the end repeat the last one), then this
         // lane's block, 28 dwords from the dword below its start (in bounds: a block that
-        // starts on a dword ends 2 bytes before the next block of its column run), all
-        // requested in straight-line code (a lane without a block reads slot 0's), the
-        // records first; they go into LDS through registers, so that every wait is exact
-        // and a lane computes its block as soon as the block has arrived. Record units
-        // past NR per thread (other shapes) are staged first, synchronously.
+        // starts on a dword ends 2 bytes before the next block of its column run), in
+        // straight-line code (a lane without a block reads slot 0's). The records go into
+        // LDS through registers before the block is requested: requested behind the
+        // other workgroups' weight loads they arrive microseconds later than on their own.
+        // The waits are exact, so a lane computes its block as soon as it has arrived.
+        // Record units past NR per thread (other shapes) are staged first, synchronously.
         auto rec_unit = [&](int u) {
             const int f = min(u * bd + tid, ng * rec16 - 1);
             const int q = f / rec16, k = f % rec16;
@@ -338,11 +339,12 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(ExpertArgs a, int ro
         const uint32_t mis = (uint32_t)((uintptr_t)blk & 3);
         const uint32_t sh = mis * 8u;
         const uint32_t* wp = reinterpret_cast<const uint32_t*>(blk - mis);   // pointer arithmetic keeps it global
+#pragma unroll
+        for (int u = 0; u < NR; ++u) reinterpret_cast<uint4*>(hrec)[u * bd + tid] = R[u];
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the block's loads stay behind the records' stores
         uint32_t W[28];
 #pragma unroll
         for (int q = 0; q < 28; ++q) W[q] = wp[q];
-#pragma unroll
-        for (int u = 0; u < NR; ++u) reinterpret_cast<uint4*>(hrec)[u * bd + tid] = R[u];
         barrier_lds();
         if (slot != -1) {
             // realigned block: hmask dwords 0..7, qs 8..23, scales 24..26, d in 27
