@@ -296,7 +296,7 @@ int check_weights(const moe_ctx* ctx, const moe_weights* w) {
 // second stream then.
 struct CallPlan {
     bool small, use_mmq, fp4, decode, shared_fused;
-    bool fold_topk;   // one token on the decode kernels: the router launch also selects
+    bool fold_topk;   // up to 8 tokens on the decode kernels: the router launch also selects
     int sh_router_rows, sh_topk_rows, sh_gateup_rows;
 };
 
@@ -307,7 +307,7 @@ CallPlan plan_call(const moe_ctx* ctx, int m, int shared_fmt) {
     pl.use_mmq = !pl.small && ctx->mmq_ok;
     pl.fp4 = c.expert_fmt == MOE_EXPERT_MXFP4;
     pl.decode = pl.small && ctx->decode_ok;
-    pl.fold_topk = m == 1 && pl.decode && !pl.fp4 && router_select_m1_ok(c.n_routed, c.topk);
+    pl.fold_topk = pl.decode && !pl.fp4 && router_select_ok(c.n_routed, c.topk, m);
     pl.shared_fused = shared_fmt == MOE_SHARED_BF16 && pl.small && (ctx->decode_ok || pl.fp4) &&
                       ctx->host_arena == nullptr;
     if (pl.shared_fused) {
@@ -792,7 +792,7 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
     const bool kq = w->shared_fmt == MOE_SHARED_KQUANT;
     const ChunkPlan plan = mmq_chunk_plan(m, c.topk, c.n_routed, kq, ctx->mixed && !fp4);
     if (pl.fold_topk) {
-        RouteM1 ro{};
+        RouteSel ro{};
         ro.bias = w->router_bias;
         ro.E = c.n_routed;
         ro.k = c.topk;
@@ -813,8 +813,8 @@ int moe_forward_ex(moe_ctx* ctx, const moe_weights* w, const void* x_bf16, int32
         ro.slot_table = ctx->slot_table_dev;
         ro.arrive = ctx->arrive;
         rc = timed(ctx, st, MOE_K_ROUTER, [&] {
-            return launch_router_select_m1(x, (const uint16_t*)w->router_w, c.dim, ctx->logits, ctx->xq, ctx->xd,
-                                           ctx->xs16, ctx->xs16f, ro, st, shared_fused ? &sr_a : nullptr);
+            return launch_router_select(x, m, (const uint16_t*)w->router_w, c.dim, ctx->logits, ctx->xq, ctx->xd,
+                                        ctx->xs16, ctx->xs16f, ro, st, shared_fused ? &sr_a : nullptr);
         });
         if (rc != MOE_OK) return rc;
     } else if (small) {

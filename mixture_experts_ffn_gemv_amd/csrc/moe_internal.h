@@ -85,14 +85,14 @@ inline ChunkPlan mmq_chunk_plan(int m, int k, int E, bool shared, bool mixed) {
 hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int D, int E, float* logits,
                                int8_t* xq, float* xd, int32_t* xs16, float* xs16f, hipStream_t st,
                                const SharedRows* sr = nullptr);
-// The one-token selection's parameters and outputs (the top-k, its weights and
-// the chunk list of route_m1). `arrive`: ROUTER_ARRIVE_WORDS words of arrival
+// The selection's parameters and outputs when the router launch selects (the
+// top-k, its weights, the bucketing and the chunk list of route_m1 / route_small). `arrive`: ROUTER_ARRIVE_WORDS words of arrival
 // counters (a top counter, then one per group of router workgroups, one 128-byte
 // line apart), every one 0 between calls.
 constexpr int ARRIVE_GROUPS = 16;
 constexpr int ARRIVE_STRIDE = 32;
 constexpr int ROUTER_ARRIVE_WORDS = (1 + ARRIVE_GROUPS) * ARRIVE_STRIDE;
-struct RouteM1 {
+struct RouteSel {
     const float* bias;
     int E, k;
     float gate_temp;
@@ -108,12 +108,13 @@ struct RouteM1 {
     const int32_t* slot_table;
     uint32_t* arrive;
 };
-// One token: the router launch also selects (its last router workgroup to finish
-// runs the top-k), so that no top-k launch follows. E <= 1024, k <= 64.
-bool router_select_m1_ok(int E, int k);
-hipError_t launch_router_select_m1(const uint16_t* x, const uint16_t* wr, int D, float* logits, int8_t* xq,
-                                   float* xd, int32_t* xs16, float* xs16f, const RouteM1& ro, hipStream_t st,
-                                   const SharedRows* sr = nullptr);
+// Up to 8 tokens: the router launch also selects (its last router workgroup to
+// finish runs the top-k, and at 2..8 tokens the bucketing), so that no top-k
+// launch follows. k <= 64; E <= 1024 at one token, E <= 384 and m k <= 512 above.
+bool router_select_ok(int E, int k, int m);
+hipError_t launch_router_select(const uint16_t* x, int m, const uint16_t* wr, int D, float* logits, int8_t* xq,
+                                float* xd, int32_t* xs16, float* xs16f, const RouteSel& ro, hipStream_t st,
+                                const SharedRows* sr = nullptr);
 // top-k and bucketing in one workgroup, for m * topk <= 512 and m <= 8
 constexpr int ROUTE_SMALL_MAX_M = 8;
 constexpr int ROUTE_SMALL_MAX_PAIRS = 512;

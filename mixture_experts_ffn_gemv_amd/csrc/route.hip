@@ -84,13 +84,32 @@ MOE_DEV void quantize_block_bf16(const uint16_t* __restrict__ x, int b, int8_t* 
 // the one-token selection by the last router workgroup (defined with the top-k
 // kernels); b[i], sl[i]: bias and slot of expert threadIdx.x + 256 i
 template <int KPL>
-MOE_DEV void select_tail_m1(const float* scores_in, const RouteM1& ro, const float (&b)[M1_PREFETCH],
+MOE_DEV void select_tail_m1(const float* scores_in, const RouteSel& ro, const float (&b)[M1_PREFETCH],
                             const int (&sl)[M1_PREFETCH]);
 
-// KPL > 0 (one token, TT = 1): each router workgroup counts its arrival after its
-// logit is stored, and the last of the E to arrive runs the top-k of route_m1 on
-// all E logits (no workgroup waits for another: the last one finds every logit
-// already written). The count runs in two levels: workgroup e counts in group
+// the small-batch selection by one workgroup (defined with the top-k kernels)
+template <int KPL, int NT, bool FROM_SCORES>
+MOE_DEV void select_small(const float* src, const float* bias, int m, int E, int k, float gate_temp, int norm,
+                          float route_scale, int32_t* idx, float* gw, int32_t* err, int shared_chunks,
+                          int32_t* offsets, int32_t* active, int32_t* n_active, int32_t* perm, int32_t* inv,
+                          Chunk* chunks, int32_t* n_chunks, const int32_t* slot_table);
+
+// Thread 0 of router workgroup e (of E), after its scores are stored and waited
+// for: counts the arrival in two levels and tells whether this workgroup was the
+// last of all (the counters wrap to 0 after their last arrival).
+MOE_DEV bool count_arrival(const RouteSel& ro, int e, int E) {
+    const int g = e % ARRIVE_GROUPS, ng = min(E, ARRIVE_GROUPS);
+    const unsigned n_in_g = (unsigned)((E - g + ARRIVE_GROUPS - 1) / ARRIVE_GROUPS);
+    bool l = atomicInc(ro.arrive + ARRIVE_STRIDE * (1 + g), n_in_g - 1) == n_in_g - 1;
+    if (l) l = atomicInc(ro.arrive, (unsigned)(ng - 1)) == (unsigned)(ng - 1);
+    return l;
+}
+
+// KPL > 0 (the router launch also selects): each router workgroup counts its
+// arrival after its scores are stored, and the last of the E to arrive runs the
+// selection on all of them (no workgroup waits for another: the last one finds
+// every score already written). One token: the top-k of route_m1; 2..8 tokens:
+// the selection and bucketing of route_small. The count runs in two levels: workgroup e counts in group
 // e % ARRIVE_GROUPS, the last of each group in the top counter (each counter on
 // a cache line of its own), since increments of one address are performed one
 // after another. Every router workgroup requests the bias and slot-table
@@ -100,7 +119,7 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ wr, int D, int E, int ntg,
                                                            float* __restrict__ logits, int8_t* __restrict__ xq,
                                                            float* __restrict__ xd, int32_t* __restrict__ xs16, float* __restrict__ xs16f,
-                                                           SharedRows sr, RouteM1 ro) {
+                                                           SharedRows sr, RouteSel ro) {
     const int nrouter = E * ntg, bd = blockDim.x;
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + bd - 1) / bd;
     if ((int)blockIdx.x >= nrouter + nq) {   // the shared expert's gate/up rows
@@ -154,6 +173,26 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
             if (lane == 0) part8[wv8][t] = sm;
         }
         __syncthreads();
+        if constexpr (KPL > 0) {   // scores out device-coherently, as at one token
+            __shared__ int last8;
+            if (tid < m) {
+                float z = part8[0][tid];
+                for (int w = 1; w < 8; ++w) z += part8[w][tid];
+                float sv, kv;
+                bool bad;
+                score_of(z, 0.f, ro.gate_temp, sv, kv, bad);
+                __hip_atomic_store(logits + (size_t)tid * E + e, sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+            __syncthreads();
+            if (tid == 0) last8 = count_arrival(ro, e, E);
+            __syncthreads();
+            if (last8)
+                select_small<KPL, 512, true>(logits, ro.bias, m, E, ro.k, ro.gate_temp, ro.norm, ro.route_scale, ro.idx,
+                                             ro.gw, ro.err, ro.shared_chunks, ro.offsets, ro.active, ro.n_active,
+                                             ro.perm, ro.inv, ro.chunks, ro.n_chunks, ro.slot_table);
+            return;
+        }
         if (tid < TT && tid < m) {
             float z = part8[0][tid];
             for (int w = 1; w < 8; ++w) z += part8[w][tid];
@@ -226,12 +265,7 @@ __global__ __launch_bounds__(512) void router_quant_kernel(const uint16_t* __res
             score_of(z, 0.f, ro.gate_temp, sv, kv, bad);
             __hip_atomic_store(logits + e, sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_s_waitcnt(0);
-            // counters wrap to 0 after their last arrival
-            const int g = e % ARRIVE_GROUPS, ng = min(E, ARRIVE_GROUPS);
-            const unsigned n_in_g = (unsigned)((E - g + ARRIVE_GROUPS - 1) / ARRIVE_GROUPS);
-            bool l = atomicInc(ro.arrive + ARRIVE_STRIDE * (1 + g), n_in_g - 1) == n_in_g - 1;
-            if (l) l = atomicInc(ro.arrive, (unsigned)(ng - 1)) == (unsigned)(ng - 1);
-            last = l;
+            last = count_arrival(ro, e, E);
         }
         __syncthreads();
         if (last) select_tail_m1<KPL>(logits, ro, pb, psl);
@@ -445,53 +479,59 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------- small batches: top-k + bucketing
-// One workgroup of 1024 threads for m <= 8 tokens: every (token, expert) logit
-// is requested at once (thread e loads expert e of each token), then wavefront t
+// One workgroup of NT threads (E <= NT) for m <= 8 tokens: every (token, expert)
+// key is formed with all of a thread's loads requested at once (thread e takes
+// expert e, e + NT, ... of each token; with the experts' slots), then wavefront t
 // takes token t's top-k (the one-wavefront selection, no block barriers), then
 // the bucketing of the m * k picks (counts, offsets, active experts, stable
 // placement, and one single-row chunk per pick, then one per token for a
-// K-quant shared expert) without leaving the workgroup.
-template <int KPL>
-__global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits,
-                                                           const float* __restrict__ bias, int m, int E, int k,
-                                                           float gate_temp, int norm, float route_scale,
-                                                           int32_t* __restrict__ idx, float* __restrict__ gw,
-                                                           int32_t* __restrict__ err, int shared_chunks,
-                                                           int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ active,
-                                                           int32_t* __restrict__ n_active,
-                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-                                                           Chunk* __restrict__ chunks,
-                                                           int32_t* __restrict__ n_chunks,
-                                                           const int32_t* __restrict__ slot_table, SharedRows sr) {
-    if (blockIdx.x > 0) {   // the shared expert's rows
-        shared_down_block<SR_DOWN_PIECES>(sr, blockIdx.x - 1);
-        return;
-    }
+// K-quant shared expert) without leaving the workgroup. FROM_SCORES: src holds
+// the scores (the router launch's own workgroups wrote them device-coherently);
+// else the logits.
+template <int KPL, int NT, bool FROM_SCORES>
+MOE_DEV void select_small(const float* __restrict__ src, const float* __restrict__ bias, int m, int E, int k,
+                          float gate_temp, int norm, float route_scale, int32_t* __restrict__ idx,
+                          float* __restrict__ gw, int32_t* __restrict__ err, int shared_chunks,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                          int32_t* __restrict__ perm, int32_t* __restrict__ inv, Chunk* __restrict__ chunks,
+                          int32_t* __restrict__ n_chunks, const int32_t* __restrict__ slot_table) {
     constexpr int MT = ROUTE_SMALL_MAX_M;
     __shared__ float keys[MT][64 * KPL], scores[MT][64 * KPL];
     __shared__ float pick_w[ROUTE_SMALL_MAX_PAIRS];
     __shared__ int pick_e[ROUTE_SMALL_MAX_PAIRS];
-    __shared__ int cnt[1024];
-    __shared__ int offs[1025];
+    __shared__ int cnt[NT];
+    __shared__ int offs[NT + 1];
+    __shared__ int slots[NT];
     __shared__ int scan_lds[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     bool bad_any = false;
-    if (tid < 64 * KPL) {
+    for (int e = tid; e < 64 * KPL; e += NT) {
         // tokens past m and experts past E repeat the last ones (in bounds, not kept)
-        const int ec = min(tid, E - 1);
+        const int ec = min(e, E - 1);
         const float b = bias[ec];
+        const int sl = slot_table[ec];
         float z[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) z[t] = logits[(size_t)min(t, m - 1) * E + ec];
+        for (int t = 0; t < MT; ++t) {
+            const float* q = src + (size_t)min(t, m - 1) * E + ec;
+            z[t] = FROM_SCORES ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *q;
+        }
+        if (e < E) slots[e] = sl;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             float sv, kv;
             bool bad;
-            score_of(z[t], b, gate_temp, sv, kv, bad);
-            keys[t][tid] = kv;
-            scores[t][tid] = sv;
-            bad_any |= bad && t < m && tid < E;
+            if (FROM_SCORES) {   // the key as score_of forms it: score + bias, NaN -> -inf
+                sv = z[t];
+                kv = sv + b;
+                bad = kv != kv;
+                if (bad) kv = -INFINITY;
+            } else {
+                score_of(z[t], b, gate_temp, sv, kv, bad);
+            }
+            keys[t][e] = e < E ? kv : -INFINITY;
+            scores[t][e] = sv;
+            bad_any |= bad && t < m && e < E;
         }
     }
     __syncthreads();
@@ -513,7 +553,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     const int P = m * k;
     cnt[tid] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[pick_e[p]], 1);
+    for (int p = tid; p < P; p += NT) atomicAdd(&cnt[pick_e[p]], 1);
     __syncthreads();
     const int v = tid < E ? cnt[tid] : 0;
     int total;
@@ -535,7 +575,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
     // stable placement: position = offset of the expert + earlier pairs that picked
     // it; one chunk per position (a single row), carrying what the decode kernels
     // need without further lookups: the expert's slot, the token and the weight
-    for (int p = tid; p < P; p += 1024) {
+    for (int p = tid; p < P; p += NT) {
         const int pe = pick_e[p];
         int before = 0;
         for (int q = 0; q < p; ++q) before += pick_e[q] == pe ? 1 : 0;
@@ -546,7 +586,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
         c.expert = pe;
         c.row0 = pos;
         c.nrows = 1;
-        c.slot = slot_table[pe];
+        c.slot = slots[pe];
         c.token = p / k;
         c.weight = pick_w[p];
         c.pad0 = c.pad1 = 0;
@@ -563,6 +603,27 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const float* __restri
         c.pad0 = c.pad1 = 0;
         chunks[total + tid] = c;
     }
+}
+
+template <int KPL>
+__global__ __launch_bounds__(1024) void route_small_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ bias, int m, int E, int k,
+                                                           float gate_temp, int norm, float route_scale,
+                                                           int32_t* __restrict__ idx, float* __restrict__ gw,
+                                                           int32_t* __restrict__ err, int shared_chunks,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ active,
+                                                           int32_t* __restrict__ n_active,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                           Chunk* __restrict__ chunks,
+                                                           int32_t* __restrict__ n_chunks,
+                                                           const int32_t* __restrict__ slot_table, SharedRows sr) {
+    if (blockIdx.x > 0) {   // the shared expert's rows
+        shared_down_block<SR_DOWN_PIECES>(sr, blockIdx.x - 1);
+        return;
+    }
+    select_small<KPL, 1024, false>(logits, bias, m, E, k, gate_temp, norm, route_scale, idx, gw, err, shared_chunks,
+                                   offsets, active, n_active, perm, inv, chunks, n_chunks, slot_table);
 }
 
 // One token (decode): every thread scores one expert, then the first
@@ -654,7 +715,7 @@ MOE_DEV void select_m1(const float* keys, const float* scores, int E, int k, int
 // tid, tid + 256, ... from their scores (read device-coherently) and prefetched
 // biases into LDS, then the first wavefront selects.
 template <int KPL>
-MOE_DEV void select_tail_m1(const float* scores_in, const RouteM1& ro, const float (&b)[M1_PREFETCH],
+MOE_DEV void select_tail_m1(const float* scores_in, const RouteSel& ro, const float (&b)[M1_PREFETCH],
                             const int (&sl)[M1_PREFETCH]) {
     static_assert(64 * KPL <= 256 * M1_PREFETCH, "one key per prefetched entry");
     __shared__ float keys[64 * KPL], scores[64 * KPL];
@@ -792,28 +853,36 @@ hipError_t launch_router_quant(const uint16_t* x, int m, const uint16_t* wr, int
     const int nq = xq == nullptr ? 0 : (m * (D / QB) + th - 1) / th;
     const int nsh = sr ? shared_rows_blocks(*sr, th) : 0;
     const int grid = E + nq + nsh;
-    const RouteM1 no{};
+    const RouteSel no{};
     if (m == 1) return launch_kernel(router_quant_kernel<1>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
     if (m == 2) return launch_kernel(router_quant_kernel<2>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
     if (m <= 4) return launch_kernel(router_quant_kernel<4>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
     return launch_kernel(router_quant_kernel<8>, grid, th, 0, st, x, m, wr, D, E, 1, logits, xq, xd, xs16, xs16f, s, no);
 }
 
-bool router_select_m1_ok(int E, int k) { return E >= 1 && E <= 64 * M1_MAX_KEYS && k >= 1 && k <= 64 && k <= E; }
+bool router_select_ok(int E, int k, int m) {
+    if (E < 1 || k < 1 || k > 64 || k > E || m < 1 || m > ROUTE_SMALL_MAX_M) return false;
+    if (m == 1) return E <= 64 * M1_MAX_KEYS;
+    return topk_kpl(E) <= 6 && m * k <= ROUTE_SMALL_MAX_PAIRS;   // E <= 384 (the selection's LDS in every workgroup)
+}
 
-hipError_t launch_router_select_m1(const uint16_t* x, const uint16_t* wr, int D, float* logits, int8_t* xq,
-                                   float* xd, int32_t* xs16, float* xs16f, const RouteM1& ro, hipStream_t st,
-                                   const SharedRows* sr) {
-    if (!router_select_m1_ok(ro.E, ro.k) || ro.arrive == nullptr) return hipErrorInvalidValue;
+hipError_t launch_router_select(const uint16_t* x, int m, const uint16_t* wr, int D, float* logits, int8_t* xq,
+                                float* xd, int32_t* xs16, float* xs16f, const RouteSel& ro, hipStream_t st,
+                                const SharedRows* sr) {
+    if (!router_select_ok(ro.E, ro.k, m) || ro.arrive == nullptr) return hipErrorInvalidValue;
     SharedRows none{};
     const SharedRows& s = sr ? *sr : none;
-    const int th = 256;
-    const int nq = xq == nullptr ? 0 : (D / QB + th - 1) / th;
+    const int th = m == 1 ? 256 : 512;
+    const int nq = xq == nullptr ? 0 : (m * (D / QB) + th - 1) / th;
     const int grid = ro.E + nq + (sr ? shared_rows_blocks(*sr, th) : 0);
     const int kpl = topk_kpl(ro.E);
-    if (kpl == 2) return launch_kernel(router_quant_kernel<1, 2>, grid, th, 0, st, x, 1, wr, D, ro.E, 1, logits, xq, xd, xs16, xs16f, s, ro);
-    if (kpl == 6) return launch_kernel(router_quant_kernel<1, 6>, grid, th, 0, st, x, 1, wr, D, ro.E, 1, logits, xq, xd, xs16, xs16f, s, ro);
-    return launch_kernel(router_quant_kernel<1, 16>, grid, th, 0, st, x, 1, wr, D, ro.E, 1, logits, xq, xd, xs16, xs16f, s, ro);
+#define RSEL(TT, KPL) launch_kernel(router_quant_kernel<TT, KPL>, grid, th, 0, st, x, m, wr, D, ro.E, 1, logits, xq, xd, \
+                                    xs16, xs16f, s, ro)
+    if (m == 1) return kpl == 2 ? RSEL(1, 2) : kpl == 6 ? RSEL(1, 6) : RSEL(1, 16);
+    if (m == 2) return kpl == 2 ? RSEL(2, 2) : RSEL(2, 6);
+    if (m <= 4) return kpl == 2 ? RSEL(4, 2) : RSEL(4, 6);
+    return kpl == 2 ? RSEL(8, 2) : RSEL(8, 6);
+#undef RSEL
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int m, int D, int8_t* xq, float* xd, int32_t* xs16,
