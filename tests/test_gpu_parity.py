@@ -119,6 +119,31 @@ def test_mid_decode_bf16_shared(m):
         layer.close()
 
 
+@pytest.mark.parametrize("E", [16, 384, 512])
+def test_router_launch_selects_interleaved_sizes(E):
+    # up to 8 tokens on the decode kernels the router launch's last workgroup selects
+    # (and buckets above one token, while E <= 384): its arrival counters must be back at
+    # zero after every call, so calls of different sizes interleave on one context; each
+    # matches the oracle the first time and repeats bit for bit. E = 512 takes the top-k
+    # launch above one token.
+    shape = S.LayerShape(512, 256, E, 6)
+    layer = Layer(shape, 7, max_tokens=8)
+    try:
+        for m in (1, 3, 8):
+            p = moe.moe_plan_call(layer.ctx, m, moe.MOE_SHARED_BF16)
+            assert p["small_routing"] == 1 and p["expert_path"] == moe.MOE_PATH_DECODE
+            assert (p["shared_rows_topk"] == 0) == (m == 1 or E <= 384), p
+        first = {}
+        for m in (1, 3, 8, 3, 1, 8, 1):
+            x = S.make_tokens(m, shape.dim, 7, index=m)
+            if m not in first:
+                first[m] = bits(check_layer(layer, x, f"E={E} m={m}")[0])
+            else:
+                assert np.array_equal(bits(layer.forward(x.to(layer.dev))[0]), first[m]), f"E={E} m={m} repeat"
+    finally:
+        layer.close()
+
+
 FP4_SHAPE = S.LayerShape(512, 256, 16, 3)     # dim != inter, so a transposed operand fails
 
 
