@@ -571,6 +571,7 @@ class Bench:
             "ms_per_step_with_kernel_events": round(ms_profiled / steps, 5),
             "kernel_avg_ms": {k: round(avg_ms(k), 5) for k in ktimes if ktimes[k][1]},
             "gateup_bytes_per_launch": int(gateup_bytes),
+            "shared_rows_in_gateup": int(plan["shared_rows_gateup"]) if spec["shared"] == "bf16" else 0,
             "gateup_avg_launch_ms": round(ga, 5),
             "gateup_GB_per_s": round(gateup_bytes / (ga / 1e3) / 1e9, 1),
             # the routed experts' W1 / W3 blocks alone over the same launch time (the
@@ -712,7 +713,7 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": ("gateup_q8 (routed gate/up + SwiGLU + q8_1 of h; with a bf16 shared expert also "
-                       "half of its down rows)" if head["m"] <= 8
+                       f"{head['shared_rows_in_gateup']} of its down rows)" if head["m"] <= 8
                        else "mmq_gateup_q2k (routed gate/up + SwiGLU)"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
