@@ -417,12 +417,49 @@ def test_real_decode_m1(real_experts):
         layer.close()
 
 
+def test_real_decode_pool_every_token(real_experts):
+    # every token of the 256-token decode pool through the one-token path (router
+    # launch with its selection, gate/up, down + combine): routing against the
+    # oracle for all of them, outputs for eight spread over the pool
+    layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=8, experts=real_experts)
+    try:
+        pool = S.make_tokens(256, S.REAL.dim, 1)
+        d_pool = pool.to(layer.dev)
+        outs, gws, idxs = [], [], []
+        say("[decode pool] 256 one-token calls")
+        for t in range(256):
+            out, gw, idx = layer.forward(d_pool[t:t + 1])
+            outs.append(out)
+            gws.append(gw)
+            idxs.append(idx)
+        rc = layer.check()
+        assert rc == moe.MOE_OK, moe.strerror(rc)
+        idx_h = torch.cat(idxs).cpu().numpy()
+        gw_h = torch.cat(gws).cpu().numpy()
+        ridx, rg, rkeys, _ = layer.oracle_route(pool)
+        exempt = compare_routing(idx_h, gw_h, ridx, rg, rkeys)
+        say(f"[decode pool] routing of 256 tokens ok ({exempt} near-tie exemptions)")
+        rows = [3, 40, 77, 111, 150, 188, 222, 255]
+        ref = layer.oracle_parallel(pool[rows])
+        got = torch.cat([outs[t] for t in rows]).float().cpu().numpy().astype(np.float64)
+        worst = 0.0
+        for j, t in enumerate(rows):
+            if list(idx_h[t]) != list(ref["idx"][j]):
+                continue   # an exempted near-tie
+            ok, ratio = oracle.within_tolerance(got[j], ref["y"][j])
+            assert ok, f"decode pool: token {t} off by {ratio:.3f} x tolerance"
+            worst = max(worst, ratio)
+        say(f"[decode pool] outputs of tokens {rows} ok, worst {worst:.4f} of tolerance")
+    finally:
+        layer.close()
+
+
 def test_real_small_batch_m8_kquant_shared(real_experts):
     layer = Layer(S.REAL, 1, bias=(-0.05, 0.05), router_std=0.02, max_tokens=8, experts=real_experts,
                   shared_fmt="kquant")
     try:
         x = S.make_tokens(8, S.REAL.dim, 1, index=1)
-        check_layer(layer, x, "small batch m=8", sample_rows=[0, 7])
+        check_layer(layer, x, "small batch m=8")   # all eight rows
     finally:
         layer.close()
 
