@@ -444,7 +444,11 @@ __global__ __launch_bounds__(1024) void bucket_count_kernel(const int32_t* __res
 }
 
 // Stable placement: workgroup e lists the pairs that picked expert e in pair
-// order (token-major), so positions inside a group follow token order.
+// order (token-major), so positions inside a group follow token order. The
+// picks are read PLACE_STEPS steps of 256 at a time, every load of a batch
+// requested at once; one barrier per batch publishes each wavefront's match
+// count of every step.
+constexpr int PLACE_STEPS = 16;
 __global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __restrict__ idx, int P,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm,
@@ -453,28 +457,42 @@ __global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __rest
     const int base = offsets[e];
     const int cnt = offsets[e + 1] - base;
     if (cnt == 0) return;
-    __shared__ int wtot[4];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __shared__ int wtot[PLACE_STEPS][4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const unsigned long long below = (1ull << lane) - 1ull;
     int running = 0;
-    for (int p0 = 0; p0 < P && running < cnt; p0 += 256) {
-        const int p = p0 + threadIdx.x;
-        const bool match = p < P && idx[p] == e;
-        const unsigned long long bal = __ballot(match);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wtot[wv] = __popcll(bal);
-        __syncthreads();
-        int woff = 0, all = 0;
-        for (int w = 0; w < 4; ++w) {
-            if (w < wv) woff += wtot[w];
-            all += wtot[w];
+    for (int p0 = 0; p0 < P && running < cnt; p0 += 256 * PLACE_STEPS) {
+        int v[PLACE_STEPS];
+#pragma unroll
+        for (int j = 0; j < PLACE_STEPS; ++j) v[j] = idx[min(p0 + 256 * j + tid, P - 1)];
+        unsigned match = 0u;
+        int pre[PLACE_STEPS];
+#pragma unroll
+        for (int j = 0; j < PLACE_STEPS; ++j) {
+            const bool mt = p0 + 256 * j + tid < P && v[j] == e;
+            const unsigned long long bal = __ballot(mt);
+            pre[j] = __popcll(bal & below);
+            if (lane == 0) wtot[j][wv] = __popcll(bal);
+            match |= mt ? 1u << j : 0u;
         }
-        if (match) {
-            const int pos = base + running + woff + pre;
-            perm[pos] = p;
-            inv[p] = pos;
-        }
-        running += all;
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < PLACE_STEPS; ++j) {
+            int woff = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                woff += w < wv ? wtot[j][w] : 0;
+                all += wtot[j][w];
+            }
+            if (match >> j & 1u) {
+                const int p = p0 + 256 * j + tid;
+                const int pos = base + running + woff + pre[j];
+                perm[pos] = p;
+                inv[p] = pos;
+            }
+            running += all;
+        }
+        __syncthreads();   // wtot is rewritten by the next batch
     }
 }
 
