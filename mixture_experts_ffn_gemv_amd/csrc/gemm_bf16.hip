@@ -8,8 +8,10 @@
 // C[M, N] = A[M, K] B[N, K]^T, both operands K-contiguous bf16. Workgroup tile
 // 64 (A rows) x 128 (B rows) x 64 (K), four wavefronts, each owning 32 B rows;
 // v_mfma_f32_16x16x32_bf16 tiles. Each K step's tiles go from global memory
-// straight into LDS (global-to-LDS loads, 16 bytes per lane), double-buffered:
-// step k + 1 is in flight while step k is multiplied. A tile row is 128 bytes
+// straight into LDS (global-to-LDS loads, 16 bytes per lane) in a ring of four
+// buffers: steps k + 1 .. k + 3 are in flight while step k is multiplied (with
+// one step in flight each workgroup waited out most of a load's latency per
+// step). A tile row is 128 bytes
 // (8 chunks of 16); chunk c of row r is stored at slot c ^ ((r >> 1) & 7), so
 // the 16 rows one operand read touches fall on distinct banks. The f32 output
 // may be split over K (grid z): split s sums K steps [s nk / S, (s + 1) nk / S)
@@ -28,6 +30,7 @@ namespace {
 
 constexpr int BM = 64, BN = 128, BK = 64;
 constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+constexpr int NSTAGE = 4;   // K steps in LDS: one computed, three in flight
 
 enum Epilogue { EPI_F32 = 0, EPI_SWIGLU = 1 };
 
@@ -85,11 +88,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 
     const int l16 = lane & 15, g = lane >> 4;
     stage(0, smem);
+    if (nk > 1) stage(1, smem + STAGE);
+    if (nk > 2) stage(2, smem + 2 * STAGE);
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vm_loads<0>();   // step kt is in LDS ...
-        barrier_lds();        // ... for every wave; the other buffer is free
-        const uint8_t* buf = smem + (kt & 1) * STAGE;
-        if (kt + 1 < nk) stage(kt + 1, smem + ((kt + 1) & 1) * STAGE);
+        // step kt is in LDS (each later step in flight holds six loads per thread) ...
+        if (kt + 2 < nk) wait_vm_loads<12>();
+        else if (kt + 1 < nk) wait_vm_loads<6>();
+        else wait_vm_loads<0>();
+        barrier_lds();        // ... for every wave; the buffer of step kt - 1 is free
+        const uint8_t* buf = smem + (kt % NSTAGE) * STAGE;
+        if (kt + 3 < nk) stage(kt + 3, smem + ((kt + 3) % NSTAGE) * STAGE);
 #pragma unroll
         for (int kk = 0; kk < BK / 32; ++kk) {
             const int c = 4 * kk + g;   // this lane's K values 32 kk + 8 g .. + 7
@@ -143,17 +151,17 @@ hipError_t launch_router_gemm(const uint16_t* x, int m, const uint16_t* wr, int 
     s = std::max(1, std::min({s, 8, D / BK, max_rows / m}));
     *splits = s;
     dim3 grid((E + BN - 1) / BN, (m + BM - 1) / BM, s);
-    return launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, 2 * STAGE, st, x, m, wr, wr, E, D, logits, 0.f);
+    return launch_kernel(gemm_bf16_kernel<EPI_F32>, grid, 256, NSTAGE * STAGE, st, x, m, wr, wr, E, D, logits, 0.f);
 }
 
 // h bf16 [m, I] = SwiGLU(x W1^T, x W3^T);  ys f32 [m, D] = h W2^T
 hipError_t launch_shared_bf16_gemm(const uint16_t* x, int m, int D, int I, const uint16_t* w1, const uint16_t* w3,
                                    const uint16_t* w2, uint16_t* h, float* ys, float limit, hipStream_t st) {
     dim3 g1(I / (BN / 2), (m + BM - 1) / BM);
-    hipError_t e = launch_kernel(gemm_bf16_kernel<EPI_SWIGLU>, g1, 256, 2 * STAGE, st, x, m, w1, w3, I, D, h, limit);
+    hipError_t e = launch_kernel(gemm_bf16_kernel<EPI_SWIGLU>, g1, 256, NSTAGE * STAGE, st, x, m, w1, w3, I, D, h, limit);
     if (e != hipSuccess) return e;
     dim3 g2(D / BN, (m + BM - 1) / BM);
-    return launch_kernel(gemm_bf16_kernel<EPI_F32>, g2, 256, 2 * STAGE, st, h, m, w2, w2, D, I, ys, 0.f);
+    return launch_kernel(gemm_bf16_kernel<EPI_F32>, g2, 256, NSTAGE * STAGE, st, h, m, w2, w2, D, I, ys, 0.f);
 }
 
 }  // namespace moe
