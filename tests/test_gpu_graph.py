@@ -1,6 +1,9 @@
 """GPU: the decode step captured in a HIP graph replays bit for bit like the
 eager call (the pages' compute_m1: no per-token host arguments, so one graph
-of it replays for any token written into its input buffer).
+of it replays for any token written into its input buffer); likewise small
+batches (the router launch's selection and bucketing) and a batched call (the
+split-K router product, top-k, bucketing, MMQ classes and a bf16 shared expert
+forked to a second stream inside the capture).
 
 Every replay is checked against an eager call of the same token, with the
 eager work and a synchronisation between replays.
@@ -16,20 +19,19 @@ from test_gpu_parity import real_experts  # noqa: F401 (module fixture)
 pytestmark = pytest.mark.gpu
 
 
-def capture_and_compare(layer, tokens, label):
+def capture_and_compare(layer, tokens, label, m=1):
     dev = layer.dev
-    m = 1
     x_static = torch.zeros((m, layer.shape.dim), dtype=torch.bfloat16, device=dev)
     out_static = torch.empty((m, layer.shape.dim), dtype=torch.bfloat16, device=dev)
-    x_static.copy_(tokens[0:1].to(dev))
+    x_static.copy_(tokens[0:m].to(dev))
     moe.moe_forward(layer.ctx, layer.w, x_static, m, out_static)   # uploads the slot table before capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         moe.moe_forward(layer.ctx, layer.w, x_static, m, out_static)
     torch.cuda.synchronize()
-    for t in range(tokens.shape[0]):
-        x = tokens[t:t + 1].to(dev)
+    for t in range(tokens.shape[0] // m):
+        x = tokens[t * m:(t + 1) * m].to(dev)
         x_static.copy_(x)
         graph.replay()
         torch.cuda.synchronize()
@@ -39,7 +41,7 @@ def capture_and_compare(layer, tokens, label):
         torch.cuda.synchronize()
         assert layer.check() == moe.MOE_OK
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"{label}: token {t} differs"
-    print(f"[{label}] {tokens.shape[0]} replays bit-identical to eager", flush=True)
+    print(f"[{label}] {tokens.shape[0] // m} replays bit-identical to eager", flush=True)
 
 
 @pytest.mark.parametrize("shared", ["bf16", "kquant", "none"])
@@ -47,6 +49,18 @@ def test_tiny_decode_graph(shared):
     layer = Layer(S.TINY, 0, max_tokens=8, shared_fmt=shared)
     try:
         capture_and_compare(layer, S.make_tokens(6, S.TINY.dim, 0, index=50), f"tiny graph {shared}")
+    finally:
+        layer.close()
+
+
+@pytest.mark.parametrize("shared", ["bf16", "kquant"])
+@pytest.mark.parametrize("m", [3, 8, 13])
+def test_tiny_batch_graph(shared, m):
+    # m = 3 and 8: the small-batch path (selection and bucketing in the router launch);
+    # m = 13: router GEMM split over K, top-k, bucketing, MMQ (bf16 shared: a second stream)
+    layer = Layer(S.TINY, 0, max_tokens=16, shared_fmt=shared)
+    try:
+        capture_and_compare(layer, S.make_tokens(4 * m, S.TINY.dim, 0, index=70 + m), f"tiny graph m={m} {shared}", m=m)
     finally:
         layer.close()
 
