@@ -584,3 +584,33 @@ def test_compute_time_with_profiling():
         assert st["compute_ms"] > 0 and st["calls"] == 3
     finally:
         layer.close()
+
+
+# ----------------------------------------------------------------------------- drawn configurations
+
+def drawn_configs(n, seed):
+    """n layer configurations drawn from the ones the library accepts (dims multiples
+    of 256, any expert count, top-k up to min(E, 64)), small enough for the oracle,
+    each with a token count on one of the paths (1, 2..8, above 8)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dim = 256 * int(rng.integers(1, 5))
+        inter = 256 * int(rng.integers(1, 5))
+        E = int(rng.choice([3, 8, 17, 37, 64, 100, 129, 200, 385]))
+        k = int(rng.integers(1, min(E, 9) + 1))
+        m = int(rng.choice([1, 2, 5, 8, 9, 20, 47]))
+        shared = str(rng.choice(["bf16", "kquant", "none"]))
+        out.append((dim, inter, E, k, m, shared))
+    return out
+
+
+@pytest.mark.parametrize("dim,inter,E,k,m,shared", drawn_configs(16, 2024))
+def test_drawn_configuration(dim, inter, E, k, m, shared):
+    layer = Layer(S.LayerShape(dim, inter, E, k), 7, max_tokens=m, shared_fmt=shared)
+    try:
+        x = S.make_tokens(m, dim, 7, index=E + k)
+        check_layer(layer, x, f"drawn {dim}x{inter} E={E} k={k} m={m} {shared}")
+    finally:
+        layer.close()
