@@ -614,3 +614,14 @@ def test_drawn_configuration(dim, inter, E, k, m, shared):
         check_layer(layer, x, f"drawn {dim}x{inter} E={E} k={k} m={m} {shared}")
     finally:
         layer.close()
+
+
+@pytest.mark.parametrize("dim,inter,E,k,m,shared", [(d, i, e, k, m, "none" if s == "kquant" else s)
+                                                     for d, i, e, k, m, s in drawn_configs(8, 77)])
+def test_drawn_configuration_fp4(dim, inter, E, k, m, shared):
+    layer = Layer(S.LayerShape(dim, inter, E, k), 8, max_tokens=m, shared_fmt=shared, expert_fmt="fp4")
+    try:
+        x = S.make_tokens(m, dim, 8, index=E + k)
+        check_layer(layer, x, f"drawn fp4 {dim}x{inter} E={E} k={k} m={m} {shared}")
+    finally:
+        layer.close()
