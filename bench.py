@@ -649,7 +649,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", choices=tuple(WORKLOADS), default="decode")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' summaries")
     ap.add_argument("--cpu-sample", type=int, default=-1,
@@ -680,7 +680,7 @@ def main():
     if wl == "decode" and not args.no_extra:
         for other in ("small", "decode_fp4", "prefill", "prefill_fp4", "prefill_mixed", "prefill_hot", "skewed"):
             st = 100 if WORKLOADS[other]["m"] <= 8 else 5 if other == "skewed" else 10
-            wu = 3 if other == "skewed" else 20   # as the headline's default: the first calls of a workload run slower
+            wu = 3 if other == "skewed" else 20   # the first calls of a workload run slower
             log(f"{other}: {wu} warmup + {st} timed steps")
             r = b.run(other, st, wu)
             r.pop("_layers"), r.pop("_tokens")
