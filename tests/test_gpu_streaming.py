@@ -152,3 +152,29 @@ def test_real_streamed_skewed_prefill(real_experts):
         assert st["waves"] > 1 and st["misses"] > 0
     finally:
         layer.close()
+
+
+def drawn_streamed(n, seed):
+    from test_gpu_parity import drawn_configs
+    rng = np.random.default_rng(seed)
+    return [(*c, int(rng.choice([2, 3, 5, 8]))) for c in drawn_configs(n, seed)]
+
+
+@pytest.mark.parametrize("dim,inter,E,k,m,shared,n_slots", drawn_streamed(8, 555))
+def test_drawn_streamed(dim, inter, E, k, m, shared, n_slots):
+    # drawn layer configurations with a few device slots: misses copied from the host
+    # arena, waves when the picks outnumber the slots
+    n_slots = min(n_slots, E)
+    shape = S.LayerShape(dim, inter, E, k)
+    layer = Layer(shape, 9, max_tokens=m, shared_fmt=shared, n_slots=n_slots, bind_all=False, host_arena=True)
+    try:
+        x = S.make_tokens(m, dim, 9, index=300 + m)
+        moe.moe_reset_stats(layer.ctx)
+        check_layer(layer, x, f"drawn streamed {dim}x{inter} E={E} k={k} m={m} {shared} slots={n_slots}")
+        st = moe.moe_get_stats(layer.ctx)
+        distinct = len(set(layer.oracle_route(x)[0].reshape(-1).tolist()))
+        assert st["misses"] >= distinct - min(distinct, n_slots)
+        assert st["bytes_copied"] == st["misses"] * layer.arena_src.shape[1]
+        assert st["waves"] == (1 if distinct <= n_slots else -(-distinct // max(1, n_slots // 2)))
+    finally:
+        layer.close()
