@@ -87,6 +87,34 @@ def test_static_matches_context_real():
         torch.cuda.empty_cache()
 
 
+def drawn_decode_configs(n, seed):
+    """layer configurations drawn from the accepted range, each with two token
+    counts of the decode path (m <= 8), the second smaller"""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dim = 256 * int(rng.integers(1, 5))
+        inter = 256 * int(rng.integers(1, 5))
+        E = int(rng.choice([3, 8, 17, 37, 64, 100, 129, 200, 385]))
+        k = int(rng.integers(1, min(E, 9) + 1))
+        m1 = int(rng.integers(2, 9))
+        m2 = int(rng.integers(1, m1))
+        shared = str(rng.choice(["bf16", "kquant", "none"]))
+        out.append((dim, inter, E, k, m1, m2, shared))
+    return out
+
+
+@pytest.mark.parametrize("dim,inter,E,k,m1,m2,shared", drawn_decode_configs(8, 31))
+def test_static_matches_context_drawn(dim, inter, E, k, m1, m2, shared):
+    shape = S.LayerShape(dim, inter, E, k)
+    layer = Layer(shape, 6, max_tokens=8, shared_fmt=shared)
+    try:
+        check_pair(layer, S.make_tokens(m1, dim, 6, index=E), f"drawn {dim}x{inter} E={E} k={k} {shared} first")
+        check_pair(layer, S.make_tokens(m2, dim, 6, index=E + 1), f"drawn {dim}x{inter} E={E} k={k} second")
+    finally:
+        layer.close()
+
+
 def test_static_status_words():
     layer = Layer(S.TINY, 0, max_tokens=8)
     try:
