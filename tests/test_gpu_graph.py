@@ -80,3 +80,13 @@ def test_real_decode_graph(real_experts):
         capture_and_compare(layer, S.make_tokens(4, S.REAL.dim, 1, index=0), "real decode graph")
     finally:
         layer.close()
+
+
+@pytest.mark.parametrize("dim,inter,E,k,m,shared", [c for c in __import__("test_gpu_parity").drawn_configs(6, 4242)])
+def test_drawn_graph(dim, inter, E, k, m, shared):
+    layer = Layer(S.LayerShape(dim, inter, E, k), 3, max_tokens=m, shared_fmt=shared)
+    try:
+        capture_and_compare(layer, S.make_tokens(3 * m, dim, 3, index=400 + m),
+                            f"drawn graph {dim}x{inter} E={E} k={k} m={m} {shared}", m=m)
+    finally:
+        layer.close()
